@@ -1,0 +1,187 @@
+/*
+ * hils.h -- C ABI of libhils, an MI355X (gfx950) implementation of the
+ * HiLS (Hierarchical Landmark Sparse) attention forward pass.
+ *
+ * Method source: "HiLS: Hierarchical Landmark Sparse Attention", paper
+ * summary on hyper.ai, section 方法:
+ *   - the sequence is cut into chunks of S tokens; each query attends a
+ *     causal sliding window of W tokens aligned to chunk boundaries plus the
+ *     top-K distant chunks (naive block-sparse attention paragraph);
+ *   - a landmark query q'_c per chunk induces a distribution p over the
+ *     chunk's keys; the compressed key is k'_c = sum_j p_j k_j and the bias
+ *     b'_c is the entropy of p (paragraph after the surrogate-score
+ *     equation);
+ *   - surrogate chunk score s^_ic = q_i.k'_c / sqrt(d) + b'_c (surrogate-score
+ *     equation); chunks are ranked by it and the top K kept;
+ *   - partition estimate Z^_i = sum_{c in I_i} exp(s^_ic) + Z_{i,swa}, and the
+ *     attention weight of a selected key is its intra-chunk softmax weight
+ *     times exp(s^_ic) / Z^_i (hierarchical factorisation equation);
+ *   - Q-Cal: the scoring query is q_i + W_up W_down h_i (low-rank query
+ *     calibration paragraph);
+ *   - GQA: per-head chunk scores are max-aggregated over the heads of a
+ *     group and one top-K set is chosen per group (same paragraph).
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are caller-owned DEVICE pointers (hipMalloc or
+ *     torch CUDA tensors), contiguous in the stated layout, 16-byte aligned.
+ *     The library never allocates, frees or keeps a pointer beyond the work
+ *     it enqueues on `stream`.
+ *   - Work is enqueued asynchronously on `stream`; results are ready when
+ *     the stream is synchronised.  Asynchronous device faults surface there.
+ *   - Every argument is validated on the host before anything is launched;
+ *     on a non-OK status nothing has been written.  hils_last_error() then
+ *     returns a message (thread-local).
+ *   - Results are deterministic run to run (no atomics in accumulation).
+ *   - Calls are thread-safe; concurrent calls must not share output or
+ *     workspace buffers.
+ *
+ * Layouts (row-major, innermost last):
+ *   q      [B, H_q,  N, d]        k, v   [B, H_kv, N, d]
+ *   q_lm   [B, H_lm, C, d]        k_sum  [B, H_lm, C, d]   b_sum [B, H_lm, C]
+ *   sel_idx   [B, H_kv, N, K] int32 -- ascending chunk ids, -1 padded
+ *   sel_score [B, H_q,  N, K] fp32  -- s^ of each selected chunk, -inf padded
+ *   out    [B, H_q,  N, d]        lse    [B, H_q, N] fp32
+ * with C = floor(N / S) completed chunks.  Query head h belongs to GQA
+ * group g = h / (H_q / H_kv); it scores with landmark head
+ * l = h * H_lm / H_q; landmark head l reads kv head l * H_kv / H_lm.
+ *
+ * Window and candidates (the pages leave the bounds open; reading adopted):
+ * query i attends keys [max(0, floor(i/S)*S - W), i] exactly; its candidate
+ * chunks are c < floor(i/S) - W/S; it selects min(K, #candidates) of them by
+ * (group score descending, chunk index ascending).
+ */
+#ifndef HILS_H
+#define HILS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HILS_OK = 0,
+    HILS_ERR_INVALID_ARG = 1, /* null/misaligned pointer, inconsistent shape */
+    HILS_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels cover   */
+    HILS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than needed    */
+    HILS_ERR_HIP = 4          /* a HIP launch or runtime call failed         */
+} hils_status_t;
+
+typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype_t;
+
+typedef struct {
+    int32_t B;    /* batch (prefill); ignored by hils_decode                 */
+    int32_t N;    /* tokens per sequence (prefill); ignored by hils_decode   */
+    int32_t H_q;  /* query heads                                             */
+    int32_t H_kv; /* key/value heads; H_q % H_kv == 0, G = H_q/H_kv in {1,2,4,8} */
+    int32_t H_lm; /* landmark heads: H_q or H_kv                             */
+    int32_t d;    /* head dim: 64 or 128                                     */
+    int32_t S;    /* chunk size: 64 or 128                                   */
+    int32_t W;    /* window in tokens, W % S == 0                            */
+    int32_t K;    /* chunks kept per query and group, 0..128                 */
+    int32_t M;    /* query-group size: a schedule hint; results never depend on it */
+    int32_t io_dtype;      /* hils_dtype_t of q, k, v, q_lm, h, W, out, caches */
+    int32_t summary_dtype; /* hils_dtype_t of k_sum / ksum_cache; b_sum is fp32 */
+    float scale;           /* logit scale; 0 selects 1/sqrt(d)               */
+} hils_config_t;
+
+/* Workspace kinds for hils_workspace_size(). */
+enum {
+    HILS_WS_SCORE = 0,      /* hils_score_select without Q-Cal            */
+    HILS_WS_SCORE_QCAL = 1, /* hils_score_select with Q-Cal               */
+    HILS_WS_FUSED = 2,      /* hils_sparse_attend_fused                   */
+    HILS_WS_DECODE = 3      /* hils_decode                                */
+};
+
+/* Landmark summary (compressed keys).  For every completed chunk c and
+ * landmark head l: p = softmax_j(scale * q_lm[l,c] . k[g(l), cS+j]) over the
+ * chunk's S keys, k_sum[l,c] = sum_j p_j k_j, b_sum[l,c] = -sum_j p_j log p_j
+ * (hyper.ai summary, 方法: the compressed key and its entropy bias).
+ *   k     [B, H_kv, N, d]  io_dtype
+ *   q_lm  [B, H_lm, C, d]  io_dtype
+ *   k_sum [B, H_lm, C, d]  summary_dtype (written)
+ *   b_sum [B, H_lm, C]     fp32          (written)
+ * Also usable on a paged cache [P, H_kv, S, d] by passing B = P, N = S. */
+hils_status_t hils_landmark_summarize(const hils_config_t *cfg, const void *k, const void *q_lm, void *k_sum,
+                                      float *b_sum, hipStream_t stream);
+
+/* Surrogate chunk scores, GQA max-aggregation and top-K selection
+ * (hyper.ai summary, 方法: surrogate-score equation, partition estimate,
+ * Q-Cal and GQA paragraphs).  For every query i, group g and candidate
+ * chunk c: s^[h,c] = scale * qs[h,i] . k_sum[l(h),c] + b_sum[l(h),c] for the
+ * heads h of g, group score max_h s^[h,c]; the first min(K, #candidates)
+ * chunks by (group score desc, index asc) are written ascending to sel_idx
+ * (-1 padded) and each head's s^ of them to sel_score (-inf padded).
+ * qs = q, or with Q-Cal (h != NULL) qs = q + reshape(W_up (W_down h_i)),
+ * used for scoring only.
+ *   q        [B, H_q, N, d]        io_dtype
+ *   k_sum    [B, H_lm, C, d]       summary_dtype,  b_sum [B, H_lm, C] fp32
+ *   h        [B, N, d_model]       io_dtype or NULL (then w_down, w_up unused)
+ *   w_down   [r, d_model]          io_dtype
+ *   w_up     [H_q * d, r]          io_dtype (row h*d + t feeds head h, dim t)
+ *   sel_idx  [B, H_kv, N, K] int32 (written)
+ *   sel_score[B, H_q, N, K]  fp32  (written)
+ *   workspace: hils_workspace_size(cfg, HILS_WS_SCORE[_QCAL], 0, 0) bytes. */
+hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const void *k_sum, const float *b_sum,
+                                const void *h, const void *w_down, const void *w_up, int32_t d_model, int32_t r,
+                                int32_t *sel_idx, float *sel_score, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Exact attention inside each selected chunk and inside the chunk-aligned
+ * causal window, fused by the surrogate masses (hyper.ai summary, 方法:
+ * partition estimate and hierarchical factorisation equation):
+ *   L_i = log(sum_{c in I} exp(s^_c) + exp(lse_swa)),
+ *   out_i = sum_c exp(s^_c - L_i) o_c + exp(lse_swa - L_i) o_swa,
+ * where o_c / lse_c are the softmax output / log-mass of q_i over chunk c's
+ * S keys and o_swa / lse_swa those over the window.  Uses the raw q.
+ *   q [B,H_q,N,d], k, v [B,H_kv,N,d] io_dtype; sel_idx / sel_score as
+ *   written by hils_score_select; out [B,H_q,N,d] io_dtype (written);
+ *   lse [B,H_q,N] fp32 (written, may be NULL).
+ *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes. */
+hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                       const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step per sequence over a paged KV / summary cache: the steps
+ * of hils_score_select and hils_sparse_attend_fused for the single query at
+ * position t = seq_lens[b] - 1, whose own key/value are already in the
+ * cache.  Summaries are read from the cache, never recomputed.
+ *   q           [num_seqs, H_q, d]        io_dtype
+ *   k_cache,
+ *   v_cache     [P, H_kv, S, d]           io_dtype (one page = one chunk)
+ *   ksum_cache  [P, H_lm, d]              summary_dtype
+ *   bsum_cache  [P, H_lm]                 fp32
+ *   block_table [num_seqs, max_pages]     int32: logical chunk -> page
+ *   seq_lens    [num_seqs]                int32, >= 1, tokens incl. the new one
+ *   h           [num_seqs, d_model] or NULL (Q-Cal, as in hils_score_select)
+ *   out         [num_seqs, H_q, d]        io_dtype (written)
+ *   lse         [num_seqs, H_q] fp32      (written, may be NULL)
+ *   sel_idx     [num_seqs, H_kv, K] int32 (written, may be NULL)
+ *   workspace: hils_workspace_size(cfg, HILS_WS_DECODE, num_seqs, max_pages).
+ * Page ids outside [0, P) are not checked on the device: the caller owns
+ * the block table.  cfg->B and cfg->N are ignored. */
+hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,
+                          const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                          const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens, const void *h,
+                          const void *w_down, const void *w_up, int32_t d_model, int32_t r, void *out, float *lse,
+                          int32_t *sel_idx, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace the given call needs (0 if none); 0 with
+ * hils_last_error() set when the configuration is rejected.  num_seqs and
+ * max_pages are used by HILS_WS_DECODE only. */
+size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs, int32_t max_pages);
+
+/* Thread-local message describing the last non-OK status of this thread. */
+const char *hils_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int hils_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HILS_H */

@@ -1,0 +1,509 @@
+// decode.hip -- kernel 4: one HiLS decode step over a paged KV/summary cache.
+//
+// hyper.ai HiLS summary, section 方法 (same computation as prefill, for the
+// query at t = seq_len - 1 whose own key/value are already in the cache):
+// score every candidate chunk's cached summary (k'_c, b'_c), max over the
+// heads of the GQA group, keep the top K; attend exactly inside each
+// selected chunk and the chunk-aligned window; fuse with exp(s^)/Z^.
+//
+// MI355X design: decode is HBM-bound on two streams -- the summaries of
+// every candidate chunk and the K/V pages of the selected + window chunks.
+// With one query per (sequence, group) there is too little parallelism per
+// unit, so both phases split their ranges across many blocks:
+//   A  decode_score    candidate range split: fp32 dots of the cached
+//                      summaries (coalesced 16-byte loads, several
+//                      candidates per wave), local top-K per block
+//   A2 decode_merge    one wave per (seq, group): global top-K of the
+//                      partial lists, ascending ids + per-head s^
+//   B  decode_attend   chunk-list split: each block stages its pages' K/V
+//                      in LDS and returns a partial (max, mass, output)
+//   B2 decode_combine  log-sum-exp merge of the partials per (seq, head)
+// A selected chunk enters as the state (max = s^_c, mass = 1, out = its
+// normalised intra-chunk output); window chunks enter with their raw
+// softmax statistics; the merge of all states is exactly the fused output.
+#include "hils_device.hpp"
+#include "hils_internal.hpp"
+
+namespace hils {
+
+namespace {
+
+struct DecodeLayout {
+    int splits;  // phase A blocks per (seq, group)
+    int nsb;     // phase B blocks per (seq, group)
+    size_t off_qs, off_pkey, off_psc, off_sel, off_selsc, off_pm, off_pl, off_po, total;
+};
+
+DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
+    DecodeLayout L;
+    L.splits = decode_splits(s, max_pages);
+    L.nsb = std::max(1, std::min(16, (s.K + s.W / s.S + 1 + 3) / 4));
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align_up(bytes, 256);
+        return at;
+    };
+    const size_t NS = (size_t)num_seqs;
+    L.off_qs = take(NS * s.H_q * s.D * 4);
+    L.off_pkey = take(NS * s.H_kv * L.splits * s.K * 8);
+    L.off_psc = take(NS * s.H_kv * L.splits * s.K * s.G * 4);
+    L.off_sel = take(NS * s.H_kv * s.K * 4);
+    L.off_selsc = take(NS * s.H_q * s.K * 4);
+    L.off_pm = take(NS * s.H_q * L.nsb * 4);
+    L.off_pl = take(NS * s.H_q * L.nsb * 4);
+    L.off_po = take(NS * s.H_q * L.nsb * s.D * 4);
+    L.total = o;
+    return L;
+}
+
+__device__ __forceinline__ int clamp_len(int len, int max_pages, int S) {
+    return min(max(len, 1), max_pages * S);
+}
+
+__device__ __forceinline__ uint64_t dec_key(float s, int idx) {
+    return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+}  // namespace
+
+// Phase-A blocks per (seq, group): about 256 candidates each, and at most
+// 2048 partial entries for the merge wave (splits * K <= 2048).
+int decode_splits(const Shape &s, int max_pages) {
+    const int cap = std::max(1, 2048 / std::max(1, s.K));
+    return std::max(1, std::min(cap, (max_pages + 255) / 256));
+}
+
+// q_s[seq, h, :] = q (+ W_up W_down h_seq), fp32.  One block per sequence.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_qprep_kernel(const T *__restrict__ q, const T *__restrict__ h,
+                                                           const T *__restrict__ w_down, const T *__restrict__ w_up,
+                                                           float *__restrict__ qs, int H_q, int D, int d_model,
+                                                           int r) {
+    __shared__ float u[64];
+    const int64_t seq = blockIdx.x;
+    const int HD = H_q * D;
+    if (h) {
+        for (int a = threadIdx.x; a < r; a += blockDim.x) {
+            float acc = 0.f;
+            for (int x = 0; x < d_model; ++x)
+                acc = fmaf(to_f32(w_down[(int64_t)a * d_model + x]), to_f32(h[seq * d_model + x]), acc);
+            u[a] = acc;
+        }
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
+        float acc = to_f32(q[seq * HD + e]);
+        if (h) {
+            float dq = 0.f;
+            for (int a = 0; a < r; ++a) dq = fmaf(to_f32(w_up[(int64_t)e * r + a]), u[a], dq);
+            acc += dq;
+        }
+        qs[seq * HD + e] = acc;
+    }
+}
+
+// Phase A.  LPR lanes cover one landmark row (16-byte loads), CPS = 64/LPR
+// candidates per wave step.  GLM = landmark rows per candidate (G when
+// every query head has its own landmark, 1 when the group shares one).
+template <typename TS, int D, int G, int GLM>
+__global__ __launch_bounds__(256) void decode_score_kernel(
+    const float *__restrict__ qs, const TS *__restrict__ ksum_cache, const float *__restrict__ bsum_cache,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens, uint64_t *pkey,
+    float *psc, int H_q, int H_kv, int H_lm, int S, int W, int K, int splits, float scale) {
+    constexpr int E = 16 / sizeof(TS);
+    constexpr int LPR = D / E;
+    constexpr int CPS = WAVE / LPR;
+    constexpr int CAPL = DECODE_SPLIT_CAP;
+    __shared__ float agg_l[CAPL];
+    __shared__ float sc_l[CAPL][G];
+
+    const int sp = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int t = clamp_len(seq_lens[seq], max_pages, S) - 1;
+    const int n = max(0, t / S - W / S);
+    const int c_lo = (int)((int64_t)sp * n / splits), c_hi = (int)((int64_t)(sp + 1) * n / splits);
+    const int cnt = c_hi - c_lo;
+    const int col = lane % LPR, cs = lane / LPR;
+
+    float qv[G][E];
+#pragma unroll
+    for (int e = 0; e < G; ++e)
+#pragma unroll
+        for (int x = 0; x < E; ++x) qv[e][x] = qs[((int64_t)seq * H_q + g * G + e) * D + col * E + x];
+    const int32_t *bt = block_table + (int64_t)seq * max_pages;
+    const int lbase = g * G * H_lm / H_q;  // first landmark head of the group
+
+    for (int base = wave * CPS; base < cnt; base += 4 * CPS) {
+        const int lc = base + cs;
+        const bool ok = lc < cnt;
+        const int c = c_lo + (ok ? lc : 0);
+        const int64_t page = bt[c];
+        Vec16<TS> kv[GLM];
+#pragma unroll
+        for (int e = 0; e < GLM; ++e) kv[e] = load16(ksum_cache + (page * H_lm + lbase + e) * D + col * E);
+        float agg = -INFINITY;
+        float sc[G];
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int le = GLM == 1 ? 0 : e;
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < E; ++x) part = fmaf(qv[e][x], kv[le].get(x), part);
+            part = xor_sum<1, LPR / 2>(part);
+            sc[e] = fmaf(scale, part, bsum_cache[page * H_lm + lbase + le]);
+            agg = fmaxf(agg, sc[e]);
+        }
+        if (ok && col == 0) {
+            agg_l[lc] = agg;
+#pragma unroll
+            for (int e = 0; e < G; ++e) sc_l[lc][e] = sc[e];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // local top-K over cnt <= CAPL entries (8 per lane)
+    uint64_t keys[CAPL / WAVE];
+#pragma unroll
+    for (int v = 0; v < CAPL / WAVE; ++v) {
+        const int lc = v * WAVE + lane;
+        keys[v] = lc < cnt ? dec_key(agg_l[lc], c_lo + lc) : 0ull;
+    }
+    uint64_t T = 1;
+    if (cnt > K) {
+        T = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand = T | (1ull << bit);
+            int c2 = 0;
+#pragma unroll
+            for (int v = 0; v < CAPL / WAVE; ++v) c2 += __popcll(__ballot(keys[v] >= cand));
+            if (c2 >= K) T = cand;
+        }
+    }
+    const int64_t pbase = (((int64_t)seq * H_kv + g) * splits + sp) * K;
+    int outc = 0;
+#pragma unroll
+    for (int v = 0; v < CAPL / WAVE; ++v) {
+        const bool keep = keys[v] >= T && keys[v] != 0ull;
+        const uint64_t m = __ballot(keep);
+        const int pos = outc + __popcll(m & lanemask_lt());
+        if (keep && pos < K) {
+            pkey[pbase + pos] = keys[v];
+            const int lc = v * WAVE + lane;
+#pragma unroll
+            for (int e = 0; e < G; ++e) psc[(pbase + pos) * G + e] = sc_l[lc][e];
+        }
+        outc += __popcll(m);
+    }
+    for (int k = min(outc, K) + lane; k < K; k += WAVE) pkey[pbase + k] = 0ull;
+}
+
+// Phase A2.  One wave per (seq, group): top-K of splits*K partial entries.
+template <int G>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const uint64_t *__restrict__ pkey,
+                                                          const float *__restrict__ psc, int32_t *sel_ws,
+                                                          float *selsc_ws, int32_t *sel_user, int H_q, int H_kv,
+                                                          int K, int splits) {
+    constexpr int NVMAX = 32;  // splits * K <= 2048
+    __shared__ uint64_t kept[128];
+    __shared__ int kept_at[128];
+    const int g = blockIdx.x, seq = blockIdx.y, lane = lane_id();
+    const int total = splits * K;
+    const int64_t pbase = ((int64_t)seq * H_kv + g) * splits * K;
+    uint64_t keys[NVMAX];
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v) {
+        const int idx = v * WAVE + lane;
+        keys[v] = idx < total ? pkey[pbase + idx] : 0ull;
+    }
+    int nonempty = 0;
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v) nonempty += __popcll(__ballot(keys[v] != 0ull));
+    uint64_t T = 1;
+    if (nonempty > K) {
+        T = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand = T | (1ull << bit);
+            int c2 = 0;
+#pragma unroll
+            for (int v = 0; v < NVMAX; ++v) c2 += __popcll(__ballot(keys[v] >= cand));
+            if (c2 >= K) T = cand;
+        }
+    }
+    int outc = 0;
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v) {
+        const bool keep = keys[v] >= T && keys[v] != 0ull;
+        const uint64_t m = __ballot(keep);
+        const int pos = outc + __popcll(m & lanemask_lt());
+        if (keep && pos < 128) {
+            kept[pos] = keys[v];
+            kept_at[pos] = v * WAVE + lane;
+        }
+        outc += __popcll(m);
+    }
+    wave_sync();
+    const int cnt = min(outc, K);
+    const int64_t sbase = ((int64_t)seq * H_kv + g) * K;
+    for (int t = lane; t < 128; t += WAVE) {
+        if (t < cnt) {
+            const int my = (int)(0xffffffffu - (uint32_t)kept[t]);
+            int rank = 0;
+            for (int u = 0; u < cnt; ++u) rank += (int)(0xffffffffu - (uint32_t)kept[u]) < my;
+            sel_ws[sbase + rank] = my;
+            if (sel_user) sel_user[sbase + rank] = my;
+#pragma unroll
+            for (int e = 0; e < G; ++e)
+                selsc_ws[((int64_t)seq * H_q + g * G + e) * K + rank] = psc[(pbase + kept_at[t]) * G + e];
+        }
+    }
+    for (int k = cnt + lane; k < K; k += WAVE) {
+        sel_ws[sbase + k] = -1;
+        if (sel_user) sel_user[sbase + k] = -1;
+#pragma unroll
+        for (int e = 0; e < G; ++e) selsc_ws[((int64_t)seq * H_q + g * G + e) * K + k] = -INFINITY;
+    }
+}
+
+// Phase B.  Block (split, group, seq) attends positions [lo, hi) of the
+// list "selected chunks, then window chunks".
+template <typename T, int D, int S, int G>
+__global__ __launch_bounds__(256) void decode_attend_kernel(
+    const float *__restrict__ qs_raw, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel_ws, const float *__restrict__ selsc_ws, float *pm, float *pl, float *po,
+    int H_q, int H_kv, int W, int K, int nsb, float scale) {
+    constexpr int DPL = D / WAVE;  // consecutive dims per lane (1 or 2)
+    constexpr int KPL = S / WAVE;  // keys per lane
+    constexpr int E = 16 / sizeof(T);
+    extern __shared__ float dyn_f[];
+    float(*k_l)[D + 1] = (float(*)[D + 1])dyn_f;            // [S][D+1]: lane-per-key rows, no bank conflicts
+    float(*v_l)[D] = (float(*)[D])(dyn_f + S * (D + 1));    // [S][D]
+    __shared__ float q_l[G][D];
+    __shared__ float p_l[4][S];
+
+    const int sp = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id();
+    const int t = clamp_len(seq_lens[seq], max_pages, S) - 1;
+    const int tc = t / S;
+    const int wc0 = max(0, tc - W / S);
+    const int32_t *sl = sel_ws + ((int64_t)seq * H_kv + g) * K;
+    // chunk list: selected (ascending, -1 padded) then window
+    int nsel = 0;
+    for (int kk = 0; kk < K; ++kk) nsel += sl[kk] >= 0;
+    const int total = nsel + (tc - wc0 + 1);
+    const int lo = (int)((int64_t)sp * total / nsb), hi = (int)((int64_t)(sp + 1) * total / nsb);
+    for (int x = tid; x < G * D; x += blockDim.x) q_l[x / D][x % D] = qs_raw[((int64_t)seq * H_q + g * G) * D + x];
+
+    // per-head running state, heads e = wave, wave + 4, ...
+    constexpr int HPW = (G + 3) / 4;
+    float m_s[HPW], l_s[HPW], o_s[HPW][DPL];
+#pragma unroll
+    for (int a = 0; a < HPW; ++a) {
+        m_s[a] = -INFINITY;
+        l_s[a] = 0.f;
+#pragma unroll
+        for (int y = 0; y < DPL; ++y) o_s[a][y] = 0.f;
+    }
+    const int32_t *bt = block_table + (int64_t)seq * max_pages;
+    for (int pos = lo; pos < hi; ++pos) {
+        const bool is_sel = pos < nsel;
+        const int c = is_sel ? sl[pos] : wc0 + (pos - nsel);
+        const int64_t page = bt[c];
+        __syncthreads();
+        const T *kp = k_cache + (page * H_kv + g) * (int64_t)S * D;
+        const T *vp = v_cache + (page * H_kv + g) * (int64_t)S * D;
+        for (int idx = tid; idx < S * D / E; idx += blockDim.x) {
+            const int j = idx / (D / E), x0 = (idx % (D / E)) * E;
+            const Vec16<T> kk = load16(kp + (int64_t)j * D + x0);
+            const Vec16<T> vv = load16(vp + (int64_t)j * D + x0);
+#pragma unroll
+            for (int x = 0; x < E; ++x) {
+                k_l[j][x0 + x] = kk.get(x);
+                v_l[j][x0 + x] = vv.get(x);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < HPW; ++a) {
+            const int e = wave + 4 * a;
+            if (e >= G) break;
+            float lg[KPL];
+            float cm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < KPL; ++u) {
+                const int j = u * WAVE + lane;
+                float dot = 0.f;
+                for (int x = 0; x < D; ++x) dot = fmaf(q_l[e][x], k_l[j][x], dot);
+                const bool masked = !is_sel && (c * S + j > t);
+                lg[u] = masked ? -INFINITY : dot * scale;
+                cm = fmaxf(cm, lg[u]);
+            }
+            cm = wave_max(cm);
+            float ls = 0.f;
+#pragma unroll
+            for (int u = 0; u < KPL; ++u) {
+                const float p = expf(lg[u] - cm);
+                p_l[wave][u * WAVE + lane] = p;
+                ls += p;
+            }
+            ls = xor_sum<1, 32>(ls);
+            wave_sync();
+            float oc[DPL];
+#pragma unroll
+            for (int y = 0; y < DPL; ++y) oc[y] = 0.f;
+            for (int j = 0; j < S; ++j) {
+                const float p = p_l[wave][j];
+#pragma unroll
+                for (int y = 0; y < DPL; ++y) oc[y] = fmaf(p, v_l[j][lane * DPL + y], oc[y]);
+            }
+            wave_sync();
+            // state of this chunk: selected -> (s^_c, 1, o_c / l_c); window -> (cm, ls, oc)
+            float cmx, cl, cscale;
+            if (is_sel) {
+                cmx = selsc_ws[((int64_t)seq * H_q + g * G + e) * K + pos];
+                cl = 1.f;
+                cscale = 1.f / ls;
+            } else {
+                cmx = cm;
+                cl = ls;
+                cscale = 1.f;
+            }
+            const float mn = fmaxf(m_s[a], cmx);
+            const float a0 = expf(m_s[a] - mn), a1 = expf(cmx - mn);
+            l_s[a] = l_s[a] * a0 + cl * a1;
+#pragma unroll
+            for (int y = 0; y < DPL; ++y) o_s[a][y] = o_s[a][y] * a0 + oc[y] * cscale * a1;
+            m_s[a] = mn;
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < HPW; ++a) {
+        const int e = wave + 4 * a;
+        if (e >= G) break;
+        const int64_t hb = ((int64_t)seq * H_q + g * G + e) * nsb + sp;
+        if (lane == 0) {
+            pm[hb] = m_s[a];
+            pl[hb] = l_s[a];
+        }
+#pragma unroll
+        for (int y = 0; y < DPL; ++y) po[hb * D + lane * DPL + y] = o_s[a][y];
+    }
+}
+
+// Phase B2.  One wave per (seq, head).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
+                                                             const float *__restrict__ po, T *__restrict__ out,
+                                                             float *__restrict__ lse, int64_t rows, int nsb) {
+    constexpr int DPL = D / WAVE;
+    const int lane = lane_id();
+    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int s = 0; s < nsb; ++s) m = fmaxf(m, pm[row * nsb + s]);
+    float l = 0.f, o[DPL];
+#pragma unroll
+    for (int y = 0; y < DPL; ++y) o[y] = 0.f;
+    for (int s = 0; s < nsb; ++s) {
+        const float ms = pm[row * nsb + s];
+        const float a = ms == -INFINITY ? 0.f : expf(ms - m);
+        l = fmaf(pl[row * nsb + s], a, l);
+#pragma unroll
+        for (int y = 0; y < DPL; ++y) o[y] = fmaf(po[(row * nsb + s) * D + lane * DPL + y], a, o[y]);
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int y = 0; y < DPL; ++y) out[row * D + lane * DPL + y] = from_f32<T>(o[y] * inv);
+    if (lse && lane == 0) lse[row] = m + logf(l);
+}
+
+size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages) {
+    return decode_layout(s, num_seqs, max_pages).total;
+}
+
+template <typename T, typename TS, int D, int S, int G>
+static hipError_t go_decode(const Shape &s, const DecodeLayout &L, int num_seqs, const void *q, const void *k_cache,
+                            const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                            const int32_t *block_table, int max_pages, const int32_t *seq_lens, const void *h,
+                            const void *w_down, const void *w_up, int d_model, int r, void *out, float *lse,
+                            int32_t *sel_idx, char *ws, hipStream_t st) {
+    float *qs = (float *)(ws + L.off_qs);
+    uint64_t *pkey = (uint64_t *)(ws + L.off_pkey);
+    float *psc = (float *)(ws + L.off_psc);
+    int32_t *sel = (int32_t *)(ws + L.off_sel);
+    float *selsc = (float *)(ws + L.off_selsc);
+    float *pm = (float *)(ws + L.off_pm), *pl = (float *)(ws + L.off_pl), *po = (float *)(ws + L.off_po);
+    hipLaunchKernelGGL(decode_qprep_kernel<T>, dim3(num_seqs), dim3(256), 0, st, (const T *)q, (const T *)h,
+                       (const T *)w_down, (const T *)w_up, qs, s.H_q, s.D, d_model, r);
+    const dim3 ga(L.splits, s.H_kv, num_seqs);
+    if (s.GLM == 1)
+        hipLaunchKernelGGL((decode_score_kernel<TS, D, G, 1>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
+                           bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
+                           s.K, L.splits, s.scale);
+    else
+        hipLaunchKernelGGL((decode_score_kernel<TS, D, G, G>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
+                           bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
+                           s.K, L.splits, s.scale);
+    hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(s.H_kv, num_seqs), dim3(64), 0, st, pkey, psc, sel, selsc,
+                       sel_idx, s.H_q, s.H_kv, s.K, L.splits);
+    const size_t dyn = (size_t)S * (D + 1) * 4 + (size_t)S * D * 4;
+    auto att = decode_attend_kernel<T, D, S, G>;
+    if (dyn > 48 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void *)att, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(att, dim3(L.nsb, s.H_kv, num_seqs), dim3(256), dyn, st, qs,
+                       (const T *)k_cache, (const T *)v_cache, block_table, max_pages, seq_lens, sel, selsc, pm, pl,
+                       po, s.H_q, s.H_kv, s.W, s.K, L.nsb, s.scale);
+    const int64_t rows = (int64_t)num_seqs * s.H_q;
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, pm, pl, po,
+                       (T *)out, lse, rows, L.nsb);
+    return hipGetLastError();
+}
+
+template <typename T, typename TS>
+static hipError_t dispatch_decode(const Shape &s, const DecodeLayout &L, int num_seqs, const void *q,
+                                  const void *k_cache, const void *v_cache, const void *ksum_cache,
+                                  const float *bsum_cache, const int32_t *block_table, int max_pages,
+                                  const int32_t *seq_lens, const void *h, const void *w_down, const void *w_up,
+                                  int d_model, int r, void *out, float *lse, int32_t *sel_idx, char *ws,
+                                  hipStream_t st) {
+#define HILS_DEC(DD, SS, GG)                                                                                    \
+    if (s.D == DD && s.S == SS && s.G == GG)                                                                    \
+        return go_decode<T, TS, DD, SS, GG>(s, L, num_seqs, q, k_cache, v_cache, ksum_cache, bsum_cache,         \
+                                            block_table, max_pages, seq_lens, h, w_down, w_up, d_model, r, out, \
+                                            lse, sel_idx, ws, st);
+    HILS_DEC(64, 64, 1) HILS_DEC(64, 64, 2) HILS_DEC(64, 64, 4) HILS_DEC(64, 64, 8)
+    HILS_DEC(64, 128, 1) HILS_DEC(64, 128, 2) HILS_DEC(64, 128, 4) HILS_DEC(64, 128, 8)
+    HILS_DEC(128, 64, 1) HILS_DEC(128, 64, 2) HILS_DEC(128, 64, 4) HILS_DEC(128, 64, 8)
+    HILS_DEC(128, 128, 1) HILS_DEC(128, 128, 2) HILS_DEC(128, 128, 4) HILS_DEC(128, 128, 8)
+#undef HILS_DEC
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const Shape &s, int num_seqs, const void *q, const void *k_cache, const void *v_cache,
+                         const void *ksum_cache, const float *bsum_cache, const int32_t *block_table, int max_pages,
+                         const int32_t *seq_lens, int max_seq_len, const void *h, const void *w_down,
+                         const void *w_up, int d_model, int r, void *out, float *lse, int32_t *sel_idx,
+                         void *workspace, hipStream_t st) {
+    (void)max_seq_len;
+    if (num_seqs == 0) return hipSuccess;
+    const DecodeLayout L = decode_layout(s, num_seqs, max_pages);
+    char *ws = (char *)workspace;
+    if (s.io_bf16)
+        return s.sum_bf16 ? dispatch_decode<bf16, bf16>(s, L, num_seqs, q, k_cache, v_cache, ksum_cache, bsum_cache,
+                                                        block_table, max_pages, seq_lens, h, w_down, w_up, d_model,
+                                                        r, out, lse, sel_idx, ws, st)
+                          : dispatch_decode<bf16, float>(s, L, num_seqs, q, k_cache, v_cache, ksum_cache,
+                                                         bsum_cache, block_table, max_pages, seq_lens, h, w_down,
+                                                         w_up, d_model, r, out, lse, sel_idx, ws, st);
+    return s.sum_bf16 ? dispatch_decode<float, bf16>(s, L, num_seqs, q, k_cache, v_cache, ksum_cache, bsum_cache,
+                                                     block_table, max_pages, seq_lens, h, w_down, w_up, d_model, r,
+                                                     out, lse, sel_idx, ws, st)
+                      : dispatch_decode<float, float>(s, L, num_seqs, q, k_cache, v_cache, ksum_cache, bsum_cache,
+                                                      block_table, max_pages, seq_lens, h, w_down, w_up, d_model, r,
+                                                      out, lse, sel_idx, ws, st);
+}
+
+}  // namespace hils

@@ -1,0 +1,211 @@
+// hils_api.cpp -- the C ABI of libhils: argument validation, workspace
+// accounting and dispatch to the kernel launchers.  Validation happens on
+// the host before anything is enqueued; on failure nothing is written.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/hils.h"
+#include "hils_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hils_status_t fail(hils_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+hils_status_t ok() {
+    g_err[0] = '\0';
+    return HILS_OK;
+}
+
+hils_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(HILS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Resolve and validate the configuration.  need_seq: B and N matter.
+hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
+    if (!cfg) return fail(HILS_ERR_INVALID_ARG, "cfg is NULL");
+    s.B = need_seq ? cfg->B : 1;
+    s.N = need_seq ? cfg->N : 0;
+    s.H_q = cfg->H_q;
+    s.H_kv = cfg->H_kv;
+    s.H_lm = cfg->H_lm;
+    s.D = cfg->d;
+    s.S = cfg->S;
+    s.W = cfg->W;
+    s.K = cfg->K;
+    s.M = cfg->M;
+    if (need_seq && (s.B < 0 || s.N < 0)) return fail(HILS_ERR_INVALID_ARG, "B=%d N=%d must be >= 0", s.B, s.N);
+    if (s.H_q <= 0 || s.H_kv <= 0 || s.H_lm <= 0 || s.D <= 0 || s.S <= 0 || s.W < 0 || s.K < 0)
+        return fail(HILS_ERR_INVALID_ARG, "head counts, d and S must be > 0; W, K must be >= 0");
+    if (s.H_q % s.H_kv) return fail(HILS_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", s.H_q, s.H_kv);
+    if (s.H_lm != s.H_q && s.H_lm != s.H_kv)
+        return fail(HILS_ERR_INVALID_ARG, "H_lm=%d must equal H_q=%d or H_kv=%d", s.H_lm, s.H_q, s.H_kv);
+    if (s.W % s.S) return fail(HILS_ERR_INVALID_ARG, "W=%d is not a multiple of S=%d", s.W, s.S);
+    if (cfg->io_dtype != HILS_F32 && cfg->io_dtype != HILS_BF16)
+        return fail(HILS_ERR_INVALID_ARG, "io_dtype=%d unknown", cfg->io_dtype);
+    if (cfg->summary_dtype != HILS_F32 && cfg->summary_dtype != HILS_BF16)
+        return fail(HILS_ERR_INVALID_ARG, "summary_dtype=%d unknown", cfg->summary_dtype);
+    if (!(cfg->scale >= 0.f) || !isfinite(cfg->scale)) return fail(HILS_ERR_INVALID_ARG, "scale must be finite, >= 0");
+    s.G = s.H_q / s.H_kv;
+    s.GLM = s.H_lm / s.H_kv;
+    if (s.D != 64 && s.D != 128) return fail(HILS_ERR_UNSUPPORTED, "d=%d: supported 64, 128", s.D);
+    if (s.S != 64 && s.S != 128) return fail(HILS_ERR_UNSUPPORTED, "S=%d: supported 64, 128", s.S);
+    if (s.G != 1 && s.G != 2 && s.G != 4 && s.G != 8)
+        return fail(HILS_ERR_UNSUPPORTED, "G=H_q/H_kv=%d: supported 1, 2, 4, 8", s.G);
+    if (s.K > 128) return fail(HILS_ERR_UNSUPPORTED, "K=%d: supported 0..128", s.K);
+    s.C = s.S ? s.N / s.S : 0;
+    s.CA = s.S ? (s.N + s.S - 1) / s.S : 0;
+    if (need_seq && s.C > 8192) return fail(HILS_ERR_UNSUPPORTED, "N/S=%d chunks: supported up to 8192", s.C);
+    s.io_bf16 = cfg->io_dtype == HILS_BF16;
+    s.sum_bf16 = cfg->summary_dtype == HILS_BF16;
+    s.scale = cfg->scale > 0.f ? cfg->scale : 1.0f / sqrtf((float)s.D);
+    return ok();
+}
+
+hils_status_t check_ptr(const void *p, const char *name) {
+    if (!p) return fail(HILS_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(HILS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return HILS_OK;
+}
+
+hils_status_t check_qcal(const void *h, const void *w_down, const void *w_up, int32_t d_model, int32_t r) {
+    if (!h) return HILS_OK;
+    hils_status_t st;
+    if ((st = check_ptr(h, "h")) || (st = check_ptr(w_down, "w_down")) || (st = check_ptr(w_up, "w_up"))) return st;
+    if (d_model <= 0 || r <= 0) return fail(HILS_ERR_INVALID_ARG, "d_model=%d, r=%d must be > 0", d_model, r);
+    if (r > 64) return fail(HILS_ERR_UNSUPPORTED, "Q-Cal rank r=%d: supported up to 64", r);
+    return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hils_last_error(void) { return g_err; }
+
+int hils_version(void) { return 10000; }
+
+size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs, int32_t max_pages) {
+    hils::Shape s;
+    const bool seq = which != HILS_WS_DECODE;
+    if (resolve(cfg, seq, s) != HILS_OK) return 0;
+    switch (which) {
+        case HILS_WS_SCORE: return hils::score_workspace_bytes(s, false);
+        case HILS_WS_SCORE_QCAL: return hils::score_workspace_bytes(s, true);
+        case HILS_WS_FUSED: return hils::fused_workspace_bytes(s);
+        case HILS_WS_DECODE:
+            if (num_seqs < 0 || max_pages < 0) {
+                fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
+                return 0;
+            }
+            return hils::decode_workspace_bytes(s, num_seqs, max_pages);
+        default: fail(HILS_ERR_INVALID_ARG, "unknown workspace kind %d", which); return 0;
+    }
+}
+
+hils_status_t hils_landmark_summarize(const hils_config_t *cfg, const void *k, const void *q_lm, void *k_sum,
+                                      float *b_sum, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if ((int64_t)s.B * s.H_lm * s.C == 0) return ok();
+    if ((st = check_ptr(k, "k")) || (st = check_ptr(q_lm, "q_lm")) || (st = check_ptr(k_sum, "k_sum")) ||
+        (st = check_ptr(b_sum, "b_sum")))
+        return st;
+    return hip_status(hils::launch_landmark_summary(s, k, q_lm, k_sum, b_sum, stream), "landmark summary launch");
+}
+
+hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const void *k_sum, const float *b_sum,
+                                const void *h, const void *w_down, const void *w_up, int32_t d_model, int32_t r,
+                                int32_t *sel_idx, float *sel_score, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if ((int64_t)s.B * s.N == 0 || s.K == 0) return ok();
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))
+        return st;
+    if (s.C > 0 && ((st = check_ptr(k_sum, "k_sum")) || (st = check_ptr(b_sum, "b_sum")))) return st;
+    if ((st = check_qcal(h, w_down, w_up, d_model, r))) return st;
+    const bool qcal = h != nullptr;
+    const size_t need = hils::score_workspace_bytes(s, qcal);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(HILS_ERR_WORKSPACE, "score_select needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    hils::ScoreWorkspace ws;
+    hils::score_workspace_carve(s, qcal, workspace, ws);
+    return hip_status(hils::launch_score_select(s, q, k_sum, b_sum, h, w_down, w_up, d_model, r, sel_idx, sel_score,
+                                                ws, stream),
+                      "score/select launch");
+}
+
+hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                       const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if ((int64_t)s.B * s.N == 0) return ok();
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(out, "out")))
+        return st;
+    if (s.K > 0 && ((st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))) return st;
+    if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    const size_t need = hils::fused_workspace_bytes(s);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(HILS_ERR_WORKSPACE, "sparse_attend_fused needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(hils::launch_sparse_attend(s, q, k, v, sel_idx, sel_score, out, lse, workspace, stream),
+                      "sparse attention launch");
+}
+
+hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,
+                          const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                          const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens, const void *h,
+                          const void *w_down, const void *w_up, int32_t d_model, int32_t r, void *out, float *lse,
+                          int32_t *sel_idx, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, false, s);
+    if (st) return st;
+    if (num_seqs < 0 || max_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
+    if (num_seqs == 0) return ok();
+    if (max_pages == 0) return fail(HILS_ERR_INVALID_ARG, "max_pages must be >= 1");
+    if ((int64_t)max_pages > 65536) return fail(HILS_ERR_UNSUPPORTED, "max_pages=%d: supported up to 65536", max_pages);
+    if ((max_pages + hils::decode_splits(s, max_pages) - 1) / hils::decode_splits(s, max_pages) >
+        hils::DECODE_SPLIT_CAP)
+        return fail(HILS_ERR_UNSUPPORTED, "max_pages=%d with K=%d exceeds the decode scoring split capacity",
+                    max_pages, s.K);
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
+        (st = check_ptr(ksum_cache, "ksum_cache")) || (st = check_ptr(bsum_cache, "bsum_cache")) ||
+        (st = check_ptr(block_table, "block_table")) || (st = check_ptr(seq_lens, "seq_lens")) ||
+        (st = check_ptr(out, "out")))
+        return st;
+    if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    if (sel_idx && !aligned16(sel_idx)) return fail(HILS_ERR_INVALID_ARG, "sel_idx is not 16-byte aligned");
+    if ((st = check_qcal(h, w_down, w_up, d_model, r))) return st;
+    const size_t need = hils::decode_workspace_bytes(s, num_seqs, max_pages);
+    if (!workspace || workspace_bytes < need)
+        return fail(HILS_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(hils::launch_decode(s, num_seqs, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table,
+                                          max_pages, seq_lens, 0, h, w_down, w_up, d_model, r, out, lse, sel_idx,
+                                          workspace, stream),
+                      "decode launch");
+}
+
+}  // extern "C"

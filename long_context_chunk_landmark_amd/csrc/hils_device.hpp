@@ -1,0 +1,128 @@
+// hils_device.hpp -- device-side helpers shared by the HiLS kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16-byte vector of T: 8 bf16 or 4 fp32.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+    static constexpr int E = 8;
+    bf16x8 v;
+    __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
+};
+template <>
+struct Vec16<float> {
+    static constexpr int E = 4;
+    f32x4 v;
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(const T *p) {
+    Vec16<T> r;
+    r.v = *reinterpret_cast<const decltype(r.v) *>(p);
+    return r;
+}
+
+// Butterfly reductions over lanes that differ in the bits [lo_mask, hi_mask].
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+    for (int m = FROM; m <= TO; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
+    return v;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+    for (int m = FROM; m <= TO; m <<= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ int xor_sum_i(int v) {
+#pragma unroll
+    for (int m = FROM; m <= TO; m <<= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) { return xor_sum_i<1, 32>(v); }
+__device__ __forceinline__ float wave_max(float v) { return xor_max<1, 32>(v); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// Orders LDS traffic between lanes of one wavefront (lanes run in lockstep;
+// this keeps the compiler from moving LDS accesses across the point).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ord_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_key_inv(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// MFMA 16x16x32 bf16 -> fp32.  A: lane l holds row l%16, k = 8*(l/16)..+7.
+// B: lane l holds col l%16, k = 8*(l/16)..+7.  D: lane l holds rows
+// 4*(l/16)+i (i = 0..3) of col l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Ragged row offsets of the per-query candidate lists.  All queries of
+// query chunk qc have n(qc) = max(0, qc - w) candidates (w = W / S); each
+// row is padded to a multiple of 16 entries.
+__host__ __device__ __forceinline__ int64_t pad16(int64_t n) { return (n + 15) & ~int64_t(15); }
+// sum_{m=1}^{M} pad16(m) / 16 for M >= 0, i.e. sum of ceil(m/16).
+__host__ __device__ __forceinline__ int64_t sum_ceil16(int64_t M) {
+    if (M <= 0) return 0;
+    const int64_t A = M / 16, r = M % 16;
+    return 8 * A * (A + 1) + (A + 1) * r;
+}
+// Offset (in entries) of the first row of query chunk qc within one (b, g).
+__host__ __device__ __forceinline__ int64_t cand_chunk_offset(int64_t qc, int64_t w, int64_t S) {
+    // rows of chunks qc' < qc; chunk qc' contributes S * pad16(max(0, qc' - w)).
+    const int64_t M = qc - 1 - w;  // largest candidate count among them
+    return S * 16 * sum_ceil16(M);
+}
+__host__ __device__ __forceinline__ int64_t cand_row_offset(int64_t i, int64_t w, int64_t S) {
+    const int64_t qc = i / S;
+    const int64_t n = qc - w > 0 ? qc - w : 0;
+    return cand_chunk_offset(qc, w, S) + (i % S) * pad16(n);
+}
+
+}  // namespace hils

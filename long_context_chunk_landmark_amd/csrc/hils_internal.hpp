@@ -1,0 +1,63 @@
+// hils_internal.hpp -- host-side launcher interface between the C ABI layer
+// (hils_api.cpp) and the kernel translation units.  Every launcher assumes
+// its arguments were validated by the ABI layer and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+namespace hils {
+
+// Validated, resolved configuration.
+struct Shape {
+    int B, N, H_q, H_kv, H_lm, D, S, W, K, M;
+    int G;      // H_q / H_kv
+    int GLM;    // landmark heads per kv head: H_lm / H_kv (1 or G)
+    int C;      // floor(N / S) completed chunks
+    int CA;     // ceil(N / S) chunks incl. a partial last one
+    bool io_bf16, sum_bf16;
+    float scale;
+};
+
+// ---- kernel 1: landmark summary
+hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
+                                   hipStream_t st);
+
+// ---- kernel 2: score + select
+struct ScoreWorkspace {
+    void *ksb;          // [B,H_lm,C,D] bf16 copy of k_sum
+    float *knorm;       // [B,H_lm] max_c ||k'_c||
+    float *err;         // [B,H_kv,N] per-row bound of the approximate group score
+    float *agg;         // ragged approximate group scores, per (b,g): per_bg entries
+    int64_t per_bg;     // entries per (b, g)
+    float *q_s;         // [B,H_q,N,D] Q-Cal scoring queries (fp32) or null
+};
+int64_t score_agg_entries_per_bg(const Shape &s);
+size_t score_workspace_bytes(const Shape &s, bool qcal);
+void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace &ws);
+hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum, const float *b_sum, const void *h,
+                               const void *w_down, const void *w_up, int d_model, int r, int32_t *sel_idx,
+                               float *sel_score, const ScoreWorkspace &ws, hipStream_t st);
+
+// ---- kernel 3: fused sparse attention
+size_t fused_workspace_bytes(const Shape &s);
+hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
+                                const float *sel_score, void *out, float *lse, void *workspace, hipStream_t st);
+
+// ---- kernel 4: decode
+size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages);
+// Largest candidate range one phase-A block may own (LDS capacity).
+constexpr int DECODE_SPLIT_CAP = 512;
+int decode_splits(const Shape &s, int max_pages);
+hipError_t launch_decode(const Shape &s, int num_seqs, const void *q, const void *k_cache, const void *v_cache,
+                         const void *ksum_cache, const float *bsum_cache, const int32_t *block_table, int max_pages,
+                         const int32_t *seq_lens, int max_seq_len, const void *h, const void *w_down,
+                         const void *w_up, int d_model, int r, void *out, float *lse, int32_t *sel_idx,
+                         void *workspace, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace hils

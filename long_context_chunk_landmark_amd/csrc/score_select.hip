@@ -1,0 +1,546 @@
+// score_select.hip -- kernel 2: surrogate chunk scores, GQA max, top-K.
+//
+// hyper.ai HiLS summary, section 方法: s^_ic = q_i . k'_c / sqrt(d) + b'_c;
+// chunks are ranked by s^ and the top K kept; under GQA the per-head scores
+// are max-aggregated over the heads of a group and one top-K set is taken
+// per group; Q-Cal replaces the scoring query by q_i + W_up W_down h_i.
+//
+// Design (MI355X): the scoring contraction is dense (every query of a chunk
+// scores the same candidate set), so it runs on bf16 MFMA.  bf16 operands
+// round k' (and an fp32 Q-Cal query), so the MFMA scores are approximate;
+// each row carries a rigorous bound E on |approx - exact| derived from
+// |x - bf16(x)| <= 2^-8 |x| and Cauchy-Schwarz (E = scale * kappa * ||q|| *
+// max_c ||k'_c||).  The select kernel then finds the exact K-th largest
+// approximate group score tau, keeps every candidate whose approximate
+// score is >= tau - 2E (a superset of the exact top-K), recomputes those in
+// fp32 on the vector ALUs, and takes the exact top-K by (score desc, index
+// asc).  Bit-exact selection, MFMA-rate scoring.
+//
+// Kernels:
+//   ksum_prep        bf16 copy of k' + per-(b, landmark head) max ||k'||
+//   qcal             fp32 scoring queries q + W_up (W_down h)
+//   score_approx     bf16 MFMA scores -> ragged approximate group scores
+//   select           exact refine + top-K per (b, g, query)
+#include "hils_device.hpp"
+#include "hils_internal.hpp"
+
+namespace hils {
+
+// ------------------------------------------------------------ workspace
+
+int64_t score_agg_entries_per_bg(const Shape &s) {
+    // rows of every query chunk (incl. a partial last one) padded to 16
+    const int64_t w = s.W / s.S;
+    int64_t total = 0;
+    const int64_t full = s.N / s.S;
+    total = cand_chunk_offset(full, w, s.S);
+    if (s.N % s.S) {
+        const int64_t n = full - w > 0 ? full - w : 0;
+        total += (int64_t)(s.N % s.S) * pad16(n);
+    }
+    return total;
+}
+
+size_t score_workspace_bytes(const Shape &s, bool qcal) {
+    size_t b = 0;
+    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);  // ksb
+    b += align_up((size_t)s.B * s.H_lm * 4, 256);               // knorm
+    b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
+    b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
+    if (qcal) b += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
+    return b;
+}
+
+void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace &ws) {
+    char *p = (char *)base;
+    ws.ksb = p;
+    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);
+    ws.knorm = (float *)p;
+    p += align_up((size_t)s.B * s.H_lm * 4, 256);
+    ws.err = (float *)p;
+    p += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);
+    ws.per_bg = score_agg_entries_per_bg(s);
+    ws.agg = (float *)p;
+    p += align_up((size_t)s.B * s.H_kv * ws.per_bg * 4, 256);
+    ws.q_s = qcal ? (float *)p : nullptr;
+}
+
+// ------------------------------------------------------------ k' prep
+
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// 16 lanes per k' row (D/16 elements each), 4 rows per wave.
+template <typename TS, int D>
+__global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k_sum, bf16 *__restrict__ ksb,
+                                                        float *__restrict__ knorm, int C, int64_t rows) {
+    constexpr int EL = D / 16;
+    const int lane = lane_id();
+    const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * 4 + (lane >> 4);
+    const bool ok = row < rows;
+    float ss = 0.f;
+    if (ok) {
+        const TS *src = k_sum + row * D + (lane & 15) * EL;
+        bf16 *dst = ksb + row * D + (lane & 15) * EL;
+#pragma unroll
+        for (int x = 0; x < EL; ++x) {
+            const float v = to_f32(src[x]);
+            ss = fmaf(v, v, ss);
+            dst[x] = (bf16)v;
+        }
+    }
+    ss = xor_sum<1, 8>(ss);
+    // rows of one wave may belong to different (b, l); reduce per row
+    if (ok && (lane & 15) == 0) {
+        const int64_t bl = row / C;
+        atomicMax((unsigned int *)(knorm + bl), __float_as_uint(sqrtf(ss)));
+    }
+}
+
+// ------------------------------------------------------------ Q-Cal
+
+// q_s[b,h,i,:] = q[b,h,i,:] + (W_up (W_down h[b,i]))[h*D : h*D + D]
+// One block per 16 tokens.  Phase 1: u = W_down h for the 16 tokens (fp32,
+// LDS).  Phase 2: each thread owns rows e of W_up and writes 16 tokens.
+template <typename T>
+__global__ __launch_bounds__(256) void qcal_kernel(const T *__restrict__ q, const T *__restrict__ h,
+                                                   const T *__restrict__ w_down, const T *__restrict__ w_up,
+                                                   float *__restrict__ q_s, int N, int H_q, int D, int d_model,
+                                                   int r) {
+    constexpr int TB = 16;
+    extern __shared__ float u_lds[];  // [TB][r]
+    const int64_t b = blockIdx.y;
+    const int i0 = blockIdx.x * TB;
+    const int nt = min(TB, N - i0);
+    // phase 1: 256 threads over (token, a) pairs, each a d_model-long dot
+    for (int p = threadIdx.x; p < TB * r; p += blockDim.x) {
+        const int t = p / r, a = p % r;
+        float acc = 0.f;
+        if (t < nt) {
+            const T *hr = h + (b * N + i0 + t) * (int64_t)d_model;
+            const T *wr = w_down + (int64_t)a * d_model;
+            for (int x = 0; x < d_model; ++x) acc = fmaf(to_f32(hr[x]), to_f32(wr[x]), acc);
+        }
+        u_lds[t * r + a] = acc;
+    }
+    __syncthreads();
+    const int HD = H_q * D;
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
+        float wrow[64];
+        for (int a = 0; a < r; ++a) wrow[a] = to_f32(w_up[(int64_t)e * r + a]);
+        const int hh = e / D, x = e % D;
+        for (int t = 0; t < nt; ++t) {
+            float acc = 0.f;
+            for (int a = 0; a < r; ++a) acc = fmaf(wrow[a], u_lds[t * r + a], acc);
+            const int64_t o = ((b * H_q + hh) * N + i0 + t) * (int64_t)D + x;
+            q_s[o] = to_f32(q[o]) + acc;
+        }
+    }
+}
+
+// ------------------------------------------------------------ approximate scores (MFMA)
+
+// One block = 4 waves = 64 consecutive queries of one query chunk (S is a
+// multiple of 64) for one (b, g).  Wave w owns queries 16w..16w+15 as the
+// B operand (q^T, bf16) of 16x16x32 MFMAs for each of the G heads; the A
+// operand is a 16-candidate k' tile staged in LDS.  Output D: lane l holds
+// candidates 4*(l/16)+i of query l%16, so each lane stores 16 contiguous
+// bytes of its query's ragged score row.
+template <typename TQ, int D, int G>
+__global__ __launch_bounds__(256) void score_approx_kernel(
+    const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const float *__restrict__ b_sum,
+    const float *__restrict__ knorm, float *__restrict__ agg_out, float *__restrict__ err_out, int N, int H_q,
+    int H_kv, int H_lm, int C, int S, int W, int K, float scale, float kappa, int64_t per_bg) {
+    constexpr int KS = D / 32;   // MFMA k-steps over the head dim
+    constexpr int NB = D / 8;    // 16-byte blocks per k' row
+    __shared__ u32x4 kt[G][16][NB];
+    __shared__ float bt[G][16];
+
+    const int g = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int i0 = blockIdx.x * 64;
+    const int w = W / S;
+    const int qc = i0 / S;
+    const int n = max(0, qc - w);
+    if (n <= K) return;  // every candidate is selected; nothing to rank
+
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int iq = i0 + wave * 16 + (lane & 15);
+    const bool qvalid = iq < N;
+    const int iqc = qvalid ? iq : N - 1;
+    const int grp = lane >> 4;
+
+    bf16x8 qf[G][KS];
+    float emax = 0.f;
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+        const int hh = g * G + e;
+        const TQ *qr = q + (((int64_t)b * H_q + hh) * N + iqc) * D;
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int d0 = 32 * s + 8 * grp;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float v = to_f32(qr[d0 + x]);
+                ss = fmaf(v, v, ss);
+                qf[e][s][x] = (bf16)v;
+            }
+        }
+        ss = xor_sum<16, 32>(ss);
+        const int l = hh * H_lm / H_q;
+        emax = fmaxf(emax, sqrtf(ss) * knorm[b * H_lm + l]);
+    }
+    const float err = scale * kappa * emax + 1e-5f;
+    if (qvalid && grp == 0) err_out[((int64_t)b * H_kv + g) * N + iq] = err;
+
+    float *row = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset(iqc, w, S);
+
+    for (int c0 = 0; c0 < n; c0 += 16) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * 16 * NB; idx += blockDim.x) {
+            const int e = idx / (16 * NB), rem = idx % (16 * NB);
+            const int cr = rem / NB, cb = rem % NB;
+            const int c = c0 + cr;
+            const int l = (g * G + e) * H_lm / H_q;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (c < n) val = *(const u32x4 *)(ksb + (((int64_t)b * H_lm + l) * C + c) * D + cb * 8);
+            kt[e][cr][cb ^ (cr & 7)] = val;
+        }
+        if (threadIdx.x < G * 16) {
+            const int e = threadIdx.x / 16, cr = threadIdx.x % 16;
+            const int c = c0 + cr;
+            const int l = (g * G + e) * H_lm / H_q;
+            bt[e][cr] = c < n ? b_sum[((int64_t)b * H_lm + l) * C + c] : 0.f;
+        }
+        __syncthreads();
+        f32x4 best = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int cr = lane & 15;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 raw = kt[e][cr][(4 * s + grp) ^ (cr & 7)];
+                bf16x8 a;
+                __builtin_memcpy(&a, &raw, 16);
+                acc = mfma16(a, qf[e][s], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(scale, acc[i], bt[e][4 * grp + i]));
+        }
+        if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+    }
+}
+
+// ------------------------------------------------------------ exact refine + top-K
+
+constexpr int SEL_GMAX = 8;
+constexpr int SEL_KMAX = 128;
+
+// 64-bit ranking key: larger score first, then lower chunk index first.
+__device__ __forceinline__ uint64_t rank_key(float s, int idx) {
+    return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+// Largest T with #{keys >= T} >= kk (the kk-th largest key); keys == 0 are
+// empty slots.  NV keys per lane.
+template <int NV>
+__device__ __forceinline__ uint64_t kth_largest64(const uint64_t (&keys)[NV], int kk) {
+    uint64_t T = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = T | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cnt += __popcll(__ballot(keys[v] >= cand));
+        if (cnt >= kk) T = cand;
+    }
+    return T;
+}
+
+struct SelLds {
+    float q[SEL_GMAX][128];         // scoring queries of the row (fp32)
+    uint64_t run_key[SEL_KMAX];     // running exact top-K
+    float run_sc[SEL_KMAX][SEL_GMAX];
+    int batch_idx[WAVE];            // survivors awaiting refinement
+};
+
+// One wave per (b, g, query).  JMAX: registers for ceil(n/64) approximate
+// scores per lane.
+template <typename TQ, typename TS, int JMAX>
+__global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, const TS *__restrict__ k_sum,
+                                                     const float *__restrict__ b_sum,
+                                                     const float *__restrict__ agg_in,
+                                                     const float *__restrict__ err_in, int32_t *__restrict__ sel_idx,
+                                                     float *__restrict__ sel_score, int B, int N, int H_q, int H_kv,
+                                                     int H_lm, int C, int D, int S, int W, int K, float scale,
+                                                     int64_t per_bg) {
+    __shared__ SelLds lds_all[4];
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    SelLds &L = lds_all[wave];
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;  // (b*H_kv + g)*N + i
+    if (row >= (int64_t)B * H_kv * N) return;
+    const int i = (int)(row % N);
+    const int64_t bg = row / N;
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int G = H_q / H_kv;
+    const int w = W / S;
+    const int n = max(0, i / S - w);
+
+    int32_t *out_idx = sel_idx + row * K;
+    const int64_t sc_base = (b * H_q + (int64_t)g * G) * N + i;  // + e*N, then * K
+    if (n == 0) {
+        for (int k = lane; k < K; k += WAVE) out_idx[k] = -1;
+        for (int e = 0; e < G; ++e)
+            for (int k = lane; k < K; k += WAVE) sel_score[(sc_base + (int64_t)e * N) * K + k] = -INFINITY;
+        return;
+    }
+
+    // scoring query rows of the G heads -> LDS
+    for (int e = 0; e < G; ++e) {
+        const TQ *qr = q + ((b * H_q + (int64_t)g * G + e) * N + i) * D;
+        for (int x = lane; x < D; x += WAVE) L.q[e][x] = to_f32(qr[x]);
+    }
+
+    // ---- survivors of the approximate pass
+    const int J = (n + WAVE - 1) / WAVE;
+    uint32_t keys[JMAX];  // order-preserving keys of the approximate scores
+    uint32_t thr_key = 0;
+    const bool rank_needed = n > K;
+    if (rank_needed) {
+        const float *ar = agg_in + bg * per_bg + cand_row_offset(i, w, S);
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+            const int c = j * WAVE + lane;
+            keys[j] = (j < J && c < n) ? ord_key(ar[c]) : 0u;
+        }
+        // exact K-th largest approximate score (bitwise bisection on keys)
+        uint32_t T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < JMAX; ++j) cnt += (j < J) & (keys[j] >= cand);
+            cnt = wave_sum_i(cnt);
+            if (cnt >= K) T = cand;
+        }
+        // every exact top-K member has approximate score >= tau - 2E
+        thr_key = ord_key(ord_key_inv(T) - 2.f * err_in[row]);
+        if (thr_key == 0u) thr_key = 1u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) keys[j] = 0u;
+    }
+    wave_sync();
+
+    // ---- stream survivors through exact refinement, keep exact top-K
+    int run_cnt = 0;
+    int bcnt = 0;
+    const float *bsr_base = b_sum + b * (int64_t)H_lm * C;
+    auto flush = [&]() {
+        // refine batch entry `lane`
+        float sc[SEL_GMAX];
+        uint64_t bkey = 0;
+        if (lane < bcnt) {
+            const int c = L.batch_idx[lane];
+            float agg = -INFINITY;
+            for (int e = 0; e < G; ++e) {
+                const int l = (g * G + e) * H_lm / H_q;
+                const TS *kr = k_sum + ((b * H_lm + l) * (int64_t)C + c) * D;
+                float dot = 0.f;
+                for (int x = 0; x < D; x += 4) {
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) dot = fmaf(L.q[e][x + y], to_f32(kr[x + y]), dot);
+                }
+                sc[e] = fmaf(scale, dot, bsr_base[(int64_t)l * C + c]);
+                agg = fmaxf(agg, sc[e]);
+            }
+            bkey = rank_key(agg, c);
+        }
+        wave_sync();
+        // merge with the running set (entries lane and lane+64)
+        uint64_t keys[3];
+        keys[0] = lane < run_cnt ? L.run_key[lane] : 0ull;
+        keys[1] = lane + WAVE < run_cnt ? L.run_key[lane + WAVE] : 0ull;
+        keys[2] = bkey;
+        float rs0[SEL_GMAX], rs1[SEL_GMAX];
+        for (int e = 0; e < G; ++e) {
+            rs0[e] = lane < run_cnt ? L.run_sc[lane][e] : 0.f;
+            rs1[e] = lane + WAVE < run_cnt ? L.run_sc[lane + WAVE][e] : 0.f;
+        }
+        const int total = run_cnt + bcnt;
+        uint64_t T = 1;  // keep every non-empty key
+        if (total > K) T = kth_largest64<3>(keys, K);
+        // compact keys >= T into the running set, slot order 0, 1, 2
+        int base = 0;
+#pragma unroll
+        for (int v = 0; v < 3; ++v) {
+            const bool keep = keys[v] >= T && keys[v] != 0ull;
+            const uint64_t m = __ballot(keep);
+            const int pos = base + __popcll(m & lanemask_lt());
+            // all reads of the old set are done (registers); write new set
+            if (keep && pos < SEL_KMAX) {
+                L.run_key[pos] = keys[v];
+                for (int e = 0; e < G; ++e) L.run_sc[pos][e] = v == 0 ? rs0[e] : (v == 1 ? rs1[e] : sc[e]);
+            }
+            base += __popcll(m);
+        }
+        run_cnt = min(base, K);
+        bcnt = 0;
+        wave_sync();
+    };
+
+    if (!rank_needed) {
+        for (int c0 = 0; c0 < n; c0 += WAVE) {
+            const int m = min(WAVE, n - c0);
+            if (lane < m) L.batch_idx[lane] = c0 + lane;
+            bcnt = m;
+            wave_sync();
+            flush();
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+            if (j < J) {
+                const int c = j * WAVE + lane;
+                const bool surv = c < n && keys[j] >= thr_key;
+                const uint64_t m = __ballot(surv);
+                const int cnt = __popcll(m);
+                if (cnt > 0) {
+                    if (bcnt + cnt > WAVE) flush();
+                    if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = c;
+                    bcnt += cnt;
+                    wave_sync();
+                }
+            }
+        }
+        if (bcnt > 0) flush();
+    }
+
+    // ---- emit ascending by chunk index
+    wave_sync();
+    const int cnt = run_cnt;
+    for (int t = lane; t < SEL_KMAX; t += WAVE) {
+        if (t < cnt) {
+            const uint64_t my = L.run_key[t];
+            const int myidx = (int)(0xffffffffu - (uint32_t)my);
+            int rank = 0;
+            for (int u = 0; u < cnt; ++u) {
+                const int oi = (int)(0xffffffffu - (uint32_t)L.run_key[u]);
+                rank += oi < myidx;
+            }
+            out_idx[rank] = myidx;
+            for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + rank] = L.run_sc[t][e];
+        }
+    }
+    for (int k = cnt + lane; k < K; k += WAVE) {
+        out_idx[k] = -1;
+        for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + k] = -INFINITY;
+    }
+}
+
+// ------------------------------------------------------------ launch
+
+template <typename TQ, int D, int G>
+static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
+                      hipStream_t st) {
+    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(256);
+    hipLaunchKernelGGL((score_approx_kernel<TQ, D, G>), grid, block, 0, st, qv, (const bf16 *)ws.ksb, b_sum,
+                       ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
+                       ws.per_bg);
+}
+
+template <typename TQ>
+static hipError_t dispatch_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws,
+                                  float kappa, hipStream_t st) {
+#define HILS_APPROX(DD, GG)                                                  \
+    if (s.D == DD && s.G == GG) {                                            \
+        go_approx<TQ, DD, GG>(s, qv, b_sum, ws, kappa, st);                  \
+        return hipGetLastError();                                            \
+    }
+    HILS_APPROX(64, 1) HILS_APPROX(64, 2) HILS_APPROX(64, 4) HILS_APPROX(64, 8)
+    HILS_APPROX(128, 1) HILS_APPROX(128, 2) HILS_APPROX(128, 4) HILS_APPROX(128, 8)
+#undef HILS_APPROX
+    return hipErrorInvalidValue;
+}
+
+template <typename TQ, typename TS>
+static hipError_t dispatch_select(const Shape &s, const TQ *qv, const TS *ks, const float *b_sum,
+                                  const ScoreWorkspace &ws, int32_t *sel_idx, float *sel_score, hipStream_t st) {
+    const int64_t rows = (int64_t)s.B * s.H_kv * s.N;
+    const int nmax = s.N > 0 ? max(0, (s.N - 1) / s.S - s.W / s.S) : 0;
+    const int J = (nmax + WAVE - 1) / WAVE;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, qv, ks, b_sum, (const float *)ws.agg, (const float *)ws.err,
+                           sel_idx, sel_score, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.D, s.S, s.W, s.K, s.scale,
+                           ws.per_bg);
+    };
+    if (J <= 2) go(select_kernel<TQ, TS, 2>);
+    else if (J <= 8) go(select_kernel<TQ, TS, 8>);
+    else if (J <= 32) go(select_kernel<TQ, TS, 32>);
+    else if (J <= 64) go(select_kernel<TQ, TS, 64>);
+    else if (J <= 128) go(select_kernel<TQ, TS, 128>);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum, const float *b_sum, const void *h,
+                               const void *w_down, const void *w_up, int d_model, int r, int32_t *sel_idx,
+                               float *sel_score, const ScoreWorkspace &ws, hipStream_t st) {
+    if ((int64_t)s.B * s.N == 0) return hipSuccess;
+    hipError_t e;
+    // k' prep: bf16 copy + max norm per (b, landmark head)
+    const int64_t nl = (int64_t)s.B * s.H_lm;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, ws.knorm, nl);
+    const int64_t krows = (int64_t)s.B * s.H_lm * s.C;
+    if (krows > 0) {
+        const dim3 grid((unsigned)((krows + 15) / 16)), block(256);
+        if (s.sum_bf16) {
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+        } else {
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+        }
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // scoring queries
+    const bool qcal = h != nullptr;
+    if (qcal) {
+        const dim3 grid((unsigned)((s.N + 15) / 16), (unsigned)s.B), block(256);
+        const size_t lds = (size_t)16 * r * sizeof(float);
+        if (s.io_bf16)
+            hipLaunchKernelGGL(qcal_kernel<bf16>, grid, block, lds, st, (const bf16 *)q, (const bf16 *)h,
+                               (const bf16 *)w_down, (const bf16 *)w_up, ws.q_s, s.N, s.H_q, s.D, d_model, r);
+        else
+            hipLaunchKernelGGL(qcal_kernel<float>, grid, block, lds, st, (const float *)q, (const float *)h,
+                               (const float *)w_down, (const float *)w_up, ws.q_s, s.N, s.H_q, s.D, d_model, r);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+
+    // kappa: relative bound of the bf16 operand rounding (2^-8 per rounded
+    // operand, unit roundoff of an 8-bit significand), doubled for margin.
+    const bool q_rounded = qcal || !s.io_bf16;
+    const bool k_rounded = !s.sum_bf16;
+    float kappa = 1.0f / 16384.f;  // fp32 accumulation only
+    if (k_rounded) kappa += 2.f / 256.f;
+    if (q_rounded) kappa += 2.f / 256.f;
+
+    if (qcal || !s.io_bf16) {
+        const float *qv = qcal ? ws.q_s : (const float *)q;
+        if ((e = dispatch_approx<float>(s, qv, b_sum, ws, kappa, st)) != hipSuccess) return e;
+        return s.sum_bf16 ? dispatch_select<float, bf16>(s, qv, (const bf16 *)k_sum, b_sum, ws, sel_idx, sel_score, st)
+                          : dispatch_select<float, float>(s, qv, (const float *)k_sum, b_sum, ws, sel_idx, sel_score, st);
+    }
+    const bf16 *qv = (const bf16 *)q;
+    if ((e = dispatch_approx<bf16>(s, qv, b_sum, ws, kappa, st)) != hipSuccess) return e;
+    return s.sum_bf16 ? dispatch_select<bf16, bf16>(s, qv, (const bf16 *)k_sum, b_sum, ws, sel_idx, sel_score, st)
+                      : dispatch_select<bf16, float>(s, qv, (const float *)k_sum, b_sum, ws, sel_idx, sel_score, st);
+}
+
+}  // namespace hils

@@ -1,0 +1,135 @@
+// summary.hip -- kernel 1: landmark summaries (k'_c, b'_c).
+//
+// hyper.ai HiLS summary, section 方法: the landmark query q'_c of chunk c
+// induces a distribution p over the chunk's keys; the compressed key is the
+// p-weighted key sum and the bias is the entropy of p.  The logit scale of
+// that softmax is the attention scale (the reading under which the score is
+// the first-order Taylor expansion of the chunk log-mass at q'_c).
+//
+// HBM-bound: every key is read exactly once.  One wavefront owns one
+// (batch, kv head, chunk) and produces the summaries of all landmark heads
+// that read that kv head, so the S x d key tile is loaded once into
+// registers with 16-byte loads and reused GLM times.  Reductions over the
+// chunk's keys are butterfly shuffles inside the wavefront; no LDS.
+#include "hils_device.hpp"
+#include "hils_internal.hpp"
+
+namespace hils {
+
+template <typename T, typename TS, int D, int S, int GLM>
+__global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm,
+                                                               TS *__restrict__ k_sum, float *__restrict__ b_sum,
+                                                               int H_kv, int N, int C, float scale,
+                                                               int64_t total_units) {
+    constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
+    constexpr int LPR = D / E;         // lanes covering one key row
+    constexpr int RPL = WAVE / LPR;    // key rows per wave-wide load
+    constexpr int NL = S / RPL;        // loads per lane for the whole chunk
+    static_assert(WAVE % LPR == 0 && S % RPL == 0, "tile shape");
+
+    const int lane = lane_id();
+    const int64_t unit = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    if (unit >= total_units) return;
+    const int c = (int)(unit % C);
+    const int64_t bg = unit / C;  // b * H_kv + g
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int col = lane % LPR;
+    const int rsub = lane / LPR;
+
+    const T *kb = k + (bg * N + (int64_t)c * S) * D;
+    Vec16<T> kr[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) kr[t] = load16(kb + (int64_t)(t * RPL + rsub) * D + col * E);
+
+    const int H_lm = H_kv * GLM;
+    // one landmark head at a time keeps the key tile as the only large
+    // register array
+#pragma unroll 1
+    for (int e = 0; e < GLM; ++e) {
+        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;
+        const Vec16<T> qv = load16(q_lm + lrow * D + col * E);
+        float a[NL];
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < E; ++x) part = fmaf(qv.get(x), kr[t].get(x), part);
+            a[t] = xor_sum<1, LPR / 2>(part) * scale;
+            m = fmaxf(m, a[t]);
+        }
+        m = xor_max<LPR, WAVE / 2>(m);
+        float z = 0.f;
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            a[t] -= m;  // shifted logits
+            z += expf(a[t]);
+        }
+        z = xor_sum<LPR, WAVE / 2>(z);
+        const float inv_z = 1.f / z;
+        const float log_z = logf(z);
+        // entropy: -sum p log p with log p = (a - m) - log Z
+        float ent = 0.f;
+        float acc[E];
+#pragma unroll
+        for (int x = 0; x < E; ++x) acc[x] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            const float p = expf(a[t]) * inv_z;
+            ent = fmaf(p, log_z - a[t], ent);
+#pragma unroll
+            for (int x = 0; x < E; ++x) acc[x] = fmaf(p, kr[t].get(x), acc[x]);
+        }
+        ent = xor_sum<LPR, WAVE / 2>(ent);
+#pragma unroll
+        for (int x = 0; x < E; ++x) acc[x] = xor_sum<LPR, WAVE / 2>(acc[x]);
+        if (rsub == 0) {
+            TS *dst = k_sum + lrow * D + col * E;
+#pragma unroll
+            for (int x = 0; x < E; ++x) dst[x] = from_f32<TS>(acc[x]);
+            if (col == 0) b_sum[lrow] = ent;
+        }
+    }
+}
+
+template <typename T, typename TS, int D, int S>
+static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
+                           hipStream_t st) {
+    const int64_t units = (int64_t)s.B * s.H_kv * s.C;
+    if (units == 0) return hipSuccess;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const T *)k, (const T *)q_lm, (TS *)k_sum, b_sum, s.H_kv, s.N,
+                           s.C, s.scale, units);
+    };
+    switch (s.GLM) {
+        case 1: go(landmark_summary_kernel<T, TS, D, S, 1>); break;
+        case 2: go(landmark_summary_kernel<T, TS, D, S, 2>); break;
+        case 4: go(landmark_summary_kernel<T, TS, D, S, 4>); break;
+        case 8: go(landmark_summary_kernel<T, TS, D, S, 8>); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename TS>
+static hipError_t launch_t(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
+                           hipStream_t st) {
+    if (s.D == 64 && s.S == 64) return launch_s<T, TS, 64, 64>(s, k, q_lm, k_sum, b_sum, st);
+    if (s.D == 64 && s.S == 128) return launch_s<T, TS, 64, 128>(s, k, q_lm, k_sum, b_sum, st);
+    if (s.D == 128 && s.S == 64) return launch_s<T, TS, 128, 64>(s, k, q_lm, k_sum, b_sum, st);
+    if (s.D == 128 && s.S == 128) return launch_s<T, TS, 128, 128>(s, k, q_lm, k_sum, b_sum, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
+                                   hipStream_t st) {
+    if (s.io_bf16)
+        return s.sum_bf16 ? launch_t<bf16, bf16>(s, k, q_lm, k_sum, b_sum, st)
+                          : launch_t<bf16, float>(s, k, q_lm, k_sum, b_sum, st);
+    return s.sum_bf16 ? launch_t<float, bf16>(s, k, q_lm, k_sum, b_sum, st)
+                      : launch_t<float, float>(s, k, q_lm, k_sum, b_sum, st);
+}
+
+}  // namespace hils

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_chunk_landmark_amd as hils
+from long_context_chunk_landmark_amd import _binding as hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hb.LIB_PATH):
+        from long_context_chunk_landmark_amd import build
+
+        build.build()
+    return hb.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hils_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(hb.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", hb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (hils_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert hils.version() == 10000
+
+
+def _cfg(**kw):
+    c = dict(H_q=8, H_kv=2, d=128, S=64, W=256, K=16, B=1, N=4096)
+    c.update(kw)
+    return hb.Config(**c).to_c()
+
+
+A = ctypes.c_void_p(0x10000)      # aligned stand-in pointers: validation never dereferences
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10001)    # misaligned
+
+
+def _summ(lib, cfg, k=A, q_lm=A, ks=A, bs=A):
+    return lib.hils_landmark_summarize(ctypes.byref(cfg) if cfg is not None else None, k, q_lm, ks, bs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), hb.HILS_ERR_UNSUPPORTED),
+    (dict(S=32), hb.HILS_ERR_UNSUPPORTED),
+    (dict(H_q=6, H_kv=4), hb.HILS_ERR_INVALID_ARG),
+    (dict(H_q=16, H_kv=1), hb.HILS_ERR_UNSUPPORTED),
+    (dict(W=100), hb.HILS_ERR_INVALID_ARG),
+    (dict(K=129), hb.HILS_ERR_UNSUPPORTED),
+    (dict(K=-1), hb.HILS_ERR_INVALID_ARG),
+    (dict(H_lm=3), hb.HILS_ERR_INVALID_ARG),
+    (dict(N=-5), hb.HILS_ERR_INVALID_ARG),
+    (dict(N=64 * 8193), hb.HILS_ERR_UNSUPPORTED),
+])
+def test_bad_config_is_rejected(lib, kw, status):
+    cfg = _cfg(**kw)
+    assert _summ(lib, cfg) == status
+    assert hb.last_error()
+
+
+def test_null_config_and_pointers(lib):
+    assert _summ(lib, None) == hb.HILS_ERR_INVALID_ARG
+    cfg = _cfg()
+    assert _summ(lib, cfg, k=None) == hb.HILS_ERR_INVALID_ARG
+    assert "k is NULL" in hb.last_error()
+    assert _summ(lib, cfg, q_lm=MIS) == hb.HILS_ERR_INVALID_ARG
+    assert "aligned" in hb.last_error()
+
+
+def test_bad_dtype_code(lib):
+    cfg = _cfg()
+    cfg.io_dtype = 7
+    assert _summ(lib, cfg) == hb.HILS_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_ok_without_pointers(lib):
+    cfg = _cfg(N=0)
+    assert lib.hils_landmark_summarize(ctypes.byref(cfg), None, None, None, None, None) == hb.HILS_OK
+    assert lib.hils_score_select(ctypes.byref(cfg), None, None, None, None, None, None, 0, 0, None, None, None, 0,
+                                 None) == hb.HILS_OK
+    assert lib.hils_sparse_attend_fused(ctypes.byref(cfg), None, None, None, None, None, None, None, None, 0,
+                                        None) == hb.HILS_OK
+    assert lib.hils_decode(ctypes.byref(cfg), 0, None, None, None, None, None, None, 1, None, None, None, None, 0, 0,
+                           None, None, None, None, 0, None) == hb.HILS_OK
+
+
+def test_workspace_is_checked(lib):
+    cfg = _cfg()
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_SCORE, 0, 0)
+    assert need > 0
+    st = lib.hils_score_select(ctypes.byref(cfg), A, A, A, None, None, None, 0, 0, A, A, A2, need - 1, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+    st = lib.hils_score_select(ctypes.byref(cfg), A, A, A, None, None, None, 0, 0, A, A, None, 0, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+    need_f = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
+    st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need_f - 16, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+    need_d = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DECODE, 4, 100)
+    st = lib.hils_decode(ctypes.byref(cfg), 4, A, A, A, A, A, A, 100, A, None, None, None, 0, 0, A, None, None, A2,
+                         need_d - 1, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+
+
+def test_workspace_sizes_scale_with_problem(lib):
+    small, big = _cfg(N=4096), _cfg(N=8192)
+    for which in (hb.WS_SCORE, hb.WS_SCORE_QCAL, hb.WS_FUSED):
+        a = lib.hils_workspace_size(ctypes.byref(small), which, 0, 0)
+        b = lib.hils_workspace_size(ctypes.byref(big), which, 0, 0)
+        assert 0 < a < b
+    qc = lib.hils_workspace_size(ctypes.byref(small), hb.WS_SCORE_QCAL, 0, 0)
+    assert qc > lib.hils_workspace_size(ctypes.byref(small), hb.WS_SCORE, 0, 0)
+    f32 = _cfg()
+    f32.io_dtype = hb.HILS_F32
+    assert lib.hils_workspace_size(ctypes.byref(f32), hb.WS_FUSED, 0, 0) == 0
+    assert lib.hils_workspace_size(ctypes.byref(_cfg(d=96)), hb.WS_SCORE, 0, 0) == 0
+    assert "d=96" in hb.last_error()
+
+
+def test_qcal_arguments_are_checked(lib):
+    cfg = _cfg()
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_SCORE_QCAL, 0, 0)
+    st = lib.hils_score_select(ctypes.byref(cfg), A, A, A, A, None, A, 256, 16, A, A, A2, need, None)
+    assert st == hb.HILS_ERR_INVALID_ARG and "w_down" in hb.last_error()
+    st = lib.hils_score_select(ctypes.byref(cfg), A, A, A, A, A, A, 256, 65, A, A, A2, need, None)
+    assert st == hb.HILS_ERR_UNSUPPORTED
+
+
+def test_decode_argument_checks(lib):
+    cfg = _cfg()
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DECODE, 2, 10)
+    st = lib.hils_decode(ctypes.byref(cfg), 2, A, A, A, A, A, A, 0, A, None, None, None, 0, 0, A, None, None, A2,
+                         need, None)
+    assert st == hb.HILS_ERR_INVALID_ARG
+    st = lib.hils_decode(ctypes.byref(cfg), 2, A, A, A, A, A, None, 10, A, None, None, None, 0, 0, A, None, None, A2,
+                         need, None)
+    assert st == hb.HILS_ERR_INVALID_ARG and "block_table" in hb.last_error()
+    st = lib.hils_decode(ctypes.byref(cfg), 2, A, A, A, A, A, A, 70000, A, None, None, None, 0, 0, A, None, None, A2,
+                         need, None)
+    assert st == hb.HILS_ERR_UNSUPPORTED
