@@ -24,6 +24,12 @@
 //     accumulators).  V^T comes from a pre-pass that writes each chunk as
 //     [d][key] with keys of every 32-key group stored in the order the S^T
 //     accumulator layout delivers them, so P^T needs no cross-lane moves.
+//   * Q K^T runs on bf16 operands (exact products of the bf16 inputs).  The
+//     probabilities P lie in [0, 1]; they are rounded to fp16 (11-bit
+//     significand, 8x finer than bf16) and V^T is stored as fp16 (exact for
+//     bf16 values of magnitude below 65504), so V^T P^T runs on fp16 MFMA:
+//     bf16 rounding of P alone can miss a 2e-3 absolute bound on rows with
+//     few keys whose values cancel.
 //   * Selected chunk c of a row: exact softmax over its S keys, scaled by
 //     exp(s^_c - m^) where m^ = max of the row's selected s^ (known up
 //     front); the accumulator then starts the window's online softmax with
@@ -43,9 +49,9 @@ __host__ __device__ __forceinline__ int vt_slot_key(int p) {
     return 32 * s + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
 }
 
-// vt[b, g, c, d, slot] = v[b, g, c*S + vt_slot_key(slot), d] (0 past N).
+// vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]) (0 past N).
 template <int D, int S>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, bf16 *__restrict__ vt, int N,
+__global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int N,
                                                           int CA, int H_kv) {
     __shared__ bf16 tile[S][D + 8];
     const int c = blockIdx.x;
@@ -61,13 +67,13 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
         for (int e = 0; e < 8; ++e) tile[j][cb * 8 + e] = x[e];
     }
     __syncthreads();
-    bf16 *dst = vt + (bg * CA + c) * (int64_t)D * S;
+    f16 *dst = vt + (bg * CA + c) * (int64_t)D * S;
     for (int idx = threadIdx.x; idx < D * (S / 8); idx += blockDim.x) {
         const int d = idx / (S / 8), blk = idx % (S / 8);
-        bf16x8 x;
+        f16x8 x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = tile[vt_slot_key(blk * 8 + e)][d];
-        *(bf16x8 *)(dst + (int64_t)d * S + blk * 8) = x;
+        for (int e = 0; e < 8; ++e) x[e] = (f16)(float)tile[vt_slot_key(blk * 8 + e)][d];
+        *(f16x8 *)(dst + (int64_t)d * S + blk * 8) = x;
     }
 }
 
@@ -91,7 +97,7 @@ struct AttendCfg {
 //   int   scan[8]          wave totals of the prefix scan
 template <int D, int S, int G, int TPW>
 __global__ __launch_bounds__(256) void sparse_attend_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ vt,
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, bf16 *__restrict__ out,
     float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP) {
     using Cf = AttendCfg<D, S, G, TPW>;
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
     }
 
     const bf16 *kbase = k + bg * (int64_t)N * D;
-    const bf16 *vtbase = vt + bg * (int64_t)CA * D * S;
+    const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
 
     auto stage = [&](int c) {
         __syncthreads();
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
             if ((int64_t)c * S + row < N) val = *(const u32x4 *)(ks + (int64_t)row * D + cb * 8);
             k_lds[row][cb ^ (row & 7)] = val;
         }
-        const bf16 *vs = vtbase + (int64_t)c * D * S;
+        const f16 *vs = vtbase + (int64_t)c * D * S;
         for (int idx = tid; idx < D * NBV; idx += blockDim.x) {
             const int row = idx / NBV, cb = idx % NBV;
             v_lds[row][cb ^ (row & 7)] = *(const u32x4 *)(vs + (int64_t)row * S + cb * 8);
@@ -239,19 +245,19 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
     auto pv = [&](const f32x4 (&p)[KT], f32x4 (&o)[DT]) {
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps) {
-            bf16x8 bp;
+            f16x8 bp;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bp[i] = (bf16)p[2 * ps][i];
-                bp[4 + i] = (bf16)p[2 * ps + 1][i];
+                bp[i] = (f16)p[2 * ps][i];
+                bp[4 + i] = (f16)p[2 * ps + 1][i];
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int row = 16 * dt + r;
                 const u32x4 raw = v_lds[row][(4 * ps + grp) ^ (row & 7)];
-                bf16x8 a;
+                f16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
-                o[dt] = mfma16(a, bp, o[dt]);
+                o[dt] = mfma16h(a, bp, o[dt]);
             }
         }
     };
@@ -492,7 +498,7 @@ static hipError_t go_attend(const Shape &s, const void *q, const void *k, const 
     // static K/V tiles plus this dynamic part may exceed 64 KB at S = 128
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, sel_idx,
+    hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
                        sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP);
     return hipGetLastError();
 }
@@ -524,8 +530,8 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
                                s.W, s.K, s.scale);
         return hipGetLastError();
     }
-    // V^T pre-pass into the workspace
-    bf16 *vt = (bf16 *)workspace;
+    // V^T pre-pass into the workspace (fp16)
+    f16 *vt = (f16 *)workspace;
     {
         const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
         if (s.D == 64 && s.S == 64) hipLaunchKernelGGL((v_transpose_kernel<64, 64>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);

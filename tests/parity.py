@@ -29,7 +29,8 @@ def assert_close(got, ref, atol, rtol, what=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    bad = ~(np.abs(got - ref) <= atol + rtol * np.abs(ref))
+    with np.errstate(invalid="ignore"):
+        bad = ~(np.abs(got - ref) <= atol + rtol * np.abs(ref))
     # identical infinities (e.g. -inf padding) are equal
     both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
     bad &= ~both_inf
@@ -55,8 +56,9 @@ def check_selection(gpu_sel, ora_sel, ora_kth, agg_of_row, K):
         valid = arr >= 0
         n = valid.sum(-1)
         assert np.all(valid == (np.arange(K)[None, None, None, :] < n[..., None])), f"{name} selection padding"
-        d = np.diff(np.where(valid, arr, np.iinfo(np.int32).max), axis=-1)
-        assert np.all(d > 0), f"{name} selection not strictly ascending"
+        d = np.diff(arr, axis=-1)
+        both = valid[..., 1:] & valid[..., :-1]
+        assert np.all(d[both] > 0), f"{name} selection not strictly ascending"
     exempt = []
     diff_rows = np.argwhere(np.any(gpu_sel != ora_sel, axis=-1))
     for b, g, r in diff_rows:
@@ -89,17 +91,26 @@ def stratified_rows(N, S, W, count, seed):
 
 
 def oracle_prefill(cfg, inputs, rows=None, k_sum=None, b_sum=None, given_sel=None, want_agg=False):
-    """Run the oracle on a prefill workload's host copies."""
+    """Run the oracle on a prefill workload's host copies.
+
+    When the configuration stores summaries in bf16, the oracle scores from
+    its summaries as stored (fp64 values rounded to bf16), like the decode
+    step reads its cache; res["k_sum_exact"] keeps the unrounded values."""
     oc = cfg.oracle_dict()
     q, k, v, q_lm = (host(inputs[n]) for n in ("q", "k", "v", "q_lm"))
+    exact = None
     if k_sum is None:
         k_sum, b_sum = oracle.summarize(oc, k, q_lm)
+        exact = k_sum
+        if cfg.summary_dtype == torch.bfloat16:
+            k_sum = round_to(k_sum, torch.bfloat16).to(torch.float64).numpy()
     qcal = None
     if inputs.get("qcal") is not None:
         qcal = tuple(host(x) for x in inputs["qcal"])
     res = oracle.forward_rows(oc, q, k, v, k_sum, b_sum, rows=rows, qcal=qcal, given_sel=given_sel,
                               want_agg=want_agg)
     res["k_sum"], res["b_sum"] = k_sum, b_sum
+    res["k_sum_exact"] = exact if exact is not None else k_sum
     return res
 
 

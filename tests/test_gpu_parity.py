@@ -75,9 +75,9 @@ def test_summary_matches_oracle(name, dev):
     ref = _oracle_full(name, dev)
     if cfg.summary_dtype == BF:
         # bf16 storage: within one bf16 rounding of the exact value
-        assert_close(host(k_sum).float().numpy(), ref["k_sum"], 1e-5, 2 ** -8, "k_sum")
+        assert_close(host(k_sum).float().numpy(), ref["k_sum_exact"], 1e-5, 2 ** -8, "k_sum")
     else:
-        assert_close(host(k_sum).numpy(), ref["k_sum"], 1e-5, 1e-5, "k_sum")
+        assert_close(host(k_sum).numpy(), ref["k_sum_exact"], 1e-5, 1e-5, "k_sum")
     assert_close(host(b_sum).numpy(), ref["b_sum"], 1e-5, 1e-5, "b_sum")
 
 
@@ -89,7 +89,7 @@ def test_score_select_stage(name, dev):
     cfg = inp["cfg"]
     print(f"[score_select] {name}", flush=True)
     ref0 = _oracle_full(name, dev)
-    ks_t = round_to(ref0["k_sum"], cfg.summary_dtype)
+    ks_t = round_to(ref0["k_sum_exact"], cfg.summary_dtype)
     bs_t = round_to(ref0["b_sum"], F32)
     ks64 = ks_t.to(torch.float64).numpy()
     bs64 = bs_t.to(torch.float64).numpy()
@@ -104,7 +104,7 @@ def test_score_select_stage(name, dev):
     for b, g, r in exempt:
         mask[b, g * G:(g + 1) * G, r, :] = False
     assert_close(np.where(mask, ss_h, 0), np.where(mask, ref["sel_score"], 0), 2e-5, 1e-5, "sel_score")
-    assert len(exempt) <= max(2, ref["sel_idx"].size // cfg.K // 200), f"{len(exempt)} near-tie rows"
+    assert len(exempt) <= max(2, ref["sel_idx"].size // max(1, cfg.K) // 200), f"{len(exempt)} near-tie rows"
 
 
 @pytest.mark.parametrize("name", list(CASES))
