@@ -1,0 +1,325 @@
+#!/usr/bin/env python
+"""Benchmark of the HiLS attention forward hot path on one MI355X.
+
+One step = one prefill pass over the 128K-token workload (landmark summary ->
+score/select -> fused sparse attention, inputs resident in HBM), timed with
+HIP events on the stream the kernels run on.  The same run times one decode
+step over the 512K-token paged-cache workload (16 sequences) and the fp64
+CPU oracle on a bounded sample of the prefill workload.  Prints one JSON
+line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 MFMA
+METRIC = "HiLS prefill tokens/s @128K + decode μs/step @512K; % MFMA/HBM peak"
+CSRC = os.path.join(ROOT, "long_context_chunk_landmark_amd", "csrc")
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def _chunks(cfg):
+    """Per query chunk: (first query, #queries, #candidates, #selected)."""
+    S, w = cfg.S, cfg.W // cfg.S
+    out = []
+    for qc in range((cfg.N + S - 1) // S):
+        n_q = min(S, cfg.N - qc * S)
+        n_c = max(0, qc - w)
+        out.append((qc * S, n_q, n_c, min(cfg.K, n_c)))
+    return out
+
+
+def attend_flops(cfg):
+    """4 d H_q sum_i (selected keys + window keys): QK^T and PV, 2 flops/MAC."""
+    S = cfg.S
+    keys = 0
+    for i0, n_q, n_c, k in _chunks(cfg):
+        ws = max(0, i0 - cfg.W)
+        # window of query i: keys [ws, i]; sum over the chunk's queries
+        win = n_q * (i0 - ws) + n_q * (n_q + 1) // 2
+        keys += n_q * k * S + win
+    return 4.0 * cfg.d * cfg.H_q * keys * cfg.B
+
+
+def score_flops(cfg):
+    return 2.0 * cfg.d * cfg.H_q * cfg.B * sum(n_q * n_c for _, n_q, n_c, _ in _chunks(cfg))
+
+
+def summary_bytes(cfg, io_bytes, sum_bytes):
+    C = cfg.N // cfg.S
+    return cfg.B * (cfg.H_kv * C * cfg.S * cfg.d * io_bytes + cfg.H_lm * C * cfg.d * io_bytes +
+                    cfg.H_lm * C * cfg.d * sum_bytes + cfg.H_lm * C * 4)
+
+
+def decode_bytes(cfg, seq_lens, io_bytes, sum_bytes):
+    """Summaries of every candidate + K/V of the selected chunks and window
+    tokens + block-table entries + q and out."""
+    S, w = cfg.S, cfg.W // cfg.S
+    total = 0
+    for L in seq_lens:
+        t = L - 1
+        n_c = max(0, t // S - w)
+        k = min(cfg.K, n_c)
+        win = t - max(0, (t // S) * S - cfg.W) + 1
+        total += cfg.H_lm * n_c * (cfg.d * sum_bytes + 4)
+        total += cfg.H_kv * (k * S + win) * cfg.d * io_bytes * 2
+        total += ((t // S) + 1) * 4
+        total += 2 * cfg.H_q * cfg.d * io_bytes
+    return total
+
+
+# ---------------------------------------------------------------- rocprof counters
+
+def _source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, workload, sources):
+    """HBM bytes per launch from the committed counter summary, or None when
+    missing or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_file}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_sha:\s*(\w+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != _source_sha(sources):
+        return None
+    return float(b.group(1))
+
+
+# ---------------------------------------------------------------- timing
+
+def _timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        evs.append(fn())
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = {}
+    for step_evs in evs:
+        for name, (a, b) in step_evs.items():
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    return total_ms, {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def bench_prefill(args, torch, hb, W):
+    dev = torch.device("cuda:0")
+    inp = W.make_prefill(args.workload, device=dev)
+    cfg = inp["cfg"]
+    qcal = inp.get("qcal")
+    q, k, v, q_lm = inp["q"], inp["k"], inp["v"], inp["q_lm"]
+    C = cfg.C
+    k_sum = torch.empty((cfg.B, cfg.H_lm, C, cfg.d), dtype=cfg.summary_dtype, device=dev)
+    b_sum = torch.empty((cfg.B, cfg.H_lm, C), dtype=torch.float32, device=dev)
+    sel = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.K), dtype=torch.int32, device=dev)
+    ss = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.K), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H_q, cfg.N), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(hb.workspace_size(cfg, hb.WS_SCORE_QCAL if qcal else hb.WS_SCORE), dtype=torch.uint8,
+                       device=dev)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step():
+        e = [E() for _ in range(4)]
+        e[0].record()
+        hb.landmark_summarize(cfg, k, q_lm, k_sum, b_sum)
+        e[1].record()
+        hb.score_select(cfg, q, k_sum, b_sum, qcal=qcal, sel_idx=sel, sel_score=ss, workspace=ws_s)
+        e[2].record()
+        hb.sparse_attend_fused(cfg, q, k, v, sel, ss, out=out, lse=lse)
+        e[3].record()
+        return {"summary": (e[0], e[1]), "score_select": (e[1], e[2]), "fused": (e[2], e[3])}
+
+    total_ms, per = _timed(step, args.steps, args.warmup, torch)
+    res = dict(cfg=cfg, inp=inp, ms_per_step=total_ms / args.steps, per_call_ms=per, sel=sel)
+    return res
+
+
+def bench_decode(args, torch, hb, W):
+    dev = torch.device("cuda:0")
+    inp = W.make_decode(args.decode_workload, device=dev)
+    cfg = inp["cfg"]
+    B = inp["q"].shape[0]
+    out = torch.empty((B, cfg.H_q, cfg.d), dtype=cfg.io_dtype, device=dev)
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, cfg.H_kv, cfg.K), dtype=torch.int32, device=dev)
+    max_pages = inp["block_table"].shape[1]
+    ws = torch.empty(hb.workspace_size(cfg, hb.WS_DECODE, B, max_pages), dtype=torch.uint8, device=dev)
+
+    def step():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        hb.decode(cfg, inp["q"], inp["k_cache"], inp["v_cache"], inp["ksum_cache"], inp["bsum_cache"],
+                  inp["block_table"], inp["seq_lens"], out=out, lse=lse, sel_idx=sel, workspace=ws)
+        e1.record()
+        return {"decode": (e0, e1)}
+
+    total_ms, per = _timed(step, args.steps, args.warmup, torch)
+    seq_lens = inp["seq_lens"].cpu().tolist()
+    return dict(cfg=cfg, us_per_step=1000.0 * total_ms / args.steps, call_us=1000.0 * per["decode"],
+                seq_lens=seq_lens)
+
+
+def union_overlap(sel, M, sample=4096, seed=0):
+    """Mean |union of the selections of M adjacent queries| / K over a sample
+    of groups (1 = identical selections, M = disjoint)."""
+    import numpy as np
+
+    s = sel[0].cpu().numpy()  # [H_kv, N, K]
+    H_kv, N, K = s.shape
+    rng = np.random.default_rng(seed)
+    vals = []
+    for _ in range(sample):
+        g = int(rng.integers(H_kv))
+        i0 = int(rng.integers(N // M)) * M
+        blk = s[g, i0:i0 + M]
+        if (blk[:, 0] < 0).any() or (blk[:, -1] < 0).any():
+            continue
+        vals.append(len(np.unique(blk)) / K)
+    return float(np.mean(vals)) if vals else None
+
+
+def cpu_baseline(pre, budget_s):
+    """The fp64 oracle on the host cores: summaries of every chunk plus a
+    seeded stratified sample of query rows, extrapolated to tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    cfg = pre["cfg"]
+    inp = pre["inp"]
+    oc = cfg.oracle_dict()
+    q, k, v, q_lm = (inp[n].detach().to("cpu", dtype=__import__("torch").float32).numpy() for n in
+                     ("q", "k", "v", "q_lm"))
+    t0 = time.perf_counter()
+    ks, bs = oracle.summarize(oc, k, q_lm)
+    t_sum = time.perf_counter() - t0
+    rng = np.random.default_rng(11)
+    probe = np.sort(rng.choice(cfg.N, size=32, replace=False))
+    t0 = time.perf_counter()
+    oracle.forward_rows(oc, q, k, v, ks, bs, rows=probe)
+    t_probe = time.perf_counter() - t0
+    R = int(max(32, min(4096, 32 * max(0.0, budget_s - t_sum - t_probe) / max(t_probe, 1e-6))))
+    rows = np.sort(rng.choice(cfg.N, size=R, replace=False))
+    t0 = time.perf_counter()
+    oracle.forward_rows(oc, q, k, v, ks, bs, rows=rows)
+    t_rows = time.perf_counter() - t0
+    per_row = t_rows / R
+    total = t_sum + cfg.N * per_row
+    return {"value": cfg.N / total, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle: summaries of all {cfg.N // cfg.S} chunks x {cfg.H_lm} landmark heads "
+                      f"({t_sum:.2f} s) + {R} uniformly sampled query rows, all {cfg.H_q} heads "
+                      f"({t_rows:.2f} s); tokens/s extrapolated to {cfg.N} rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--decode-workload", default="decode_512k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_chunk_landmark_amd import _binding as hb
+    from long_context_chunk_landmark_amd import workloads as W
+
+    hb.load_library()
+    print(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    pre = bench_prefill(args, torch, hb, W)
+    cfg = pre["cfg"]
+    io_b = 2 if cfg.io_dtype == torch.bfloat16 else 4
+    sum_b = 2 if cfg.summary_dtype == torch.bfloat16 else 4
+    fl_att = attend_flops(cfg)
+    fl_score = score_flops(cfg)
+    by_sum = summary_bytes(cfg, io_b, sum_b)
+    ms_f = pre["per_call_ms"]["fused"]
+    ms_s = pre["per_call_ms"]["score_select"]
+    ms_m = pre["per_call_ms"]["summary"]
+    achieved = fl_att / (ms_f * 1e-3) / 1e12
+    traffic = traffic_from_profile("sparse_attend", args.workload, ["attend.hip", "hils_device.hpp"])
+    result = {
+        "metric": METRIC,
+        "value": cfg.N * cfg.B / (pre["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.io_dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": cfg.B, "N": cfg.N, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
+                   "H_lm": cfg.H_lm, "d": cfg.d, "S": cfg.S, "W": cfg.W, "K": cfg.K, "M": cfg.M,
+                   "summary_dtype": "bf16" if sum_b == 2 else "f32"},
+        "roofline": {"kernel": "sparse_attend_kernel (hils_sparse_attend_fused)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "algorithmic_tflop_per_launch": fl_att / 1e12},
+        "kernels": {
+            "summary": {"ms": ms_m, "bound": "hbm", "gbs": by_sum / (ms_m * 1e-3) / 1e9,
+                        "frac": by_sum / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by_sum},
+            "score_select": {"ms": ms_s, "bound": "mfma", "tflops": fl_score / (ms_s * 1e-3) / 1e12,
+                             "frac": fl_score / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl_score},
+            "fused": {"ms": ms_f, "tflops": achieved, "flops": fl_att},
+        },
+        "union_overlap_M": union_overlap(pre["sel"], cfg.M),
+    }
+    if not args.no_decode:
+        print(f"[bench] decode {args.decode_workload}", file=sys.stderr, flush=True)
+        dec = bench_decode(args, torch, hb, W)
+        dcfg = dec["cfg"]
+        dio = 2 if dcfg.io_dtype == torch.bfloat16 else 4
+        dsum = 2 if dcfg.summary_dtype == torch.bfloat16 else 4
+        by = decode_bytes(dcfg, dec["seq_lens"], dio, dsum)
+        gbs = by / (dec["call_us"] * 1e-6) / 1e9
+        result["decode"] = {"workload": args.decode_workload, "us_per_step": dec["us_per_step"],
+                            "num_seqs": len(dec["seq_lens"]), "seq_len": dec["seq_lens"][0],
+                            "roofline": {"kernel": "hils_decode (all phases)", "bound": "hbm", "achieved": gbs,
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                         "algorithmic_bytes": by}}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,7 +140,10 @@ hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const v
  *   q [B,H_q,N,d], k, v [B,H_kv,N,d] io_dtype; sel_idx / sel_score as
  *   written by hils_score_select; out [B,H_q,N,d] io_dtype (written);
  *   lse [B,H_q,N] fp32 (written, may be NULL).
- *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes. */
+ *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes (a
+ *   transposed fp16 copy of v; 0 for fp32 I/O).  bf16 path: values of v
+ *   must have magnitude below 65504 (v enters the probability-weighted sum
+ *   as fp16). */
 hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, const void *k, const void *v,
                                        const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
                                        void *workspace, size_t workspace_bytes, hipStream_t stream);

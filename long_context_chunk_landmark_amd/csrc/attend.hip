@@ -5,38 +5,52 @@
 // window; the per-chunk outputs are fused with weights exp(s^_c) / Z^ where
 // Z^ = sum_c exp(s^_c) + Z_swa (partition estimate and the hierarchical
 // factorisation of the attention weight).  Same page, kernel paragraph:
-// M adjacent queries x G heads of a GQA group share one pass over the union
-// of their selected chunks, so a loaded K/V chunk serves many rows.
+// adjacent queries x the G heads of a GQA group share one pass over the
+// union of their selected chunks, so a loaded K/V chunk serves many rows.
 //
 // MI355X design (bf16 path):
 //   * A block owns QB consecutive queries of one query chunk x the G heads
-//     of one kv group; 16-row MFMA tiles hold 16/G queries x G heads, each
-//     wave owns TPW tiles.  Every query of the block shares the candidate
-//     set and the window, so one staged K/V chunk tile in LDS serves all
-//     tiles that need it.
+//     of one kv group (up to 16 waves x one MFMA tile of 16 rows; 16/G
+//     queries x G heads per tile; QB = 64 for G = 4).  The queries share the candidate
+//     set and the window, so one staged K/V chunk serves every tile that
+//     needs it.  On the measured workload the union of 64 adjacent queries'
+//     selections is ~5.6 chunks per query instead of 32 for separate
+//     queries: the gather traffic, not the MFMA work, bounds this kernel.
 //   * The block builds the ascending union of its queries' selections
-//     (bitmap + prefix scan in LDS) and walks it; each row keeps a cursor
-//     into its own ascending selection list, so a row only takes the chunks
-//     it selected (the union is a schedule, the result is per query).
+//     (bitmap + prefix scan in LDS) and walks it, then the window chunks.
+//     Every row keeps its next selected chunk and score in registers, so a
+//     row only takes the chunks it selected (the union is a schedule; the
+//     result is per query).  A tile with no selecting row skips the chunk.
+//   * K and V^T chunk tiles are copied global -> LDS by global_load_lds
+//     (16 bytes per lane, no register staging) into a ring of NSTAGE
+//     buffers, issued NSTAGE-1 chunks ahead; each chunk waits only for its
+//     own loads (vmcnt) and one barrier.  A 16-byte-block XOR swizzle by
+//     row (applied through the per-lane source address, since the DMA
+//     writes lane-contiguous LDS) keeps the MFMA operand reads free of
+//     bank conflicts.
 //   * Transposed products keep every per-row quantity in lane l%16:
-//     S^T = K Q^T (A = K tile from LDS, B = Q^T in registers) and
-//     O^T += V^T P^T (A = V^T tile, B = P^T packed straight from the S^T
-//     accumulators).  V^T comes from a pre-pass that writes each chunk as
-//     [d][key] with keys of every 32-key group stored in the order the S^T
-//     accumulator layout delivers them, so P^T needs no cross-lane moves.
-//   * Q K^T runs on bf16 operands (exact products of the bf16 inputs).  The
-//     probabilities P lie in [0, 1]; they are rounded to fp16 (11-bit
-//     significand, 8x finer than bf16) and V^T is stored as fp16 (exact for
-//     bf16 values of magnitude below 65504), so V^T P^T runs on fp16 MFMA:
-//     bf16 rounding of P alone can miss a 2e-3 absolute bound on rows with
-//     few keys whose values cancel.
+//     S^T = K Q^T (A = K tile, B = Q^T in registers) and O^T += V^T P^T
+//     (A = V^T tile, B = P^T packed straight from the S^T accumulators).  A
+//     pre-pass writes V^T per chunk as fp16 [d][slot] with the keys of each
+//     32-key group in the order the S^T accumulators deliver them.
+//   * Q K^T runs on bf16 operands (exact products of the bf16 inputs).  P
+//     lies in [0, 1] and is rounded to fp16 (8x finer than bf16), V^T is
+//     fp16 (exact for bf16 values below 65504), so V^T P^T runs on fp16
+//     MFMA: bf16 rounding of P alone can miss a 2e-3 absolute bound on rows
+//     with few keys whose values cancel.
 //   * Selected chunk c of a row: exact softmax over its S keys, scaled by
 //     exp(s^_c - m^) where m^ = max of the row's selected s^ (known up
-//     front); the accumulator then starts the window's online softmax with
-//     running max m^ and running mass sum_c exp(s^_c - m^).  All exps are
-//     exp2 with log2(e) folded into the scales.
+//     front); the window then continues as an online softmax from running
+//     max m^ and running mass sum_c exp(s^_c - m^).  exp2 throughout with
+//     log2(e) folded into the scales.
+//   * Blocks are mapped XCD-aware: the 8 XCDs each walk a contiguous range
+//     of (batch, group, query block) work items, so the blocks resident on
+//     one XCD's L2 are neighbouring query blocks whose unions overlap.
 #include "hils_device.hpp"
 #include "hils_internal.hpp"
+
+#define HILS_GPTR(p) ((const void __attribute__((address_space(1))) *)(p))
+#define HILS_LPTR(p) ((void __attribute__((address_space(3))) *)(p))
 
 namespace hils {
 
@@ -49,7 +63,7 @@ __host__ __device__ __forceinline__ int vt_slot_key(int p) {
     return 32 * s + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
 }
 
-// vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]) (0 past N).
+// vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]), 0 past N.
 template <int D, int S>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int N,
                                                           int CA, int H_kv) {
@@ -60,7 +74,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
     for (int idx = threadIdx.x; idx < S * (D / 8); idx += blockDim.x) {
         const int j = idx / (D / 8), cb = idx % (D / 8);
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (c * S + j < N) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
+        if ((int64_t)c * S + j < N) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
         bf16x8 x;
         __builtin_memcpy(&x, &val, 16);
 #pragma unroll
@@ -77,70 +91,75 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
     }
 }
 
-template <int D, int S, int G, int TPW>
+// s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
 struct AttendCfg {
-    static constexpr int QPT = 16 / G;          // queries per 16-row tile
-    static constexpr int QB = 4 * TPW * QPT;    // queries per block
-    static constexpr int KS = D / 32;           // k-steps of Q K^T
-    static constexpr int KT = S / 16;           // 16-key tiles per chunk
-    static constexpr int PS = S / 32;           // k-steps of V^T P^T
-    static constexpr int DT = D / 16;           // 16-dim tiles of O^T
-    static constexpr int NBK = D / 8;           // 16-byte blocks per K row
-    static constexpr int NBV = S / 8;           // 16-byte blocks per V^T row
+    static constexpr int QPT = 16 / G;               // queries per 16-row tile
+    static constexpr int QB = NWAVE * TPW * QPT;     // queries per block
+    static constexpr int KS = D / 32;                // k-steps of Q K^T
+    static constexpr int KT = S / 16;                // 16-key tiles per chunk
+    static constexpr int PS = S / 32;                // k-steps of V^T P^T
+    static constexpr int DT = D / 16;                // 16-dim tiles of O^T
+    static constexpr int NBK = D / 8;                // 16-byte blocks per K row
+    static constexpr int NBV = S / 8;                // 16-byte blocks per V^T row
+    static constexpr int PK = S * D * 2 / 1024;      // 1 KB pieces of a K tile
+    static constexpr int PV = D * S * 2 / 1024;      // 1 KB pieces of a V^T tile
+    static constexpr int LPS = (PK + PV) / NWAVE;    // DMA loads per lane per chunk
+    static_assert((PK + PV) % NWAVE == 0, "pieces per wave");
+    static_assert(NBK >= 8 && NBV >= 8, "swizzle needs 8 blocks per row");
 };
 
-// Dynamic LDS layout after the static K/V tiles:
-//   int   sel[QB*K]        selections of the block's queries
-//   float sc[QB*G*K]       their s^ (log2 units), per head
-//   uint  bitmap[NW]       union bitmap over candidate chunks
-//   int   ulist[UCAP]      ascending union
-//   int   scan[8]          wave totals of the prefix scan
-template <int D, int S, int G, int TPW>
-__global__ __launch_bounds__(256) void sparse_attend_kernel(
+// Dynamic LDS: uint bitmap[NW]; int ulist[UCAP]; int scan[16].
+template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
+__global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, bf16 *__restrict__ out,
-    float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP) {
-    using Cf = AttendCfg<D, S, G, TPW>;
+    float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP,
+    int nqb, int64_t n_items, int64_t per_xcd) {
+    using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
-    constexpr int NBK = Cf::NBK, NBV = Cf::NBV;
-    __shared__ u32x4 k_lds[S][NBK];
-    __shared__ u32x4 v_lds[D][NBV];
+    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS;
+    constexpr int NT = NWAVE * 64;
+    __shared__ u32x4 k_st[NSTAGE][S][NBK];
+    __shared__ u32x4 v_st[NSTAGE][D][NBV];
     extern __shared__ int dyn[];
-    int *sel_l = dyn;
-    float *sc_l = (float *)(sel_l + QB * K);
-    uint32_t *bitmap = (uint32_t *)(sc_l + QB * G * K);
+    uint32_t *bitmap = (uint32_t *)dyn;
     int *ulist = (int *)(bitmap + NW);
     int *scan = ulist + UCAP;
 
-    const int g = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int i0 = blockIdx.x * QB;
+    // ---- XCD-aware work item: consecutive blocks on one XCD take
+    // consecutive (b, g, query block) items
+    const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= n_items) return;
+    const int qb = (int)(item % nqb);
+    const int64_t bg = item / nqb;
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int i0 = qb * QB;
     const int qc = i0 / S;
     const int n = max(0, qc - W / S);
     const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4;
-    const int64_t bg = b * H_kv + g;
 
-    // ---- selections of the block's queries
-    for (int t = tid; t < QB * K; t += blockDim.x) {
-        const int m = t / K, kk = t % K, iq = i0 + m;
-        sel_l[t] = iq < N ? sel_idx[(bg * N + iq) * K + kk] : -1;
-    }
-    for (int t = tid; t < QB * G * K; t += blockDim.x) {
-        const int m = t / (G * K), rem = t % (G * K), e = rem / K, kk = rem % K, iq = i0 + m;
-        sc_l[t] = iq < N ? sel_score[((b * H_q + g * G + e) * N + iq) * K + kk] * LOG2E : -INFINITY;
-    }
-    for (int t = tid; t < NW; t += blockDim.x) bitmap[t] = 0u;
+    // ---- ascending union of the block's selections
+    for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
     __syncthreads();
-    for (int t = tid; t < QB * K; t += blockDim.x) {
-        const int c = sel_l[t];
-        if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    for (int t = tid; t < QB * K; t += NT) {
+        const int m = t / K, iq = i0 + m;
+        if (iq < N) {
+            const int c = sel_idx[(bg * N + iq) * K + t % K];
+            if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+        }
     }
     __syncthreads();
-    // ---- ascending union: exclusive prefix sum of per-word popcounts
     int U = 0;
     {
         int base = 0;
-        for (int w0 = 0; w0 < NW; w0 += blockDim.x) {
+        for (int w0 = 0; w0 < NW; w0 += NT) {
             const int wi = w0 + tid;
             const uint32_t word = wi < NW ? bitmap[wi] : 0u;
             const int cnt = __popc(word);
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
             if (lane == WAVE - 1) scan[wave] = incl;
             __syncthreads();
             int wbase = 0, tot = 0;
-            for (int x = 0; x < 4; ++x) {
+            for (int x = 0; x < NWAVE; ++x) {
                 if (x < wave) wbase += scan[x];
                 tot += scan[x];
             }
@@ -170,13 +189,43 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
         }
         U = min(base, UCAP);
     }
+    const int wc0 = max(0, qc - W / S);
+    const int T = U + (qc - wc0 + 1);
+
+    const bf16 *kbase = k + bg * (int64_t)N * D;
+    const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
+    auto chunk_of = [&](int it) { return it < U ? ulist[it] : wc0 + (it - U); };
+
+    // ---- DMA of chunk tiles into the ring: piece p of wave w, lane l
+    auto issue = [&](int it) {
+        const int c = chunk_of(it);
+        const int buf = it % NSTAGE;
+#pragma unroll
+        for (int j = 0; j < LPS; ++j) {
+            const int p = wave * LPS + j;
+            if (p < PK) {
+                constexpr int RPP = 1024 / (D * 2);  // K rows per piece
+                const int row = p * RPP + lane / NBK, blk = lane % NBK;
+                const int64_t key = min((int64_t)c * S + row, (int64_t)N - 1);
+                const bf16 *src = kbase + key * D + ((blk ^ (row & 7)) * 8);
+                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&k_st[buf][p * RPP][0]), 16, 0, 0);
+            } else {
+                constexpr int RPP = 1024 / (S * 2);  // V^T rows per piece
+                const int pv = p - PK;
+                const int row = pv * RPP + lane / NBV, blk = lane % NBV;
+                const f16 *src = vtbase + ((int64_t)c * D + row) * S + ((blk ^ (row & 7)) * 8);
+                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&v_st[buf][pv * RPP][0]), 16, 0, 0);
+            }
+        }
+    };
 
     // ---- per-tile row state
     const int r = lane & 15;
     bf16x8 qf[TPW][KS];
     f32x4 O[TPW][DT];
-    float mrun[TPW], lrun[TPW];
-    int cur[TPW], nsel[TPW], qrow[TPW], hrow[TPW];
+    float mrun[TPW], lrun[TPW], nsc[TPW];
+    int cur[TPW], nsel[TPW], nch[TPW], qrow[TPW], hrow[TPW];
+    int64_t selbase[TPW], scbase[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int m = (wave * TPW + t) * QPT + r / G;
@@ -184,65 +233,52 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
         const int iq = i0 + m;
         qrow[t] = m;
         hrow[t] = g * G + e;
-        const bf16 *qr = q + ((b * H_q + hrow[t]) * N + min(iq, N - 1)) * D;
+        const int iqc = min(iq, N - 1);
+        const bf16 *qr = q + ((b * H_q + hrow[t]) * N + iqc) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[t][s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        selbase[t] = (bg * N + iqc) * K;
+        scbase[t] = ((b * H_q + hrow[t]) * N + iqc) * K;
         float mh = -INFINITY;
         int ns = 0;
-        for (int kk = 0; kk < K; ++kk) {
-            const int c = sel_l[m * K + kk];
-            if (c >= 0) {
+        if (iq < N)
+            for (int kk = 0; kk < K; ++kk) {
+                if (sel_idx[selbase[t] + kk] < 0) break;
                 ++ns;
-                mh = fmaxf(mh, sc_l[(m * G + e) * K + kk]);
+                mh = fmaxf(mh, sel_score[scbase[t] + kk] * LOG2E);
             }
-        }
         float z = 0.f;
-        for (int kk = 0; kk < ns; ++kk) z += exp2f(sc_l[(m * G + e) * K + kk] - mh);
+        for (int kk = 0; kk < ns; ++kk) z += exp2f(sel_score[scbase[t] + kk] * LOG2E - mh);
         mrun[t] = mh;
         lrun[t] = z;
         cur[t] = 0;
         nsel[t] = ns;
+        nch[t] = ns > 0 ? sel_idx[selbase[t]] : 0x7fffffff;
+        nsc[t] = ns > 0 ? sel_score[scbase[t]] * LOG2E : 0.f;
     }
 
-    const bf16 *kbase = k + bg * (int64_t)N * D;
-    const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
-
-    auto stage = [&](int c) {
-        __syncthreads();
-        const bf16 *ks = kbase + (int64_t)c * S * D;
-        for (int idx = tid; idx < S * NBK; idx += blockDim.x) {
-            const int row = idx / NBK, cb = idx % NBK;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if ((int64_t)c * S + row < N) val = *(const u32x4 *)(ks + (int64_t)row * D + cb * 8);
-            k_lds[row][cb ^ (row & 7)] = val;
-        }
-        const f16 *vs = vtbase + (int64_t)c * D * S;
-        for (int idx = tid; idx < D * NBV; idx += blockDim.x) {
-            const int row = idx / NBV, cb = idx % NBV;
-            v_lds[row][cb ^ (row & 7)] = *(const u32x4 *)(vs + (int64_t)row * S + cb * 8);
-        }
-        __syncthreads();
-    };
-
-    // S^T tile of one 16-row MFMA tile: acc[kt][i] = q_row . k_{16kt + 4grp + i}
-    auto qk = [&](const bf16x8 (&qt)[KS], f32x4 (&acc)[KT]) {
+    // S^T tile: acc[kt][i] = q_row . k_{16kt + 4grp + i}
+    // (the scheduling barriers keep one key tile's operands in flight at a
+    // time: the block holds 16 waves, 128 registers each)
+    auto qk = [&](const u32x4 (*kt_lds)[NBK], const bf16x8 (&qt)[KS], f32x4 (&acc)[KT]) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int row = 16 * kt + r;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4 raw = k_lds[row][(4 * s + grp) ^ (row & 7)];
+                const u32x4 raw = kt_lds[row][(4 * s + grp) ^ (row & 7)];
                 bf16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
                 acc[kt] = mfma16(a, qt[s], acc[kt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // O^T += V^T P^T with P^T taken from the (already exponentiated) S^T
-    auto pv = [&](const f32x4 (&p)[KT], f32x4 (&o)[DT]) {
+    // O^T += V^T P^T with P^T taken from the exponentiated S^T
+    auto pv = [&](const u32x4 (*vt_lds)[NBV], const f32x4 (&p)[KT], f32x4 (&o)[DT]) {
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps) {
             f16x8 bp;
@@ -254,90 +290,105 @@ __global__ __launch_bounds__(256) void sparse_attend_kernel(
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int row = 16 * dt + r;
-                const u32x4 raw = v_lds[row][(4 * ps + grp) ^ (row & 7)];
+                const u32x4 raw = vt_lds[row][(4 * ps + grp) ^ (row & 7)];
                 f16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
                 o[dt] = mfma16h(a, bp, o[dt]);
+                if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // ---- selected chunks (union walk)
-    for (int u = 0; u < U; ++u) {
-        const int c = ulist[u];
-        stage(c);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int m = qrow[t], e = hrow[t] - g * G;
-            const bool active = cur[t] < nsel[t] && sel_l[m * K + cur[t]] == c;
-            if (__ballot(active) == 0ull) continue;
-            f32x4 acc[KT];
-            qk(qf[t], acc);
-            float cmax = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[kt][i] *= scale_log2;
-                    cmax = fmaxf(cmax, acc[kt][i]);
-                }
-            cmax = xor_max<16, 32>(cmax);
-            float lc = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[kt][i] = exp2f(acc[kt][i] - cmax);
-                    lc += acc[kt][i];
-                }
-            lc = xor_sum<16, 32>(lc);
-            const float f = active ? exp2f(sc_l[(m * G + e) * K + cur[t]] - mrun[t]) / lc : 0.f;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[kt][i] *= f;
-            pv(acc, O[t]);
-            cur[t] += active ? 1 : 0;
+    // ---- pipelined walk: union chunks, then the window
+    for (int it = 0; it < NSTAGE - 1 && it < T; ++it) issue(it);
+    for (int it = 0; it < T; ++it) {
+        const int after = min(T - 1, it + NSTAGE - 2) - it;  // chunks issued after this one
+        if constexpr (NSTAGE >= 4) {
+            if (after >= 2) wait_vmcnt<2 * LPS>();
+            else if (after == 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else if constexpr (NSTAGE == 3) {
+            if (after >= 1) wait_vmcnt<LPS>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
         }
-    }
-
-    // ---- chunk-aligned causal window: online softmax continuing the state
-    const int wc0 = max(0, qc - W / S);
-    for (int c = wc0; c <= qc; ++c) {
-        stage(c);
-        const bool diag = c == qc;
+        __builtin_amdgcn_s_barrier();
+        if (it + NSTAGE - 1 < T) issue(it + NSTAGE - 1);
+        const int buf = it % NSTAGE;
+        const int c = chunk_of(it);
+        if (it < U) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int iq = i0 + qrow[t];
-            f32x4 acc[KT];
-            qk(qf[t], acc);
-            float cmax = -INFINITY;
+            for (int t = 0; t < TPW; ++t) {
+                const bool active = nch[t] == c;
+                if (__ballot(active) == 0ull) continue;
+                f32x4 acc[KT];
+                qk(k_st[buf], qf[t], acc);
+                float cmax = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = c * S + 16 * kt + 4 * grp + i;
-                    const float x = (diag && j > iq) ? -INFINITY : acc[kt][i] * scale_log2;
-                    acc[kt][i] = x;
-                    cmax = fmaxf(cmax, x);
+                    for (int i = 0; i < 4; ++i) {
+                        acc[kt][i] *= scale_log2;
+                        cmax = fmaxf(cmax, acc[kt][i]);
+                    }
+                cmax = xor_max<16, 32>(cmax);
+                float lc = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[kt][i] = exp2f(acc[kt][i] - cmax);
+                        lc += acc[kt][i];
+                    }
+                lc = xor_sum<16, 32>(lc);
+                const float f = active ? exp2f(nsc[t] - mrun[t]) / lc : 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[kt][i] *= f;
+                pv(v_st[buf], acc, O[t]);
+                if (active) {
+                    const int nx = ++cur[t];
+                    nch[t] = nx < nsel[t] ? sel_idx[selbase[t] + nx] : 0x7fffffff;
+                    nsc[t] = nx < nsel[t] ? sel_score[scbase[t] + nx] * LOG2E : 0.f;
                 }
-            cmax = xor_max<16, 32>(cmax);
-            const float mnew = fmaxf(mrun[t], cmax);
-            const float alpha = exp2f(mrun[t] - mnew);
-            float ls = 0.f;
+            }
+        } else {
+            const bool diag = c == qc;
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int t = 0; t < TPW; ++t) {
+                const int iq = i0 + qrow[t];
+                f32x4 acc[KT];
+                qk(k_st[buf], qf[t], acc);
+                float cmax = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[kt][i] = exp2f(acc[kt][i] - mnew);
-                    ls += acc[kt][i];
-                }
-            ls = xor_sum<16, 32>(ls);
-            lrun[t] = lrun[t] * alpha + ls;
-            mrun[t] = mnew;
+                for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
-            pv(acc, O[t]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = c * S + 16 * kt + 4 * grp + i;
+                        const float x = (diag && j > iq) ? -INFINITY : acc[kt][i] * scale_log2;
+                        acc[kt][i] = x;
+                        cmax = fmaxf(cmax, x);
+                    }
+                cmax = xor_max<16, 32>(cmax);
+                const float mnew = fmaxf(mrun[t], cmax);
+                const float alpha = exp2f(mrun[t] - mnew);
+                float ls = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[kt][i] = exp2f(acc[kt][i] - mnew);
+                        ls += acc[kt][i];
+                    }
+                ls = xor_sum<16, 32>(ls);
+                lrun[t] = lrun[t] * alpha + ls;
+                mrun[t] = mnew;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
+                pv(v_st[buf], acc, O[t]);
+            }
         }
     }
 
@@ -475,43 +526,51 @@ size_t fused_workspace_bytes(const Shape &s) {
     return align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
 }
 
-static int pick_tpw(const Shape &s) {
-    // queries per block = 4 * TPW * 16 / G must divide S; two tiles per
-    // wave only while the S^T and O^T accumulators fit the register file
-    const int qpt = 16 / s.G;
-    int tpw = 1;
-    if (s.D * s.S > 128 * 64) return 1;
-    while (tpw < 2 && 4 * (tpw * 2) * qpt <= s.S && s.S % (4 * tpw * 2 * qpt) == 0) tpw *= 2;
-    return tpw;
-}
+template <int D, int S, int G>
+struct AttendPlan {
+    // one tile per wave, up to 16 waves, as long as the block's queries fit
+    // one query chunk (64 queries x 4 heads at G = 4)
+    // (16 waves leave 128 registers per wave: enough for 64-key chunks at
+    // d = 128; 128-key chunks at d = 128 run 8 waves with 256)
+    static constexpr int TPW = 1;
+    static constexpr int WMAX = (D * S > 128 * 64) ? 8 : 16;
+    static constexpr int NWAVE = (WMAX * (16 / G) <= S) ? WMAX : S / (16 / G);
+    static constexpr int NSTAGE = (S * D * 4 <= 32 * 1024) ? 4 : 2;
+};
 
-template <int D, int S, int G, int TPW>
+template <int D, int S, int G>
 static hipError_t go_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
                             const float *sel_score, void *out, float *lse, hipStream_t st) {
-    using Cf = AttendCfg<D, S, G, TPW>;
+    using P = AttendPlan<D, S, G>;
+    using Cf = AttendCfg<D, S, G, P::TPW, P::NWAVE, P::NSTAGE>;
+    static_assert(S % Cf::QB == 0, "a block never straddles query chunks");
     const int QB = Cf::QB;
     const int NW = (s.C + 31) / 32 + 1;
     const int UCAP = std::min(s.C + 1, QB * s.K + 1);  // union size bound
-    const size_t dyn = (size_t)QB * s.K * 4 + (size_t)QB * G * s.K * 4 + (size_t)NW * 4 + (size_t)UCAP * 4 + 8 * 4;
-    const dim3 grid((unsigned)((s.N + QB - 1) / QB), (unsigned)s.H_kv, (unsigned)s.B), block(256);
-    auto kern = sparse_attend_kernel<D, S, G, TPW>;
-    // static K/V tiles plus this dynamic part may exceed 64 KB at S = 128
+    const size_t dyn = (size_t)NW * 4 + (size_t)UCAP * 4 + 16 * 4;
+    const int nqb = (s.N + QB - 1) / QB;
+    const int64_t n_items = (int64_t)s.B * s.H_kv * nqb;
+    const int64_t per_xcd = (n_items + 7) / 8;
+    const dim3 grid((unsigned)(8 * per_xcd)), block(P::NWAVE * 64);
+    auto kern = sparse_attend_kernel<D, S, G, P::TPW, P::NWAVE, P::NSTAGE>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
-                       sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP);
+                       sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP,
+                       nqb, n_items, per_xcd);
     return hipGetLastError();
 }
 
 template <int D, int S>
 static hipError_t dispatch_g(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
                              const float *sel_score, void *out, float *lse, hipStream_t st) {
-    const int tpw = pick_tpw(s);
-#define HILS_ATT(GG, TT)                                                                       \
-    if (s.G == GG && tpw == TT) return go_attend<D, S, GG, TT>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-    HILS_ATT(1, 1) HILS_ATT(1, 2) HILS_ATT(2, 1) HILS_ATT(2, 2) HILS_ATT(4, 1) HILS_ATT(4, 2) HILS_ATT(8, 1) HILS_ATT(8, 2)
-#undef HILS_ATT
-    return hipErrorInvalidValue;
+    switch (s.G) {
+        case 1: return go_attend<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 2: return go_attend<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 4: return go_attend<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 8: return go_attend<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
@@ -530,7 +589,7 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
                                s.W, s.K, s.scale);
         return hipGetLastError();
     }
-    // V^T pre-pass into the workspace (fp16)
+    // V^T pre-pass (fp16, slot order) into the workspace
     f16 *vt = (f16 *)workspace;
     {
         const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
@@ -538,7 +597,7 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
         else if (s.D == 64) hipLaunchKernelGGL((v_transpose_kernel<64, 128>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
         else if (s.S == 64) hipLaunchKernelGGL((v_transpose_kernel<128, 64>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
         else hipLaunchKernelGGL((v_transpose_kernel<128, 128>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (s.D == 64 && s.S == 64) return dispatch_g<64, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, st);

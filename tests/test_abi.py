@@ -110,6 +110,7 @@ def test_workspace_is_checked(lib):
     st = lib.hils_score_select(ctypes.byref(cfg), A, A, A, None, None, None, 0, 0, A, A, None, 0, None)
     assert st == hb.HILS_ERR_WORKSPACE
     need_f = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
+    assert need_f > 0
     st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need_f - 16, None)
     assert st == hb.HILS_ERR_WORKSPACE
     need_d = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DECODE, 4, 100)
@@ -128,7 +129,7 @@ def test_workspace_sizes_scale_with_problem(lib):
     assert qc > lib.hils_workspace_size(ctypes.byref(small), hb.WS_SCORE, 0, 0)
     f32 = _cfg()
     f32.io_dtype = hb.HILS_F32
-    assert lib.hils_workspace_size(ctypes.byref(f32), hb.WS_FUSED, 0, 0) == 0
+    assert lib.hils_workspace_size(ctypes.byref(f32), hb.WS_FUSED, 0, 0) == 0  # fp32 path needs none
     assert lib.hils_workspace_size(ctypes.byref(_cfg(d=96)), hb.WS_SCORE, 0, 0) == 0
     assert "d=96" in hb.last_error()
 
