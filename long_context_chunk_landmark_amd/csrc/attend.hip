@@ -94,7 +94,18 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
 // s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// XOR swizzle of the 16-byte block index within an LDS row so that the 16
+// lanes of one 128-bit read phase (rows r..r+15, same block) hit distinct
+// bank groups, and so do the two 8-lane halves: rows of 16 blocks use
+// r & 15; rows of 8 blocks (two rows per 256 bytes) use (r & 7) ^ ((r >> 3) & 1).
+template <int NB>
+__host__ __device__ __forceinline__ int swz(int row) {
+    static_assert(NB == 8 || NB == 16, "rows of 8 or 16 blocks");
+    return NB == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
 template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
@@ -110,11 +121,16 @@ struct AttendCfg {
     static constexpr int PK = S * D * 2 / 1024;      // 1 KB pieces of a K tile
     static constexpr int PV = D * S * 2 / 1024;      // 1 KB pieces of a V^T tile
     static constexpr int LPS = (PK + PV) / NWAVE;    // DMA loads per lane per chunk
+    static constexpr int LINES = 2 * S * D * 2 / 128;                 // 128-byte lines per chunk
+    static constexpr int PFI = (LINES / NWAVE + WAVE - 1) / WAVE;      // L2-warming loads per lane
     static_assert((PK + PV) % NWAVE == 0, "pieces per wave");
-    static_assert(NBK >= 8 && NBV >= 8, "swizzle needs 8 blocks per row");
 };
 
-// Dynamic LDS: uint bitmap[NW]; int ulist[UCAP]; int scan[16].
+// Dynamic LDS: int16 sel[QB*K] (chunk ids, -1 padded); fp16 wt[QB*G*K]
+// (fusion weights exp(s^ - m^) of each row's selections); uint bitmap[NW];
+// int ulist[UCAP]; int scan[16].  Selections live in LDS so that reading a
+// row's next selection never waits on the vector-memory counter that
+// tracks the chunk DMA.
 template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
 __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
@@ -123,12 +139,17 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     int nqb, int64_t n_items, int64_t per_xcd) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
-    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS;
+    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS, LINES = Cf::LINES, PFI = Cf::PFI;
     constexpr int NT = NWAVE * 64;
-    __shared__ u32x4 k_st[NSTAGE][S][NBK];
-    __shared__ u32x4 v_st[NSTAGE][D][NBV];
+    // chunk ring: stage s holds the K tile [S][NBK] then the V^T tile [D][NBV]
+    __shared__ u32x4 ring[NSTAGE][S * NBK + D * NBV];
+    __shared__ u32x4 sink[WAVE];  // destination of the L2-warming DMA (never read)
+    auto k_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBK]>(&ring[buf][0]); };
+    auto v_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBV]>(&ring[buf][S * NBK]); };
     extern __shared__ int dyn[];
-    uint32_t *bitmap = (uint32_t *)dyn;
+    int16_t *sel_l = (int16_t *)dyn;
+    f16 *wt_l = (f16 *)(sel_l + QB * K);
+    uint32_t *bitmap = (uint32_t *)(wt_l + QB * G * K);
     int *ulist = (int *)(bitmap + NW);
     int *scan = ulist + UCAP;
 
@@ -144,18 +165,71 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const int qc = i0 / S;
     const int n = max(0, qc - W / S);
     const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4;
+    const int r = lane & 15;
 
-    // ---- ascending union of the block's selections
+    // ---- setup: selections and scores of the block's queries.  The fp32
+    // scores are first staged in the (still idle) chunk ring; the launcher
+    // checks QB * G * K * 4 <= sizeof(ring).
+    float *sc_tmp = (float *)&ring[0][0];
     for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
-    __syncthreads();
     for (int t = tid; t < QB * K; t += NT) {
-        const int m = t / K, iq = i0 + m;
-        if (iq < N) {
-            const int c = sel_idx[(bg * N + iq) * K + t % K];
-            if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
-        }
+        const int iq = i0 + t / K;
+        const int c = iq < N ? sel_idx[(bg * N + iq) * K + t % K] : -1;
+        sel_l[t] = (int16_t)c;
+    }
+    for (int t = tid; t < QB * G * K; t += NT) {
+        const int m = t / (G * K), rem = t % (G * K), e = rem / K, iq = i0 + m;
+        sc_tmp[t] = iq < N ? sel_score[((b * H_q + g * G + e) * N + iq) * K + rem % K] * LOG2E : -INFINITY;
     }
     __syncthreads();
+    for (int t = tid; t < QB * K; t += NT) {
+        const int c = sel_l[t];
+        if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+
+    // per-tile row state; rows convert their scores to fp16 weights
+    bf16x8 qf[TPW][KS];
+    f32x4 O[TPW][DT];
+    float mrun[TPW], lrun[TPW], nwt[TPW];
+    int cur[TPW], nsel[TPW], nch[TPW], qrow[TPW], hrow[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int m = (wave * TPW + t) * QPT + r / G;
+        const int e = r % G;
+        const int iq = i0 + m;
+        qrow[t] = m;
+        hrow[t] = g * G + e;
+        const bf16 *qr = q + ((b * H_q + hrow[t]) * N + min(iq, N - 1)) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[t][s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // selections are ascending with -1 padding at the end
+        const int16_t *sl = sel_l + m * K;
+        const float *sc = sc_tmp + (m * G + e) * K;
+        float mh = -INFINITY;
+        int ns = 0;
+        for (int kk = 0; kk < K; ++kk) {
+            const bool ok = sl[kk] >= 0;
+            ns += ok;
+            mh = ok ? fmaxf(mh, sc[kk]) : mh;
+        }
+        float z = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            const float wv = sl[kk] >= 0 ? exp2f(sc[kk] - mh) : 0.f;
+            z += wv;
+            if (grp == 0) wt_l[(m * G + e) * K + kk] = (f16)wv;
+        }
+        mrun[t] = mh;
+        lrun[t] = z;
+        cur[t] = 0;
+        nsel[t] = ns;
+        nch[t] = ns > 0 ? sl[0] : 0x7fffffff;
+        nwt[t] = ns > 0 ? exp2f(sc[0] - mh) : 0.f;
+    }
+    __syncthreads();
+
+    // ---- ascending union: exclusive prefix sum of per-word popcounts
     int U = 0;
     {
         int base = 0;
@@ -196,9 +270,12 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
     auto chunk_of = [&](int it) { return it < U ? ulist[it] : wc0 + (it - U); };
 
-    // ---- DMA of chunk tiles into the ring: piece p of wave w, lane l
+    // ---- DMA of chunk tiles into the ring: piece p of wave w, lane l.
+    // Every call issues exactly LPS loads per lane (past the end they land
+    // in the sink) so the vmcnt bookkeeping below is a constant.
     auto issue = [&](int it) {
-        const int c = chunk_of(it);
+        const bool real = it < T;
+        const int c = chunk_of(real ? it : T - 1);
         const int buf = it % NSTAGE;
 #pragma unroll
         for (int j = 0; j < LPS; ++j) {
@@ -207,61 +284,39 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                 constexpr int RPP = 1024 / (D * 2);  // K rows per piece
                 const int row = p * RPP + lane / NBK, blk = lane % NBK;
                 const int64_t key = min((int64_t)c * S + row, (int64_t)N - 1);
-                const bf16 *src = kbase + key * D + ((blk ^ (row & 7)) * 8);
-                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&k_st[buf][p * RPP][0]), 16, 0, 0);
+                const bf16 *src = kbase + key * D + ((blk ^ swz<NBK>(row)) * 8);
+                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(real ? &k_tile(buf)[p * RPP][0] : &sink[0]),
+                                                 16, 0, 0);
             } else {
                 constexpr int RPP = 1024 / (S * 2);  // V^T rows per piece
                 const int pv = p - PK;
                 const int row = pv * RPP + lane / NBV, blk = lane % NBV;
-                const f16 *src = vtbase + ((int64_t)c * D + row) * S + ((blk ^ (row & 7)) * 8);
-                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&v_st[buf][pv * RPP][0]), 16, 0, 0);
+                const f16 *src = vtbase + ((int64_t)c * D + row) * S + ((blk ^ swz<NBV>(row)) * 8);
+                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(real ? &v_tile(buf)[pv * RPP][0] : &sink[0]),
+                                                 16, 0, 0);
             }
         }
     };
-
-    // ---- per-tile row state
-    const int r = lane & 15;
-    bf16x8 qf[TPW][KS];
-    f32x4 O[TPW][DT];
-    float mrun[TPW], lrun[TPW], nsc[TPW];
-    int cur[TPW], nsel[TPW], nch[TPW], qrow[TPW], hrow[TPW];
-    int64_t selbase[TPW], scbase[TPW];
+    // L2 warming: touch each 128-byte line of chunk `it` (K lines, then V^T
+    // lines) with a DMA into the sink; PFI loads per lane, always issued.
+    // Wave w covers lines [w * LPW, (w + 1) * LPW); lanes beyond LPW repeat
+    // addresses of the same wave, which the load unit merges.
+    auto prefetch = [&](int it) {
+        constexpr int LPW = LINES / NWAVE;
+        const int c = chunk_of(min(it, T - 1));
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int m = (wave * TPW + t) * QPT + r / G;
-        const int e = r % G;
-        const int iq = i0 + m;
-        qrow[t] = m;
-        hrow[t] = g * G + e;
-        const int iqc = min(iq, N - 1);
-        const bf16 *qr = q + ((b * H_q + hrow[t]) * N + iqc) * D;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[t][s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        selbase[t] = (bg * N + iqc) * K;
-        scbase[t] = ((b * H_q + hrow[t]) * N + iqc) * K;
-        float mh = -INFINITY;
-        int ns = 0;
-        if (iq < N)
-            for (int kk = 0; kk < K; ++kk) {
-                if (sel_idx[selbase[t] + kk] < 0) break;
-                ++ns;
-                mh = fmaxf(mh, sel_score[scbase[t] + kk] * LOG2E);
-            }
-        float z = 0.f;
-        for (int kk = 0; kk < ns; ++kk) z += exp2f(sel_score[scbase[t] + kk] * LOG2E - mh);
-        mrun[t] = mh;
-        lrun[t] = z;
-        cur[t] = 0;
-        nsel[t] = ns;
-        nch[t] = ns > 0 ? sel_idx[selbase[t]] : 0x7fffffff;
-        nsc[t] = ns > 0 ? sel_score[scbase[t]] * LOG2E : 0.f;
-    }
+        for (int j = 0; j < PFI; ++j) {
+            const int line = wave * LPW + (j * WAVE + lane) % LPW;
+            const char *src = line < LINES / 2
+                                  ? (const char *)(kbase + min((int64_t)c * S * D + line * 64, (int64_t)N * D - 64))
+                                  : (const char *)(vtbase + ((int64_t)c * D * S + (line - LINES / 2) * 64));
+            __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&sink[0]), 16, 0, 0);
+        }
+    };
 
     // S^T tile: acc[kt][i] = q_row . k_{16kt + 4grp + i}
     // (the scheduling barriers keep one key tile's operands in flight at a
-    // time: the block holds 16 waves, 128 registers each)
+    // time: the block holds up to 16 waves, 128 registers each)
     auto qk = [&](const u32x4 (*kt_lds)[NBK], const bf16x8 (&qt)[KS], f32x4 (&acc)[KT]) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
@@ -269,12 +324,12 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             const int row = 16 * kt + r;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4 raw = kt_lds[row][(4 * s + grp) ^ (row & 7)];
+                const u32x4 raw = kt_lds[row][(4 * s + grp) ^ swz<NBK>(row)];
                 bf16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
                 acc[kt] = mfma16(a, qt[s], acc[kt]);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NWAVE == 16) __builtin_amdgcn_sched_barrier(0);
         }
     };
     // O^T += V^T P^T with P^T taken from the exponentiated S^T
@@ -290,31 +345,30 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int row = 16 * dt + r;
-                const u32x4 raw = vt_lds[row][(4 * ps + grp) ^ (row & 7)];
+                const u32x4 raw = vt_lds[row][(4 * ps + grp) ^ swz<NBV>(row)];
                 f16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
                 o[dt] = mfma16h(a, bp, o[dt]);
-                if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NWAVE == 16)
+                    if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // ---- pipelined walk: union chunks, then the window
-    for (int it = 0; it < NSTAGE - 1 && it < T; ++it) issue(it);
+    // ---- pipelined walk: union chunks, then the window.  Step j issues
+    // chunk j + NSTAGE - 1 into the ring and warms chunk j + NSTAGE + 1.
+#pragma unroll
+    for (int it = 0; it < NSTAGE - 1; ++it) {
+        issue(it);
+        prefetch(it + 2);
+    }
     for (int it = 0; it < T; ++it) {
-        const int after = min(T - 1, it + NSTAGE - 2) - it;  // chunks issued after this one
-        if constexpr (NSTAGE >= 4) {
-            if (after >= 2) wait_vmcnt<2 * LPS>();
-            else if (after == 1) wait_vmcnt<LPS>();
-            else wait_vmcnt<0>();
-        } else if constexpr (NSTAGE == 3) {
-            if (after >= 1) wait_vmcnt<LPS>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        // younger than chunk it's loads: its own step's prefetch and the
+        // NSTAGE - 2 later steps
+        wait_vmcnt<PFI + (NSTAGE - 2) * (LPS + PFI)>();
         __builtin_amdgcn_s_barrier();
-        if (it + NSTAGE - 1 < T) issue(it + NSTAGE - 1);
+        issue(it + NSTAGE - 1);
+        prefetch(it + NSTAGE + 1);
         const int buf = it % NSTAGE;
         const int c = chunk_of(it);
         if (it < U) {
@@ -323,7 +377,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                 const bool active = nch[t] == c;
                 if (__ballot(active) == 0ull) continue;
                 f32x4 acc[KT];
-                qk(k_st[buf], qf[t], acc);
+                qk(k_tile(buf), qf[t], acc);
                 float cmax = -INFINITY;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
@@ -332,7 +386,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         acc[kt][i] *= scale_log2;
                         cmax = fmaxf(cmax, acc[kt][i]);
                     }
-                cmax = xor_max<16, 32>(cmax);
+                cmax = rows4_max(cmax);
                 float lc = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
@@ -341,17 +395,18 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         acc[kt][i] = exp2f(acc[kt][i] - cmax);
                         lc += acc[kt][i];
                     }
-                lc = xor_sum<16, 32>(lc);
-                const float f = active ? exp2f(nsc[t] - mrun[t]) / lc : 0.f;
+                lc = rows4_sum(lc);
+                const float f = active ? nwt[t] / lc : 0.f;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[kt][i] *= f;
-                pv(v_st[buf], acc, O[t]);
+                pv(v_tile(buf), acc, O[t]);
                 if (active) {
                     const int nx = ++cur[t];
-                    nch[t] = nx < nsel[t] ? sel_idx[selbase[t] + nx] : 0x7fffffff;
-                    nsc[t] = nx < nsel[t] ? sel_score[scbase[t] + nx] * LOG2E : 0.f;
+                    const int m = qrow[t], e = hrow[t] - g * G;
+                    nch[t] = nx < nsel[t] ? (int)sel_l[m * K + nx] : 0x7fffffff;
+                    nwt[t] = nx < nsel[t] ? (float)wt_l[(m * G + e) * K + nx] : 0.f;
                 }
             }
         } else {
@@ -360,7 +415,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             for (int t = 0; t < TPW; ++t) {
                 const int iq = i0 + qrow[t];
                 f32x4 acc[KT];
-                qk(k_st[buf], qf[t], acc);
+                qk(k_tile(buf), qf[t], acc);
                 float cmax = -INFINITY;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
@@ -371,7 +426,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         acc[kt][i] = x;
                         cmax = fmaxf(cmax, x);
                     }
-                cmax = xor_max<16, 32>(cmax);
+                cmax = rows4_max(cmax);
                 const float mnew = fmaxf(mrun[t], cmax);
                 const float alpha = exp2f(mrun[t] - mnew);
                 float ls = 0.f;
@@ -382,15 +437,16 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         acc[kt][i] = exp2f(acc[kt][i] - mnew);
                         ls += acc[kt][i];
                     }
-                ls = xor_sum<16, 32>(ls);
+                ls = rows4_sum(ls);
                 lrun[t] = lrun[t] * alpha + ls;
                 mrun[t] = mnew;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
-                pv(v_st[buf], acc, O[t]);
+                pv(v_tile(buf), acc, O[t]);
             }
         }
     }
+    wait_vmcnt<0>();  // no DMA outstanding when the block retires
 
     // ---- epilogue
 #pragma unroll
@@ -526,33 +582,44 @@ size_t fused_workspace_bytes(const Shape &s) {
     return align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
 }
 
-template <int D, int S, int G>
+// Block shapes: NWAVE waves of one 16-row tile each (QB = NWAVE * 16/G
+// queries, dividing S).  16 waves leave 128 registers per wave, enough for
+// 64-key chunks at d = 128 only.  The ring holds 3 chunks when a chunk is
+// 32 KB, else 2.
+template <int D, int S, int G, int NWAVE, int TPW_ = 1>
 struct AttendPlan {
-    // one tile per wave, up to 16 waves, as long as the block's queries fit
-    // one query chunk (64 queries x 4 heads at G = 4)
-    // (16 waves leave 128 registers per wave: enough for 64-key chunks at
-    // d = 128; 128-key chunks at d = 128 run 8 waves with 256)
-    static constexpr int TPW = 1;
-    static constexpr int WMAX = (D * S > 128 * 64) ? 8 : 16;
-    static constexpr int NWAVE = (WMAX * (16 / G) <= S) ? WMAX : S / (16 / G);
+    static constexpr int TPW = TPW_;
+    static constexpr int QB = NWAVE * TPW * (16 / G);
+    static constexpr bool valid = QB <= S && S % QB == 0 && !(NWAVE == 16 && D * S > 128 * 64) &&
+                                  !(TPW == 2 && D * S > 128 * 64) && (2 * S * D * 2 / 1024) % NWAVE == 0;
     static constexpr int NSTAGE = (S * D * 4 <= 32 * 1024) ? 4 : 2;
+    static constexpr size_t ring_bytes = (size_t)NSTAGE * 2 * S * D * 2;
+    static constexpr size_t static_lds = ring_bytes + 16 * 64;
 };
 
-template <int D, int S, int G>
+constexpr size_t LDS_BYTES = 160 * 1024;
+
+template <int D, int S, int G, int NWAVE, int TPW>
+static size_t attend_dyn_lds(const Shape &s) {
+    constexpr int QB = AttendPlan<D, S, G, NWAVE, TPW>::QB;
+    const int NW = (s.C + 31) / 32 + 1;
+    const int UCAP = std::min(s.C + 1, QB * s.K + 1);
+    return align_up((size_t)QB * s.K * 2 + (size_t)QB * G * s.K * 2, 16) + (size_t)NW * 4 + (size_t)UCAP * 4 + 16 * 4;
+}
+
+template <int D, int S, int G, int NWAVE, int TPW>
 static hipError_t go_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
                             const float *sel_score, void *out, float *lse, hipStream_t st) {
-    using P = AttendPlan<D, S, G>;
-    using Cf = AttendCfg<D, S, G, P::TPW, P::NWAVE, P::NSTAGE>;
-    static_assert(S % Cf::QB == 0, "a block never straddles query chunks");
-    const int QB = Cf::QB;
+    using P = AttendPlan<D, S, G, NWAVE, TPW>;
+    const int QB = P::QB;
     const int NW = (s.C + 31) / 32 + 1;
     const int UCAP = std::min(s.C + 1, QB * s.K + 1);  // union size bound
-    const size_t dyn = (size_t)NW * 4 + (size_t)UCAP * 4 + 16 * 4;
+    const size_t dyn = attend_dyn_lds<D, S, G, NWAVE, TPW>(s);
     const int nqb = (s.N + QB - 1) / QB;
     const int64_t n_items = (int64_t)s.B * s.H_kv * nqb;
     const int64_t per_xcd = (n_items + 7) / 8;
-    const dim3 grid((unsigned)(8 * per_xcd)), block(P::NWAVE * 64);
-    auto kern = sparse_attend_kernel<D, S, G, P::TPW, P::NWAVE, P::NSTAGE>;
+    const dim3 grid((unsigned)(8 * per_xcd)), block(NWAVE * 64);
+    auto kern = sparse_attend_kernel<D, S, G, TPW, NWAVE, P::NSTAGE>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
@@ -561,14 +628,73 @@ static hipError_t go_attend(const Shape &s, const void *q, const void *k, const 
     return hipGetLastError();
 }
 
+template <int D, int S, int G, int NWAVE, int TPW>
+static bool fits(const Shape &s) {
+    using P = AttendPlan<D, S, G, NWAVE, TPW>;
+    if constexpr (!P::valid) return false;
+    else
+        return P::static_lds + attend_dyn_lds<D, S, G, NWAVE, TPW>(s) <= LDS_BYTES &&
+               (size_t)P::QB * G * s.K * 4 <= P::ring_bytes;  // setup staging of the scores
+}
+
+// Largest block whose LDS (chunk ring + selections + union) fits.
+template <int D, int S, int G, int NWAVE, int TPW>
+static bool try_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
+                       const float *sel_score, void *out, float *lse, hipStream_t st, hipError_t &err) {
+    if constexpr (!AttendPlan<D, S, G, NWAVE, TPW>::valid) {
+        return false;
+    } else {
+        if (!fits<D, S, G, NWAVE, TPW>(s)) return false;
+        err = go_attend<D, S, G, NWAVE, TPW>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        return true;
+    }
+}
+
+template <int D, int S, int G>
+static hipError_t dispatch_w(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
+                             const float *sel_score, void *out, float *lse, hipStream_t st) {
+    hipError_t err = hipErrorInvalidValue;
+    if (try_attend<D, S, G, 16, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
+    if (try_attend<D, S, G, 8, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
+    if (try_attend<D, S, G, 4, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
+    if (try_attend<D, S, G, 2, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
+    return hipErrorInvalidValue;
+}
+
+template <int D, int S, int G>
+static bool fits_any(const Shape &s) {
+    return fits<D, S, G, 8, 2>(s) || fits<D, S, G, 16, 1>(s) || fits<D, S, G, 8, 1>(s) || fits<D, S, G, 4, 1>(s) ||
+           fits<D, S, G, 2, 1>(s);
+}
+
+template <int D, int S>
+static bool fits_g(const Shape &s) {
+    switch (s.G) {
+        case 1: return fits_any<D, S, 1>(s);
+        case 2: return fits_any<D, S, 2>(s);
+        case 4: return fits_any<D, S, 4>(s);
+        case 8: return fits_any<D, S, 8>(s);
+        default: return false;
+    }
+}
+
+bool sparse_attend_supported(const Shape &s) {
+    if (!s.io_bf16) return true;
+    if (s.D == 64 && s.S == 64) return fits_g<64, 64>(s);
+    if (s.D == 64 && s.S == 128) return fits_g<64, 128>(s);
+    if (s.D == 128 && s.S == 64) return fits_g<128, 64>(s);
+    if (s.D == 128 && s.S == 128) return fits_g<128, 128>(s);
+    return false;
+}
+
 template <int D, int S>
 static hipError_t dispatch_g(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
                              const float *sel_score, void *out, float *lse, hipStream_t st) {
     switch (s.G) {
-        case 1: return go_attend<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 2: return go_attend<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 4: return go_attend<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 8: return go_attend<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 1: return dispatch_w<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 2: return dispatch_w<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 4: return dispatch_w<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 8: return dispatch_w<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -164,6 +164,9 @@ hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, 
         return st;
     if (s.K > 0 && ((st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))) return st;
     if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    if (!hils::sparse_attend_supported(s))
+        return fail(HILS_ERR_UNSUPPORTED, "no fused-attention block shape fits LDS for G=%d, S=%d, d=%d, K=%d", s.G, s.S,
+                    s.D, s.K);
     const size_t need = hils::fused_workspace_bytes(s);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(HILS_ERR_WORKSPACE, "sparse_attend_fused needs %zu workspace bytes, got %zu", need,

@@ -71,6 +71,24 @@ __device__ __forceinline__ int xor_sum_i(int v) {
     return v;
 }
 
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane-swap instructions, which stay in the VALU
+// instead of a ds_bpermute round trip.  Swapping a register with itself
+// leaves each lane holding both values of its pair (l, l^32) resp.
+// (l, l^16), lower-numbered lane's value first.
+__device__ __forceinline__ float rows4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) { return xor_sum_i<1, 32>(v); }
 __device__ __forceinline__ float wave_max(float v) { return xor_max<1, 32>(v); }
 

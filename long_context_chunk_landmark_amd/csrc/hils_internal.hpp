@@ -29,6 +29,7 @@ hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_
 // ---- kernel 2: score + select
 struct ScoreWorkspace {
     void *ksb;          // [B,H_lm,C,D] bf16 copy of k_sum
+    float *kcm;         // [B,H_kv,C,GLM,D] fp32 chunk-major copy of k_sum
     float *knorm;       // [B,H_lm] max_c ||k'_c||
     float *err;         // [B,H_kv,N] per-row bound of the approximate group score
     float *agg;         // ragged approximate group scores, per (b,g): per_bg entries
@@ -44,6 +45,9 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
 
 // ---- kernel 3: fused sparse attention
 size_t fused_workspace_bytes(const Shape &s);
+// Whether the fused kernel has a block shape whose LDS fits this shape
+// (every combination with K <= 32 does; large K with G = 1 at S = 128 may not).
+bool sparse_attend_supported(const Shape &s);
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
                                 const float *sel_score, void *out, float *lse, void *workspace, hipStream_t st);
 

@@ -44,6 +44,7 @@ int64_t score_agg_entries_per_bg(const Shape &s) {
 size_t score_workspace_bytes(const Shape &s, bool qcal) {
     size_t b = 0;
     b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);  // ksb
+    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // kcm
     b += align_up((size_t)s.B * s.H_lm * 4, 256);               // knorm
     b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
     b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
@@ -55,6 +56,8 @@ void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace
     char *p = (char *)base;
     ws.ksb = p;
     p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);
+    ws.kcm = (float *)p;
+    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
     ws.knorm = (float *)p;
     p += align_up((size_t)s.B * s.H_lm * 4, 256);
     ws.err = (float *)p;
@@ -72,10 +75,14 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
     if (i < n) p[i] = 0.f;
 }
 
-// 16 lanes per k' row (D/16 elements each), 4 rows per wave.
+// 16 lanes per k' row (D/16 elements each), 4 rows per wave.  Writes the
+// bf16 copy (same layout) for the MFMA pass, an fp32 chunk-major copy
+// [B, H_kv, C, GLM, D] (the GLM landmark rows of a group contiguous per
+// chunk) for the exact refinement, and the max norm per (b, landmark head).
 template <typename TS, int D>
 __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k_sum, bf16 *__restrict__ ksb,
-                                                        float *__restrict__ knorm, int C, int64_t rows) {
+                                                        float *__restrict__ kcm, float *__restrict__ knorm, int C,
+                                                        int GLM, int64_t rows) {
     constexpr int EL = D / 16;
     const int lane = lane_id();
     const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * 4 + (lane >> 4);
@@ -84,18 +91,28 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
     if (ok) {
         const TS *src = k_sum + row * D + (lane & 15) * EL;
         bf16 *dst = ksb + row * D + (lane & 15) * EL;
+        // row = (b * H_lm + l) * C + c with l = g * GLM + e
+        const int64_t c = row % C, bl = row / C;
+        const int64_t e = bl % GLM, bg = bl / GLM;
+        float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
 #pragma unroll
         for (int x = 0; x < EL; ++x) {
             const float v = to_f32(src[x]);
             ss = fmaf(v, v, ss);
             dst[x] = (bf16)v;
+            dcm[x] = v;
         }
     }
     ss = xor_sum<1, 8>(ss);
-    // rows of one wave may belong to different (b, l); reduce per row
-    if (ok && (lane & 15) == 0) {
-        const int64_t bl = row / C;
-        atomicMax((unsigned int *)(knorm + bl), __float_as_uint(sqrtf(ss)));
+    // one atomic per wave when its four rows belong to the same (b, l)
+    const float nrm = ok ? sqrtf(ss) : 0.f;
+    const int64_t row0 = row - (lane >> 4);
+    const int64_t last = min(row0 + 3, rows - 1);
+    if (row0 / C == last / C) {
+        const float m = xor_max<16, 32>(nrm);
+        if (lane == 0) atomicMax((unsigned int *)(knorm + row0 / C), __float_as_uint(m));
+    } else if (ok && (lane & 15) == 0) {
+        atomicMax((unsigned int *)(knorm + row / C), __float_as_uint(nrm));
     }
 }
 
@@ -245,38 +262,93 @@ __device__ __forceinline__ uint64_t rank_key(float s, int idx) {
     return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
 }
 
-// Largest T with #{keys >= T} >= kk (the kk-th largest key); keys == 0 are
-// empty slots.  NV keys per lane.
+// kk-th largest of the non-zero 64-bit keys held NV per lane (keys == 0 are
+// empty slots): bisection on the upper 32 bits (the score), then on the low
+// bits (the inverted chunk index) only when the score ties at the boundary.
+// Counting is ballot + popcount (scalar), no cross-lane data movement.
 template <int NV>
 __device__ __forceinline__ uint64_t kth_largest64(const uint64_t (&keys)[NV], int kk) {
-    uint64_t T = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t cand = T | (1ull << bit);
+    uint32_t hi = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = hi | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) cnt += __popcll(__ballot(keys[v] >= cand));
-        if (cnt >= kk) T = cand;
+        for (int v = 0; v < NV; ++v) cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) >= cand));
+        if (cnt >= kk) hi = cand;
     }
-    return T;
+    int above = 0, tied = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint32_t h = (uint32_t)(keys[v] >> 32);
+        above += __popcll(__ballot(h > hi));
+        tied += __popcll(__ballot(h == hi && keys[v] != 0ull));
+    }
+    const int need = kk - above;  // 1 <= need <= tied
+    if (tied == need) return (uint64_t)hi << 32;
+    uint32_t lo = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = lo | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) == hi && (uint32_t)keys[v] >= cand));
+        if (cnt >= need) lo = cand;
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum over the 16 lanes of a DPP row (every lane gets the row total).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
+}
+// Sum over aligned groups of L lanes (L = 2..64), result in every lane.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (L >= 16) {
+        v = row_sum16(v);
+        if constexpr (L >= 32) v += __shfl_xor(v, 16, WAVE);
+        if constexpr (L >= 64) v += __shfl_xor(v, 32, WAVE);
+        return v;
+    } else {
+        return xor_sum<1, L / 2>(v);
+    }
 }
 
 struct SelLds {
-    float q[SEL_GMAX][128];         // scoring queries of the row (fp32)
     uint64_t run_key[SEL_KMAX];     // running exact top-K
     float run_sc[SEL_KMAX][SEL_GMAX];
     int batch_idx[WAVE];            // survivors awaiting refinement
+    uint64_t bkey[WAVE];            // their exact ranking keys
+    float bsc[WAVE][SEL_GMAX];      // and per-head exact scores
 };
 
-// One wave per (b, g, query).  JMAX: registers for ceil(n/64) approximate
-// scores per lane.
-template <typename TQ, typename TS, int JMAX>
-__global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, const TS *__restrict__ k_sum,
+// One wave per (b, g, query).  SHARED: the G heads of a group share one
+// landmark (H_lm == H_kv); otherwise each head has its own.
+//
+// Exact refinement reads each survivor's landmark rows from the fp32
+// chunk-major copy: the GLM rows of a group are contiguous, so one
+// survivor is one coalesced read spread over the wave (EPL elements per
+// lane), reduced with DPP.
+template <typename TQ, int D, int G, bool SHARED>
+__global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, const float *__restrict__ kcm,
                                                      const float *__restrict__ b_sum,
                                                      const float *__restrict__ agg_in,
                                                      const float *__restrict__ err_in, int32_t *__restrict__ sel_idx,
                                                      float *__restrict__ sel_score, int B, int N, int H_q, int H_kv,
-                                                     int H_lm, int C, int D, int S, int W, int K, float scale,
+                                                     int H_lm, int C, int S, int W, int K, float scale,
                                                      int64_t per_bg) {
+    constexpr int GLM = SHARED ? 1 : G;
+    constexpr int EPL = GLM * D / WAVE;   // elements of a survivor row per lane
+    constexpr int LR = D / EPL;           // lanes covering one landmark row
+    static_assert(EPL >= 1 && EPL <= 16 && (EPL % 4 == 0 || EPL < 4), "lane slice");
     __shared__ SelLds lds_all[4];
     const int wave = threadIdx.x / WAVE, lane = lane_id();
     SelLds &L = lds_all[wave];
@@ -286,7 +358,6 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     const int64_t bg = row / N;
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
-    const int G = H_q / H_kv;
     const int w = W / S;
     const int n = max(0, i / S - w);
 
@@ -299,81 +370,124 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
         return;
     }
 
-    // scoring query rows of the G heads -> LDS
-    for (int e = 0; e < G; ++e) {
-        const TQ *qr = q + ((b * H_q + (int64_t)g * G + e) * N + i) * D;
-        for (int x = lane; x < D; x += WAVE) L.q[e][x] = to_f32(qr[x]);
+    // scoring-query slices: lane covers elements [lane*EPL, lane*EPL + EPL)
+    // of a survivor row, i.e. landmark row el = lane / LR, dims d0..d0+EPL
+    const int el = lane / LR, d0 = (lane % LR) * EPL;
+    float qv[SHARED ? G : 1][EPL];
+#pragma unroll
+    for (int e = 0; e < (SHARED ? G : 1); ++e) {
+        const int head = SHARED ? e : el;
+        const TQ *qr = q + ((b * H_q + (int64_t)g * G + head) * N + i) * D + d0;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) qv[e][x] = to_f32(qr[x]);
     }
+    const float *kcm_g = kcm + bg * (int64_t)C * GLM * D;
+    const float *bs_g = b_sum + (b * (int64_t)H_lm + (int64_t)g * GLM) * C;  // + e*C + c
 
-    // ---- survivors of the approximate pass
+    // ---- threshold of the approximate pass (two streaming passes over the
+    // row's approximate scores; the second one is served by the caches)
     const int J = (n + WAVE - 1) / WAVE;
-    uint32_t keys[JMAX];  // order-preserving keys of the approximate scores
+    const float *ar = agg_in + bg * per_bg + cand_row_offset(i, w, S);
     uint32_t thr_key = 0;
     const bool rank_needed = n > K;
     if (rank_needed) {
-        const float *ar = agg_in + bg * per_bg + cand_row_offset(i, w, S);
-#pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
+        // tau' = K-th largest of the per-lane top-R approximate scores
+        // (R = ceil(K/64)); those are >= K distinct candidates (n > K), so
+        // tau' <= the K-th largest approximate score overall
+        uint32_t m1 = 0u, m2 = 0u;
+        for (int j = 0; j < J; ++j) {
             const int c = j * WAVE + lane;
-            keys[j] = (j < J && c < n) ? ord_key(ar[c]) : 0u;
+            const uint32_t x = c < n ? ord_key(ar[c]) : 0u;
+            m2 = max(m2, min(m1, x));
+            m1 = max(m1, x);
         }
-        // exact K-th largest approximate score (bitwise bisection on keys)
+        const bool two = K > WAVE;
         uint32_t T = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < JMAX; ++j) cnt += (j < J) & (keys[j] >= cand);
-            cnt = wave_sum_i(cnt);
+            int cnt = __popcll(__ballot(m1 >= cand));
+            if (two) cnt += __popcll(__ballot(m2 >= cand));
             if (cnt >= K) T = cand;
         }
-        // every exact top-K member has approximate score >= tau - 2E
+        // every exact top-K member has approximate score >= tau' - 2E
         thr_key = ord_key(ord_key_inv(T) - 2.f * err_in[row]);
         if (thr_key == 0u) thr_key = 1u;
-    } else {
-#pragma unroll
-        for (int j = 0; j < JMAX; ++j) keys[j] = 0u;
     }
-    wave_sync();
 
     // ---- stream survivors through exact refinement, keep exact top-K
     int run_cnt = 0;
     int bcnt = 0;
-    const float *bsr_base = b_sum + b * (int64_t)H_lm * C;
-    auto flush = [&]() {
-        // refine batch entry `lane`
-        float sc[SEL_GMAX];
-        uint64_t bkey = 0;
-        if (lane < bcnt) {
-            const int c = L.batch_idx[lane];
-            float agg = -INFINITY;
-            for (int e = 0; e < G; ++e) {
-                const int l = (g * G + e) * H_lm / H_q;
-                const TS *kr = k_sum + ((b * H_lm + l) * (int64_t)C + c) * D;
-                float dot = 0.f;
-                for (int x = 0; x < D; x += 4) {
+    // exact scores of survivors batch[k0 .. k0+RB) (all lanes): per-head s^
+    // of survivor k land in bsc[k], its ranking key in bkey[k].  RB rows are
+    // loaded before any is reduced so that their latencies overlap.
+    constexpr int RB = 4;
+    auto refine = [&](int k0, int cnt) {
+        float kx[RB][EPL];
+        int cs[RB];
 #pragma unroll
-                    for (int y = 0; y < 4; ++y) dot = fmaf(L.q[e][x + y], to_f32(kr[x + y]), dot);
+        for (int u = 0; u < RB; ++u) {
+            cs[u] = L.batch_idx[k0 + min(u, cnt - 1)];
+            const float *kr = kcm_g + (int64_t)cs[u] * GLM * D + lane * EPL;
+            if constexpr (EPL >= 4) {
+#pragma unroll
+                for (int x = 0; x < EPL; x += 4) {
+                    const f32x4 v4 = *(const f32x4 *)(kr + x);
+                    kx[u][x] = v4[0], kx[u][x + 1] = v4[1], kx[u][x + 2] = v4[2], kx[u][x + 3] = v4[3];
                 }
-                sc[e] = fmaf(scale, dot, bsr_base[(int64_t)l * C + c]);
-                agg = fmaxf(agg, sc[e]);
+            } else {
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) kx[u][x] = kr[x];
             }
-            bkey = rank_key(agg, c);
         }
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            if (u >= cnt) break;
+            const int c = cs[u], slot = k0 + u;
+            float agg = -INFINITY;
+            if constexpr (SHARED) {
+                const float bb = bs_g[c];
+#pragma unroll
+                for (int e = 0; e < G; ++e) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int x = 0; x < EPL; ++x) part = fmaf(qv[e][x], kx[u][x], part);
+                    const float sc = fmaf(scale, group_sum<WAVE>(part), bb);
+                    if (lane == 0) L.bsc[slot][e] = sc;
+                    agg = fmaxf(agg, sc);
+                }
+            } else {
+                float part = 0.f;
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) part = fmaf(qv[0][x], kx[u][x], part);
+                const float sc = fmaf(scale, group_sum<LR>(part), bs_g[(int64_t)el * C + c]);
+                if (lane % LR == 0) L.bsc[slot][el] = sc;
+                agg = sc;
+#pragma unroll
+                for (int m = LR; m < WAVE; m <<= 1) agg = fmaxf(agg, __shfl_xor(agg, m, WAVE));
+            }
+            if (lane == 0) L.bkey[slot] = rank_key(agg, c);
+        }
+    };
+    auto flush = [&]() {
+        wave_sync();
+        for (int k = 0; k < bcnt; k += RB) refine(k, min(RB, bcnt - k));
         wave_sync();
         // merge with the running set (entries lane and lane+64)
         uint64_t keys[3];
         keys[0] = lane < run_cnt ? L.run_key[lane] : 0ull;
         keys[1] = lane + WAVE < run_cnt ? L.run_key[lane + WAVE] : 0ull;
-        keys[2] = bkey;
-        float rs0[SEL_GMAX], rs1[SEL_GMAX];
+        keys[2] = lane < bcnt ? L.bkey[lane] : 0ull;
+        float rs[3][G];
+#pragma unroll
         for (int e = 0; e < G; ++e) {
-            rs0[e] = lane < run_cnt ? L.run_sc[lane][e] : 0.f;
-            rs1[e] = lane + WAVE < run_cnt ? L.run_sc[lane + WAVE][e] : 0.f;
+            rs[0][e] = lane < run_cnt ? L.run_sc[lane][e] : 0.f;
+            rs[1][e] = lane + WAVE < run_cnt ? L.run_sc[lane + WAVE][e] : 0.f;
+            rs[2][e] = lane < bcnt ? L.bsc[lane][e] : 0.f;
         }
         const int total = run_cnt + bcnt;
         uint64_t T = 1;  // keep every non-empty key
         if (total > K) T = kth_largest64<3>(keys, K);
+        wave_sync();
         // compact keys >= T into the running set, slot order 0, 1, 2
         int base = 0;
 #pragma unroll
@@ -381,10 +495,10 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
             const bool keep = keys[v] >= T && keys[v] != 0ull;
             const uint64_t m = __ballot(keep);
             const int pos = base + __popcll(m & lanemask_lt());
-            // all reads of the old set are done (registers); write new set
             if (keep && pos < SEL_KMAX) {
                 L.run_key[pos] = keys[v];
-                for (int e = 0; e < G; ++e) L.run_sc[pos][e] = v == 0 ? rs0[e] : (v == 1 ? rs1[e] : sc[e]);
+#pragma unroll
+                for (int e = 0; e < G; ++e) L.run_sc[pos][e] = rs[v][e];
             }
             base += __popcll(m);
         }
@@ -398,23 +512,18 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
             const int m = min(WAVE, n - c0);
             if (lane < m) L.batch_idx[lane] = c0 + lane;
             bcnt = m;
-            wave_sync();
             flush();
         }
     } else {
-#pragma unroll
-        for (int j = 0; j < JMAX; ++j) {
-            if (j < J) {
-                const int c = j * WAVE + lane;
-                const bool surv = c < n && keys[j] >= thr_key;
-                const uint64_t m = __ballot(surv);
-                const int cnt = __popcll(m);
-                if (cnt > 0) {
-                    if (bcnt + cnt > WAVE) flush();
-                    if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = c;
-                    bcnt += cnt;
-                    wave_sync();
-                }
+        for (int j = 0; j < J; ++j) {
+            const int c = j * WAVE + lane;
+            const bool surv = c < n && ord_key(ar[c]) >= thr_key;
+            const uint64_t m = __ballot(surv);
+            const int cnt = __popcll(m);
+            if (cnt > 0) {
+                if (bcnt + cnt > WAVE) flush();
+                if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = c;
+                bcnt += cnt;
             }
         }
         if (bcnt > 0) flush();
@@ -433,11 +542,13 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
                 rank += oi < myidx;
             }
             out_idx[rank] = myidx;
+#pragma unroll
             for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + rank] = L.run_sc[t][e];
         }
     }
     for (int k = cnt + lane; k < K; k += WAVE) {
         out_idx[k] = -1;
+#pragma unroll
         for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + k] = -INFINITY;
     }
 }
@@ -467,25 +578,32 @@ static hipError_t dispatch_approx(const Shape &s, const TQ *qv, const float *b_s
     return hipErrorInvalidValue;
 }
 
-template <typename TQ, typename TS>
-static hipError_t dispatch_select(const Shape &s, const TQ *qv, const TS *ks, const float *b_sum,
-                                  const ScoreWorkspace &ws, int32_t *sel_idx, float *sel_score, hipStream_t st) {
+template <typename TQ, int D, int G>
+static void go_select(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, int32_t *sel_idx,
+                      float *sel_score, hipStream_t st) {
     const int64_t rows = (int64_t)s.B * s.H_kv * s.N;
-    const int nmax = s.N > 0 ? max(0, (s.N - 1) / s.S - s.W / s.S) : 0;
-    const int J = (nmax + WAVE - 1) / WAVE;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, st, qv, ks, b_sum, (const float *)ws.agg, (const float *)ws.err,
-                           sel_idx, sel_score, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.D, s.S, s.W, s.K, s.scale,
-                           ws.per_bg);
+        hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const float *)ws.kcm, b_sum, (const float *)ws.agg,
+                           (const float *)ws.err, sel_idx, sel_score, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W,
+                           s.K, s.scale, ws.per_bg);
     };
-    if (J <= 2) go(select_kernel<TQ, TS, 2>);
-    else if (J <= 8) go(select_kernel<TQ, TS, 8>);
-    else if (J <= 32) go(select_kernel<TQ, TS, 32>);
-    else if (J <= 64) go(select_kernel<TQ, TS, 64>);
-    else if (J <= 128) go(select_kernel<TQ, TS, 128>);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (s.GLM == 1 && G > 1) go(select_kernel<TQ, D, G, true>);
+    else go(select_kernel<TQ, D, G, false>);
+}
+
+template <typename TQ>
+static hipError_t dispatch_select(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws,
+                                  int32_t *sel_idx, float *sel_score, hipStream_t st) {
+#define HILS_SEL(DD, GG)                                                     \
+    if (s.D == DD && s.G == GG) {                                            \
+        go_select<TQ, DD, GG>(s, qv, b_sum, ws, sel_idx, sel_score, st);     \
+        return hipGetLastError();                                            \
+    }
+    HILS_SEL(64, 1) HILS_SEL(64, 2) HILS_SEL(64, 4) HILS_SEL(64, 8)
+    HILS_SEL(128, 1) HILS_SEL(128, 2) HILS_SEL(128, 4) HILS_SEL(128, 8)
+#undef HILS_SEL
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum, const float *b_sum, const void *h,
@@ -500,11 +618,11 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     if (krows > 0) {
         const dim3 grid((unsigned)((krows + 15) / 16)), block(256);
         if (s.sum_bf16) {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
         } else {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.knorm, s.C, krows);
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
         }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -534,13 +652,11 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     if (qcal || !s.io_bf16) {
         const float *qv = qcal ? ws.q_s : (const float *)q;
         if ((e = dispatch_approx<float>(s, qv, b_sum, ws, kappa, st)) != hipSuccess) return e;
-        return s.sum_bf16 ? dispatch_select<float, bf16>(s, qv, (const bf16 *)k_sum, b_sum, ws, sel_idx, sel_score, st)
-                          : dispatch_select<float, float>(s, qv, (const float *)k_sum, b_sum, ws, sel_idx, sel_score, st);
+        return dispatch_select<float>(s, qv, b_sum, ws, sel_idx, sel_score, st);
     }
     const bf16 *qv = (const bf16 *)q;
     if ((e = dispatch_approx<bf16>(s, qv, b_sum, ws, kappa, st)) != hipSuccess) return e;
-    return s.sum_bf16 ? dispatch_select<bf16, bf16>(s, qv, (const bf16 *)k_sum, b_sum, ws, sel_idx, sel_score, st)
-                      : dispatch_select<bf16, float>(s, qv, (const float *)k_sum, b_sum, ws, sel_idx, sel_score, st);
+    return dispatch_select<bf16>(s, qv, b_sum, ws, sel_idx, sel_score, st);
 }
 
 }  // namespace hils

@@ -155,3 +155,12 @@ def test_decode_argument_checks(lib):
     st = lib.hils_decode(ctypes.byref(cfg), 2, A, A, A, A, A, A, 70000, A, None, None, None, 0, 0, A, None, None, A2,
                          need, None)
     assert st == hb.HILS_ERR_UNSUPPORTED
+
+
+def test_fused_shape_beyond_lds_is_unsupported(lib):
+    """G = 1 at S = 128, d = 128 with K = 128 and 4096 chunks has no block
+    shape whose LDS fits: rejected before launch."""
+    cfg = _cfg(H_q=2, H_kv=2, S=128, W=256, K=128, N=128 * 4096)
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
+    st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need, None)
+    assert st == hb.HILS_ERR_UNSUPPORTED and "LDS" in hb.last_error()

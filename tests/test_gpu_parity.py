@@ -37,6 +37,9 @@ CASES = {
     "fp32_g4_s128": dict(seed=27, io=F32, B=1, H_q=4, H_kv=1, d=128, N=1500, S=128, W=128, K=3),
     "qcal_small": dict(seed=28, io=BF, B=1, H_q=4, H_kv=1, d=128, N=2048, S=128, W=256, K=4, d_model=256, r=16),
     "few_candidates": dict(seed=29, io=BF, B=1, H_q=4, H_kv=2, d=128, N=1024, S=64, W=512, K=16),
+    # block shapes picked by LDS capacity: 4-wave blocks at S=128 with K=64 / G=2
+    "s128_k64": dict(seed=33, io=BF, B=1, H_q=8, H_kv=2, d=128, N=9000, S=128, W=256, K=64),
+    "s128_g2": dict(seed=34, io=BF, B=1, H_q=4, H_kv=2, d=128, N=6000, S=128, W=128, K=32),
 }
 
 
