@@ -249,6 +249,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy a MIB-MiB buffer twice (a device-to-device copy and an "
+                         "elementwise negation), the known-size reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -315,6 +318,17 @@ def main():
                             "roofline": {"kernel": "hils_decode (all phases)", "bound": "hbm", "achieved": gbs,
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "algorithmic_bytes": by}}
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                                      "kernels": ["device-to-device copy", "elementwise neg"]}
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
