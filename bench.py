@@ -226,7 +226,7 @@ def cpu_baseline(pre, budget_s):
     t0 = time.perf_counter()
     oracle.forward_rows(oc, q, k, v, ks, bs, rows=probe)
     t_probe = time.perf_counter() - t0
-    R = int(max(32, min(4096, 32 * max(0.0, budget_s - t_sum - t_probe) / max(t_probe, 1e-6))))
+    R = int(max(32, min(cfg.N, 32 * max(0.0, budget_s - t_sum - t_probe) / max(t_probe, 1e-6))))
     rows = np.sort(rng.choice(cfg.N, size=R, replace=False))
     t0 = time.perf_counter()
     oracle.forward_rows(oc, q, k, v, ks, bs, rows=rows)

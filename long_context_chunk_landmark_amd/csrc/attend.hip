@@ -47,10 +47,15 @@
 //     of (batch, group, query block) work items, so the blocks resident on
 //     one XCD's L2 are neighbouring query blocks whose unions overlap.
 #include "hils_device.hpp"
+#include <type_traits>
+
 #include "hils_internal.hpp"
 
 #define HILS_GPTR(p) ((const void __attribute__((address_space(1))) *)(p))
 #define HILS_LPTR(p) ((void __attribute__((address_space(3))) *)(p))
+// Word 3 of a raw buffer resource on CDNA: 32-bit data format (untyped
+// dword loads), no swizzle, no index stride.
+#define BUF_RSRC_WORD3 0x00020000
 
 namespace hils {
 
@@ -108,6 +113,12 @@ __host__ __device__ __forceinline__ int swz(int row) {
     return NB == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
+#ifndef LA_QK
+#define LA_QK 4
+#endif
+#ifndef LA_PV
+#define LA_PV 4
+#endif
 template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
 struct AttendCfg {
     static constexpr int QPT = 16 / G;               // queries per 16-row tile
@@ -121,8 +132,6 @@ struct AttendCfg {
     static constexpr int PK = S * D * 2 / 1024;      // 1 KB pieces of a K tile
     static constexpr int PV = D * S * 2 / 1024;      // 1 KB pieces of a V^T tile
     static constexpr int LPS = (PK + PV) / NWAVE;    // DMA loads per lane per chunk
-    static constexpr int LINES = 2 * S * D * 2 / 128;                 // 128-byte lines per chunk
-    static constexpr int PFI = (LINES / NWAVE + WAVE - 1) / WAVE;      // L2-warming loads per lane
     static_assert((PK + PV) % NWAVE == 0, "pieces per wave");
 };
 
@@ -139,11 +148,11 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     int nqb, int64_t n_items, int64_t per_xcd) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
-    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS, LINES = Cf::LINES, PFI = Cf::PFI;
+    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS;
     constexpr int NT = NWAVE * 64;
     // chunk ring: stage s holds the K tile [S][NBK] then the V^T tile [D][NBV]
     __shared__ u32x4 ring[NSTAGE][S * NBK + D * NBV];
-    __shared__ u32x4 sink[WAVE];  // destination of the L2-warming DMA (never read)
+    __shared__ u32x4 sink[WAVE];  // destination of the DMA issued past the last chunk (never read)
     auto k_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBK]>(&ring[buf][0]); };
     auto v_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBV]>(&ring[buf][S * NBK]); };
     extern __shared__ int dyn[];
@@ -272,158 +281,198 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
 
     // ---- DMA of chunk tiles into the ring: piece p of wave w, lane l.
     // Every call issues exactly LPS loads per lane (past the end they land
-    // in the sink) so the vmcnt bookkeeping below is a constant.
+    // in the sink) so the vmcnt bookkeeping below is a constant.  Buffer
+    // loads: the resource starts at the chunk and ends at token N, so rows
+    // of a partial last chunk read as zeros (those keys are masked), and the
+    // per-lane address is a 32-bit offset.
     auto issue = [&](int it) {
         const bool real = it < T;
-        const int c = chunk_of(real ? it : T - 1);
+        const int c = __builtin_amdgcn_readfirstlane(chunk_of(real ? it : T - 1));
         const int buf = it % NSTAGE;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kbase + (int64_t)c * S * D), (short)0, (N - c * S) * D * 2, BUF_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vtbase + (int64_t)c * D * S), (short)0, D * S * 2, BUF_RSRC_WORD3);
 #pragma unroll
         for (int j = 0; j < LPS; ++j) {
             const int p = wave * LPS + j;
             if (p < PK) {
                 constexpr int RPP = 1024 / (D * 2);  // K rows per piece
                 const int row = p * RPP + lane / NBK, blk = lane % NBK;
-                const int64_t key = min((int64_t)c * S + row, (int64_t)N - 1);
-                const bf16 *src = kbase + key * D + ((blk ^ swz<NBK>(row)) * 8);
-                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(real ? &k_tile(buf)[p * RPP][0] : &sink[0]),
-                                                 16, 0, 0);
+                const int off = (row * D + (blk ^ swz<NBK>(row)) * 8) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    kr, HILS_LPTR(real ? &k_tile(buf)[p * RPP][0] : &sink[0]), 16, off, 0, 0, 0);
             } else {
                 constexpr int RPP = 1024 / (S * 2);  // V^T rows per piece
                 const int pv = p - PK;
                 const int row = pv * RPP + lane / NBV, blk = lane % NBV;
-                const f16 *src = vtbase + ((int64_t)c * D + row) * S + ((blk ^ swz<NBV>(row)) * 8);
-                __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(real ? &v_tile(buf)[pv * RPP][0] : &sink[0]),
-                                                 16, 0, 0);
+                const int off = (row * S + (blk ^ swz<NBV>(row)) * 8) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    vr, HILS_LPTR(real ? &v_tile(buf)[pv * RPP][0] : &sink[0]), 16, off, 0, 0, 0);
             }
         }
     };
-    // L2 warming: touch each 128-byte line of chunk `it` (K lines, then V^T
-    // lines) with a DMA into the sink; PFI loads per lane, always issued.
-    // Wave w covers lines [w * LPW, (w + 1) * LPW); lanes beyond LPW repeat
-    // addresses of the same wave, which the load unit merges.
-    auto prefetch = [&](int it) {
-        constexpr int LPW = LINES / NWAVE;
-        const int c = chunk_of(min(it, T - 1));
+    // Software pipeline of n LDS fragment reads, each feeding M MFMAs (one
+    // per tile of the wave): the scheduler issues LA reads ahead, then
+    // alternates M MFMAs with one read, so about LA fragments are live.
+    auto pipeline = [&](auto n_c, auto m_c, auto la_c) {
+        constexpr int n = decltype(n_c)::value, M = decltype(m_c)::value, LA = decltype(la_c)::value;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
 #pragma unroll
-        for (int j = 0; j < PFI; ++j) {
-            const int line = wave * LPW + (j * WAVE + lane) % LPW;
-            const char *src = line < LINES / 2
-                                  ? (const char *)(kbase + min((int64_t)c * S * D + line * 64, (int64_t)N * D - 64))
-                                  : (const char *)(vtbase + ((int64_t)c * D * S + (line - LINES / 2) * 64));
-            __builtin_amdgcn_global_load_lds(HILS_GPTR(src), HILS_LPTR(&sink[0]), 16, 0, 0);
+        for (int i = 0; i < n - LA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, M * LA, 0);
     };
-
-    // S^T tile: acc[kt][i] = q_row . k_{16kt + 4grp + i}
-    // (the scheduling barriers keep one key tile's operands in flight at a
-    // time: the block holds up to 16 waves, 128 registers each)
-    auto qk = [&](const u32x4 (*kt_lds)[NBK], const bf16x8 (&qt)[KS], f32x4 (&acc)[KT]) {
+    // S^T tiles: acc[t][kt][i] = q_row(t) . k_{16kt + 4grp + i}.  One K
+    // fragment read feeds the MFMA of every tile of the wave; the KT key
+    // tiles are independent accumulators, visited k-step major.
+    auto qk = [&](auto mask_c, const u32x4 (*kt_lds)[NBK], f32x4 (&acc)[TPW][KT]) {
+        constexpr int MASK = decltype(mask_c)::value, NM = __builtin_popcount(MASK);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int row = 16 * kt + r;
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+            for (int kt = 0; kt < KT; ++kt) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        (void)NM;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int row = 16 * kt + r;
                 const u32x4 raw = kt_lds[row][(4 * s + grp) ^ swz<NBK>(row)];
                 bf16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
-                acc[kt] = mfma16(a, qt[s], acc[kt]);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if ((MASK >> t) & 1) acc[t][kt] = mfma16(a, qf[t][s], acc[t][kt]);
             }
-            if constexpr (NWAVE == 16) __builtin_amdgcn_sched_barrier(0);
-        }
+        pipeline(std::integral_constant<int, KS * KT>{}, std::integral_constant<int, NM>{},
+                 std::integral_constant<int, LA_QK>{});
+        __builtin_amdgcn_sched_barrier(0);
     };
-    // O^T += V^T P^T with P^T taken from the exponentiated S^T
-    auto pv = [&](const u32x4 (*vt_lds)[NBV], const f32x4 (&p)[KT], f32x4 (&o)[DT]) {
+    // O^T += V^T P^T for every tile of the wave, P^T packed from the
+    // exponentiated S^T; one V^T fragment read feeds every tile.
+    auto pv = [&](auto mask_c, const u32x4 (*vt_lds)[NBV], const f32x4 (&p)[TPW][KT]) {
+        constexpr int MASK = decltype(mask_c)::value, NM = __builtin_popcount(MASK);
+        f16x8 bp[TPW][PS];
 #pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-            f16x8 bp;
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bp[i] = (f16)p[2 * ps][i];
-                bp[4 + i] = (f16)p[2 * ps + 1][i];
-            }
+            for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bp[t][ps][i] = (f16)p[t][2 * ps][i];
+                    bp[t][ps][4 + i] = (f16)p[t][2 * ps + 1][i];
+                }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int row = 16 * dt + r;
                 const u32x4 raw = vt_lds[row][(4 * ps + grp) ^ swz<NBV>(row)];
                 f16x8 a;
                 __builtin_memcpy(&a, &raw, 16);
-                o[dt] = mfma16h(a, bp, o[dt]);
-                if constexpr (NWAVE == 16)
-                    if ((dt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if ((MASK >> t) & 1) O[t][dt] = mfma16h(a, bp[t][ps], O[t][dt]);
             }
-        }
+        pipeline(std::integral_constant<int, PS * DT>{}, std::integral_constant<int, NM>{},
+                 std::integral_constant<int, LA_PV>{});
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- pipelined walk: union chunks, then the window.  Step j issues
-    // chunk j + NSTAGE - 1 into the ring and warms chunk j + NSTAGE + 1.
+    // chunk j + NSTAGE - 1 into the ring.
 #pragma unroll
-    for (int it = 0; it < NSTAGE - 1; ++it) {
-        issue(it);
-        prefetch(it + 2);
-    }
+    for (int it = 0; it < NSTAGE - 1; ++it) issue(it);
     for (int it = 0; it < T; ++it) {
-        // younger than chunk it's loads: its own step's prefetch and the
-        // NSTAGE - 2 later steps
-        wait_vmcnt<PFI + (NSTAGE - 2) * (LPS + PFI)>();
+        // younger than chunk it's loads: those of the NSTAGE - 2 later chunks
+        wait_vmcnt<(NSTAGE - 2) * LPS>();
         __builtin_amdgcn_s_barrier();
         issue(it + NSTAGE - 1);
-        prefetch(it + NSTAGE + 1);
         const int buf = it % NSTAGE;
         const int c = chunk_of(it);
+        f32x4 acc[TPW][KT];
         if (it < U) {
+            // a wave computes its tiles when one of its rows selected chunk c;
+            // rows that did not select it get weight 0 (exact zeros in O)
+            bool act[TPW];
+            bool any = false;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                const bool active = nch[t] == c;
-                if (__ballot(active) == 0ull) continue;
-                f32x4 acc[KT];
-                qk(k_tile(buf), qf[t], acc);
-                float cmax = -INFINITY;
+                act[t] = nch[t] == c;
+                any |= act[t];
+            }
+            if (__ballot(any) == 0ull) continue;
+            // tiles of the wave with a selecting row (wave-uniform)
+            int wmask = 0;
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+            for (int t = 0; t < TPW; ++t) wmask |= (__ballot(act[t]) != 0ull) << t;
+            auto sel_step = [&](auto mask_c) {
+                constexpr int MASK = decltype(mask_c)::value;
+                qk(mask_c, k_tile(buf), acc);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[kt][i] *= scale_log2;
-                        cmax = fmaxf(cmax, acc[kt][i]);
-                    }
-                cmax = rows4_max(cmax);
-                float lc = 0.f;
+                for (int t = 0; t < TPW; ++t) {
+                    if (!((MASK >> t) & 1)) continue;
+                    float cmax = -INFINITY;
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[kt][i] = exp2f(acc[kt][i] - cmax);
-                        lc += acc[kt][i];
-                    }
-                lc = rows4_sum(lc);
-                const float f = active ? nwt[t] / lc : 0.f;
+                        for (int i = 0; i < 4; ++i) {
+                            acc[t][kt][i] *= scale_log2;
+                            cmax = fmaxf(cmax, acc[t][kt][i]);
+                        }
+                    cmax = rows4_max(cmax);
+                    float lc = 0.f;
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[kt][i] *= f;
-                pv(v_tile(buf), acc, O[t]);
-                if (active) {
+                        for (int i = 0; i < 4; ++i) {
+                            acc[t][kt][i] = exp2f(acc[t][kt][i] - cmax);
+                            lc += acc[t][kt][i];
+                        }
+                    lc = rows4_sum(lc);
+                    const float f = act[t] ? nwt[t] / lc : 0.f;
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[t][kt][i] *= f;
+                }
+                pv(mask_c, v_tile(buf), acc);
+            };
+            if constexpr (TPW == 1) {
+                sel_step(std::integral_constant<int, 1>{});
+            } else {
+                if (wmask == 1) sel_step(std::integral_constant<int, 1>{});
+                else if (wmask == 2) sel_step(std::integral_constant<int, 2>{});
+                else sel_step(std::integral_constant<int, 3>{});
+            }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                if (act[t]) {
                     const int nx = ++cur[t];
                     const int m = qrow[t], e = hrow[t] - g * G;
                     nch[t] = nx < nsel[t] ? (int)sel_l[m * K + nx] : 0x7fffffff;
                     nwt[t] = nx < nsel[t] ? (float)wt_l[(m * G + e) * K + nx] : 0.f;
                 }
-            }
         } else {
             const bool diag = c == qc;
+            constexpr int ALL = (1 << TPW) - 1;
+            qk(std::integral_constant<int, ALL>{}, k_tile(buf), acc);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int iq = i0 + qrow[t];
-                f32x4 acc[KT];
-                qk(k_tile(buf), qf[t], acc);
                 float cmax = -INFINITY;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int j = c * S + 16 * kt + 4 * grp + i;
-                        const float x = (diag && j > iq) ? -INFINITY : acc[kt][i] * scale_log2;
-                        acc[kt][i] = x;
+                        const float x = (diag && j > iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
+                        acc[t][kt][i] = x;
                         cmax = fmaxf(cmax, x);
                     }
                 cmax = rows4_max(cmax);
@@ -434,16 +483,16 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        acc[kt][i] = exp2f(acc[kt][i] - mnew);
-                        ls += acc[kt][i];
+                        acc[t][kt][i] = exp2f(acc[t][kt][i] - mnew);
+                        ls += acc[t][kt][i];
                     }
                 ls = rows4_sum(ls);
                 lrun[t] = lrun[t] * alpha + ls;
                 mrun[t] = mnew;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
-                pv(v_tile(buf), acc, O[t]);
             }
+            pv(std::integral_constant<int, ALL>{}, v_tile(buf), acc);
         }
     }
     wait_vmcnt<0>();  // no DMA outstanding when the block retires
@@ -663,7 +712,7 @@ static hipError_t dispatch_w(const Shape &s, const void *q, const void *k, const
 
 template <int D, int S, int G>
 static bool fits_any(const Shape &s) {
-    return fits<D, S, G, 8, 2>(s) || fits<D, S, G, 16, 1>(s) || fits<D, S, G, 8, 1>(s) || fits<D, S, G, 4, 1>(s) ||
+    return fits<D, S, G, 16, 1>(s) || fits<D, S, G, 8, 1>(s) || fits<D, S, G, 4, 1>(s) ||
            fits<D, S, G, 2, 1>(s);
 }
 
