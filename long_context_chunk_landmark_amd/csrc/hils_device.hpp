@@ -89,6 +89,47 @@ __device__ __forceinline__ float rows4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// DPP move within 16-lane rows (CTRL: quad_perm 0x00-0xFF, row_mirror
+// 0x140, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum / max over the 16 lanes of a DPP row (every lane gets the result).
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) { return rows4_sum(row_sum16(v)); }
+__device__ __forceinline__ float wave_max_f(float v) { return rows4_max(row_max16(v)); }
+
+// Transpose-reduce over the 16 lanes of a DPP row: lane c of the row holds
+// v[0..15]; on return it holds sum over the row's lanes of v[c].  Four
+// butterfly steps; each partner differs in the bit of c that picks which
+// half of the remaining values a lane keeps (row_mirror flips bit 3,
+// row_half_mirror bit 2, the quad permutations bits 1 and 0).
+__device__ __forceinline__ float transpose_sum16(const float (&v)[16], int c) {
+    float w[8], x[4], y[2];
+    const bool b3 = (c >> 3) & 1, b2 = (c >> 2) & 1, b1 = (c >> 1) & 1, b0 = c & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = (b3 ? v[j + 8] : v[j]) + dpp<0x140>(b3 ? v[j] : v[j + 8]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (b2 ? w[j + 4] : w[j]) + dpp<0x141>(b2 ? w[j] : w[j + 4]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) y[j] = (b1 ? x[j + 2] : x[j]) + dpp<0x4E>(b1 ? x[j] : x[j + 2]);
+    return (b0 ? y[1] : y[0]) + dpp<0xB1>(b0 ? y[0] : y[1]);
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) { return xor_sum_i<1, 32>(v); }
 __device__ __forceinline__ float wave_max(float v) { return xor_max<1, 32>(v); }
 

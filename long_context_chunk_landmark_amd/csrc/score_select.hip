@@ -297,18 +297,6 @@ __device__ __forceinline__ uint64_t kth_largest64(const uint64_t (&keys)[NV], in
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Sum over the 16 lanes of a DPP row (every lane gets the row total).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x140>(v);  // row_mirror
-    return v;
-}
 // Sum over aligned groups of L lanes (L = 2..64), result in every lane.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
@@ -391,22 +379,24 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     uint32_t thr_key = 0;
     const bool rank_needed = n > K;
     if (rank_needed) {
-        // tau' = K-th largest of the per-lane top-R approximate scores
-        // (R = ceil(K/64)); those are >= K distinct candidates (n > K), so
-        // tau' <= the K-th largest approximate score overall
-        uint32_t m1 = 0u, m2 = 0u;
+        // tau' = K-th largest of the multiset of per-lane top-4 approximate
+        // scores: those entries are distinct candidates, so at least K
+        // candidates score >= tau' and tau' <= the K-th largest approximate
+        // score (equal to it unless a lane holds more than four of the top K)
+        uint32_t m0 = 0u, m1 = 0u, m2 = 0u, m3 = 0u;
         for (int j = 0; j < J; ++j) {
             const int c = j * WAVE + lane;
             const uint32_t x = c < n ? ord_key(ar[c]) : 0u;
+            m3 = max(m3, min(m2, x));
             m2 = max(m2, min(m1, x));
-            m1 = max(m1, x);
+            m1 = max(m1, min(m0, x));
+            m0 = max(m0, x);
         }
-        const bool two = K > WAVE;
         uint32_t T = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
-            int cnt = __popcll(__ballot(m1 >= cand));
-            if (two) cnt += __popcll(__ballot(m2 >= cand));
+            const int cnt = __popcll(__ballot(m0 >= cand)) + __popcll(__ballot(m1 >= cand)) +
+                            __popcll(__ballot(m2 >= cand)) + __popcll(__ballot(m3 >= cand));
             if (cnt >= K) T = cand;
         }
         // every exact top-K member has approximate score >= tau' - 2E

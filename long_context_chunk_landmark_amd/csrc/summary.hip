@@ -11,10 +11,13 @@
 // that read that kv head, so the S x d key tile is loaded once into
 // registers with 16-byte loads and reused GLM times.  Reductions over the
 // chunk's keys are butterfly shuffles inside the wavefront; no LDS.
+#include <type_traits>
+
 #include "hils_device.hpp"
 #include "hils_internal.hpp"
 
 namespace hils {
+
 
 template <typename T, typename TS, int D, int S, int GLM>
 __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm,
@@ -93,6 +96,122 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
     }
 }
 
+// Fast path for bf16 keys at d = 128 (16 lanes per key row).  Keys go in
+// blocks of 64 rows: lane (col, rsub) holds rows 4t + rsub of the block,
+// t < 16, as packed bf16.  Per landmark head, the partial dots (packed
+// bf16 dot2 instructions, fp32 accumulation) are transpose-reduced over the
+// 16 lanes of the DPP row, after which the lane holds the logit of block
+// row 4*col + rsub (base-2 scaled).  p goes through LDS, transposed per
+// rsub, to every lane for the weighted key sum.  A 128-key chunk keeps one
+// block in registers and re-reads the other (from L2) when it needs it.
+template <typename TS, int S, int GLM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void landmark_summary_d128_kernel(
+    const bf16 *__restrict__ k, const bf16 *__restrict__ q_lm, TS *__restrict__ k_sum, float *__restrict__ b_sum,
+    int H_kv, int N, int C, float scale, int64_t total_units) {
+    constexpr int D = 128, NB = S / 64;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    __shared__ float p_lds[4][4][S / 4];  // [wave of block][rsub][block * 16 + t]
+    const int lane = lane_id();
+    const int64_t unit = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    if (unit >= total_units) return;
+    const int c = (int)(unit % C);
+    const int64_t bg = unit / C;  // b * H_kv + g
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int col = lane & 15, rsub = lane >> 4;
+    float(*pw)[S / 4] = p_lds[(threadIdx.x / WAVE) & 3];
+    const bf16 *kb = k + (bg * N + (int64_t)c * S) * D + col * 8;
+    const float sl2 = scale * LOG2E;
+    const int H_lm = H_kv * GLM;
+
+    u32x4 kx[16];
+    auto load_block = [&](int blk) {
+        // an opaque block offset keeps the reloads inside the head loop
+        // (hoisted, both blocks would stay live in registers)
+        int off = 64 * blk * D;
+        asm volatile("" : "+s"(off));
+#pragma unroll
+        for (int t = 0; t < 16; ++t) kx[t] = *(const u32x4 *)(kb + off + (t * 4 + rsub) * D);
+    };
+    load_block(NB - 1);
+#pragma unroll 1
+    for (int e = 0; e < GLM; ++e) {
+        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;
+        const u32x4 qr = *(const u32x4 *)(q_lm + lrow * D + col * 8);
+        float lg[NB];
+#pragma unroll
+        for (int blk = NB - 1; blk >= 0; --blk) {
+            if (blk != NB - 1) load_block(blk);
+            float part[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float acc = 0.f;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t qa = qr[x], kb2 = kx[t][x];
+                    bf16x2 a2, b2;
+                    __builtin_memcpy(&a2, &qa, 4);
+                    __builtin_memcpy(&b2, &kb2, 4);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, acc, false);
+                }
+                part[t] = acc;
+            }
+            lg[blk] = transpose_sum16(part, col) * sl2;
+        }
+        float m = lg[0];
+#pragma unroll
+        for (int h = 1; h < NB; ++h) m = fmaxf(m, lg[h]);
+        m = wave_max_f(m);
+        float ex[NB], z = 0.f, ez = 0.f;
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+            ex[h] = exp2f(lg[h] - m);
+            z += ex[h];
+            ez = fmaf(ex[h], lg[h] - m, ez);
+        }
+        z = wave_sum_f(z);
+        ez = wave_sum_f(ez);
+        const float inv_z = 1.f / z;
+        // entropy = ln 2 * (log2 Z - sum_j p_j (a2_j - m)), a2 = base-2 logits
+        const float ent = LN2 * (log2f(z) - ez * inv_z);
+        wave_sync();
+#pragma unroll
+        for (int h = 0; h < NB; ++h) pw[rsub][16 * h + col] = ex[h] * inv_z;
+        wave_sync();
+        float acc[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            if (NB > 1) load_block(blk);
+#pragma unroll
+            for (int t0 = 0; t0 < 16; t0 += 4) {
+                const f32x4 p4 = *(const f32x4 *)&pw[rsub][16 * blk + t0];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        // widen inside the head loop (an opaque copy keeps the
+                        // compiler from hoisting 128 widened values out of it)
+                        uint32_t w = kx[t0 + u][x];
+                        asm volatile("" : "+v"(w));
+                        acc[2 * x] = fmaf(p4[u], __uint_as_float(w << 16), acc[2 * x]);
+                        acc[2 * x + 1] = fmaf(p4[u], __uint_as_float(w & 0xffff0000u), acc[2 * x + 1]);
+                    }
+            }
+        }
+        if (NB > 1) load_block(NB - 1);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = rows4_sum(acc[x]);
+        if (rsub == 0) {
+            TS *dst = k_sum + lrow * D + col * 8;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) dst[x] = from_f32<TS>(acc[x]);
+            if (col == 0) b_sum[lrow] = ent;
+        }
+    }
+}
+
 template <typename T, typename TS, int D, int S>
 static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
                            hipStream_t st) {
@@ -103,6 +222,16 @@ static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const T *)k, (const T *)q_lm, (TS *)k_sum, b_sum, s.H_kv, s.N,
                            s.C, s.scale, units);
     };
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
+        switch (s.GLM) {
+            case 1: go(landmark_summary_d128_kernel<TS, S, 1>); break;
+            case 2: go(landmark_summary_d128_kernel<TS, S, 2>); break;
+            case 4: go(landmark_summary_d128_kernel<TS, S, 4>); break;
+            case 8: go(landmark_summary_d128_kernel<TS, S, 8>); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (s.GLM) {
         case 1: go(landmark_summary_kernel<T, TS, D, S, 1>); break;
         case 2: go(landmark_summary_kernel<T, TS, D, S, 2>); break;
