@@ -21,6 +21,8 @@
 // A selected chunk enters as the state (max = s^_c, mass = 1, out = its
 // normalised intra-chunk output); window chunks enter with their raw
 // softmax statistics; the merge of all states is exactly the fused output.
+#include <type_traits>
+
 #include "hils_device.hpp"
 #include "hils_internal.hpp"
 
@@ -30,7 +32,9 @@ namespace {
 
 struct DecodeLayout {
     int splits;  // phase A blocks per (seq, group)
-    int nsb;     // phase B blocks per (seq, group)
+    int nsb;     // phase B blocks per (seq, group) (generic attend)
+    int np;      // partial (m, l, o) slots per (seq, query head)
+    bool fast;   // bf16, d = 128, S = 64: one wave per chunk of the list
     size_t off_qs, off_pkey, off_psc, off_sel, off_selsc, off_pm, off_pl, off_po, total;
 };
 
@@ -38,6 +42,8 @@ DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
     DecodeLayout L;
     L.splits = decode_splits(s, max_pages);
     L.nsb = std::max(1, std::min(16, (s.K + s.W / s.S + 1 + 3) / 4));
+    L.fast = s.io_bf16 && s.D == 128 && s.S == 64;
+    L.np = L.fast ? s.K + s.W / s.S + 1 : L.nsb;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -50,9 +56,9 @@ DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
     L.off_psc = take(NS * s.H_kv * L.splits * s.K * s.G * 4);
     L.off_sel = take(NS * s.H_kv * s.K * 4);
     L.off_selsc = take(NS * s.H_q * s.K * 4);
-    L.off_pm = take(NS * s.H_q * L.nsb * 4);
-    L.off_pl = take(NS * s.H_q * L.nsb * 4);
-    L.off_po = take(NS * s.H_q * L.nsb * s.D * 4);
+    L.off_pm = take(NS * s.H_q * L.np * 4);
+    L.off_pl = take(NS * s.H_q * L.np * 4);
+    L.off_po = take(NS * s.H_q * L.np * s.D * 4);
     L.total = o;
     return L;
 }
@@ -134,52 +140,63 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int32_t *bt = block_table + (int64_t)seq * max_pages;
     const int lbase = g * G * H_lm / H_q;  // first landmark head of the group
 
-    for (int base = wave * CPS; base < cnt; base += 4 * CPS) {
-        const int lc = base + cs;
-        const bool ok = lc < cnt;
-        const int c = c_lo + (ok ? lc : 0);
-        const int64_t page = bt[c];
-        Vec16<TS> kv[GLM];
+    // each wave scores a contiguous range of the split (at most 128
+    // candidates); its block-table entries are fetched once, then U steps
+    // of CPS candidates have their summary rows in flight together
+    constexpr int U = 4;
+    const int per_w = (cnt + 3) / 4;
+    const int w_lo = min(cnt, wave * per_w), w_hi = min(cnt, w_lo + per_w);
+    const int pg0 = w_lo + lane < w_hi ? bt[c_lo + w_lo + lane] : 0;
+    const int pg1 = w_lo + 64 + lane < w_hi ? bt[c_lo + w_lo + 64 + lane] : 0;
+    for (int base = w_lo; base < w_hi; base += U * CPS) {
+        Vec16<TS> kv[U][GLM];
+        float bias[U][GLM];
+        bool okv[U];
 #pragma unroll
-        for (int e = 0; e < GLM; ++e) kv[e] = load16(ksum_cache + (page * H_lm + lbase + e) * D + col * E);
-        float agg = -INFINITY;
-        float sc[G];
+        for (int u = 0; u < U; ++u) {
+            const int lc = base + u * CPS + cs;
+            okv[u] = lc < w_hi;
+            const int rel = (okv[u] ? lc : w_lo) - w_lo;
+            const int p0 = __shfl(pg0, rel & 63, WAVE), p1 = __shfl(pg1, rel & 63, WAVE);
+            const int64_t page = rel < 64 ? p0 : p1;
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const int le = GLM == 1 ? 0 : e;
-            float part = 0.f;
-#pragma unroll
-            for (int x = 0; x < E; ++x) part = fmaf(qv[e][x], kv[le].get(x), part);
-            part = xor_sum<1, LPR / 2>(part);
-            sc[e] = fmaf(scale, part, bsum_cache[page * H_lm + lbase + le]);
-            agg = fmaxf(agg, sc[e]);
+            for (int e = 0; e < GLM; ++e) {
+                kv[u][e] = load16(ksum_cache + (page * H_lm + lbase + e) * D + col * E);
+                bias[u][e] = bsum_cache[page * H_lm + lbase + e];
+            }
         }
-        if (ok && col == 0) {
-            agg_l[lc] = agg;
 #pragma unroll
-            for (int e = 0; e < G; ++e) sc_l[lc][e] = sc[e];
+        for (int u = 0; u < U; ++u) {
+            const int lc = base + u * CPS + cs;
+            float agg = -INFINITY;
+            float sc[G];
+#pragma unroll
+            for (int e = 0; e < G; ++e) {
+                const int le = GLM == 1 ? 0 : e;
+                float part = 0.f;
+#pragma unroll
+                for (int x = 0; x < E; ++x) part = fmaf(qv[e][x], kv[u][le].get(x), part);
+                part = seg_sum<LPR>(part);
+                sc[e] = fmaf(scale, part, bias[u][le]);
+                agg = fmaxf(agg, sc[e]);
+            }
+            if (okv[u] && col == 0) {
+                agg_l[lc] = agg;
+#pragma unroll
+                for (int e = 0; e < G; ++e) sc_l[lc][e] = sc[e];
+            }
         }
     }
     __syncthreads();
     if (wave != 0) return;
-    // local top-K over cnt <= CAPL entries (8 per lane)
+    // local top-K over cnt <= CAPL entries (CAPL / 64 per lane)
     uint64_t keys[CAPL / WAVE];
 #pragma unroll
     for (int v = 0; v < CAPL / WAVE; ++v) {
         const int lc = v * WAVE + lane;
         keys[v] = lc < cnt ? dec_key(agg_l[lc], c_lo + lc) : 0ull;
     }
-    uint64_t T = 1;
-    if (cnt > K) {
-        T = 0;
-        for (int bit = 63; bit >= 0; --bit) {
-            const uint64_t cand = T | (1ull << bit);
-            int c2 = 0;
-#pragma unroll
-            for (int v = 0; v < CAPL / WAVE; ++v) c2 += __popcll(__ballot(keys[v] >= cand));
-            if (c2 >= K) T = cand;
-        }
-    }
+    const uint64_t T = cnt > K ? kth_largest64<CAPL / WAVE>(keys, K) : 1ull;
     const int64_t pbase = (((int64_t)seq * H_kv + g) * splits + sp) * K;
     int outc = 0;
 #pragma unroll
@@ -199,12 +216,12 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
 }
 
 // Phase A2.  One wave per (seq, group): top-K of splits*K partial entries.
-template <int G>
+template <int G, int NVMAX>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const uint64_t *__restrict__ pkey,
                                                           const float *__restrict__ psc, int32_t *sel_ws,
                                                           float *selsc_ws, int32_t *sel_user, int H_q, int H_kv,
                                                           int K, int splits) {
-    constexpr int NVMAX = 32;  // splits * K <= 2048
+    // NVMAX * 64 >= splits * K partial entries
     __shared__ uint64_t kept[128];
     __shared__ int kept_at[128];
     const int g = blockIdx.x, seq = blockIdx.y, lane = lane_id();
@@ -219,17 +236,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const uint64_t *__rest
     int nonempty = 0;
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) nonempty += __popcll(__ballot(keys[v] != 0ull));
-    uint64_t T = 1;
-    if (nonempty > K) {
-        T = 0;
-        for (int bit = 63; bit >= 0; --bit) {
-            const uint64_t cand = T | (1ull << bit);
-            int c2 = 0;
-#pragma unroll
-            for (int v = 0; v < NVMAX; ++v) c2 += __popcll(__ballot(keys[v] >= cand));
-            if (c2 >= K) T = cand;
-        }
-    }
+    const uint64_t T = nonempty > K ? kth_largest64<NVMAX>(keys, K) : 1ull;
     int outc = 0;
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) {
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const uint64_t *__rest
 // list "selected chunks, then window chunks".
 template <typename T, int D, int S, int G>
 __global__ __launch_bounds__(256) void decode_attend_kernel(
-    const float *__restrict__ qs_raw, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
+    const T *__restrict__ q_raw, const T *__restrict__ k_cache, const T *__restrict__ v_cache,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel_ws, const float *__restrict__ selsc_ws, float *pm, float *pl, float *po,
     int H_q, int H_kv, int W, int K, int nsb, float scale) {
@@ -293,7 +300,8 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
     for (int kk = 0; kk < K; ++kk) nsel += sl[kk] >= 0;
     const int total = nsel + (tc - wc0 + 1);
     const int lo = (int)((int64_t)sp * total / nsb), hi = (int)((int64_t)(sp + 1) * total / nsb);
-    for (int x = tid; x < G * D; x += blockDim.x) q_l[x / D][x % D] = qs_raw[((int64_t)seq * H_q + g * G) * D + x];
+    // exact attention uses the raw query (the calibration is for scoring only)
+    for (int x = tid; x < G * D; x += blockDim.x) q_l[x / D][x % D] = to_f32(q_raw[((int64_t)seq * H_q + g * G) * D + x]);
 
     // per-head running state, heads e = wave, wave + 4, ...
     constexpr int HPW = (G + 3) / 4;
@@ -391,6 +399,141 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
     }
 }
 
+// Phase B, fast path (bf16 caches, d = 128, S = 64).  One wave per entry
+// pos of the list "selected chunks, then window chunks" of (seq, group),
+// writing that chunk's partial state per query head: a selected chunk
+// enters as (s^_c, 1, o_c) with o_c its normalised intra-chunk output, a
+// window chunk as its raw softmax statistics (max, mass, unnormalised sum).
+// Lane (col, rsub) holds key rows 4t + rsub, dims 8col..8col+7, of K and V.
+// Logits: packed bf16 dot2 of the raw query with the key slice,
+// transpose-reduced over the 16-lane DPP row (afterwards the lane holds
+// key 4col + rsub).  PV: V rows are repacked as fp16 pairs (keys t, t+1)
+// and combined with fp16 pairs of p by fp16 dot2 with fp32 accumulation;
+// p is exchanged through LDS.  (fp16 holds bf16 values below 65504 exactly;
+// p lies in [0, 1].)
+template <int G>
+__global__ __launch_bounds__(256) void decode_attend_fast_kernel(
+    const bf16 *__restrict__ q_raw, const bf16 *__restrict__ k_cache, const bf16 *__restrict__ v_cache,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel_ws, const float *__restrict__ selsc_ws, float *pm, float *pl, float *po,
+    int H_q, int H_kv, int W, int K, int np, float scale) {
+    constexpr int D = 128, S = 64;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    __shared__ float p_l[4][G][4][16];  // [wave][head][rsub][t]
+    const int g = blockIdx.y, seq = blockIdx.z;
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int col = lane & 15, rsub = lane >> 4;
+    const int pos = blockIdx.x * 4 + wave;
+    if (pos >= np) return;
+    const int t_last = clamp_len(seq_lens[seq], max_pages, S) - 1;
+    const int tc = t_last / S;
+    const int wc0 = max(0, tc - W / S);
+    const int32_t *sl = sel_ws + ((int64_t)seq * H_kv + g) * K;
+    int nsel = 0;
+    for (int k0 = 0; k0 < K; k0 += WAVE) nsel += __popcll(__ballot(k0 + lane < K && sl[k0 + lane] >= 0));
+    const int total = nsel + (tc - wc0 + 1);
+    const int64_t hrow0 = (int64_t)seq * H_q + g * G;  // first query head of the group
+    if (pos >= total) {
+        // unused slot: an empty state
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int64_t hb = (hrow0 + e) * np + pos;
+            if (lane == 0) {
+                pm[hb] = -INFINITY;
+                pl[hb] = 0.f;
+            }
+            po[hb * D + lane] = 0.f;
+            po[hb * D + 64 + lane] = 0.f;
+        }
+        return;
+    }
+    const bool is_sel = pos < nsel;
+    const int c = is_sel ? sl[pos] : wc0 + (pos - nsel);
+    const int64_t page = block_table[(int64_t)seq * max_pages + c];
+    const bf16 *kp = k_cache + (page * H_kv + g) * (int64_t)S * D + col * 8;
+    const bf16 *vp = v_cache + (page * H_kv + g) * (int64_t)S * D + col * 8;
+    u32x4 kx[16], vx[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) kx[t] = *(const u32x4 *)(kp + (t * 4 + rsub) * D);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) vx[t] = *(const u32x4 *)(vp + (t * 4 + rsub) * D);
+    const float sl2 = scale * LOG2E;
+    const int j = 4 * col + rsub;  // key of this lane after the transpose-reduce
+    const bool masked = !is_sel && (c * S + j > t_last);
+
+    float (*pw)[4][16] = p_l[wave];
+    float lsum[G], mx[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+        const u32x4 qr = *(const u32x4 *)(q_raw + (hrow0 + e) * D + col * 8);
+        float part[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t qa = qr[x], kb2 = kx[t][x];
+                bf16x2 a2, b2;
+                __builtin_memcpy(&a2, &qa, 4);
+                __builtin_memcpy(&b2, &kb2, 4);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, acc, false);
+            }
+            part[t] = acc;
+        }
+        // the cross-lane reduction runs on every lane; masking comes after
+        // (inside a conditional it would run with masked lanes disabled)
+        const float tr = transpose_sum16(part, col);
+        const float lg = masked ? -INFINITY : tr * sl2;
+        const float m2 = wave_max_f(lg);
+        const float ex = exp2f(lg - m2);
+        const float l = wave_sum_f(ex);
+        mx[e] = m2;
+        lsum[e] = l;
+        pw[e][rsub][col] = is_sel ? ex / l : ex;
+    }
+    wave_sync();
+    // V as fp16 pairs of consecutive rows: vh[tp][d] = (v[2tp][d], v[2tp+1][d])
+    f16x2 vh[8][8];
+#pragma unroll
+    for (int tp = 0; tp < 8; ++tp)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t a = vx[2 * tp][x], b = vx[2 * tp + 1][x];
+            vh[tp][2 * x] = f16x2{(_Float16)__uint_as_float(a << 16), (_Float16)__uint_as_float(b << 16)};
+            vh[tp][2 * x + 1] =
+                f16x2{(_Float16)__uint_as_float(a & 0xffff0000u), (_Float16)__uint_as_float(b & 0xffff0000u)};
+        }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+        f16x2 bp[8];
+#pragma unroll
+        for (int t0 = 0; t0 < 16; t0 += 4) {
+            const f32x4 p4 = *(const f32x4 *)&pw[e][rsub][t0];
+            bp[t0 / 2] = f16x2{(_Float16)p4[0], (_Float16)p4[1]};
+            bp[t0 / 2 + 1] = f16x2{(_Float16)p4[2], (_Float16)p4[3]};
+        }
+        float o[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            float acc = 0.f;
+#pragma unroll
+            for (int tp = 0; tp < 8; ++tp) acc = __builtin_amdgcn_fdot2(vh[tp][d], bp[tp], acc, false);
+            o[d] = rows4_sum(acc);
+        }
+        const int64_t hb = (hrow0 + e) * np + pos;
+        if (rsub == 0) {
+            float *dst = po + hb * D + col * 8;
+            *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+            *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+        if (lane == 0) {
+            pm[hb] = is_sel ? selsc_ws[(hrow0 + e) * K + pos] : mx[e] * LN2;
+            pl[hb] = is_sel ? 1.f : lsum[e];
+        }
+    }
+}
+
 // Phase B2.  One wave per (seq, head).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
@@ -445,20 +588,36 @@ static hipError_t go_decode(const Shape &s, const DecodeLayout &L, int num_seqs,
         hipLaunchKernelGGL((decode_score_kernel<TS, D, G, G>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
                            bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
                            s.K, L.splits, s.scale);
-    hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(s.H_kv, num_seqs), dim3(64), 0, st, pkey, psc, sel, selsc,
-                       sel_idx, s.H_q, s.H_kv, s.K, L.splits);
-    const size_t dyn = (size_t)S * (D + 1) * 4 + (size_t)S * D * 4;
-    auto att = decode_attend_kernel<T, D, S, G>;
-    if (dyn > 48 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void *)att, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (e != hipSuccess) return e;
+    {
+        const int nv = (L.splits * s.K + WAVE - 1) / WAVE;
+        auto mg = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(s.H_kv, num_seqs), dim3(64), 0, st, pkey, psc, sel, selsc, sel_idx, s.H_q,
+                               s.H_kv, s.K, L.splits);
+        };
+        if (nv <= 4) mg(decode_merge_kernel<G, 4>);
+        else if (nv <= 8) mg(decode_merge_kernel<G, 8>);
+        else if (nv <= 16) mg(decode_merge_kernel<G, 16>);
+        else mg(decode_merge_kernel<G, 32>);
     }
-    hipLaunchKernelGGL(att, dim3(L.nsb, s.H_kv, num_seqs), dim3(256), dyn, st, qs,
-                       (const T *)k_cache, (const T *)v_cache, block_table, max_pages, seq_lens, sel, selsc, pm, pl,
-                       po, s.H_q, s.H_kv, s.W, s.K, L.nsb, s.scale);
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && S == 64) {
+        hipLaunchKernelGGL(decode_attend_fast_kernel<G>, dim3((L.np + 3) / 4, s.H_kv, num_seqs), dim3(256), 0, st,
+                           (const bf16 *)q, (const bf16 *)k_cache, (const bf16 *)v_cache, block_table, max_pages,
+                           seq_lens, sel, selsc, pm, pl, po, s.H_q, s.H_kv, s.W, s.K, L.np, s.scale);
+    } else {
+        const size_t dyn = (size_t)S * (D + 1) * 4 + (size_t)S * D * 4;
+        auto att = decode_attend_kernel<T, D, S, G>;
+        if (dyn > 48 * 1024) {
+            const hipError_t e =
+                hipFuncSetAttribute((const void *)att, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(att, dim3(L.nsb, s.H_kv, num_seqs), dim3(256), dyn, st, (const T *)q,
+                           (const T *)k_cache, (const T *)v_cache, block_table, max_pages, seq_lens, sel, selsc, pm,
+                           pl, po, s.H_q, s.H_kv, s.W, s.K, L.nsb, s.scale);
+    }
     const int64_t rows = (int64_t)num_seqs * s.H_q;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, pm, pl, po,
-                       (T *)out, lse, rows, L.nsb);
+                       (T *)out, lse, rows, L.np);
     return hipGetLastError();
 }
 

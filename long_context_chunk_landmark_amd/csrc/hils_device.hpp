@@ -168,6 +168,62 @@ __device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// kk-th largest of the non-zero 64-bit keys held NV per lane (keys == 0 are
+// empty slots): bisection on the upper 32 bits (the score), then on the low
+// bits (the inverted chunk index) only when the score ties at the boundary.
+// Counting is ballot + popcount (scalar), no cross-lane data movement.
+template <int NV>
+__device__ __forceinline__ uint64_t kth_largest64(const uint64_t (&keys)[NV], int kk) {
+    uint32_t hi = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = hi | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) >= cand));
+        if (cnt >= kk) hi = cand;
+    }
+    int above = 0, tied = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint32_t h = (uint32_t)(keys[v] >> 32);
+        above += __popcll(__ballot(h > hi));
+        tied += __popcll(__ballot(h == hi && keys[v] != 0ull));
+    }
+    const int need = kk - above;  // 1 <= need <= tied
+    if (tied == need) return (uint64_t)hi << 32;
+    uint32_t lo = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = lo | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) == hi && (uint32_t)keys[v] >= cand));
+        if (cnt >= need) lo = cand;
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum over aligned segments of L lanes (L = 4..64), every lane of a
+// segment gets the segment total.  DPP within 16-lane rows, lane swaps
+// across rows.
+template <int L>
+__device__ __forceinline__ float seg_sum(float v) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "segment width");
+    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if constexpr (L >= 16) v += dpp<0x140>(v);  // row_mirror
+    if constexpr (L >= 32) {
+        const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    }
+    if constexpr (L >= 64) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    return v;
+}
+
 // Ragged row offsets of the per-query candidate lists.  All queries of
 // query chunk qc have n(qc) = max(0, qc - w) candidates (w = W / S); each
 // row is padded to a multiple of 16 entries.

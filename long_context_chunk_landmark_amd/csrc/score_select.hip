@@ -262,41 +262,6 @@ __device__ __forceinline__ uint64_t rank_key(float s, int idx) {
     return ((uint64_t)ord_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
 }
 
-// kk-th largest of the non-zero 64-bit keys held NV per lane (keys == 0 are
-// empty slots): bisection on the upper 32 bits (the score), then on the low
-// bits (the inverted chunk index) only when the score ties at the boundary.
-// Counting is ballot + popcount (scalar), no cross-lane data movement.
-template <int NV>
-__device__ __forceinline__ uint64_t kth_largest64(const uint64_t (&keys)[NV], int kk) {
-    uint32_t hi = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = hi | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) >= cand));
-        if (cnt >= kk) hi = cand;
-    }
-    int above = 0, tied = 0;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const uint32_t h = (uint32_t)(keys[v] >> 32);
-        above += __popcll(__ballot(h > hi));
-        tied += __popcll(__ballot(h == hi && keys[v] != 0ull));
-    }
-    const int need = kk - above;  // 1 <= need <= tied
-    if (tied == need) return (uint64_t)hi << 32;
-    uint32_t lo = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = lo | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-            cnt += __popcll(__ballot((uint32_t)(keys[v] >> 32) == hi && (uint32_t)keys[v] >= cand));
-        if (cnt >= need) lo = cand;
-    }
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // Sum over aligned groups of L lanes (L = 2..64), result in every lane.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {

@@ -177,5 +177,12 @@ def make_decode(name_or_params="decode_512k", device="cuda", **overrides):
     seq_lens = torch.full((B,), L, dtype=torch.int32)
     if "seq_lens" in p:
         seq_lens = torch.tensor(p["seq_lens"], dtype=torch.int32)
-    return dict(cfg=cfg, q=q, k_cache=k_cache, v_cache=v_cache, ksum_cache=ksum.to(device),
-                bsum_cache=bsum.to(device), block_table=perm.to(device), seq_lens=seq_lens.to(device))
+    out = dict(cfg=cfg, q=q, k_cache=k_cache, v_cache=v_cache, ksum_cache=ksum.to(device),
+               bsum_cache=bsum.to(device), block_table=perm.to(device), seq_lens=seq_lens.to(device))
+    if p.get("d_model"):
+        dm, r = p["d_model"], p["r"]
+        h = _randn(gen, (B, dm), gdev, dt)
+        w_down = _randn(gen, (r, dm), gdev, dt, std=1.0 / math.sqrt(dm))
+        w_up = _randn(gen, (cfg.H_q * cfg.d, r), gdev, dt, std=1.0 / math.sqrt(dm))
+        out["qcal"] = tuple(x.to(device) for x in (h, w_down, w_up))
+    return out

@@ -213,13 +213,19 @@ def _decode_case(dev, **kw):
     return p
 
 
+def _qcal_host(inp):
+    return None if inp.get("qcal") is None else tuple(host(x) for x in inp["qcal"])
+
+
 def _oracle_decode(cfg, inp, seq_lens, given_sel=None):
     oc = cfg.oracle_dict()
     return oracle.decode(oc, host(inp["q"]), host(inp["k_cache"]), host(inp["v_cache"]), host(inp["ksum_cache"]),
-                         host(inp["bsum_cache"]), host(inp["block_table"]), seq_lens, given_sel=given_sel)
+                         host(inp["bsum_cache"]), host(inp["block_table"]), seq_lens, given_sel=given_sel,
+                         qcal=_qcal_host(inp))
 
 
-@pytest.mark.parametrize("variant", ["bf16_hq", "bf16_hkv", "fp32sum", "fp32io", "ragged", "g8_s128"])
+@pytest.mark.parametrize("variant", ["bf16_hq", "bf16_hkv", "fp32sum", "fp32io", "ragged", "g8_s128", "qcal",
+                                     "qcal_fp32io"])
 def test_decode_matches_oracle(variant, dev):
     kw = {
         "bf16_hq": dict(seq_len=3000, seq_lens=[3000, 2113, 64]),
@@ -228,12 +234,15 @@ def test_decode_matches_oracle(variant, dev):
         "fp32io": dict(seq_len=2000, io=F32, summary=F32, d=64, seq_lens=[2000, 1500, 333]),
         "ragged": dict(seq_len=4000, seq_lens=[3999, 257, 1280], K=40, W=128),
         "g8_s128": dict(seq_len=6000, H_q=8, H_kv=1, S=128, pages=160, seq_lens=[6000, 4097, 129]),
+        # Q-Cal calibrates the scoring query only; attention uses the raw q
+        "qcal": dict(seq_len=3000, seq_lens=[3000, 1500, 900], d_model=256, r=16),
+        "qcal_fp32io": dict(seq_len=2000, io=F32, summary=F32, d=64, seq_lens=[2000, 1111, 700], d_model=128, r=8),
     }[variant]
     inp = W.make_decode(_decode_case(dev, **kw), device=dev)
     cfg = inp["cfg"]
     print(f"[decode] {variant}", flush=True)
     out, lse, sel = hb.decode(cfg, inp["q"], inp["k_cache"], inp["v_cache"], inp["ksum_cache"], inp["bsum_cache"],
-                              inp["block_table"], inp["seq_lens"])
+                              inp["block_table"], inp["seq_lens"], qcal=inp.get("qcal"))
     torch.cuda.synchronize()
     sl = host(inp["seq_lens"]).numpy()
     ref = _oracle_decode(cfg, inp, sl)
@@ -242,7 +251,7 @@ def test_decode_matches_oracle(variant, dev):
 
     def agg_of(b, g, r):
         res = oracle.decode(oc, host(inp["q"]), None, None, host(inp["ksum_cache"]), host(inp["bsum_cache"]),
-                            host(inp["block_table"]), sl, attend=False, want_agg=True)
+                            host(inp["block_table"]), sl, attend=False, want_agg=True, qcal=_qcal_host(inp))
         return res["agg"][b, g]
 
     exempt = check_selection(gsel[:, :, None, :], ref["sel_idx"][:, :, None, :], ref["kth"][:, :, None, :],
