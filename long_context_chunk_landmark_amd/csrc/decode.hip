@@ -28,6 +28,8 @@
 
 namespace hils {
 
+constexpr int DECODE_PAGES_CAP = 256;  // candidates per block of the page-contiguous scorer
+
 namespace {
 
 struct DecodeLayout {
@@ -35,6 +37,7 @@ struct DecodeLayout {
     int nsb;     // phase B blocks per (seq, group) (generic attend)
     int np;      // partial (m, l, o) slots per (seq, query head)
     bool fast;   // bf16, d = 128, S = 64: one wave per chunk of the list
+    bool pages;  // bf16 summaries, d = 128, H_lm = H_q: page-contiguous scoring
     size_t off_qs, off_pkey, off_psc, off_sel, off_selsc, off_pm, off_pl, off_po, total;
 };
 
@@ -44,6 +47,8 @@ DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
     L.nsb = std::max(1, std::min(16, (s.K + s.W / s.S + 1 + 3) / 4));
     L.fast = s.io_bf16 && s.D == 128 && s.S == 64;
     L.np = L.fast ? s.K + s.W / s.S + 1 : L.nsb;
+    L.pages = s.sum_bf16 && s.D == 128 && s.H_lm == s.H_q && (s.H_q == 8 || s.H_q == 16 || s.H_q == 32) &&
+              (max_pages + L.splits - 1) / L.splits <= DECODE_PAGES_CAP;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -213,6 +218,134 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
         outc += __popcll(m);
     }
     for (int k = min(outc, K) + lane; k < K; k += WAVE) pkey[pbase + k] = 0ull;
+}
+
+// Phase A, page-contiguous variant (bf16 summaries, d = 128, one landmark
+// head per query head).  A block scores a candidate range of one sequence
+// for every kv group at once, so each candidate's summary row of all HQ
+// landmark heads (HQ * 256 bytes, contiguous in the page) is read in one
+// sweep.  Lane (slice, rg) holds dims 8slice..8slice+7 of landmark rows
+// rg + 4k (k < HQ / 4) and the matching query slices.  Per-head scores and
+// group maxima go to LDS; then each kv group takes its local top-K.
+template <int HQ, int G>
+__global__ __launch_bounds__(256) void decode_score_pages_kernel(
+    const float *__restrict__ qs, const bf16 *__restrict__ q_raw, const bf16 *__restrict__ ksum_cache,
+    const float *__restrict__ bsum_cache, const int32_t *__restrict__ block_table, int max_pages,
+    const int32_t *__restrict__ seq_lens, uint64_t *pkey, float *psc, int S, int W, int K, int splits,
+    float scale) {
+    constexpr int D = 128, NR = HQ / 4, NG = HQ / G, CAP = DECODE_PAGES_CAP;
+    __shared__ float sc_l[CAP][HQ];
+    __shared__ float agg_l[NG][CAP];
+    const int sp = blockIdx.x, seq = blockIdx.y;
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int slice = lane & 15, rg = lane >> 4;
+    const int t = clamp_len(seq_lens[seq], max_pages, S) - 1;
+    const int n = max(0, t / S - W / S);
+    const int c_lo = (int)((int64_t)sp * n / splits), c_hi = (int)((int64_t)(sp + 1) * n / splits);
+    const int cnt = c_hi - c_lo;
+
+    // scoring query slices of heads rg + 4k (calibrated fp32 when given)
+    float qv[NR][8];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const int64_t off = ((int64_t)seq * HQ + rg + 4 * k) * D + slice * 8;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) qv[k][x] = qs ? qs[off + x] : (float)q_raw[off + x];
+    }
+    const int32_t *bt = block_table + (int64_t)seq * max_pages;
+    const int per_w = (cnt + 3) / 4;
+    const int w_lo = min(cnt, wave * per_w), w_hi = min(cnt, w_lo + per_w);  // <= 64 candidates
+    const int pg = w_lo + lane < w_hi ? bt[c_lo + w_lo + lane] : 0;
+    constexpr int U = 2;
+    for (int base = w_lo; base < w_hi; base += U) {
+        u32x4 kv[U][NR];
+        float bias[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int lc = min(base + u, w_hi - 1);
+            const int64_t page = __shfl(pg, lc - w_lo, WAVE);
+            const bf16 *row = ksum_cache + page * HQ * D + slice * 8;
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                kv[u][k] = *(const u32x4 *)(row + (rg + 4 * k) * D);
+                bias[u][k] = bsum_cache[page * HQ + rg + 4 * k];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int lc = base + u;
+            float sc[NR];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                float part = 0.f;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t w = kv[u][k][x];
+                    part = fmaf(qv[k][2 * x], __uint_as_float(w << 16), part);
+                    part = fmaf(qv[k][2 * x + 1], __uint_as_float(w & 0xffff0000u), part);
+                }
+                sc[k] = fmaf(scale, seg_sum<16>(part), bias[u][k]);
+            }
+            // group maxima: head h = rg + 4k belongs to group h / G
+            float ag[NR];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                float a = sc[k];
+                if constexpr (G >= 2) {
+                    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+                    a = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+                }
+                if constexpr (G >= 4) {
+                    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+                    a = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+                }
+                ag[k] = a;
+            }
+            if (lc < w_hi && slice == 0) {
+#pragma unroll
+                for (int k = 0; k < NR; ++k) sc_l[lc][rg + 4 * k] = sc[k];
+#pragma unroll
+                for (int k = 0; k < NR; ++k) {
+                    if constexpr (G == 1) {
+                        agg_l[rg + 4 * k][lc] = ag[k];
+                    } else if constexpr (G == 2) {
+                        if ((rg & 1) == 0) agg_l[(rg + 4 * k) / 2][lc] = ag[k];
+                    } else if constexpr (G == 4) {
+                        if (rg == 0) agg_l[k][lc] = ag[k];
+                    } else {  // G == 8: heads 8gg .. 8gg+7 are rows k = 2gg, 2gg+1
+                        if (rg == 0 && (k & 1)) agg_l[k / 2][lc] = fmaxf(ag[k], ag[k - 1]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // local top-K of each kv group (groups wave, wave + 4, ...)
+    for (int gg = wave; gg < NG; gg += 4) {
+        uint64_t keys[CAP / WAVE];
+#pragma unroll
+        for (int v = 0; v < CAP / WAVE; ++v) {
+            const int lc = v * WAVE + lane;
+            keys[v] = lc < cnt ? dec_key(agg_l[gg][lc], c_lo + lc) : 0ull;
+        }
+        const uint64_t T = cnt > K ? kth_largest64<CAP / WAVE>(keys, K) : 1ull;
+        const int64_t pbase = (((int64_t)seq * NG + gg) * splits + sp) * K;
+        int outc = 0;
+#pragma unroll
+        for (int v = 0; v < CAP / WAVE; ++v) {
+            const bool keep = keys[v] >= T && keys[v] != 0ull;
+            const uint64_t m = __ballot(keep);
+            const int pos = outc + __popcll(m & lanemask_lt());
+            if (keep && pos < K) {
+                pkey[pbase + pos] = keys[v];
+                const int lc = v * WAVE + lane;
+#pragma unroll
+                for (int e = 0; e < G; ++e) psc[(pbase + pos) * G + e] = sc_l[lc][gg * G + e];
+            }
+            outc += __popcll(m);
+        }
+        for (int k = min(outc, K) + lane; k < K; k += WAVE) pkey[pbase + k] = 0ull;
+    }
 }
 
 // Phase A2.  One wave per (seq, group): top-K of splits*K partial entries.
@@ -534,31 +667,61 @@ __global__ __launch_bounds__(256) void decode_attend_fast_kernel(
     }
 }
 
-// Phase B2.  One wave per (seq, head).
+// Phase B2.  One wave per (seq, head): the wave's four 16-lane groups
+// each merge every fourth partial state (lane covering D/16 dims), then
+// the four group states are joined with lane swaps.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
                                                              const float *__restrict__ po, T *__restrict__ out,
-                                                             float *__restrict__ lse, int64_t rows, int nsb) {
-    constexpr int DPL = D / WAVE;
-    const int lane = lane_id();
+                                                             float *__restrict__ lse, int64_t rows, int np) {
+    constexpr int DPL = D / 16;
+    const int lane = lane_id(), sub = lane & 15, pgp = lane >> 4;
     const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / WAVE;
     if (row >= rows) return;
-    float m = -INFINITY;
-    for (int s = 0; s < nsb; ++s) m = fmaxf(m, pm[row * nsb + s]);
-    float l = 0.f, o[DPL];
+    float m = -INFINITY, l = 0.f, o[DPL];
 #pragma unroll
     for (int y = 0; y < DPL; ++y) o[y] = 0.f;
-    for (int s = 0; s < nsb; ++s) {
-        const float ms = pm[row * nsb + s];
-        const float a = ms == -INFINITY ? 0.f : expf(ms - m);
-        l = fmaf(pl[row * nsb + s], a, l);
+    auto add = [&](float ms, float ls, const float (&os)[DPL]) {
+        if (ms == -INFINITY) return;
+        const float mn = fmaxf(m, ms);
+        const float a0 = m == -INFINITY ? 0.f : expf(m - mn), a1 = expf(ms - mn);
+        l = l * a0 + ls * a1;
 #pragma unroll
-        for (int y = 0; y < DPL; ++y) o[y] = fmaf(po[(row * nsb + s) * D + lane * DPL + y], a, o[y]);
+        for (int y = 0; y < DPL; ++y) o[y] = o[y] * a0 + os[y] * a1;
+        m = mn;
+    };
+    constexpr int U = 4;
+    for (int s0 = pgp; s0 < np; s0 += 4 * U) {
+        float ms[U], ls[U], os[U][DPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sidx = min(s0 + 4 * u, np - 1);
+            const bool ok = s0 + 4 * u < np;
+            ms[u] = ok ? pm[row * np + sidx] : -INFINITY;
+            ls[u] = pl[row * np + sidx];
+            const float *src = po + (row * np + sidx) * D + sub * DPL;
+#pragma unroll
+            for (int y = 0; y < DPL; y += 4) {
+                const f32x4 v = *(const f32x4 *)(src + y);
+                os[u][y] = v[0], os[u][y + 1] = v[1], os[u][y + 2] = v[2], os[u][y + 3] = v[3];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(ms[u], ls[u], os[u]);
     }
-    const float inv = 1.f / l;
+    // join the four groups (lanes sub, sub + 16, sub + 32, sub + 48)
+    const float M = rows4_max(m);
+    const float a = m == -INFINITY ? 0.f : expf(m - M);
+    const float L = rows4_sum(l * a);
+    float r[DPL];
 #pragma unroll
-    for (int y = 0; y < DPL; ++y) out[row * D + lane * DPL + y] = from_f32<T>(o[y] * inv);
-    if (lse && lane == 0) lse[row] = m + logf(l);
+    for (int y = 0; y < DPL; ++y) r[y] = rows4_sum(o[y] * a);
+    if (pgp == 0) {
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int y = 0; y < DPL; ++y) out[row * D + sub * DPL + y] = from_f32<T>(r[y] * inv);
+        if (lse && sub == 0) lse[row] = M + logf(L);
+    }
 }
 
 size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages) {
@@ -577,10 +740,26 @@ static hipError_t go_decode(const Shape &s, const DecodeLayout &L, int num_seqs,
     int32_t *sel = (int32_t *)(ws + L.off_sel);
     float *selsc = (float *)(ws + L.off_selsc);
     float *pm = (float *)(ws + L.off_pm), *pl = (float *)(ws + L.off_pl), *po = (float *)(ws + L.off_po);
-    hipLaunchKernelGGL(decode_qprep_kernel<T>, dim3(num_seqs), dim3(256), 0, st, (const T *)q, (const T *)h,
-                       (const T *)w_down, (const T *)w_up, qs, s.H_q, s.D, d_model, r);
+    const bool pages = std::is_same<T, bf16>::value && std::is_same<TS, bf16>::value && D == 128 && L.pages;
+    if (!pages || h)
+        hipLaunchKernelGGL(decode_qprep_kernel<T>, dim3(num_seqs), dim3(256), 0, st, (const T *)q, (const T *)h,
+                           (const T *)w_down, (const T *)w_up, qs, s.H_q, s.D, d_model, r);
     const dim3 ga(L.splits, s.H_kv, num_seqs);
-    if (s.GLM == 1)
+    if constexpr (std::is_same<T, bf16>::value && std::is_same<TS, bf16>::value && D == 128) {
+        if (pages) {
+            const float *qsp = h ? qs : nullptr;
+            auto sc = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3(L.splits, num_seqs), dim3(256), 0, st, qsp, (const bf16 *)q,
+                                   (const bf16 *)ksum_cache, bsum_cache, block_table, max_pages, seq_lens, pkey, psc,
+                                   s.S, s.W, s.K, L.splits, s.scale);
+            };
+            if (s.H_q == 8) sc(decode_score_pages_kernel<8, G>);
+            else if (s.H_q == 16) sc(decode_score_pages_kernel<16, G>);
+            else sc(decode_score_pages_kernel<32, G>);
+        }
+    }
+    if (pages) {
+    } else if (s.GLM == 1)
         hipLaunchKernelGGL((decode_score_kernel<TS, D, G, 1>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
                            bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
                            s.K, L.splits, s.scale);
