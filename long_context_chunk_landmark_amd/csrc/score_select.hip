@@ -337,10 +337,21 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     const float *kcm_g = kcm + bg * (int64_t)C * GLM * D;
     const float *bs_g = b_sum + (b * (int64_t)H_lm + (int64_t)g * GLM) * C;  // + e*C + c
 
-    // ---- threshold of the approximate pass (two streaming passes over the
-    // row's approximate scores; the second one is served by the caches)
+    // ---- threshold of the approximate pass.  Rows of up to 64 * JR
+    // candidates keep their approximate keys in registers (all loads in
+    // flight at once, no second read); longer rows stream twice.
+    constexpr int JR = 32;
     const int J = (n + WAVE - 1) / WAVE;
+    const bool cached = J <= JR;
     const float *ar = agg_in + bg * per_bg + cand_row_offset(i, w, S);
+    uint32_t kreg[JR];
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
+            const int c = j * WAVE + lane;
+            kreg[j] = (j < J && c < n) ? ord_key(ar[c]) : 0u;
+        }
+    }
     uint32_t thr_key = 0;
     const bool rank_needed = n > K;
     if (rank_needed) {
@@ -349,13 +360,20 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
         // candidates score >= tau' and tau' <= the K-th largest approximate
         // score (equal to it unless a lane holds more than four of the top K)
         uint32_t m0 = 0u, m1 = 0u, m2 = 0u, m3 = 0u;
-        for (int j = 0; j < J; ++j) {
-            const int c = j * WAVE + lane;
-            const uint32_t x = c < n ? ord_key(ar[c]) : 0u;
+        auto insert = [&](uint32_t x) {
             m3 = max(m3, min(m2, x));
             m2 = max(m2, min(m1, x));
             m1 = max(m1, min(m0, x));
             m0 = max(m0, x);
+        };
+        if (cached) {
+#pragma unroll
+            for (int j = 0; j < JR; ++j) insert(kreg[j]);
+        } else {
+            for (int j = 0; j < J; ++j) {
+                const int c = j * WAVE + lane;
+                insert(c < n ? ord_key(ar[c]) : 0u);
+            }
         }
         uint32_t T = 0;
         for (int bit = 31; bit >= 0; --bit) {
@@ -470,15 +488,36 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
             flush();
         }
     } else {
-        for (int j = 0; j < J; ++j) {
-            const int c = j * WAVE + lane;
-            const bool surv = c < n && ord_key(ar[c]) >= thr_key;
+        auto take = [&](int c, bool surv) {
             const uint64_t m = __ballot(surv);
             const int cnt = __popcll(m);
             if (cnt > 0) {
                 if (bcnt + cnt > WAVE) flush();
                 if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = c;
                 bcnt += cnt;
+            }
+        };
+        // survivors straight from the cached keys when they fit one batch
+        // (the usual case); otherwise stream them from memory in batches
+        int total = WAVE + 1;
+        if (cached) {
+            total = 0;
+#pragma unroll
+            for (int j = 0; j < JR; ++j) total += __popcll(__ballot(j < J && kreg[j] >= thr_key));
+            if (total <= WAVE) {
+#pragma unroll
+                for (int j = 0; j < JR; ++j) {
+                    const bool surv = j < J && kreg[j] >= thr_key;  // kreg = 0 past n
+                    const uint64_t m = __ballot(surv);
+                    if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = j * WAVE + lane;
+                    bcnt += __popcll(m);
+                }
+            }
+        }
+        if (total > WAVE) {
+            for (int j = 0; j < J; ++j) {
+                const int c = j * WAVE + lane;
+                take(c, c < n && ord_key(ar[c]) >= thr_key);
             }
         }
         if (bcnt > 0) flush();
