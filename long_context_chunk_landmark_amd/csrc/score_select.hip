@@ -18,7 +18,8 @@
 //
 // Kernels:
 //   ksum_prep        bf16 copy of k' + per-(b, landmark head) max ||k'||
-//   qcal             fp32 scoring queries q + W_up (W_down h)
+//   qcal_mfma        fp32 scoring queries q + W_up (W_down h), bf16 MFMA
+//   qcal             the same for other shapes and fp32 inputs (VALU)
 //   score_approx     bf16 MFMA scores -> ragged approximate group scores
 //   select           exact refine + top-K per (b, g, query)
 #include "hils_device.hpp"
@@ -153,6 +154,122 @@ __global__ __launch_bounds__(256) void qcal_kernel(const T *__restrict__ q, cons
             for (int a = 0; a < r; ++a) acc = fmaf(wrow[a], u_lds[t * r + a], acc);
             const int64_t o = ((b * H_q + hh) * N + i0 + t) * (int64_t)D + x;
             q_s[o] = to_f32(q[o]) + acc;
+        }
+    }
+}
+
+// Split an fp32 value into three bf16 terms whose sum is the value (exact
+// for normal values: each residual carries the next 8 significand bits).
+__device__ __forceinline__ void split_bf16x3(float v, bf16 &a, bf16 &b, bf16 &c) {
+    a = (bf16)v;
+    const float r1 = v - (float)a;
+    b = (bf16)r1;
+    c = (bf16)(r1 - (float)b);
+}
+
+// bf16 Q-Cal on MFMA (r % 16 == 0, r <= 64, d_model % 32 == 0).  One wave
+// owns 64 tokens as four 16-token column tiles.
+//   Phase 1: U^T = W_down h^T, rows a padded to RP (rows >= r read as 0).
+//     Products of bf16 values are exact in fp32, so this equals an fp32 FMA
+//     chain up to the summation order.
+//   Phase 2: Delta^T = W_up U^T over K = RP.  U (fp32) enters the bf16 MFMA
+//     as its exact three-term split, so again only the fp32 accumulation
+//     rounds.  The accumulator starts at q, so the chain yields q + Delta.
+// An MFMA sums its K slots in any order, so lane group j of the phase-2
+// operands carries U's rows 32s + 4j + {0..3} and 32s + 16 + 4j + {0..3}:
+// exactly the rows phase 1 left in that lane (no data movement), with the
+// W_up fragment read in the same order.
+template <int RP>
+__global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ h,
+                                                        const bf16 *__restrict__ w_down,
+                                                        const bf16 *__restrict__ w_up, float *__restrict__ q_s,
+                                                        int N, int H_q, int D, int d_model, int r) {
+    constexpr int NA = RP / 16;  // phase-1 row tiles
+    constexpr int NK = RP / 32;  // phase-2 k-steps
+    constexpr int NT = 4;        // 16-token column tiles per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, j = lane >> 4;
+    const int64_t b = blockIdx.y;
+    const int t0 = (blockIdx.x * 4 + wave) * (16 * NT);
+    if (t0 >= N) return;
+
+    int tok[NT];
+    const bf16 *hrow[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        tok[n] = t0 + 16 * n + col;
+        hrow[n] = h + (b * N + min(tok[n], N - 1)) * (int64_t)d_model + 8 * j;  // clamped rows are never stored
+    }
+    const bf16 *wrow[NA];
+    bool a_ok[NA];
+#pragma unroll
+    for (int m = 0; m < NA; ++m) {
+        a_ok[m] = 16 * m + col < r;
+        wrow[m] = w_down + (int64_t)min(16 * m + col, r - 1) * d_model + 8 * j;
+    }
+    f32x4 acc[NA][NT];
+#pragma unroll
+    for (int m = 0; m < NA; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 zero8 = {};
+#pragma unroll 2
+    for (int x = 0; x < d_model; x += 32) {
+        bf16x8 af[NA], bfr[NT];
+#pragma unroll
+        for (int m = 0; m < NA; ++m) {
+            const bf16x8 t = *(const bf16x8 *)(wrow[m] + x);
+            af[m] = a_ok[m] ? t : zero8;
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) bfr[n] = *(const bf16x8 *)(hrow[n] + x);
+#pragma unroll
+        for (int m = 0; m < NA; ++m)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[m][n] = mfma16(af[m], bfr[n], acc[m][n]);
+    }
+
+    // phase-2 B operands: split U into bf16 terms in the K order above
+    bf16x8 u[NT][NK][3];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = i < 4 ? acc[2 * s][n][i] : acc[2 * s + 1][n][i - 4];
+                bf16 x1, x2, x3;
+                split_bf16x3(v, x1, x2, x3);
+                u[n][s][0][i] = x1;
+                u[n][s][1][i] = x2;
+                u[n][s][2][i] = x3;
+            }
+
+    const int HD = H_q * D;
+    for (int e0 = 0; e0 < HD; e0 += 16) {
+        const bf16 *wr = w_up + (int64_t)(e0 + col) * r;
+        bf16x8 wf[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            const int alo = 32 * s + 4 * j, ahi = alo + 16;
+            bf16x4 lo = {}, hi = {};
+            if (alo < r) lo = *(const bf16x4 *)(wr + alo);
+            if (ahi < r) hi = *(const bf16x4 *)(wr + ahi);
+            wf[s] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        const int hh = e0 / D, x0 = e0 % D + 4 * j;  // a 16-row tile stays inside one head (D % 16 == 0)
+        const int64_t hb = (b * H_q + hh) * (int64_t)N;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const bool ok = tok[n] < N;
+            const int64_t o = (hb + min(tok[n], N - 1)) * D + x0;
+            const bf16x4 qv = *(const bf16x4 *)(q + o);
+            f32x4 c = {(float)qv[0], (float)qv[1], (float)qv[2], (float)qv[3]};
+#pragma unroll
+            for (int s = 0; s < NK; ++s)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) c = mfma16(wf[s], u[n][s][k], c);
+            if (ok) *(f32x4 *)(q_s + o) = c;
         }
     }
 }
@@ -626,7 +743,14 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     if (qcal) {
         const dim3 grid((unsigned)((s.N + 15) / 16), (unsigned)s.B), block(256);
         const size_t lds = (size_t)16 * r * sizeof(float);
-        if (s.io_bf16)
+        const dim3 mgrid((unsigned)((s.N + 255) / 256), (unsigned)s.B);
+        if (s.io_bf16 && r % 16 == 0 && r <= 32 && d_model % 32 == 0)
+            hipLaunchKernelGGL(qcal_mfma_kernel<32>, mgrid, block, 0, st, (const bf16 *)q, (const bf16 *)h,
+                               (const bf16 *)w_down, (const bf16 *)w_up, ws.q_s, s.N, s.H_q, s.D, d_model, r);
+        else if (s.io_bf16 && r % 16 == 0 && r <= 64 && d_model % 32 == 0)
+            hipLaunchKernelGGL(qcal_mfma_kernel<64>, mgrid, block, 0, st, (const bf16 *)q, (const bf16 *)h,
+                               (const bf16 *)w_down, (const bf16 *)w_up, ws.q_s, s.N, s.H_q, s.D, d_model, r);
+        else if (s.io_bf16)
             hipLaunchKernelGGL(qcal_kernel<bf16>, grid, block, lds, st, (const bf16 *)q, (const bf16 *)h,
                                (const bf16 *)w_down, (const bf16 *)w_up, ws.q_s, s.N, s.H_q, s.D, d_model, r);
         else

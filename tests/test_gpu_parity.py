@@ -36,6 +36,11 @@ CASES = {
     "k0": dict(seed=26, io=BF, B=1, H_q=4, H_kv=1, d=128, N=1024, S=64, W=128, K=0),
     "fp32_g4_s128": dict(seed=27, io=F32, B=1, H_q=4, H_kv=1, d=128, N=1500, S=128, W=128, K=3),
     "qcal_small": dict(seed=28, io=BF, B=1, H_q=4, H_kv=1, d=128, N=2048, S=128, W=256, K=4, d_model=256, r=16),
+    # Q-Cal on MFMA with rank 32 / 64 and a ragged token tail; VALU Q-Cal for other shapes
+    "qcal_r32_b2": dict(seed=35, io=BF, B=2, H_q=8, H_kv=2, d=64, N=1300, S=64, W=128, K=8, d_model=512, r=32),
+    "qcal_r64": dict(seed=36, io=BF, B=1, H_q=4, H_kv=1, d=128, N=2500, S=128, W=256, K=8, d_model=384, r=64),
+    "qcal_valu_r12": dict(seed=37, io=BF, B=1, H_q=4, H_kv=2, d=64, N=1100, S=64, W=64, K=4, d_model=200, r=12),
+    "qcal_fp32": dict(seed=38, io=F32, B=1, H_q=2, H_kv=1, d=64, N=700, S=64, W=64, K=3, d_model=96, r=8),
     "few_candidates": dict(seed=29, io=BF, B=1, H_q=4, H_kv=2, d=128, N=1024, S=64, W=512, K=16),
     # block shapes picked by LDS capacity: 4-wave blocks at S=128 with K=64 / G=2
     "s128_k64": dict(seed=33, io=BF, B=1, H_q=8, H_kv=2, d=128, N=9000, S=128, W=256, K=64),
