@@ -28,7 +28,8 @@ hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_
 
 // ---- kernel 2: score + select
 struct ScoreWorkspace {
-    void *ksb;          // [B,H_lm,C,D] bf16 copy of k_sum
+    void *ksb;          // [B,H_lm,C,D] bf16 k1 = bf16(k_sum)
+    void *ksb2;         // [B,H_lm,C,D] bf16 k2 = bf16(k_sum - k1) (fp32 summaries)
     float *kcm;         // [B,H_kv,C,GLM,D] fp32 chunk-major copy of k_sum
     float *knorm;       // [B,H_lm] max_c ||k'_c||
     float *err;         // [B,H_kv,N] per-row bound of the approximate group score

@@ -44,7 +44,7 @@ int64_t score_agg_entries_per_bg(const Shape &s) {
 
 size_t score_workspace_bytes(const Shape &s, bool qcal) {
     size_t b = 0;
-    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);  // ksb
+    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // ksb: two bf16 terms
     b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // kcm
     b += align_up((size_t)s.B * s.H_lm * 4, 256);               // knorm
     b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
@@ -56,7 +56,8 @@ size_t score_workspace_bytes(const Shape &s, bool qcal) {
 void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace &ws) {
     char *p = (char *)base;
     ws.ksb = p;
-    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 2, 256);
+    ws.ksb2 = p + (size_t)s.B * s.H_lm * s.C * s.D * 2;
+    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
     ws.kcm = (float *)p;
     p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
     ws.knorm = (float *)p;
@@ -77,13 +78,14 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
 }
 
 // 16 lanes per k' row (D/16 elements each), 4 rows per wave.  Writes the
-// bf16 copy (same layout) for the MFMA pass, an fp32 chunk-major copy
+// two-term bf16 split k1 = bf16(k'), k2 = bf16(k' - k1) (same layout; k2
+// only for fp32 summaries) for the MFMA pass, an fp32 chunk-major copy
 // [B, H_kv, C, GLM, D] (the GLM landmark rows of a group contiguous per
 // chunk) for the exact refinement, and the max norm per (b, landmark head).
 template <typename TS, int D>
 __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k_sum, bf16 *__restrict__ ksb,
-                                                        float *__restrict__ kcm, float *__restrict__ knorm, int C,
-                                                        int GLM, int64_t rows) {
+                                                        bf16 *__restrict__ ksb2, float *__restrict__ kcm,
+                                                        float *__restrict__ knorm, int C, int GLM, int64_t rows) {
     constexpr int EL = D / 16;
     const int lane = lane_id();
     const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * 4 + (lane >> 4);
@@ -92,6 +94,7 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
     if (ok) {
         const TS *src = k_sum + row * D + (lane & 15) * EL;
         bf16 *dst = ksb + row * D + (lane & 15) * EL;
+        bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
         // row = (b * H_lm + l) * C + c with l = g * GLM + e
         const int64_t c = row % C, bl = row / C;
         const int64_t e = bl % GLM, bg = bl / GLM;
@@ -100,7 +103,9 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
         for (int x = 0; x < EL; ++x) {
             const float v = to_f32(src[x]);
             ss = fmaf(v, v, ss);
-            dst[x] = (bf16)v;
+            const bf16 v1 = (bf16)v;
+            dst[x] = v1;
+            if constexpr (std::is_same<TS, float>::value) dst2[x] = (bf16)(v - (float)v1);
             dcm[x] = v;
         }
     }
@@ -276,21 +281,39 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 
 // ------------------------------------------------------------ approximate scores (MFMA)
 
-// One block = 4 waves = 64 consecutive queries of one query chunk (S is a
-// multiple of 64) for one (b, g).  Wave w owns queries 16w..16w+15 as the
-// B operand (q^T, bf16) of 16x16x32 MFMAs for each of the G heads; the A
-// operand is a 16-candidate k' tile staged in LDS.  Output D: lane l holds
-// candidates 4*(l/16)+i of query l%16, so each lane stores 16 contiguous
-// bytes of its query's ragged score row.
-template <typename TQ, int D, int G>
-__global__ __launch_bounds__(256) void score_approx_kernel(
-    const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const float *__restrict__ b_sum,
-    const float *__restrict__ knorm, float *__restrict__ agg_out, float *__restrict__ err_out, int N, int H_q,
-    int H_kv, int H_lm, int C, int S, int W, int K, float scale, float kappa, int64_t per_bg) {
-    constexpr int KS = D / 32;   // MFMA k-steps over the head dim
-    constexpr int NB = D / 8;    // 16-byte blocks per k' row
-    __shared__ u32x4 kt[G][16][NB];
+// One block = 64 consecutive queries of one query chunk (S is a multiple of
+// 64) for one (b, g): four 16-query tiles x WPQ groups of HPW heads, one
+// wave each.  The B operand of the 16x16x32 MFMAs is q^T of the wave's 16
+// queries (bf16 terms, in registers); the A operand is a 16-candidate k'
+// tile staged in LDS.  D: lane l holds candidates 4*(l/16)+i of query l%16;
+// the head groups of a tile meet through LDS and the first stores 16
+// contiguous bytes of its query's ragged score row.
+//
+// Split products: the scoring query q_s = t1 + t2 and k' = k1 + k2 with
+// t1 = bf16(q_s), t2 = bf16(q_s - t1) (k likewise); the MFMAs sum
+// t1 k1 + t1 k2 + t2 k1.  Terms that are exactly zero are skipped: bf16
+// queries have t2 = 0, bf16 summaries k2 = 0.  Each two-term split is
+// within 2^-18 |x| of x, the dropped t2 k2 term within 2^-18 |q||k|
+// elementwise, so by Cauchy-Schwarz |exact - approx| <= scale * kappa *
+// ||q_s|| * max_c ||k'_c|| with kappa (set by the launcher) adding those
+// terms to a bound on the fp32 accumulation.
+template <typename TQ, int D, int G, bool KSPLIT>
+__global__ __launch_bounds__(256 * (G >= 4 ? G / 2 : 1)) void score_approx_kernel(
+    const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const bf16 *__restrict__ ksb2,
+    const float *__restrict__ b_sum, const float *__restrict__ knorm, float *__restrict__ agg_out,
+    float *__restrict__ err_out, int N, int H_q, int H_kv, int H_lm, int C, int S, int W, int K, float scale,
+    float kappa, int64_t per_bg) {
+    constexpr bool QSPLIT = std::is_same<TQ, float>::value;
+    constexpr int NQT = QSPLIT ? 2 : 1;   // query terms
+    constexpr int NKT = KSPLIT ? 2 : 1;   // k' terms
+    constexpr int HPW = G >= 2 ? 2 : 1;   // heads per wave
+    constexpr int WPQ = G / HPW;          // waves per 16-query tile
+    constexpr int NT = 256 * WPQ;
+    constexpr int KS = D / 32;            // MFMA k-steps over the head dim
+    constexpr int NB = D / 8;             // 16-byte blocks per k' row
+    __shared__ u32x4 kt[NKT][G][16][NB];
     __shared__ float bt[G][16];
+    __shared__ f32x4 px[WPQ > 1 ? WPQ - 1 : 1][4][WAVE];
 
     const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
@@ -301,78 +324,114 @@ __global__ __launch_bounds__(256) void score_approx_kernel(
     if (n <= K) return;  // every candidate is selected; nothing to rank
 
     const int wave = threadIdx.x / WAVE, lane = lane_id();
-    const int iq = i0 + wave * 16 + (lane & 15);
+    const int qt = wave % 4, hh = wave / 4;
+    const int iq = i0 + qt * 16 + (lane & 15);
     const bool qvalid = iq < N;
     const int iqc = qvalid ? iq : N - 1;
     const int grp = lane >> 4;
 
-    bf16x8 qf[G][KS];
-    float emax = 0.f;
+    bf16x8 qf[HPW][NQT][KS];
 #pragma unroll
-    for (int e = 0; e < G; ++e) {
-        const int hh = g * G + e;
-        const TQ *qr = q + (((int64_t)b * H_q + hh) * N + iqc) * D;
-        float ss = 0.f;
+    for (int j = 0; j < HPW; ++j) {
+        const TQ *qr = q + (((int64_t)b * H_q + g * G + hh * HPW + j) * N + iqc) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = 32 * s + 8 * grp;
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
                 const float v = to_f32(qr[d0 + x]);
-                ss = fmaf(v, v, ss);
-                qf[e][s][x] = (bf16)v;
+                const bf16 v1 = (bf16)v;
+                qf[j][0][s][x] = v1;
+                if constexpr (QSPLIT) qf[j][1][s][x] = (bf16)(v - (float)v1);
             }
         }
-        ss = xor_sum<16, 32>(ss);
-        const int l = hh * H_lm / H_q;
-        emax = fmaxf(emax, sqrtf(ss) * knorm[b * H_lm + l]);
     }
-    const float err = scale * kappa * emax + 1e-5f;
-    if (qvalid && grp == 0) err_out[((int64_t)b * H_kv + g) * N + iq] = err;
+    if (hh == 0) {
+        // bound of the group score: the largest per-head bound of the group
+        float emax = 0.f;
+        for (int e = 0; e < G; ++e) {
+            const int hd = g * G + e;
+            const TQ *qr = q + (((int64_t)b * H_q + hd) * N + iqc) * D;
+            float ss = 0.f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float v = to_f32(qr[32 * s + 8 * grp + x]);
+                    ss = fmaf(v, v, ss);
+                }
+            ss = xor_sum<16, 32>(ss);
+            emax = fmaxf(emax, sqrtf(ss) * knorm[b * H_lm + hd * H_lm / H_q]);
+        }
+        const float err = scale * kappa * emax + 1e-5f;
+        if (qvalid && grp == 0) err_out[((int64_t)b * H_kv + g) * N + iq] = err;
+    }
 
     float *row = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset(iqc, w, S);
+    const int cr = lane & 15;
 
     for (int c0 = 0; c0 < n; c0 += 16) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < G * 16 * NB; idx += blockDim.x) {
-            const int e = idx / (16 * NB), rem = idx % (16 * NB);
-            const int cr = rem / NB, cb = rem % NB;
-            const int c = c0 + cr;
+        for (int idx = threadIdx.x; idx < NKT * G * 16 * NB; idx += NT) {
+            const int kk = idx / (G * 16 * NB), rem0 = idx % (G * 16 * NB);
+            const int e = rem0 / (16 * NB), rem = rem0 % (16 * NB);
+            const int rr = rem / NB, cb = rem % NB;
+            const int c = c0 + rr;
             const int l = (g * G + e) * H_lm / H_q;
             u32x4 val = {0u, 0u, 0u, 0u};
-            if (c < n) val = *(const u32x4 *)(ksb + (((int64_t)b * H_lm + l) * C + c) * D + cb * 8);
-            kt[e][cr][cb ^ (cr & 7)] = val;
+            if (c < n) val = *(const u32x4 *)((kk ? ksb2 : ksb) + (((int64_t)b * H_lm + l) * C + c) * D + cb * 8);
+            kt[kk][e][rr][cb ^ (rr & 7)] = val;
         }
         if (threadIdx.x < G * 16) {
-            const int e = threadIdx.x / 16, cr = threadIdx.x % 16;
-            const int c = c0 + cr;
+            const int e = threadIdx.x / 16, rr = threadIdx.x % 16;
+            const int c = c0 + rr;
             const int l = (g * G + e) * H_lm / H_q;
-            bt[e][cr] = c < n ? b_sum[((int64_t)b * H_lm + l) * C + c] : 0.f;
+            bt[e][rr] = c < n ? b_sum[((int64_t)b * H_lm + l) * C + c] : 0.f;
         }
         __syncthreads();
         f32x4 best = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
+        for (int j = 0; j < HPW; ++j) {
+            const int e = hh * HPW + j;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int cr = lane & 15;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4 raw = kt[e][cr][(4 * s + grp) ^ (cr & 7)];
-                bf16x8 a;
-                __builtin_memcpy(&a, &raw, 16);
-                acc = mfma16(a, qf[e][s], acc);
+                const int blk = (4 * s + grp) ^ (cr & 7);
+                bf16x8 a1;
+                const u32x4 raw1 = kt[0][e][cr][blk];
+                __builtin_memcpy(&a1, &raw1, 16);
+                acc = mfma16(a1, qf[j][0][s], acc);
+                if constexpr (KSPLIT) {
+                    bf16x8 a2;
+                    const u32x4 raw2 = kt[NKT - 1][e][cr][blk];
+                    __builtin_memcpy(&a2, &raw2, 16);
+                    acc = mfma16(a2, qf[j][0][s], acc);
+                }
+                if constexpr (QSPLIT) acc = mfma16(a1, qf[j][NQT - 1][s], acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(scale, acc[i], bt[e][4 * grp + i]));
         }
-        if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+        if constexpr (WPQ > 1) {
+            if (hh > 0) px[hh - 1][qt][lane] = best;
+            __syncthreads();
+            if (hh == 0) {
+#pragma unroll
+                for (int x = 0; x < WPQ - 1; ++x) {
+                    const f32x4 o = px[x][qt][lane];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], o[i]);
+                }
+                if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+            }
+        } else {
+            if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+        }
     }
 }
 
 // ------------------------------------------------------------ exact refine + top-K
 
-constexpr int SEL_GMAX = 8;
-constexpr int SEL_KMAX = 128;
 
 // 64-bit ranking key: larger score first, then lower chunk index first.
 __device__ __forceinline__ uint64_t rank_key(float s, int idx) {
@@ -392,21 +451,30 @@ __device__ __forceinline__ float group_sum(float v) {
     }
 }
 
+// Per-wave survivor list: chunk ids in ascending order, their exact
+// ranking keys and per-head exact scores.  Entries [0, nref) are refined.
+constexpr int SEL_CAP = 3 * WAVE;
+template <int G>
 struct SelLds {
-    uint64_t run_key[SEL_KMAX];     // running exact top-K
-    float run_sc[SEL_KMAX][SEL_GMAX];
-    int batch_idx[WAVE];            // survivors awaiting refinement
-    uint64_t bkey[WAVE];            // their exact ranking keys
-    float bsc[WAVE][SEL_GMAX];      // and per-head exact scores
+    int idx[SEL_CAP];
+    uint64_t key[SEL_CAP];
+    float sc[SEL_CAP][G];
 };
 
 // One wave per (b, g, query).  SHARED: the G heads of a group share one
 // landmark (H_lm == H_kv); otherwise each head has its own.
 //
-// Exact refinement reads each survivor's landmark rows from the fp32
-// chunk-major copy: the GLM rows of a group are contiguous, so one
-// survivor is one coalesced read spread over the wave (EPL elements per
-// lane), reduced with DPP.
+// 1. Threshold from the approximate group scores: tau' = K-th largest of the
+//    per-lane top-4 (a lower bound of the K-th largest approximate score).
+// 2. Survivors: approximate score >= tau' - 2E, a superset of the exact
+//    top-K (E bounds |exact - approx|).  They are appended to the list in
+//    ascending chunk order.
+// 3. Exact refinement of the survivors from the fp32 chunk-major copy of k'
+//    (the GLM rows of a group are contiguous: one coalesced read spread over
+//    the wave, EPL elements per lane, reduced with DPP).
+// 4. When the list would overflow, it is refined and cut in place to its
+//    exact top-K (order kept); at the end the exact top-K of the list are
+//    emitted in list order, i.e. ascending.
 template <typename TQ, int D, int G, bool SHARED>
 __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, const float *__restrict__ kcm,
                                                      const float *__restrict__ b_sum,
@@ -419,9 +487,9 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     constexpr int EPL = GLM * D / WAVE;   // elements of a survivor row per lane
     constexpr int LR = D / EPL;           // lanes covering one landmark row
     static_assert(EPL >= 1 && EPL <= 16 && (EPL % 4 == 0 || EPL < 4), "lane slice");
-    __shared__ SelLds lds_all[4];
+    __shared__ SelLds<G> lds_all[4];
     const int wave = threadIdx.x / WAVE, lane = lane_id();
-    SelLds &L = lds_all[wave];
+    SelLds<G> &L = lds_all[wave];
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;  // (b*H_kv + g)*N + i
     if (row >= (int64_t)B * H_kv * N) return;
     const int i = (int)(row % N);
@@ -504,160 +572,160 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
         if (thr_key == 0u) thr_key = 1u;
     }
 
-    // ---- stream survivors through exact refinement, keep exact top-K
-    int run_cnt = 0;
-    int bcnt = 0;
-    // exact scores of survivors batch[k0 .. k0+RB) (all lanes): per-head s^
-    // of survivor k land in bsc[k], its ranking key in bkey[k].  RB rows are
-    // loaded before any is reduced so that their latencies overlap.
+    // ---- exact refinement of list entries [k0, k1): per-head s^ into
+    // L.sc, ranking key into L.key.  RB rows are loaded before any is
+    // reduced so that their latencies overlap.
     constexpr int RB = 4;
-    auto refine = [&](int k0, int cnt) {
-        float kx[RB][EPL];
-        int cs[RB];
+    auto refine = [&](int k0, int k1) {
+        for (int kb = k0; kb < k1; kb += RB) {
+            const int cnt = min(RB, k1 - kb);
+            float kx[RB][EPL];
+            int cs[RB];
 #pragma unroll
-        for (int u = 0; u < RB; ++u) {
-            cs[u] = L.batch_idx[k0 + min(u, cnt - 1)];
-            const float *kr = kcm_g + (int64_t)cs[u] * GLM * D + lane * EPL;
-            if constexpr (EPL >= 4) {
+            for (int u = 0; u < RB; ++u) {
+                cs[u] = L.idx[kb + min(u, cnt - 1)];
+                const float *kr = kcm_g + (int64_t)cs[u] * GLM * D + lane * EPL;
+                if constexpr (EPL >= 4) {
 #pragma unroll
-                for (int x = 0; x < EPL; x += 4) {
-                    const f32x4 v4 = *(const f32x4 *)(kr + x);
-                    kx[u][x] = v4[0], kx[u][x + 1] = v4[1], kx[u][x + 2] = v4[2], kx[u][x + 3] = v4[3];
+                    for (int x = 0; x < EPL; x += 4) {
+                        const f32x4 v4 = *(const f32x4 *)(kr + x);
+                        kx[u][x] = v4[0], kx[u][x + 1] = v4[1], kx[u][x + 2] = v4[2], kx[u][x + 3] = v4[3];
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < EPL; ++x) kx[u][x] = kr[x];
                 }
-            } else {
-#pragma unroll
-                for (int x = 0; x < EPL; ++x) kx[u][x] = kr[x];
             }
-        }
 #pragma unroll
-        for (int u = 0; u < RB; ++u) {
-            if (u >= cnt) break;
-            const int c = cs[u], slot = k0 + u;
-            float agg = -INFINITY;
-            if constexpr (SHARED) {
-                const float bb = bs_g[c];
+            for (int u = 0; u < RB; ++u) {
+                if (u >= cnt) break;
+                const int c = cs[u], slot = kb + u;
+                float agg = -INFINITY;
+                if constexpr (SHARED) {
+                    const float bb = bs_g[c];
 #pragma unroll
-                for (int e = 0; e < G; ++e) {
+                    for (int e = 0; e < G; ++e) {
+                        float part = 0.f;
+#pragma unroll
+                        for (int x = 0; x < EPL; ++x) part = fmaf(qv[e][x], kx[u][x], part);
+                        const float sc = fmaf(scale, group_sum<WAVE>(part), bb);
+                        if (lane == 0) L.sc[slot][e] = sc;
+                        agg = fmaxf(agg, sc);
+                    }
+                } else {
                     float part = 0.f;
 #pragma unroll
-                    for (int x = 0; x < EPL; ++x) part = fmaf(qv[e][x], kx[u][x], part);
-                    const float sc = fmaf(scale, group_sum<WAVE>(part), bb);
-                    if (lane == 0) L.bsc[slot][e] = sc;
-                    agg = fmaxf(agg, sc);
+                    for (int x = 0; x < EPL; ++x) part = fmaf(qv[0][x], kx[u][x], part);
+                    const float sc = fmaf(scale, group_sum<LR>(part), bs_g[(int64_t)el * C + c]);
+                    if (lane % LR == 0) L.sc[slot][el] = sc;
+                    agg = sc;
+#pragma unroll
+                    for (int m = LR; m < WAVE; m <<= 1) agg = fmaxf(agg, __shfl_xor(agg, m, WAVE));
                 }
-            } else {
-                float part = 0.f;
-#pragma unroll
-                for (int x = 0; x < EPL; ++x) part = fmaf(qv[0][x], kx[u][x], part);
-                const float sc = fmaf(scale, group_sum<LR>(part), bs_g[(int64_t)el * C + c]);
-                if (lane % LR == 0) L.bsc[slot][el] = sc;
-                agg = sc;
-#pragma unroll
-                for (int m = LR; m < WAVE; m <<= 1) agg = fmaxf(agg, __shfl_xor(agg, m, WAVE));
+                if (lane == 0) L.key[slot] = rank_key(agg, c);
             }
-            if (lane == 0) L.bkey[slot] = rank_key(agg, c);
         }
     };
-    auto flush = [&]() {
-        wave_sync();
-        for (int k = 0; k < bcnt; k += RB) refine(k, min(RB, bcnt - k));
-        wave_sync();
-        // merge with the running set (entries lane and lane+64)
-        uint64_t keys[3];
-        keys[0] = lane < run_cnt ? L.run_key[lane] : 0ull;
-        keys[1] = lane + WAVE < run_cnt ? L.run_key[lane + WAVE] : 0ull;
-        keys[2] = lane < bcnt ? L.bkey[lane] : 0ull;
-        float rs[3][G];
+    // keys of the (refined) list, three slots per lane, 0 past cnt
+    auto list_keys = [&](int cnt, uint64_t (&keys)[3]) {
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-            rs[0][e] = lane < run_cnt ? L.run_sc[lane][e] : 0.f;
-            rs[1][e] = lane + WAVE < run_cnt ? L.run_sc[lane + WAVE][e] : 0.f;
-            rs[2][e] = lane < bcnt ? L.bsc[lane][e] : 0.f;
-        }
-        const int total = run_cnt + bcnt;
-        uint64_t T = 1;  // keep every non-empty key
-        if (total > K) T = kth_largest64<3>(keys, K);
+        for (int v = 0; v < 3; ++v) keys[v] = lane + WAVE * v < cnt ? L.key[lane + WAVE * v] : 0ull;
+    };
+
+    int cnt = 0, nref = 0;
+    // cut the list to its exact top K, keeping the order
+    auto shrink = [&]() {
         wave_sync();
-        // compact keys >= T into the running set, slot order 0, 1, 2
+        refine(nref, cnt);
+        wave_sync();
+        uint64_t keys[3];
+        list_keys(cnt, keys);
+        const uint64_t T = kth_largest64<3>(keys, K);
+        // forward compaction: a kept entry moves to pos <= its slot, and
+        // every slot of a 64-slot round is read before the round writes
         int base = 0;
 #pragma unroll
         for (int v = 0; v < 3; ++v) {
+            const int slot = lane + WAVE * v;
             const bool keep = keys[v] >= T && keys[v] != 0ull;
             const uint64_t m = __ballot(keep);
             const int pos = base + __popcll(m & lanemask_lt());
-            if (keep && pos < SEL_KMAX) {
-                L.run_key[pos] = keys[v];
+            int id = 0;
+            float scv[G];
+            if (keep) {
+                id = L.idx[slot];
 #pragma unroll
-                for (int e = 0; e < G; ++e) L.run_sc[pos][e] = rs[v][e];
+                for (int e = 0; e < G; ++e) scv[e] = L.sc[slot][e];
             }
+            wave_sync();
+            if (keep) {
+                L.idx[pos] = id;
+                L.key[pos] = keys[v];
+#pragma unroll
+                for (int e = 0; e < G; ++e) L.sc[pos][e] = scv[e];
+            }
+            wave_sync();
             base += __popcll(m);
         }
-        run_cnt = min(base, K);
-        bcnt = 0;
+        cnt = nref = base;
         wave_sync();
+    };
+    // append the candidates whose lanes hold surv (one 64-candidate slice)
+    auto push = [&](int c, bool surv) {
+        const uint64_t m = __ballot(surv);
+        if (surv) L.idx[cnt + __popcll(m & lanemask_lt())] = c;
+        cnt += __popcll(m);
+    };
+    auto take = [&](int c, bool surv) {
+        if (cnt + __popcll(__ballot(surv)) > SEL_CAP) shrink();
+        push(c, surv);
     };
 
     if (!rank_needed) {
-        for (int c0 = 0; c0 < n; c0 += WAVE) {
-            const int m = min(WAVE, n - c0);
-            if (lane < m) L.batch_idx[lane] = c0 + lane;
-            bcnt = m;
-            flush();
-        }
+        for (int c0 = 0; c0 < n; c0 += WAVE) push(c0 + lane, c0 + lane < n);  // n <= K < SEL_CAP
     } else {
-        auto take = [&](int c, bool surv) {
-            const uint64_t m = __ballot(surv);
-            const int cnt = __popcll(m);
-            if (cnt > 0) {
-                if (bcnt + cnt > WAVE) flush();
-                if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = c;
-                bcnt += cnt;
-            }
-        };
-        // survivors straight from the cached keys when they fit one batch
-        // (the usual case); otherwise stream them from memory in batches
-        int total = WAVE + 1;
+        // survivors straight from the cached keys when the list holds them
+        // all (the usual case); otherwise stream them, cutting the list to
+        // its top K whenever it fills
+        int total = SEL_CAP + 1;
         if (cached) {
             total = 0;
 #pragma unroll
             for (int j = 0; j < JR; ++j) total += __popcll(__ballot(j < J && kreg[j] >= thr_key));
-            if (total <= WAVE) {
-#pragma unroll
-                for (int j = 0; j < JR; ++j) {
-                    const bool surv = j < J && kreg[j] >= thr_key;  // kreg = 0 past n
-                    const uint64_t m = __ballot(surv);
-                    if (surv) L.batch_idx[bcnt + __popcll(m & lanemask_lt())] = j * WAVE + lane;
-                    bcnt += __popcll(m);
-                }
-            }
         }
-        if (total > WAVE) {
+        if (total <= SEL_CAP) {
+#pragma unroll
+            for (int j = 0; j < JR; ++j) push(j * WAVE + lane, j < J && kreg[j] >= thr_key);  // kreg = 0 past n
+        } else {
             for (int j = 0; j < J; ++j) {
                 const int c = j * WAVE + lane;
                 take(c, c < n && ord_key(ar[c]) >= thr_key);
             }
         }
-        if (bcnt > 0) flush();
     }
-
-    // ---- emit ascending by chunk index
     wave_sync();
-    const int cnt = run_cnt;
-    for (int t = lane; t < SEL_KMAX; t += WAVE) {
-        if (t < cnt) {
-            const uint64_t my = L.run_key[t];
-            const int myidx = (int)(0xffffffffu - (uint32_t)my);
-            int rank = 0;
-            for (int u = 0; u < cnt; ++u) {
-                const int oi = (int)(0xffffffffu - (uint32_t)L.run_key[u]);
-                rank += oi < myidx;
-            }
-            out_idx[rank] = myidx;
+    refine(nref, cnt);
+    wave_sync();
+
+    // ---- emit the exact top K of the list, in list (= ascending) order
+    uint64_t keys[3];
+    list_keys(cnt, keys);
+    const uint64_t T = cnt > K ? kth_largest64<3>(keys, K) : 1ull;
+    int base = 0;
 #pragma unroll
-            for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + rank] = L.run_sc[t][e];
+    for (int v = 0; v < 3; ++v) {
+        const int slot = lane + WAVE * v;
+        const bool win = keys[v] >= T && keys[v] != 0ull;
+        const uint64_t m = __ballot(win);
+        const int pos = base + __popcll(m & lanemask_lt());
+        if (win) {
+            out_idx[pos] = L.idx[slot];
+#pragma unroll
+            for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + pos] = L.sc[slot][e];
         }
+        base += __popcll(m);
     }
-    for (int k = cnt + lane; k < K; k += WAVE) {
+    for (int k = base + lane; k < K; k += WAVE) {
         out_idx[k] = -1;
 #pragma unroll
         for (int e = 0; e < G; ++e) sel_score[(sc_base + (int64_t)e * N) * K + k] = -INFINITY;
@@ -669,10 +737,14 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 template <typename TQ, int D, int G>
 static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
                       hipStream_t st) {
-    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(256);
-    hipLaunchKernelGGL((score_approx_kernel<TQ, D, G>), grid, block, 0, st, qv, (const bf16 *)ws.ksb, b_sum,
-                       ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
-                       ws.per_bg);
+    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(256 * (G >= 4 ? G / 2 : 1));
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const bf16 *)ws.ksb, (const bf16 *)ws.ksb2, b_sum,
+                           ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
+                           ws.per_bg);
+    };
+    if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false>);
+    else go(score_approx_kernel<TQ, D, G, true>);
 }
 
 template <typename TQ>
@@ -729,11 +801,11 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     if (krows > 0) {
         const dim3 grid((unsigned)((krows + 15) / 16)), block(256);
         if (s.sum_bf16) {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
         } else {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
         }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -759,13 +831,12 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    // kappa: relative bound of the bf16 operand rounding (2^-8 per rounded
-    // operand, unit roundoff of an 8-bit significand), doubled for margin.
-    const bool q_rounded = qcal || !s.io_bf16;
-    const bool k_rounded = !s.sum_bf16;
-    float kappa = 1.0f / 16384.f;  // fp32 accumulation only
-    if (k_rounded) kappa += 2.f / 256.f;
-    if (q_rounded) kappa += 2.f / 256.f;
+    // kappa, relative to ||q_s|| ||k'||: fp32 accumulation (at most 2^9
+    // roundings of unit 2^-24 over d <= 128 products and three split terms,
+    // bounded by 2^-14), plus 2^-18 for each two-term split (fp32 queries,
+    // fp32 summaries) and 2^-18 for the dropped t2 k2 term, doubled.
+    const int nq = (qcal || !s.io_bf16) ? 1 : 0, nk = s.sum_bf16 ? 0 : 1;
+    const float kappa = 1.0f / 16384.f + 2.f * (float)(nq + nk + nq * nk) / 262144.f;
 
     if (qcal || !s.io_bf16) {
         const float *qv = qcal ? ws.q_s : (const float *)q;
