@@ -21,10 +21,14 @@
 //     Every row keeps its next selected chunk and score in registers, so a
 //     row only takes the chunks it selected (the union is a schedule; the
 //     result is per query).  A tile with no selecting row skips the chunk.
-//   * K and V^T chunk tiles are copied global -> LDS by global_load_lds
+//   * K and V^T chunk tiles are copied global -> LDS by buffer_load_lds
 //     (16 bytes per lane, no register staging) into a ring of NSTAGE
-//     buffers, issued NSTAGE-1 chunks ahead; each chunk waits only for its
-//     own loads (vmcnt) and one barrier.  A 16-byte-block XOR swizzle by
+//     stages.  There is no block barrier in the walk: a wave waits only for
+//     the chunks its tiles compute (a flag the DMA writes behind the data),
+//     counts itself out of each stage, and the last wave out refills the
+//     stage NSTAGE chunks ahead, so waves drift up to NSTAGE - 1 chunks
+//     apart and the uneven per-chunk work of the tiles evens out.  A
+//     16-byte-block XOR swizzle by
 //     row (applied through the per-lane source address, since the DMA
 //     writes lane-contiguous LDS) keeps the MFMA operand reads free of
 //     bank conflicts.
@@ -58,6 +62,9 @@
 #define BUF_RSRC_WORD3 0x00020000
 
 namespace hils {
+
+// Source of the ring flags: the parity of a stage's round (read by DMA).
+__device__ int32_t ring_parity[2] = {0, 1};
 
 // Key held by slot p of a chunk's transposed V rows.  In the S^T
 // accumulators of 16-key tiles 2s and 2s+1, lane group gq holds keys
@@ -131,8 +138,7 @@ struct AttendCfg {
     static constexpr int NBV = S / 8;                // 16-byte blocks per V^T row
     static constexpr int PK = S * D * 2 / 1024;      // 1 KB pieces of a K tile
     static constexpr int PV = D * S * 2 / 1024;      // 1 KB pieces of a V^T tile
-    static constexpr int LPS = (PK + PV) / NWAVE;    // DMA loads per lane per chunk
-    static_assert((PK + PV) % NWAVE == 0, "pieces per wave");
+    static constexpr int NP = PK + PV;               // 1 KB DMA pieces per chunk
 };
 
 // Dynamic LDS: int16 sel[QB*K] (chunk ids, -1 padded); fp16 wt[QB*G*K]
@@ -148,11 +154,15 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     int nqb, int64_t n_items, int64_t per_xcd) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
-    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, LPS = Cf::LPS;
+    constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, NP = Cf::NP;
     constexpr int NT = NWAVE * 64;
     // chunk ring: stage s holds the K tile [S][NBK] then the V^T tile [D][NBV]
     __shared__ u32x4 ring[NSTAGE][S * NBK + D * NBV];
-    __shared__ u32x4 sink[WAVE];  // destination of the DMA issued past the last chunk (never read)
+    // ring protocol: rel[s] counts the waves done with the chunks stage s
+    // has held; flag[s] is written by DMA behind the data of each chunk
+    // loaded into stage s (the parity of its round through the ring)
+    __shared__ int rel[NSTAGE];
+    __shared__ int flag[NSTAGE];
     auto k_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBK]>(&ring[buf][0]); };
     auto v_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBV]>(&ring[buf][S * NBK]); };
     extern __shared__ int dyn[];
@@ -180,6 +190,10 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     // scores are first staged in the (still idle) chunk ring; the launcher
     // checks QB * G * K * 4 <= sizeof(ring).
     float *sc_tmp = (float *)&ring[0][0];
+    if (tid < NSTAGE) {
+        rel[tid] = 0;
+        flag[tid] = -1;
+    }
     for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
     for (int t = tid; t < QB * K; t += NT) {
         const int iq = i0 + t / K;
@@ -279,38 +293,43 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
     auto chunk_of = [&](int it) { return it < U ? ulist[it] : wc0 + (it - U); };
 
-    // ---- DMA of chunk tiles into the ring: piece p of wave w, lane l.
-    // Every call issues exactly LPS loads per lane (past the end they land
-    // in the sink) so the vmcnt bookkeeping below is a constant.  Buffer
-    // loads: the resource starts at the chunk and ends at token N, so rows
-    // of a partial last chunk read as zeros (those keys are masked), and the
-    // per-lane address is a 32-bit offset.
+    // ---- DMA of one chunk into its ring stage by one wave: NP pieces of
+    // 1 KB, 16 bytes per lane, then (lane 0 only) the stage's flag from
+    // the parity table.  A wave's loads complete in issue order, so the
+    // flag lands after the data.  Buffer loads: the resource starts at the
+    // chunk and ends at token N, so rows of a partial last chunk read as
+    // zeros (those keys are masked), and the per-lane address is 32 bits.
+    const __amdgpu_buffer_rsrc_t par_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)&ring_parity[0], (short)0, 8, BUF_RSRC_WORD3);
     auto issue = [&](int it) {
-        const bool real = it < T;
-        const int c = __builtin_amdgcn_readfirstlane(chunk_of(real ? it : T - 1));
+        const int c = __builtin_amdgcn_readfirstlane(chunk_of(it));
         const int buf = it % NSTAGE;
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(kbase + (int64_t)c * S * D), (short)0, (N - c * S) * D * 2, BUF_RSRC_WORD3);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vtbase + (int64_t)c * D * S), (short)0, D * S * 2, BUF_RSRC_WORD3);
+        // the swizzle repeats every 16 rows: the lane part of a piece's
+        // source offset takes PPx distinct values, the rest is scalar
 #pragma unroll
-        for (int j = 0; j < LPS; ++j) {
-            const int p = wave * LPS + j;
+        for (int p = 0; p < NP; ++p) {
             if (p < PK) {
-                constexpr int RPP = 1024 / (D * 2);  // K rows per piece
-                const int row = p * RPP + lane / NBK, blk = lane % NBK;
+                constexpr int RPP = 1024 / (D * 2), PPK = 16 / RPP;  // K rows per piece, pieces per 16 rows
+                const int row = (p % PPK) * RPP + lane / NBK, blk = lane % NBK;
                 const int off = (row * D + (blk ^ swz<NBK>(row)) * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    kr, HILS_LPTR(real ? &k_tile(buf)[p * RPP][0] : &sink[0]), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, HILS_LPTR(&k_tile(buf)[p * RPP][0]), 16, off,
+                                                         (p / PPK) * 16 * D * 2, 0, 0);
             } else {
-                constexpr int RPP = 1024 / (S * 2);  // V^T rows per piece
+                constexpr int RPP = 1024 / (S * 2), PPV = 16 / RPP;  // V^T rows per piece, pieces per 16 rows
                 const int pv = p - PK;
-                const int row = pv * RPP + lane / NBV, blk = lane % NBV;
+                const int row = (pv % PPV) * RPP + lane / NBV, blk = lane % NBV;
                 const int off = (row * S + (blk ^ swz<NBV>(row)) * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    vr, HILS_LPTR(real ? &v_tile(buf)[pv * RPP][0] : &sink[0]), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, HILS_LPTR(&v_tile(buf)[pv * RPP][0]), 16, off,
+                                                         (pv / PPV) * 16 * S * 2, 0, 0);
             }
         }
+        if (lane == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(par_rsrc, HILS_LPTR(&flag[buf]), 4, ((it / NSTAGE) & 1) * 4, 0,
+                                                     0, 0);
     };
     // Software pipeline of n LDS fragment reads, each feeding M MFMAs (one
     // per tile of the wave): the scheduler issues LA reads ahead, then
@@ -384,118 +403,148 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- pipelined walk: union chunks, then the window.  Step j issues
-    // chunk j + NSTAGE - 1 into the ring.
-#pragma unroll
-    for (int it = 0; it < NSTAGE - 1; ++it) issue(it);
+    // ---- walk: union chunks, then the window.  Waves are decoupled: a
+    // wave waits only for each chunk's data to land (its flag), and
+    // announces in rel when it is done with a stage; the last wave to leave
+    // a stage refills it with the chunk NSTAGE steps ahead.  So a wave runs
+    // up to NSTAGE - 1 chunks ahead of the slowest, and the work of the
+    // tiles that a chunk activates spreads over several chunks' time.
+    // Every wait is bounded, and the slowest wave never waits on another
+    // wave: its chunk was issued when it left that chunk's stage.
+    for (int j = wave; j < NSTAGE && j < T; j += NWAVE) issue(j);
     for (int it = 0; it < T; ++it) {
-        // younger than chunk it's loads: those of the NSTAGE - 2 later chunks
-        wait_vmcnt<(NSTAGE - 2) * LPS>();
-        __builtin_amdgcn_s_barrier();
-        issue(it + NSTAGE - 1);
         const int buf = it % NSTAGE;
         const int c = chunk_of(it);
-        f32x4 acc[TPW][KT];
-        if (it < U) {
-            // a wave computes its tiles when one of its rows selected chunk c;
-            // rows that did not select it get weight 0 (exact zeros in O)
-            bool act[TPW];
-            bool any = false;
+        const bool window = it >= U;
+        bool act[TPW];
+        bool any = false;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                act[t] = nch[t] == c;
-                any |= act[t];
+        for (int t = 0; t < TPW; ++t) {
+            act[t] = window || nch[t] == c;
+            any |= act[t];
+        }
+        // Every wave waits for every chunk to land, also one it skips: so no
+        // wave leaves a stage before its current round is in (a wave can
+        // lead the slowest by at most NSTAGE - 1 chunks, rel[s] never mixes
+        // rounds) and, having seen the previous round's flag, a wave only
+        // finds this round's or the previous round's parity in flag[buf].
+        // (LDS operations of a wave execute in order, so a plain flag read
+        // orders the flag before the data reads, and those before the
+        // release below; the asm statements are compiler barriers.)
+        {
+            const int want = (it / NSTAGE) & 1;
+            const uint32_t faddr = (uint32_t)(uintptr_t)&flag[buf];  // LDS offset
+            for (int spin = 0; spin < (1 << 18); ++spin) {
+                // read in asm: the compiler would otherwise first wait for
+                // all of this wave's DMA in flight (the flag is a DMA target)
+                int fv;
+                asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(fv) : "v"(faddr) : "memory");
+                if (fv == want) break;
+                __builtin_amdgcn_s_sleep(1);
             }
-            if (__ballot(any) == 0ull) continue;
-            // tiles of the wave with a selecting row (wave-uniform)
-            int wmask = 0;
+        }
+        if (__ballot(any) != 0ull) {
+            f32x4 acc[TPW][KT];
+            if (!window) {
+                // a wave computes its tiles when one of its rows selected chunk c;
+                // rows that did not select it get weight 0 (exact zeros in O)
+                int wmask = 0;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) wmask |= (__ballot(act[t]) != 0ull) << t;
-            auto sel_step = [&](auto mask_c) {
-                constexpr int MASK = decltype(mask_c)::value;
-                qk(mask_c, k_tile(buf), acc);
+                for (int t = 0; t < TPW; ++t) wmask |= (__ballot(act[t]) != 0ull) << t;
+                auto sel_step = [&](auto mask_c) {
+                    constexpr int MASK = decltype(mask_c)::value;
+                    qk(mask_c, k_tile(buf), acc);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        if (!((MASK >> t) & 1)) continue;
+                        float cmax = -INFINITY;
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, acc[t][kt][i]);
+                        cmax = rows4_max(cmax) * scale_log2;
+                        float lc = 0.f;
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                acc[t][kt][i] = exp2f(fmaf(acc[t][kt][i], scale_log2, -cmax));
+                                lc += acc[t][kt][i];
+                            }
+                        lc = rows4_sum(lc);
+                        const float f = act[t] ? nwt[t] / lc : 0.f;
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[t][kt][i] *= f;
+                    }
+                    pv(mask_c, v_tile(buf), acc);
+                };
+                if constexpr (TPW == 1) {
+                    sel_step(std::integral_constant<int, 1>{});
+                } else {
+                    if (wmask == 1) sel_step(std::integral_constant<int, 1>{});
+                    else if (wmask == 2) sel_step(std::integral_constant<int, 2>{});
+                    else sel_step(std::integral_constant<int, 3>{});
+                }
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if (act[t]) {
+                        const int nx = ++cur[t];
+                        const int m = qrow[t], e = hrow[t] - g * G;
+                        nch[t] = nx < nsel[t] ? (int)sel_l[m * K + nx] : 0x7fffffff;
+                        nwt[t] = nx < nsel[t] ? (float)wt_l[(m * G + e) * K + nx] : 0.f;
+                    }
+            } else {
+                const bool diag = c == qc;
+                constexpr int ALL = (1 << TPW) - 1;
+                qk(std::integral_constant<int, ALL>{}, k_tile(buf), acc);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
-                    if (!((MASK >> t) & 1)) continue;
+                    const int iq = i0 + qrow[t];
                     float cmax = -INFINITY;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            acc[t][kt][i] *= scale_log2;
-                            cmax = fmaxf(cmax, acc[t][kt][i]);
+                            const int j = c * S + 16 * kt + 4 * grp + i;
+                            const float x = (diag && j > iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
+                            acc[t][kt][i] = x;
+                            cmax = fmaxf(cmax, x);
                         }
                     cmax = rows4_max(cmax);
-                    float lc = 0.f;
+                    const float mnew = fmaxf(mrun[t], cmax);
+                    const float alpha = exp2f(mrun[t] - mnew);
+                    float ls = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            acc[t][kt][i] = exp2f(acc[t][kt][i] - cmax);
-                            lc += acc[t][kt][i];
+                            acc[t][kt][i] = exp2f(acc[t][kt][i] - mnew);
+                            ls += acc[t][kt][i];
                         }
-                    lc = rows4_sum(lc);
-                    const float f = act[t] ? nwt[t] / lc : 0.f;
+                    ls = rows4_sum(ls);
+                    lrun[t] = lrun[t] * alpha + ls;
+                    mrun[t] = mnew;
 #pragma unroll
-                    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[t][kt][i] *= f;
+                    for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
                 }
-                pv(mask_c, v_tile(buf), acc);
-            };
-            if constexpr (TPW == 1) {
-                sel_step(std::integral_constant<int, 1>{});
-            } else {
-                if (wmask == 1) sel_step(std::integral_constant<int, 1>{});
-                else if (wmask == 2) sel_step(std::integral_constant<int, 2>{});
-                else sel_step(std::integral_constant<int, 3>{});
+                pv(std::integral_constant<int, ALL>{}, v_tile(buf), acc);
             }
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                if (act[t]) {
-                    const int nx = ++cur[t];
-                    const int m = qrow[t], e = hrow[t] - g * G;
-                    nch[t] = nx < nsel[t] ? (int)sel_l[m * K + nx] : 0x7fffffff;
-                    nwt[t] = nx < nsel[t] ? (float)wt_l[(m * G + e) * K + nx] : 0.f;
-                }
-        } else {
-            const bool diag = c == qc;
-            constexpr int ALL = (1 << TPW) - 1;
-            qk(std::integral_constant<int, ALL>{}, k_tile(buf), acc);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int iq = i0 + qrow[t];
-                float cmax = -INFINITY;
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = c * S + 16 * kt + 4 * grp + i;
-                        const float x = (diag && j > iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
-                        acc[t][kt][i] = x;
-                        cmax = fmaxf(cmax, x);
-                    }
-                cmax = rows4_max(cmax);
-                const float mnew = fmaxf(mrun[t], cmax);
-                const float alpha = exp2f(mrun[t] - mnew);
-                float ls = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[t][kt][i] = exp2f(acc[t][kt][i] - mnew);
-                        ls += acc[t][kt][i];
-                    }
-                ls = rows4_sum(ls);
-                lrun[t] = lrun[t] * alpha + ls;
-                mrun[t] = mnew;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
-            }
-            pv(std::integral_constant<int, ALL>{}, v_tile(buf), acc);
         }
+        // leave the stage (after this wave's reads of it: LDS operations of
+        // a wave complete in order); the last wave out refills it
+        // (in asm for the same reason as the flag read)
+        int old = 0;
+        if (lane == 0) {
+            const uint32_t raddr = (uint32_t)(uintptr_t)&rel[buf];
+            asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(raddr), "v"(1)
+                         : "memory");
+        }
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old == NWAVE * (it / NSTAGE + 1) - 1 && it + NSTAGE < T) issue(it + NSTAGE);
     }
-    wait_vmcnt<0>();  // no DMA outstanding when the block retires
+    wait_vmcnt<0>();  // no DMA outstanding when the wave retires
 
     // ---- epilogue
 #pragma unroll
@@ -640,10 +689,10 @@ struct AttendPlan {
     static constexpr int TPW = TPW_;
     static constexpr int QB = NWAVE * TPW * (16 / G);
     static constexpr bool valid = QB <= S && S % QB == 0 && !(NWAVE == 16 && D * S > 128 * 64) &&
-                                  !(TPW == 2 && D * S > 128 * 64) && (2 * S * D * 2 / 1024) % NWAVE == 0;
+                                  !(TPW == 2 && D * S > 128 * 64);
     static constexpr int NSTAGE = (S * D * 4 <= 32 * 1024) ? 4 : 2;
     static constexpr size_t ring_bytes = (size_t)NSTAGE * 2 * S * D * 2;
-    static constexpr size_t static_lds = ring_bytes + 16 * 64;
+    static constexpr size_t static_lds = ring_bytes + 64;
 };
 
 constexpr size_t LDS_BYTES = 160 * 1024;
