@@ -440,7 +440,9 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                 int fv;
                 asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(fv) : "v"(faddr) : "memory");
                 if (fv == want) break;
-                __builtin_amdgcn_s_sleep(1);
+                // a waiting wave yields its SIMD to the working ones (the
+                // longer pause suits the deeper ring: its waits are longer)
+                __builtin_amdgcn_s_sleep(NSTAGE >= 4 ? 8 : 1);
             }
         }
         if (__ballot(any) != 0ull) {
