@@ -181,6 +181,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
         float acc[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+        // widen inside the head loop: an opaque shift and mask keep the
+        // compiler from hoisting 128 widened values out of it (without
+        // copying the keys)
+        uint32_t sh = 16, mk = 0xffff0000u;
+        asm volatile("" : "+v"(sh), "+v"(mk));
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             if (NB > 1) load_block(blk);
@@ -191,12 +196,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        // widen inside the head loop (an opaque copy keeps the
-                        // compiler from hoisting 128 widened values out of it)
-                        uint32_t w = kx[t0 + u][x];
-                        asm volatile("" : "+v"(w));
-                        acc[2 * x] = fmaf(p4[u], __uint_as_float(w << 16), acc[2 * x]);
-                        acc[2 * x + 1] = fmaf(p4[u], __uint_as_float(w & 0xffff0000u), acc[2 * x + 1]);
+                        const uint32_t w = kx[t0 + u][x];
+                        acc[2 * x] = fmaf(p4[u], __uint_as_float(w << sh), acc[2 * x]);
+                        acc[2 * x + 1] = fmaf(p4[u], __uint_as_float(w & mk), acc[2 * x + 1]);
                     }
             }
         }
