@@ -282,12 +282,13 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 // ------------------------------------------------------------ approximate scores (MFMA)
 
 // One block = 64 consecutive queries of one query chunk (S is a multiple of
-// 64) for one (b, g): four 16-query tiles x WPQ groups of HPW heads, one
-// wave each.  The B operand of the 16x16x32 MFMAs is q^T of the wave's 16
-// queries (bf16 terms, in registers); the A operand is a 16-candidate k'
-// tile staged in LDS.  D: lane l holds candidates 4*(l/16)+i of query l%16;
-// the head groups of a tile meet through LDS and the first stores 16
-// contiguous bytes of its query's ragged score row.
+// 64) for one (b, g): 2G waves, wave (qp, e) owns query tiles 2qp, 2qp+1
+// (16 queries each) of head e of the group.  The B operands of the
+// 16x16x32 MFMAs are q^T of those 32 queries (bf16 terms, in registers);
+// the A operand is a 16-candidate k' tile staged in LDS, each fragment read
+// feeding both query tiles.  D: lane l holds candidates 4*(l/16)+i of query
+// l%16; the G heads of a query pair meet through LDS and wave (qp, 0) stores
+// 16 contiguous bytes of each query's ragged score row.
 //
 // Split products: the scoring query q_s = t1 + t2 and k' = k1 + k2 with
 // t1 = bf16(q_s), t2 = bf16(q_s - t1) (k likewise); the MFMAs sum
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 // ||q_s|| * max_c ||k'_c|| with kappa (set by the launcher) adding those
 // terms to a bound on the fp32 accumulation.
 template <typename TQ, int D, int G, bool KSPLIT>
-__global__ __launch_bounds__(256 * (G >= 4 ? G / 2 : 1)) void score_approx_kernel(
+__global__ __launch_bounds__(128 * G) void score_approx_kernel(
     const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const bf16 *__restrict__ ksb2,
     const float *__restrict__ b_sum, const float *__restrict__ knorm, float *__restrict__ agg_out,
     float *__restrict__ err_out, int N, int H_q, int H_kv, int H_lm, int C, int S, int W, int K, float scale,
@@ -306,14 +307,12 @@ __global__ __launch_bounds__(256 * (G >= 4 ? G / 2 : 1)) void score_approx_kerne
     constexpr bool QSPLIT = std::is_same<TQ, float>::value;
     constexpr int NQT = QSPLIT ? 2 : 1;   // query terms
     constexpr int NKT = KSPLIT ? 2 : 1;   // k' terms
-    constexpr int HPW = G >= 2 ? 2 : 1;   // heads per wave
-    constexpr int WPQ = G / HPW;          // waves per 16-query tile
-    constexpr int NT = 256 * WPQ;
+    constexpr int NT = 128 * G;
     constexpr int KS = D / 32;            // MFMA k-steps over the head dim
     constexpr int NB = D / 8;             // 16-byte blocks per k' row
     __shared__ u32x4 kt[NKT][G][16][NB];
     __shared__ float bt[G][16];
-    __shared__ f32x4 px[WPQ > 1 ? WPQ - 1 : 1][4][WAVE];
+    __shared__ f32x4 px[G > 1 ? G - 1 : 1][2][2][WAVE];
 
     const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
@@ -324,16 +323,21 @@ __global__ __launch_bounds__(256 * (G >= 4 ? G / 2 : 1)) void score_approx_kerne
     if (n <= K) return;  // every candidate is selected; nothing to rank
 
     const int wave = threadIdx.x / WAVE, lane = lane_id();
-    const int qt = wave % 4, hh = wave / 4;
-    const int iq = i0 + qt * 16 + (lane & 15);
-    const bool qvalid = iq < N;
-    const int iqc = qvalid ? iq : N - 1;
+    const int qp = wave % 2, e = wave / 2;
     const int grp = lane >> 4;
-
-    bf16x8 qf[HPW][NQT][KS];
+    int iq[2], iqc[2];
+    bool qvalid[2];
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-        const TQ *qr = q + (((int64_t)b * H_q + g * G + hh * HPW + j) * N + iqc) * D;
+    for (int u = 0; u < 2; ++u) {
+        iq[u] = i0 + (2 * qp + u) * 16 + (lane & 15);
+        qvalid[u] = iq[u] < N;
+        iqc[u] = qvalid[u] ? iq[u] : N - 1;
+    }
+
+    bf16x8 qf[2][NQT][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const TQ *qr = q + (((int64_t)b * H_q + g * G + e) * N + iqc[u]) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = 32 * s + 8 * grp;
@@ -341,91 +345,126 @@ __global__ __launch_bounds__(256 * (G >= 4 ? G / 2 : 1)) void score_approx_kerne
             for (int x = 0; x < 8; ++x) {
                 const float v = to_f32(qr[d0 + x]);
                 const bf16 v1 = (bf16)v;
-                qf[j][0][s][x] = v1;
-                if constexpr (QSPLIT) qf[j][1][s][x] = (bf16)(v - (float)v1);
+                qf[u][0][s][x] = v1;
+                if constexpr (QSPLIT) qf[u][NQT - 1][s][x] = (bf16)(v - (float)v1);
             }
         }
     }
-    if (hh == 0) {
+    if (e == 0) {
         // bound of the group score: the largest per-head bound of the group
-        float emax = 0.f;
-        for (int e = 0; e < G; ++e) {
-            const int hd = g * G + e;
-            const TQ *qr = q + (((int64_t)b * H_q + hd) * N + iqc) * D;
-            float ss = 0.f;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+        for (int u = 0; u < 2; ++u) {
+            float emax = 0.f;
+            for (int h = 0; h < G; ++h) {
+                const int hd = g * G + h;
+                const TQ *qr = q + (((int64_t)b * H_q + hd) * N + iqc[u]) * D;
+                float ss = 0.f;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const float v = to_f32(qr[32 * s + 8 * grp + x]);
-                    ss = fmaf(v, v, ss);
-                }
-            ss = xor_sum<16, 32>(ss);
-            emax = fmaxf(emax, sqrtf(ss) * knorm[b * H_lm + hd * H_lm / H_q]);
+                for (int s = 0; s < KS; ++s)
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const float v = to_f32(qr[32 * s + 8 * grp + x]);
+                        ss = fmaf(v, v, ss);
+                    }
+                ss = xor_sum<16, 32>(ss);
+                emax = fmaxf(emax, sqrtf(ss) * knorm[b * H_lm + hd * H_lm / H_q]);
+            }
+            const float err = scale * kappa * emax + 1e-5f;
+            if (qvalid[u] && grp == 0) err_out[((int64_t)b * H_kv + g) * N + iq[u]] = err;
         }
-        const float err = scale * kappa * emax + 1e-5f;
-        if (qvalid && grp == 0) err_out[((int64_t)b * H_kv + g) * N + iq] = err;
     }
 
-    float *row = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset(iqc, w, S);
+    float *row[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) row[u] = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset(iqc[u], w, S);
     const int cr = lane & 15;
 
-    for (int c0 = 0; c0 < n; c0 += 16) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < NKT * G * 16 * NB; idx += NT) {
+    // k' tiles are staged through registers one tile ahead: the loads of
+    // tile c0 + 16 are in flight while tile c0 is multiplied
+    constexpr int NPRE = NKT * NB / 8;  // 16-byte pieces per thread and tile
+    static_assert(NKT * G * 16 * NB == NPRE * NT, "staging pieces");
+    u32x4 pre[NPRE];
+    float bpre = 0.f;
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int j = 0; j < NPRE; ++j) {
+            const int idx = threadIdx.x + j * NT;
             const int kk = idx / (G * 16 * NB), rem0 = idx % (G * 16 * NB);
-            const int e = rem0 / (16 * NB), rem = rem0 % (16 * NB);
+            const int h = rem0 / (16 * NB), rem = rem0 % (16 * NB);
             const int rr = rem / NB, cb = rem % NB;
             const int c = c0 + rr;
-            const int l = (g * G + e) * H_lm / H_q;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (c < n) val = *(const u32x4 *)((kk ? ksb2 : ksb) + (((int64_t)b * H_lm + l) * C + c) * D + cb * 8);
-            kt[kk][e][rr][cb ^ (rr & 7)] = val;
+            const int l = (g * G + h) * H_lm / H_q;
+            pre[j] = u32x4{0u, 0u, 0u, 0u};
+            if (c < n) pre[j] = *(const u32x4 *)((kk ? ksb2 : ksb) + (((int64_t)b * H_lm + l) * C + c) * D + cb * 8);
         }
         if (threadIdx.x < G * 16) {
-            const int e = threadIdx.x / 16, rr = threadIdx.x % 16;
+            const int h = threadIdx.x / 16, rr = threadIdx.x % 16;
             const int c = c0 + rr;
-            const int l = (g * G + e) * H_lm / H_q;
-            bt[e][rr] = c < n ? b_sum[((int64_t)b * H_lm + l) * C + c] : 0.f;
+            const int l = (g * G + h) * H_lm / H_q;
+            bpre = c < n ? b_sum[((int64_t)b * H_lm + l) * C + c] : 0.f;
         }
+    };
+    fetch(0);
+    for (int c0 = 0; c0 < n; c0 += 16) {
         __syncthreads();
-        f32x4 best = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-            const int e = hh * HPW + j;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int blk = (4 * s + grp) ^ (cr & 7);
-                bf16x8 a1;
-                const u32x4 raw1 = kt[0][e][cr][blk];
-                __builtin_memcpy(&a1, &raw1, 16);
-                acc = mfma16(a1, qf[j][0][s], acc);
-                if constexpr (KSPLIT) {
-                    bf16x8 a2;
-                    const u32x4 raw2 = kt[NKT - 1][e][cr][blk];
-                    __builtin_memcpy(&a2, &raw2, 16);
-                    acc = mfma16(a2, qf[j][0][s], acc);
-                }
-                if constexpr (QSPLIT) acc = mfma16(a1, qf[j][NQT - 1][s], acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(scale, acc[i], bt[e][4 * grp + i]));
+        for (int j = 0; j < NPRE; ++j) {
+            const int idx = threadIdx.x + j * NT;
+            const int kk = idx / (G * 16 * NB), rem0 = idx % (G * 16 * NB);
+            const int h = rem0 / (16 * NB), rem = rem0 % (16 * NB);
+            const int rr = rem / NB, cb = rem % NB;
+            kt[kk][h][rr][cb ^ (rr & 7)] = pre[j];
         }
-        if constexpr (WPQ > 1) {
-            if (hh > 0) px[hh - 1][qt][lane] = best;
-            __syncthreads();
-            if (hh == 0) {
+        if (threadIdx.x < G * 16) bt[threadIdx.x / 16][threadIdx.x % 16] = bpre;
+        if (c0 + 16 < n) fetch(c0 + 16);
+        __syncthreads();
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int x = 0; x < WPQ - 1; ++x) {
-                    const f32x4 o = px[x][qt][lane];
+        for (int s = 0; s < KS; ++s) {
+            const int blk = (4 * s + grp) ^ (cr & 7);
+            bf16x8 a1;
+            const u32x4 raw1 = kt[0][e][cr][blk];
+            __builtin_memcpy(&a1, &raw1, 16);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], o[i]);
-                }
-                if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+            for (int u = 0; u < 2; ++u) acc[u] = mfma16(a1, qf[u][0][s], acc[u]);
+            if constexpr (KSPLIT) {
+                bf16x8 a2;
+                const u32x4 raw2 = kt[NKT - 1][e][cr][blk];
+                __builtin_memcpy(&a2, &raw2, 16);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) acc[u] = mfma16(a2, qf[u][0][s], acc[u]);
             }
-        } else {
-            if (qvalid) *(f32x4 *)(row + c0 + 4 * grp) = best;
+            if constexpr (QSPLIT) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) acc[u] = mfma16(a1, qf[u][NQT - 1][s], acc[u]);
+            }
+        }
+        f32x4 best[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best[u][i] = fmaf(scale, acc[u][i], bt[e][4 * grp + i]);
+        if constexpr (G > 1) {
+            if (e > 0) {
+                px[e - 1][qp][0][lane] = best[0];
+                px[e - 1][qp][1][lane] = best[1];
+            }
+            __syncthreads();
+            if (e == 0) {
+#pragma unroll
+                for (int x = 0; x < G - 1; ++x)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const f32x4 o = px[x][qp][u][lane];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) best[u][i] = fmaxf(best[u][i], o[i]);
+                    }
+            }
+        }
+        if (e == 0) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (qvalid[u]) *(f32x4 *)(row[u] + c0 + 4 * grp) = best[u];
         }
     }
 }
@@ -737,7 +776,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 template <typename TQ, int D, int G>
 static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
                       hipStream_t st) {
-    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(256 * (G >= 4 ? G / 2 : 1));
+    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(128 * G);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const bf16 *)ws.ksb, (const bf16 *)ws.ksb2, b_sum,
                            ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
