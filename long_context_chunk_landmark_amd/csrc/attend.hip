@@ -296,28 +296,32 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     // ---- DMA of one chunk into its ring stage by one wave: NP pieces of
     // 1 KB, 16 bytes per lane, then (lane 0 only) the stage's flag from
     // the parity table.  A wave's loads complete in issue order, so the
-    // flag lands after the data.  Buffer loads: the resource starts at the
-    // chunk and ends at token N, so rows of a partial last chunk read as
-    // zeros (those keys are masked), and the per-lane address is 32 bits.
+    // flag lands after the data.  Buffer loads: K resources end at token N,
+    // so rows of a partial last chunk read as zeros (those keys are
+    // masked), and the per-lane address is 32 bits.
     const __amdgpu_buffer_rsrc_t par_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)&ring_parity[0], (short)0, 8, BUF_RSRC_WORD3);
     auto issue = [&](int it) {
         const int c = __builtin_amdgcn_readfirstlane(chunk_of(it));
         const int buf = it % NSTAGE;
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + (int64_t)c * S * D), (short)0, (N - c * S) * D * 2, BUF_RSRC_WORD3);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vtbase + (int64_t)c * D * S), (short)0, D * S * 2, BUF_RSRC_WORD3);
-        // the swizzle repeats every 16 rows: the lane part of a piece's
-        // source offset takes PPx distinct values, the rest is scalar
+        // The swizzle repeats every 16 rows, so the lane part of a piece's
+        // source offset takes PPx distinct values.  The rest of a V^T
+        // piece's offset goes in the scalar offset.  That one is not
+        // range-checked, so the K tile instead takes one resource per 16
+        // rows, each ending at token N: rows past N read as zeros.
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (p < PK) {
                 constexpr int RPP = 1024 / (D * 2), PPK = 16 / RPP;  // K rows per piece, pieces per 16 rows
+                const int r16 = (p / PPK) * 16;
+                const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(kbase + ((int64_t)c * S + r16) * D), (short)0, max(0, N - c * S - r16) * D * 2,
+                    BUF_RSRC_WORD3);
                 const int row = (p % PPK) * RPP + lane / NBK, blk = lane % NBK;
                 const int off = (row * D + (blk ^ swz<NBK>(row)) * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, HILS_LPTR(&k_tile(buf)[p * RPP][0]), 16, off,
-                                                         (p / PPK) * 16 * D * 2, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, HILS_LPTR(&k_tile(buf)[p * RPP][0]), 16, off, 0, 0, 0);
             } else {
                 constexpr int RPP = 1024 / (S * 2), PPV = 16 / RPP;  // V^T rows per piece, pieces per 16 rows
                 const int pv = p - PK;
