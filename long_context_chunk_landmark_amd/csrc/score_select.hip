@@ -613,8 +613,9 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 
     // ---- exact refinement of list entries [k0, k1): per-head s^ into
     // L.sc, ranking key into L.key.  RB rows are loaded before any is
-    // reduced so that their latencies overlap.
-    constexpr int RB = 4;
+    // reduced; one row at a time measured fastest (fewer registers, more
+    // rows in flight per SIMD than a batch of loads per wave buys).
+    constexpr int RB = 1;
     auto refine = [&](int k0, int k1) {
         for (int kb = k0; kb < k1; kb += RB) {
             const int cnt = min(RB, k1 - kb);
