@@ -63,7 +63,7 @@
 
 namespace hils {
 
-// Source of the ring flags: the parity of a stage's round (read by DMA).
+// Source of the ring flags: the parity of a stage's lap (read by DMA).
 __device__ int32_t ring_parity[2] = {0, 1};
 
 // Key held by slot p of a chunk's transposed V rows.  In the S^T
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     __shared__ u32x4 ring[NSTAGE][S * NBK + D * NBV];
     // ring protocol: rel[s] counts the waves done with the chunks stage s
     // has held; flag[s] is written by DMA behind the data of each chunk
-    // loaded into stage s (the parity of its round through the ring)
+    // loaded into stage s (the parity of its lap through the ring)
     __shared__ int rel[NSTAGE];
     __shared__ int flag[NSTAGE];
     auto k_tile = [&](int buf) { return reinterpret_cast<u32x4(*)[NBK]>(&ring[buf][0]); };
@@ -428,10 +428,10 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             any |= act[t];
         }
         // Every wave waits for every chunk to land, also one it skips: so no
-        // wave leaves a stage before its current round is in (a wave can
+        // wave leaves a stage before its current lap is in (a wave can
         // lead the slowest by at most NSTAGE - 1 chunks, rel[s] never mixes
-        // rounds) and, having seen the previous round's flag, a wave only
-        // finds this round's or the previous round's parity in flag[buf].
+        // laps) and, having seen the previous lap's flag, a wave only
+        // finds this lap's or the previous lap's parity in flag[buf].
         // (LDS operations of a wave execute in order, so a plain flag read
         // orders the flag before the data reads, and those before the
         // release below; the asm statements are compiler barriers.)
