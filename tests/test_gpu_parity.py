@@ -42,9 +42,12 @@ CASES = {
     "qcal_valu_r12": dict(seed=37, io=BF, B=1, H_q=4, H_kv=2, d=64, N=1100, S=64, W=64, K=4, d_model=200, r=12),
     "qcal_fp32": dict(seed=38, io=F32, B=1, H_q=2, H_kv=1, d=64, N=700, S=64, W=64, K=3, d_model=96, r=8),
     "few_candidates": dict(seed=29, io=BF, B=1, H_q=4, H_kv=2, d=128, N=1024, S=64, W=512, K=16),
-    # block shapes picked by LDS capacity: 4-wave blocks at S=128 with K=64 / G=2
+    # block shapes picked by LDS capacity: 8-wave blocks at S=128 with K=64 / G=2, and
+    # 2-wave blocks (fewer waves than ring stages at S=64) with G=1, K=128
     "s128_k64": dict(seed=33, io=BF, B=1, H_q=8, H_kv=2, d=128, N=9000, S=128, W=256, K=64),
     "s128_g2": dict(seed=34, io=BF, B=1, H_q=4, H_kv=2, d=128, N=6000, S=128, W=128, K=32),
+    "g1_k128_s64": dict(seed=39, io=BF, B=1, H_q=2, H_kv=2, d=128, N=9000, S=64, W=128, K=128),
+    "g1_k128_s128": dict(seed=40, io=BF, B=1, H_q=1, H_kv=1, d=128, N=20000, S=128, W=256, K=128),
 }
 
 
