@@ -6,18 +6,20 @@
 // per group; Q-Cal replaces the scoring query by q_i + W_up W_down h_i.
 //
 // Design (MI355X): the scoring contraction is dense (every query of a chunk
-// scores the same candidate set), so it runs on bf16 MFMA.  bf16 operands
-// round k' (and an fp32 Q-Cal query), so the MFMA scores are approximate;
-// each row carries a rigorous bound E on |approx - exact| derived from
-// |x - bf16(x)| <= 2^-8 |x| and Cauchy-Schwarz (E = scale * kappa * ||q|| *
-// max_c ||k'_c||).  The select kernel then finds the exact K-th largest
-// approximate group score tau, keeps every candidate whose approximate
-// score is >= tau - 2E (a superset of the exact top-K), recomputes those in
-// fp32 on the vector ALUs, and takes the exact top-K by (score desc, index
-// asc).  Bit-exact selection, MFMA-rate scoring.
+// scores the same candidate set), so it runs on bf16 MFMA.  fp32 operands
+// (k', a Q-Cal or fp32 query) enter as two-term bf16 splits, so the MFMA
+// scores are approximate within a rigorous bound E on |approx - exact|
+// (two-term residuals <= 2^-18 |x|, fp32 accumulation, Cauchy-Schwarz:
+// E = scale * kappa * ||q|| * max_c ||k'_c||).  The select kernel then
+// takes a lower bound tau' of the K-th largest approximate group score,
+// keeps every candidate whose approximate score is >= tau' - 2E (a superset
+// of the exact top-K, about K + 1 candidates), recomputes those in fp32 on
+// the vector ALUs, and takes the exact top-K by (score desc, index asc).
+// Bit-exact selection, MFMA-rate scoring.
 //
 // Kernels:
-//   ksum_prep        bf16 copy of k' + per-(b, landmark head) max ||k'||
+//   ksum_prep        bf16 split k1 + k2 of k', its fp32 chunk-major copy,
+//                    and per-(b, landmark head) max ||k'||
 //   qcal_mfma        fp32 scoring queries q + W_up (W_down h), bf16 MFMA
 //   qcal             the same for other shapes and fp32 inputs (VALU)
 //   score_approx     bf16 MFMA scores -> ragged approximate group scores
