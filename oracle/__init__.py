@@ -263,6 +263,70 @@ def decode(cfg: dict, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table, 
     return res
 
 
+def summarize_pages(cfg: dict, k_cache, q_lm, pages):
+    """Summaries of the chunks held by pages of a paged key cache.
+
+    Item i summarises page pages[i] of k_cache [P, H_kv, S, d] (one completed
+    chunk) with the landmark queries q_lm[i] [H_lm, d]: the summary of
+    ``summarize`` for a one-chunk sequence made of that page.  Items whose id
+    lies outside [0, P) are skipped; their rows are NaN.
+    Returns (k_sum [n, H_lm, d], b_sum [n, H_lm]) float64.
+    """
+    c = _cfg(cfg)
+    kc, ql = _f32(k_cache), _f32(q_lm)
+    pg = np.asarray(pages, dtype=np.int64).reshape(-1)
+    P = kc.shape[0]
+    n = len(pg)
+    assert kc.shape == (P, c.H_kv, c.S, c.d), kc.shape
+    assert ql.shape == (n, c.H_lm, c.d), ql.shape
+    k_sum = np.full((n, c.H_lm, c.d), np.nan)
+    b_sum = np.full((n, c.H_lm), np.nan)
+    ok = np.nonzero((pg >= 0) & (pg < P))[0]
+    if len(ok):
+        one = dict(cfg, B=len(ok), N=c.S)
+        ks, bs = summarize(one, kc[pg[ok]], ql[ok][:, :, None, :])
+        k_sum[ok], b_sum[ok] = ks[:, :, 0, :], bs[:, :, 0]
+    return k_sum, b_sum
+
+
+def prefill_paged(cfg: dict, q_start: int, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table, qcal=None,
+                  given_sel=None, attend: bool = True, want_agg: bool = False):
+    """Chunked prefill over a paged cache: the new tokens at positions
+    q_start .. q_start + n - 1 of each sequence.
+
+    Row t of sequence b is, by definition, the decode step of that sequence
+    at position q_start + t: the same keys (those up to and including its
+    own), the same summaries read from the cache, its own query (and Q-Cal
+    hidden state).  q [B, H_q, n, d]; block_table [B, max_pages]; qcal =
+    (h [B, n, d_model], w_down, w_up) or None; given_sel [B, H_kv, n, K].
+    Returns sel_idx [B,H_kv,n,K], sel_score [B,H_q,n,K], kth [B,H_kv,n,2],
+    out [B,H_q,n,d], lse [B,H_q,n] (and agg [B,H_kv,n,max_pages]).
+    """
+    q32 = _f32(q)
+    B, H_q, n, d = q32.shape
+    bt = _i32(block_table)
+    # one decode query per (sequence, new token), b-major
+    qd = np.ascontiguousarray(q32.transpose(0, 2, 1, 3).reshape(B * n, H_q, d))
+    btd = np.ascontiguousarray(np.repeat(bt, n, axis=0))
+    seq_lens = (q_start + 1 + np.tile(np.arange(n), B)).astype(np.int32)
+    qc = None
+    if qcal is not None:
+        h, wd, wu = (_f32(x) for x in qcal)
+        qc = (np.ascontiguousarray(h.reshape(B * n, h.shape[-1])), wd, wu)
+    gs = None
+    if given_sel is not None:
+        g = _i32(given_sel)
+        gs = np.ascontiguousarray(g.transpose(0, 2, 1, 3).reshape(B * n, g.shape[1], g.shape[3]))
+    r = decode(cfg, qd, k_cache, v_cache, ksum_cache, bsum_cache, btd, seq_lens, qcal=qc, given_sel=gs,
+               attend=attend, want_agg=want_agg)
+
+    def back(x):  # [B*n, H, ...] -> [B, H, n, ...]
+        x = x.reshape((B, n) + x.shape[1:])
+        return np.ascontiguousarray(np.moveaxis(x, 1, 2))
+
+    return {key: back(val) for key, val in r.items()}
+
+
 def dense_causal_rows(cfg: dict, q, k, v, rows=None):
     """Textbook causal softmax attention (keys 0..i) for the given rows."""
     c = _cfg(cfg)

@@ -582,3 +582,87 @@ def test_decode_equals_prefill_row():
         np.testing.assert_allclose(dec["out"][0], pre["out"][0, :, 0], atol=1e-13)
         np.testing.assert_allclose(dec["lse"][0], pre["lse"][0, :, 0], atol=1e-13)
         np.testing.assert_allclose(dec["sel_score"][0], pre["sel_score"][0, :, 0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- paged serving pins
+
+
+def _paged_layout(rng, k, v, ks32, bs32, S, extra=5):
+    """Scatter contiguous [B, H, N, d] keys/values (and [B, H_lm, C, ...]
+    summaries) into a paged cache at a random page placement."""
+    B, H_kv, N, d = k.shape
+    H_lm = ks32.shape[1]
+    n_pages = (N + S - 1) // S
+    P = B * n_pages + extra
+    bt = rng.permutation(P)[:B * n_pages].reshape(B, n_pages).astype(np.int32)
+    kc = np.zeros((P, H_kv, S, d), np.float32)
+    vc = np.zeros((P, H_kv, S, d), np.float32)
+    ksc = np.zeros((P, H_lm, d), np.float32)
+    bsc = np.zeros((P, H_lm), np.float32)
+    for b in range(B):
+        for c in range(n_pages):
+            n = min(S, N - c * S)
+            kc[bt[b, c], :, :n] = k[b, :, c * S:c * S + n]
+            vc[bt[b, c], :, :n] = v[b, :, c * S:c * S + n]
+            if c < N // S:
+                ksc[bt[b, c]] = ks32[b, :, c]
+                bsc[bt[b, c]] = bs32[b, :, c]
+    return kc, vc, ksc, bsc, bt
+
+
+def test_summarize_pages_equals_contiguous_summaries():
+    """Summaries computed page by page, at any page placement, are those of
+    the contiguous sequence (placement independence); ids outside [0, P)
+    are skipped."""
+    rng = _rng(131)
+    S, d, H_kv, H_lm, B = 8, 16, 2, 4, 2
+    N = 6 * S
+    k = rng.standard_normal((B, H_kv, N, d)).astype(np.float32)
+    ql = rng.standard_normal((B, H_lm, N // S, d)).astype(np.float32)
+    cfg = _cfg(B=B, N=N, S=S, d=d, H_q=H_lm, H_kv=H_kv, H_lm=H_lm)
+    ks, bs = oracle.summarize(cfg, k, ql)
+    kc, _, _, _, bt = _paged_layout(rng, k, k, ks.astype(np.float32), bs.astype(np.float32), S)
+    P = kc.shape[0]
+    items = [(b, c) for b in range(B) for c in range(N // S)]
+    order = rng.permutation(len(items))
+    pages = np.array([bt[items[i]] for i in order] + [-1, P], np.int32)
+    q_items = np.stack([ql[items[i][0], :, items[i][1]] for i in order] + [ql[0, :, 0]] * 2)
+    got_k, got_b = oracle.summarize_pages(cfg, kc, q_items, pages)
+    for j, i in enumerate(order):
+        b, c = items[i]
+        np.testing.assert_allclose(got_k[j], ks[b, :, c], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(got_b[j], bs[b, :, c], rtol=0, atol=1e-14)
+    assert np.isnan(got_k[-2:]).all() and np.isnan(got_b[-2:]).all()
+
+
+@pytest.mark.parametrize("q_start,n,qcal", [(0, 70, False), (48, 100, False), (96, 61, True)])
+def test_prefill_paged_equals_prefill_rows(q_start, n, qcal):
+    """Chunked prefill of rows q_start .. q_start + n - 1 over a paged cache
+    (random page placement) equals those rows of the whole-sequence prefill:
+    selection, selected scores, output and log-partition."""
+    rng = _rng(141 + q_start)
+    S, d, G, H_kv, B = 8, 16, 2, 2, 2
+    H_q = G * H_kv
+    N = q_start + n
+    cfg = _cfg(B=B, N=N, S=S, d=d, W=2 * S, K=3, H_q=H_q, H_kv=H_kv)
+    q = rng.standard_normal((B, H_q, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, H_kv, N, d)).astype(np.float32)
+    v = rng.standard_normal((B, H_kv, N, d)).astype(np.float32)
+    ql = rng.standard_normal((B, H_q, N // S, d)).astype(np.float32)
+    ks, bs = oracle.summarize(cfg, k, ql)
+    ks32, bs32 = ks.astype(np.float32), bs.astype(np.float32)
+    kc, vc, ksc, bsc, bt = _paged_layout(rng, k, v, ks32, bs32, S)
+    qc_full = qc_new = None
+    if qcal:
+        h, wd, wu = _qcal_inputs(7, N, H_q, d)
+        h = np.concatenate([h, rng.standard_normal(h.shape).astype(np.float32)])  # B = 2
+        qc_full = (h, wd, wu)
+        qc_new = (h[:, q_start:], wd, wu)
+    rows = np.arange(q_start, N)
+    pre = oracle.forward_rows(cfg, q, k, v, ks32.astype(np.float64), bs32.astype(np.float64), rows=rows,
+                              qcal=qc_full)
+    got = oracle.prefill_paged(cfg, q_start, q[:, :, q_start:], kc, vc, ksc, bsc, bt, qcal=qc_new)
+    np.testing.assert_array_equal(got["sel_idx"], pre["sel_idx"])
+    assert (got["sel_idx"] >= 0).any()  # some rows have candidates
+    for key in ("sel_score", "out", "lse", "kth"):
+        np.testing.assert_allclose(got[key], pre[key], rtol=0, atol=1e-12, err_msg=key)
