@@ -172,6 +172,65 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
                           const void *w_down, const void *w_up, int32_t d_model, int32_t r, void *out, float *lse,
                           int32_t *sel_idx, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Landmark summaries of chunks that complete while a sequence is served:
+ * item i summarises the S keys held by page pages[i] of the paged key cache
+ * with the landmark queries q_lm[i] (the summary definition of
+ * hils_landmark_summarize: hyper.ai summary, 方法, the compressed key and
+ * its entropy bias; the landmark query of a chunk exists once its S tokens
+ * have arrived) and writes row pages[i] of the summary caches.
+ *   k_cache     [num_pages, H_kv, S, d]   io_dtype; the page must be full
+ *   q_lm        [num_items, H_lm, d]      io_dtype
+ *   pages       [num_items] int32 (device); an id outside [0, num_pages)
+ *               skips the item (nothing written), so a batch may carry -1
+ *               for sequences with no completed chunk this step
+ *   ksum_cache  [num_pages, H_lm, d]      summary_dtype (rows written)
+ *   bsum_cache  [num_pages, H_lm]         fp32 (rows written)
+ * Two items naming the same page race; the caller keeps ids distinct.
+ * cfg->B and cfg->N are ignored. */
+hils_status_t hils_summarize_pages(const hils_config_t *cfg, int32_t num_items, const void *k_cache,
+                                   int32_t num_pages, const void *q_lm, const int32_t *pages, void *ksum_cache,
+                                   float *bsum_cache, hipStream_t stream);
+
+/* Chunked prefill over the paged cache: for each of cfg->B sequences, the
+ * cfg->N new tokens at positions q_start .. q_start + N - 1 take the steps
+ * of hils_score_select and hils_sparse_attend_fused (hyper.ai summary,
+ * 方法: surrogate score, top-K, partition estimate and hierarchical
+ * factorisation), with keys, values and summaries read through the block
+ * table.  Row t of the result equals row q_start + t of a whole-sequence
+ * prefill (and the decode step at that position).
+ *   q_start     multiple of S, >= 0 (host value, shared by the B sequences)
+ *   q           [B, H_q, N, d]            io_dtype, the new tokens
+ *   k_cache,
+ *   v_cache     [num_pages, H_kv, S, d]   io_dtype: keys 0 .. q_start+N-1
+ *               already written (the new tokens' too)
+ *   ksum_cache  [num_pages, H_lm, d]      summary_dtype; bsum_cache
+ *               [num_pages, H_lm] fp32: rows of every chunk
+ *               c < floor((q_start + N - 1) / S) - W/S already written
+ *               (hils_summarize_pages / hils_landmark_summarize)
+ *   block_table [B, max_pages] int32: logical chunk -> page; entries of
+ *               chunks 0 .. ceil((q_start + N)/S) - 1 must lie in
+ *               [0, num_pages) (not checked on the device)
+ *   h, w_down, w_up, d_model, r: Q-Cal as in hils_score_select, h rows
+ *               [B, N, d_model] of the new tokens (or NULL)
+ *   sel_idx     [B, H_kv, N, K] int32, sel_score [B, H_q, N, K] fp32
+ *               (written; may be NULL when K = 0)
+ *   out         [B, H_q, N, d] io_dtype (written); lse [B, H_q, N] fp32
+ *               (written, may be NULL)
+ *   workspace   hils_prefill_paged_workspace_size(cfg, q_start, max_pages,
+ *               h != NULL) bytes.
+ * num_pages <= 262144; q_start + N <= 8192 * S. */
+hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, const void *q, const void *k_cache,
+                                 const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                                 int32_t num_pages, const int32_t *block_table, int32_t max_pages, const void *h,
+                                 const void *w_down, const void *w_up, int32_t d_model, int32_t r, int32_t *sel_idx,
+                                 float *sel_score, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Workspace bytes of hils_prefill_paged (0 with hils_last_error() set when
+ * the configuration is rejected). */
+size_t hils_prefill_paged_workspace_size(const hils_config_t *cfg, int32_t q_start, int32_t max_pages,
+                                         int32_t with_qcal);
+
 /* Bytes of workspace the given call needs (0 if none); 0 with
  * hils_last_error() set when the configuration is rejected.  num_seqs and
  * max_pages are used by HILS_WS_DECODE only. */

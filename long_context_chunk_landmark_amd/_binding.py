@@ -28,6 +28,9 @@ EXPORTED_SYMBOLS = (
     "hils_score_select",
     "hils_sparse_attend_fused",
     "hils_decode",
+    "hils_summarize_pages",
+    "hils_prefill_paged",
+    "hils_prefill_paged_workspace_size",
     "hils_workspace_size",
     "hils_last_error",
     "hils_version",
@@ -109,11 +112,17 @@ def load_library(path: str = LIB_PATH):
     lib.hils_sparse_attend_fused.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_decode.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz,
                                 vp]
+    lib.hils_summarize_pages.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, vp]
+    lib.hils_prefill_paged.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp,
+                                       vp, vp, sz, vp]
+    lib.hils_prefill_paged_workspace_size.argtypes = [cfgp, i32, i32, i32]
+    lib.hils_prefill_paged_workspace_size.restype = sz
     lib.hils_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32]
     lib.hils_workspace_size.restype = sz
     lib.hils_last_error.restype = ctypes.c_char_p
     lib.hils_version.restype = ctypes.c_int
-    for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode"):
+    for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode",
+               "hils_summarize_pages", "hils_prefill_paged"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -278,6 +287,74 @@ def decode(cfg: Config, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table
                                       _ptr(seq_lens), _ptr(h), _ptr(wd), _ptr(wu), d_model, r, _ptr(out), _ptr(lse),
                                       _ptr(sel_idx), _ptr(ws), nbytes, _stream()))
     return out, lse, sel_idx
+
+
+def summarize_pages(cfg: Config, k_cache, q_lm, pages, ksum_cache, bsum_cache):
+    """Summaries of the pages ``pages`` (one completed chunk each) written into the summary caches in place."""
+    dev = k_cache.device
+    P = k_cache.shape[0]
+    n = pages.shape[0]
+    _want(k_cache, "k_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(q_lm, "q_lm", (n, cfg.H_lm, cfg.d), cfg.io_dtype, dev)
+    _want(pages, "pages", (n,), torch.int32, dev)
+    _want(ksum_cache, "ksum_cache", (P, cfg.H_lm, cfg.d), cfg.summary_dtype, dev)
+    _want(bsum_cache, "bsum_cache", (P, cfg.H_lm), torch.float32, dev)
+    c = cfg.to_c()
+    _check(load_library().hils_summarize_pages(ctypes.byref(c), n, _ptr(k_cache), P, _ptr(q_lm), _ptr(pages),
+                                               _ptr(ksum_cache), _ptr(bsum_cache), _stream()))
+    return ksum_cache, bsum_cache
+
+
+def prefill_paged_workspace_size(cfg: Config, q_start: int, max_pages: int, qcal: bool = False) -> int:
+    n = load_library().hils_prefill_paged_workspace_size(ctypes.byref(cfg.to_c()), q_start, max_pages, int(qcal))
+    if n == 0 and last_error():
+        raise HilsError(HILS_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def prefill_paged(cfg: Config, q_start: int, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table, qcal=None,
+                  out=None, lse=None, sel_idx=None, sel_score=None, workspace=None):
+    """Chunked prefill of cfg.N new tokens per sequence at positions q_start.. over the paged cache.
+
+    Returns (out, lse, sel_idx, sel_score)."""
+    dev = q.device
+    P = k_cache.shape[0]
+    max_pages = block_table.shape[1]
+    _want(q, "q", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(k_cache, "k_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(v_cache, "v_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(ksum_cache, "ksum_cache", (ksum_cache.shape[0], cfg.H_lm, cfg.d), cfg.summary_dtype, dev)
+    _want(bsum_cache, "bsum_cache", (ksum_cache.shape[0], cfg.H_lm), torch.float32, dev)
+    _want(block_table, "block_table", (cfg.B, max_pages), torch.int32, dev)
+    h = wd = wu = None
+    d_model = r = 0
+    if qcal is not None:
+        h, wd, wu = qcal
+        r, d_model = wd.shape
+        _want(h, "h", (cfg.B, cfg.N, d_model), cfg.io_dtype, dev)
+        _want(wd, "w_down", (r, d_model), cfg.io_dtype, dev)
+        _want(wu, "w_up", (cfg.H_q * cfg.d, r), cfg.io_dtype, dev)
+    if out is None:
+        out = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.d), dtype=cfg.io_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((cfg.B, cfg.H_q, cfg.N), dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.K), dtype=torch.int32, device=dev)
+    if sel_score is None:
+        sel_score = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.K), dtype=torch.float32, device=dev)
+    _want(out, "out", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(lse, "lse", (cfg.B, cfg.H_q, cfg.N), torch.float32, dev)
+    _want(sel_idx, "sel_idx", (cfg.B, cfg.H_kv, cfg.N, cfg.K), torch.int32, dev)
+    _want(sel_score, "sel_score", (cfg.B, cfg.H_q, cfg.N, cfg.K), torch.float32, dev)
+    nbytes = prefill_paged_workspace_size(cfg, q_start, max_pages, qcal is not None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    c = cfg.to_c()
+    _check(load_library().hils_prefill_paged(ctypes.byref(c), q_start, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(ksum_cache), _ptr(bsum_cache), P, _ptr(block_table), max_pages,
+                                             _ptr(h), _ptr(wd), _ptr(wu), d_model, r, _ptr(sel_idx), _ptr(sel_score),
+                                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, sel_idx, sel_score
 
 
 def prefill(cfg: Config, q, k, v, q_lm, qcal=None):

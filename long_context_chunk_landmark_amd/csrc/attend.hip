@@ -75,18 +75,22 @@ __host__ __device__ __forceinline__ int vt_slot_key(int p) {
     return 32 * s + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
 }
 
-// vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]), 0 past N.
+// vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]), 0 past
+// key Nk.  With a block table, chunk c of sequence b is page
+// bt[b * max_pages + c] of a paged cache [P, H_kv, S, D].
 template <int D, int S>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int N,
-                                                          int CA, int H_kv) {
+__global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int Nk,
+                                                          int CA, int H_kv, const int32_t *__restrict__ bt,
+                                                          int max_pages) {
     __shared__ bf16 tile[S][D + 8];
     const int c = blockIdx.x;
     const int64_t bg = (int64_t)blockIdx.z * H_kv + blockIdx.y;
-    const bf16 *src = v + (bg * N + (int64_t)c * S) * D;
+    const bf16 *src = bt ? v + ((int64_t)bt[(int64_t)blockIdx.z * max_pages + c] * H_kv + blockIdx.y) * S * D
+                         : v + (bg * Nk + (int64_t)c * S) * D;
     for (int idx = threadIdx.x; idx < S * (D / 8); idx += blockDim.x) {
         const int j = idx / (D / 8), cb = idx % (D / 8);
         u32x4 val = {0u, 0u, 0u, 0u};
-        if ((int64_t)c * S + j < N) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
+        if ((int64_t)c * S + j < Nk) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
         bf16x8 x;
         __builtin_memcpy(&x, &val, 16);
 #pragma unroll
@@ -143,7 +147,9 @@ struct AttendCfg {
 
 // Dynamic LDS: int16 sel[QB*K] (chunk ids, -1 padded); fp16 wt[QB*G*K]
 // (fusion weights exp(s^ - m^) of each row's selections); uint bitmap[NW];
-// int ulist[UCAP]; int scan[16].  Selections live in LDS so that reading a
+// int ulist[UCAP + W/S + 1] (the walk: union chunks, then window chunks;
+// chunk id in the low 14 bits, its page of a paged cache above); int
+// scan[16].  Selections live in LDS so that reading a
 // row's next selection never waits on the vector-memory counter that
 // tracks the chunk DMA.
 template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, bf16 *__restrict__ out,
     float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP,
-    int nqb, int64_t n_items, int64_t per_xcd) {
+    int nqb, int64_t n_items, int64_t per_xcd, int q0, int Nk, const int32_t *__restrict__ bt, int max_pages) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
     constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, NP = Cf::NP;
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     f16 *wt_l = (f16 *)(sel_l + QB * K);
     uint32_t *bitmap = (uint32_t *)(wt_l + QB * G * K);
     int *ulist = (int *)(bitmap + NW);
-    int *scan = ulist + UCAP;
+    int *scan = ulist + UCAP + W / S + 1;
 
     // ---- XCD-aware work item: consecutive blocks on one XCD take
     // consecutive (b, g, query block) items
@@ -180,8 +186,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const int64_t bg = item / nqb;
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
-    const int i0 = qb * QB;
-    const int qc = i0 / S;
+    const int i0 = qb * QB;        // local row; rows are positions q0 + i (q0 % S == 0)
+    const int qc = (q0 + i0) / S;  // query chunk
     const int n = max(0, qc - W / S);
     const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4;
     const int r = lane & 15;
@@ -252,6 +258,10 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     }
     __syncthreads();
 
+    // a walk entry: chunk id, and above it the chunk's page (paged cache)
+    const int32_t *btb = bt ? bt + b * (int64_t)max_pages : nullptr;
+    auto entry = [&](int c) { return btb ? (int)(((uint32_t)btb[c] << 14) | (uint32_t)c) : c; };
+
     // ---- ascending union: exclusive prefix sum of per-word popcounts
     int U = 0;
     {
@@ -278,7 +288,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             while (wv) {
                 const int bit = __ffs(wv) - 1;
                 wv &= wv - 1;
-                if (pos < UCAP) ulist[pos] = wi * 32 + bit;
+                if (pos < UCAP) ulist[pos] = entry(wi * 32 + bit);
                 ++pos;
             }
             base += tot;
@@ -288,21 +298,25 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     }
     const int wc0 = max(0, qc - W / S);
     const int T = U + (qc - wc0 + 1);
+    for (int t = tid; t < T - U; t += NT) ulist[U + t] = entry(wc0 + t);
+    __syncthreads();
 
-    const bf16 *kbase = k + bg * (int64_t)N * D;
+    const bf16 *kbase = k + bg * (int64_t)Nk * D;
     const f16 *vtbase = vt + bg * (int64_t)CA * D * S;
-    auto chunk_of = [&](int it) { return it < U ? ulist[it] : wc0 + (it - U); };
+    auto chunk_of = [&](int it) { return ulist[it] & 0x3fff; };
 
     // ---- DMA of one chunk into its ring stage by one wave: NP pieces of
     // 1 KB, 16 bytes per lane, then (lane 0 only) the stage's flag from
     // the parity table.  A wave's loads complete in issue order, so the
-    // flag lands after the data.  Buffer loads: K resources end at token N,
+    // flag lands after the data.  Buffer loads: K resources end at key Nk,
     // so rows of a partial last chunk read as zeros (those keys are
     // masked), and the per-lane address is 32 bits.
     const __amdgpu_buffer_rsrc_t par_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)&ring_parity[0], (short)0, 8, BUF_RSRC_WORD3);
     auto issue = [&](int it) {
-        const int c = __builtin_amdgcn_readfirstlane(chunk_of(it));
+        const int ent = __builtin_amdgcn_readfirstlane(ulist[it]);
+        const int c = ent & 0x3fff;
+        const bf16 *kc = btb ? k + ((int64_t)((uint32_t)ent >> 14) * H_kv + g) * S * D : kbase + (int64_t)c * S * D;
         const int buf = it % NSTAGE;
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vtbase + (int64_t)c * D * S), (short)0, D * S * 2, BUF_RSRC_WORD3);
@@ -310,15 +324,14 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         // source offset takes PPx distinct values.  The rest of a V^T
         // piece's offset goes in the scalar offset.  That one is not
         // range-checked, so the K tile instead takes one resource per 16
-        // rows, each ending at token N: rows past N read as zeros.
+        // rows, each ending at key Nk: rows past Nk read as zeros.
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (p < PK) {
                 constexpr int RPP = 1024 / (D * 2), PPK = 16 / RPP;  // K rows per piece, pieces per 16 rows
                 const int r16 = (p / PPK) * 16;
                 const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(kbase + ((int64_t)c * S + r16) * D), (short)0, max(0, N - c * S - r16) * D * 2,
-                    BUF_RSRC_WORD3);
+                    (void *)(kc + (int64_t)r16 * D), (short)0, max(0, Nk - c * S - r16) * D * 2, BUF_RSRC_WORD3);
                 const int row = (p % PPK) * RPP + lane / NBK, blk = lane % NBK;
                 const int off = (row * D + (blk ^ swz<NBK>(row)) * 8) * 2;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, HILS_LPTR(&k_tile(buf)[p * RPP][0]), 16, off, 0, 0, 0);
@@ -514,7 +527,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int j = c * S + 16 * kt + 4 * grp + i;
-                            const float x = (diag && j > iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
+                            const float x = (diag && j > q0 + iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
                             acc[t][kt][i] = x;
                             cmax = fmaxf(cmax, x);
                         }
@@ -584,7 +597,8 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
                                                                 const float *__restrict__ sel_score,
                                                                 float *__restrict__ out, float *__restrict__ lse,
                                                                 int B, int N, int H_q, int H_kv, int S, int W, int K,
-                                                                float scale) {
+                                                                float scale, int q0, int Nk,
+                                                                const int32_t *__restrict__ bt, int max_pages) {
     constexpr int DPL = D / WAVE;  // dims per lane (1 or 2)
     __shared__ float q_l[4][D];
     __shared__ float p_l[4][128];
@@ -596,8 +610,12 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
     const int h = (int)(bh % H_q);
     const int64_t b = bh / H_q;
     const int G = H_q / H_kv, g = h / G;
-    const float *kb = k + (b * H_kv + g) * (int64_t)N * D;
-    const float *vb = v + (b * H_kv + g) * (int64_t)N * D;
+    const int pi = q0 + i;  // position of row i
+    // key / value row j: contiguous [B, H_kv, Nk, D] or paged [P, H_kv, S, D]
+    auto kv_row = [&](const float *base, int j) -> const float * {
+        if (!bt) return base + ((b * H_kv + g) * (int64_t)Nk + j) * D;
+        return base + (((int64_t)bt[b * max_pages + j / S] * H_kv + g) * S + j % S) * D;
+    };
     for (int x = lane; x < D; x += WAVE) q_l[wave][x] = q[row * D + x];
     wave_sync();
 
@@ -611,7 +629,7 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
             const int j = j0 + u * WAVE + lane;
             lg[u] = -INFINITY;
             if (j <= j1) {
-                const float *kr = kb + (int64_t)j * D;
+                const float *kr = kv_row(k, j);
                 float dot = 0.f;
                 for (int x = 0; x < D; ++x) dot = fmaf(q_l[wave][x], kr[x], dot);
                 lg[u] = dot * scale;
@@ -636,17 +654,17 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
         for (int y = 0; y < DPL; ++y) {
             float acc = o[y] * alpha;
             const int x = lane + y * WAVE;
-            for (int j = j0; j <= j1; ++j) acc = fmaf(p_l[wave][j - j0], vb[(int64_t)j * D + x], acc);
+            for (int j = j0; j <= j1; ++j) acc = fmaf(p_l[wave][j - j0], kv_row(v, j)[x], acc);
             o[y] = acc;
         }
         wave_sync();
     };
 
-    const int w0 = max(0, (i / S) * S - W);
+    const int w0 = max(0, (pi / S) * S - W);
     float mw = -INFINITY, lw = 0.f, ow[DPL];
 #pragma unroll
     for (int y = 0; y < DPL; ++y) ow[y] = 0.f;
-    for (int j = w0; j <= i; j += 2 * WAVE) attend_block(j, min(i, j + 2 * WAVE - 1), mw, lw, ow);
+    for (int j = w0; j <= pi; j += 2 * WAVE) attend_block(j, min(pi, j + 2 * WAVE - 1), mw, lw, ow);
     const float lse_sw = mw + logf(lw);
 
     const int32_t *sl = sel_idx + ((b * H_kv + g) * N + i) * K;
@@ -708,7 +726,8 @@ static size_t attend_dyn_lds(const Shape &s) {
     constexpr int QB = AttendPlan<D, S, G, NWAVE, TPW>::QB;
     const int NW = (s.C + 31) / 32 + 1;
     const int UCAP = std::min(s.C + 1, QB * s.K + 1);
-    return align_up((size_t)QB * s.K * 2 + (size_t)QB * G * s.K * 2, 16) + (size_t)NW * 4 + (size_t)UCAP * 4 + 16 * 4;
+    return align_up((size_t)QB * s.K * 2 + (size_t)QB * G * s.K * 2, 16) + (size_t)NW * 4 +
+           (size_t)(UCAP + s.W / s.S + 1) * 4 + 16 * 4;
 }
 
 template <int D, int S, int G, int NWAVE, int TPW>
@@ -728,7 +747,7 @@ static hipError_t go_attend(const Shape &s, const void *q, const void *k, const 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
                        sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP,
-                       nqb, n_items, per_xcd);
+                       nqb, n_items, per_xcd, s.q0, s.Nk, s.bt, s.max_pages);
     return hipGetLastError();
 }
 
@@ -812,21 +831,24 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
         if (s.D == 64)
             hipLaunchKernelGGL(sparse_attend_f32_kernel<64>, grid, block, 0, st, (const float *)q, (const float *)k,
                                (const float *)v, sel_idx, sel_score, (float *)out, lse, s.B, s.N, s.H_q, s.H_kv, s.S,
-                               s.W, s.K, s.scale);
+                               s.W, s.K, s.scale, s.q0, s.Nk, s.bt, s.max_pages);
         else
             hipLaunchKernelGGL(sparse_attend_f32_kernel<128>, grid, block, 0, st, (const float *)q, (const float *)k,
                                (const float *)v, sel_idx, sel_score, (float *)out, lse, s.B, s.N, s.H_q, s.H_kv, s.S,
-                               s.W, s.K, s.scale);
+                               s.W, s.K, s.scale, s.q0, s.Nk, s.bt, s.max_pages);
         return hipGetLastError();
     }
     // V^T pre-pass (fp16, slot order) into the workspace
     f16 *vt = (f16 *)workspace;
     {
         const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
-        if (s.D == 64 && s.S == 64) hipLaunchKernelGGL((v_transpose_kernel<64, 64>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
-        else if (s.D == 64) hipLaunchKernelGGL((v_transpose_kernel<64, 128>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
-        else if (s.S == 64) hipLaunchKernelGGL((v_transpose_kernel<128, 64>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
-        else hipLaunchKernelGGL((v_transpose_kernel<128, 128>), grid, block, 0, st, (const bf16 *)v, vt, s.N, s.CA, s.H_kv);
+        auto vtr = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16 *)v, vt, s.Nk, s.CA, s.H_kv, s.bt, s.max_pages);
+        };
+        if (s.D == 64 && s.S == 64) vtr(v_transpose_kernel<64, 64>);
+        else if (s.D == 64) vtr(v_transpose_kernel<64, 128>);
+        else if (s.S == 64) vtr(v_transpose_kernel<128, 64>);
+        else vtr(v_transpose_kernel<128, 128>);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

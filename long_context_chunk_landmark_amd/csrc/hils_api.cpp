@@ -71,7 +71,46 @@ hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
     s.io_bf16 = cfg->io_dtype == HILS_BF16;
     s.sum_bf16 = cfg->summary_dtype == HILS_BF16;
     s.scale = cfg->scale > 0.f ? cfg->scale : 1.0f / sqrtf((float)s.D);
+    s.q0 = 0;
+    s.Nk = s.N;
+    s.bt = nullptr;
+    s.max_pages = 0;
     return ok();
+}
+
+// Largest page count of a paged cache the walk entries of the fused kernel
+// can address (18 bits above a 14-bit chunk id).
+constexpr int32_t PAGED_MAX_PAGES = 1 << 18;
+
+// Paged prefill: B sequences, N new rows each at positions q_start ..
+// q_start + N - 1, keys 0 .. q_start + N - 1 in the paged cache.
+hils_status_t resolve_paged(const hils_config_t *cfg, int32_t q_start, int32_t num_pages, int32_t max_pages,
+                            hils::Shape &s) {
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if (q_start < 0 || q_start % s.S)
+        return fail(HILS_ERR_INVALID_ARG, "q_start=%d must be >= 0 and a multiple of S=%d", q_start, s.S);
+    if (num_pages <= 0 || max_pages <= 0)
+        return fail(HILS_ERR_INVALID_ARG, "num_pages=%d, max_pages=%d must be >= 1", num_pages, max_pages);
+    if (num_pages > PAGED_MAX_PAGES)
+        return fail(HILS_ERR_UNSUPPORTED, "num_pages=%d: supported up to %d", num_pages, PAGED_MAX_PAGES);
+    const int64_t Nk = (int64_t)q_start + s.N;
+    const int64_t CA = (Nk + s.S - 1) / s.S;
+    if (CA > 8192) return fail(HILS_ERR_UNSUPPORTED, "q_start + N = %lld keys: supported up to 8192 chunks", (long long)Nk);
+    if (CA > max_pages)
+        return fail(HILS_ERR_INVALID_ARG, "q_start + N = %lld keys need %lld pages, block table has %d", (long long)Nk,
+                    (long long)CA, max_pages);
+    s.q0 = q_start;
+    s.Nk = (int)Nk;
+    s.CA = (int)CA;
+    // candidates of the last row: chunks below its window
+    s.C = s.N > 0 ? std::max(0, (int)((Nk - 1) / s.S) - s.W / s.S) : 0;
+    s.max_pages = max_pages;
+    return ok();
+}
+
+size_t paged_workspace_bytes(const hils::Shape &s, bool qcal) {
+    return hils::align_up(hils::score_workspace_bytes(s, qcal), 256) + hils::fused_workspace_bytes(s);
 }
 
 hils_status_t check_ptr(const void *p, const char *name) {
@@ -124,7 +163,28 @@ hils_status_t hils_landmark_summarize(const hils_config_t *cfg, const void *k, c
     if ((st = check_ptr(k, "k")) || (st = check_ptr(q_lm, "q_lm")) || (st = check_ptr(k_sum, "k_sum")) ||
         (st = check_ptr(b_sum, "b_sum")))
         return st;
-    return hip_status(hils::launch_landmark_summary(s, k, q_lm, k_sum, b_sum, stream), "landmark summary launch");
+    return hip_status(hils::launch_landmark_summary(s, k, q_lm, k_sum, b_sum, nullptr, 0, stream),
+                      "landmark summary launch");
+}
+
+hils_status_t hils_summarize_pages(const hils_config_t *cfg, int32_t num_items, const void *k_cache,
+                                   int32_t num_pages, const void *q_lm, const int32_t *pages, void *ksum_cache,
+                                   float *bsum_cache, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, false, s);
+    if (st) return st;
+    if (num_items < 0 || num_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_items, num_pages must be >= 0");
+    if (num_items == 0 || num_pages == 0) return ok();
+    if ((st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(q_lm, "q_lm")) || (st = check_ptr(pages, "pages")) ||
+        (st = check_ptr(ksum_cache, "ksum_cache")) || (st = check_ptr(bsum_cache, "bsum_cache")))
+        return st;
+    // item b = one "sequence" of a single S-key chunk (page pages[b])
+    s.B = num_items;
+    s.N = s.S;
+    s.C = s.CA = 1;
+    s.Nk = s.N;
+    return hip_status(hils::launch_landmark_summary(s, k_cache, q_lm, ksum_cache, bsum_cache, pages, num_pages, stream),
+                      "paged landmark summary launch");
 }
 
 hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const void *k_sum, const float *b_sum,
@@ -209,6 +269,55 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
                                           max_pages, seq_lens, 0, h, w_down, w_up, d_model, r, out, lse, sel_idx,
                                           workspace, stream),
                       "decode launch");
+}
+
+size_t hils_prefill_paged_workspace_size(const hils_config_t *cfg, int32_t q_start, int32_t max_pages,
+                                         int32_t with_qcal) {
+    hils::Shape s;
+    if (resolve_paged(cfg, q_start, 1, max_pages, s) != HILS_OK) return 0;
+    return paged_workspace_bytes(s, with_qcal != 0);
+}
+
+hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, const void *q, const void *k_cache,
+                                 const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                                 int32_t num_pages, const int32_t *block_table, int32_t max_pages, const void *h,
+                                 const void *w_down, const void *w_up, int32_t d_model, int32_t r, int32_t *sel_idx,
+                                 float *sel_score, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve_paged(cfg, q_start, num_pages, max_pages, s);
+    if (st) return st;
+    if ((int64_t)s.B * s.N == 0) return ok();
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
+        (st = check_ptr(block_table, "block_table")) || (st = check_ptr(out, "out")))
+        return st;
+    if (s.K > 0 && ((st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))) return st;
+    if (s.K > 0 && s.C > 0 && ((st = check_ptr(ksum_cache, "ksum_cache")) || (st = check_ptr(bsum_cache, "bsum_cache"))))
+        return st;
+    if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    if ((st = check_qcal(h, w_down, w_up, d_model, r))) return st;
+    s.bt = block_table;
+    if (!hils::sparse_attend_supported(s))
+        return fail(HILS_ERR_UNSUPPORTED, "no fused-attention block shape fits LDS for G=%d, S=%d, d=%d, K=%d", s.G, s.S,
+                    s.D, s.K);
+    const bool qcal = h != nullptr;
+    const size_t need = paged_workspace_bytes(s, qcal);
+    if (!workspace || workspace_bytes < need)
+        return fail(HILS_ERR_WORKSPACE, "prefill_paged needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const size_t score_bytes = hils::align_up(hils::score_workspace_bytes(s, qcal), 256);
+    if (s.K > 0) {
+        hils::ScoreWorkspace ws;
+        hils::score_workspace_carve(s, qcal, workspace, ws);
+        if ((st = hip_status(hils::launch_score_select(s, q, ksum_cache, bsum_cache, h, w_down, w_up, d_model, r,
+                                                       sel_idx, sel_score, ws, stream),
+                             "paged score/select launch")))
+            return st;
+    }
+    return hip_status(hils::launch_sparse_attend(s, q, k_cache, v_cache, sel_idx, sel_score, out, lse,
+                                                 (char *)workspace + score_bytes, stream),
+                      "paged sparse attention launch");
 }
 
 }  // extern "C"

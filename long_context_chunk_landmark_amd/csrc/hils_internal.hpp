@@ -20,11 +20,25 @@ struct Shape {
     int CA;     // ceil(N / S) chunks incl. a partial last one
     bool io_bf16, sum_bf16;
     float scale;
+    // Paged prefill (q0 = 0, Nk = N, bt = null for the contiguous layout):
+    // the N query rows are positions q0 .. q0 + N - 1 (q0 % S == 0) of
+    // sequences whose keys 0 .. Nk - 1 = q0 + N - 1 live in a paged cache
+    // [P, H_kv, S, D]; chunk c of sequence b is page bt[b * max_pages + c],
+    // and its summaries are row bt[b * max_pages + c] of the paged summary
+    // cache.  C is then the candidate bound of the last row and CA the
+    // chunks holding keys 0 .. Nk - 1.  max_pages > 0 marks the paged layout.
+    int q0, Nk;
+    const int32_t *bt;
+    int max_pages;
 };
 
 // ---- kernel 1: landmark summary
+// pages == null: every completed chunk of k [B, H_kv, N, D].  Otherwise
+// item b < B summarises page pages[b] of a paged cache (N = S, C = 1) with
+// landmark queries q_lm[b] and writes summary row pages[b]; items whose id
+// is outside [0, num_pages) are skipped.
 hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
-                                   hipStream_t st);
+                                   const int32_t *pages, int num_pages, hipStream_t st);
 
 // ---- kernel 2: score + select
 struct ScoreWorkspace {
@@ -36,6 +50,7 @@ struct ScoreWorkspace {
     float *agg;         // ragged approximate group scores, per (b,g): per_bg entries
     int64_t per_bg;     // entries per (b, g)
     float *q_s;         // [B,H_q,N,D] Q-Cal scoring queries (fp32) or null
+    float *bsum;        // [B,H_lm,C] b_sum gathered from the paged cache (paged prefill) or null
 };
 int64_t score_agg_entries_per_bg(const Shape &s);
 size_t score_workspace_bytes(const Shape &s, bool qcal);

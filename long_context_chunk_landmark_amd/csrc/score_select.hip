@@ -32,16 +32,9 @@ namespace hils {
 // ------------------------------------------------------------ workspace
 
 int64_t score_agg_entries_per_bg(const Shape &s) {
-    // rows of every query chunk (incl. a partial last one) padded to 16
+    // rows of the query positions q0 .. q0 + N - 1, each padded to 16
     const int64_t w = s.W / s.S;
-    int64_t total = 0;
-    const int64_t full = s.N / s.S;
-    total = cand_chunk_offset(full, w, s.S);
-    if (s.N % s.S) {
-        const int64_t n = full - w > 0 ? full - w : 0;
-        total += (int64_t)(s.N % s.S) * pad16(n);
-    }
-    return total;
+    return cand_row_offset((int64_t)s.q0 + s.N, w, s.S) - cand_row_offset(s.q0, w, s.S);
 }
 
 size_t score_workspace_bytes(const Shape &s, bool qcal) {
@@ -52,6 +45,7 @@ size_t score_workspace_bytes(const Shape &s, bool qcal) {
     b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
     b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
     if (qcal) b += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
+    if (s.max_pages > 0) b += align_up((size_t)s.B * s.H_lm * s.C * 4, 256);  // paged: gathered b_sum
     return b;
 }
 
@@ -70,6 +64,8 @@ void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace
     ws.agg = (float *)p;
     p += align_up((size_t)s.B * s.H_kv * ws.per_bg * 4, 256);
     ws.q_s = qcal ? (float *)p : nullptr;
+    if (qcal) p += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
+    ws.bsum = s.max_pages > 0 ? (float *)p : nullptr;
 }
 
 // ------------------------------------------------------------ k' prep
@@ -84,22 +80,34 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
 // only for fp32 summaries) for the MFMA pass, an fp32 chunk-major copy
 // [B, H_kv, C, GLM, D] (the GLM landmark rows of a group contiguous per
 // chunk) for the exact refinement, and the max norm per (b, landmark head).
+// With a block table (bt != null) the summaries come from a paged cache
+// [P, H_lm, D] (chunk c of sequence b is row bt[b * max_pages + c]), and
+// b_sum [P, H_lm] is gathered into bsum_out [B, H_lm, C] as well.
 template <typename TS, int D>
 __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k_sum, bf16 *__restrict__ ksb,
                                                         bf16 *__restrict__ ksb2, float *__restrict__ kcm,
-                                                        float *__restrict__ knorm, int C, int GLM, int64_t rows) {
+                                                        float *__restrict__ knorm, int C, int GLM, int64_t rows,
+                                                        const int32_t *__restrict__ bt, int max_pages, int H_lm,
+                                                        const float *__restrict__ bsum_in,
+                                                        float *__restrict__ bsum_out) {
     constexpr int EL = D / 16;
     const int lane = lane_id();
     const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * 4 + (lane >> 4);
     const bool ok = row < rows;
     float ss = 0.f;
     if (ok) {
-        const TS *src = k_sum + row * D + (lane & 15) * EL;
-        bf16 *dst = ksb + row * D + (lane & 15) * EL;
-        bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
         // row = (b * H_lm + l) * C + c with l = g * GLM + e
         const int64_t c = row % C, bl = row / C;
         const int64_t e = bl % GLM, bg = bl / GLM;
+        int64_t src_row = row;
+        if (bt) {
+            const int64_t b = bl / H_lm, l = bl % H_lm;
+            src_row = (int64_t)bt[b * max_pages + c] * H_lm + l;
+            if ((lane & 15) == 0) bsum_out[row] = bsum_in[src_row];
+        }
+        const TS *src = k_sum + src_row * D + (lane & 15) * EL;
+        bf16 *dst = ksb + row * D + (lane & 15) * EL;
+        bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
         float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
 #pragma unroll
         for (int x = 0; x < EL; ++x) {
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
     const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const bf16 *__restrict__ ksb2,
     const float *__restrict__ b_sum, const float *__restrict__ knorm, float *__restrict__ agg_out,
     float *__restrict__ err_out, int N, int H_q, int H_kv, int H_lm, int C, int S, int W, int K, float scale,
-    float kappa, int64_t per_bg) {
+    float kappa, int64_t per_bg, int q0) {
     constexpr bool QSPLIT = std::is_same<TQ, float>::value;
     constexpr int NQT = QSPLIT ? 2 : 1;   // query terms
     constexpr int NKT = KSPLIT ? 2 : 1;   // k' terms
@@ -318,9 +326,9 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
 
     const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
-    const int i0 = blockIdx.x * 64;
+    const int i0 = blockIdx.x * 64;  // local row; position q0 + i0 (q0 % S == 0)
     const int w = W / S;
-    const int qc = i0 / S;
+    const int qc = (q0 + i0) / S;
     const int n = max(0, qc - w);
     if (n <= K) return;  // every candidate is selected; nothing to rank
 
@@ -378,7 +386,9 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
 
     float *row[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) row[u] = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset(iqc[u], w, S);
+    for (int u = 0; u < 2; ++u)
+        row[u] = agg_out + ((int64_t)b * H_kv + g) * per_bg + cand_row_offset((int64_t)q0 + iqc[u], w, S) -
+                 cand_row_offset(q0, w, S);
     const int cr = lane & 15;
 
     // k' tiles are staged through registers one tile ahead: the loads of
@@ -523,7 +533,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
                                                      const float *__restrict__ err_in, int32_t *__restrict__ sel_idx,
                                                      float *__restrict__ sel_score, int B, int N, int H_q, int H_kv,
                                                      int H_lm, int C, int S, int W, int K, float scale,
-                                                     int64_t per_bg) {
+                                                     int64_t per_bg, int q0) {
     constexpr int GLM = SHARED ? 1 : G;
     constexpr int EPL = GLM * D / WAVE;   // elements of a survivor row per lane
     constexpr int LR = D / EPL;           // lanes covering one landmark row
@@ -538,7 +548,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
     const int w = W / S;
-    const int n = max(0, i / S - w);
+    const int n = max(0, (q0 + i) / S - w);  // row i is position q0 + i
 
     int32_t *out_idx = sel_idx + row * K;
     const int64_t sc_base = (b * H_q + (int64_t)g * G) * N + i;  // + e*N, then * K
@@ -569,7 +579,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
     constexpr int JR = 32;
     const int J = (n + WAVE - 1) / WAVE;
     const bool cached = J <= JR;
-    const float *ar = agg_in + bg * per_bg + cand_row_offset(i, w, S);
+    const float *ar = agg_in + bg * per_bg + cand_row_offset((int64_t)q0 + i, w, S) - cand_row_offset(q0, w, S);
     uint32_t kreg[JR];
     if (cached) {
 #pragma unroll
@@ -783,7 +793,7 @@ static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const Sc
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const bf16 *)ws.ksb, (const bf16 *)ws.ksb2, b_sum,
                            ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
-                           ws.per_bg);
+                           ws.per_bg, s.q0);
     };
     if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false>);
     else go(score_approx_kernel<TQ, D, G, true>);
@@ -811,7 +821,7 @@ static void go_select(const Shape &s, const TQ *qv, const float *b_sum, const Sc
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const float *)ws.kcm, b_sum, (const float *)ws.agg,
                            (const float *)ws.err, sel_idx, sel_score, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W,
-                           s.K, s.scale, ws.per_bg);
+                           s.K, s.scale, ws.per_bg, s.q0);
     };
     if (s.GLM == 1 && G > 1) go(select_kernel<TQ, D, G, true>);
     else go(select_kernel<TQ, D, G, false>);
@@ -842,14 +852,20 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     const int64_t krows = (int64_t)s.B * s.H_lm * s.C;
     if (krows > 0) {
         const dim3 grid((unsigned)((krows + 15) / 16)), block(256);
+        auto prep = [&](auto kern, auto *src) {
+            hipLaunchKernelGGL(kern, grid, block, 0, st, src, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C,
+                               s.GLM, krows, s.bt, s.max_pages, s.H_lm, b_sum, ws.bsum);
+        };
         if (s.sum_bf16) {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<bf16, 64>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<bf16, 128>), grid, block, 0, st, (const bf16 *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            if (s.D == 64) prep(ksum_prep_kernel<bf16, 64>, (const bf16 *)k_sum);
+            else prep(ksum_prep_kernel<bf16, 128>, (const bf16 *)k_sum);
         } else {
-            if (s.D == 64) hipLaunchKernelGGL((ksum_prep_kernel<float, 64>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
-            else hipLaunchKernelGGL((ksum_prep_kernel<float, 128>), grid, block, 0, st, (const float *)k_sum, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C, s.GLM, krows);
+            if (s.D == 64) prep(ksum_prep_kernel<float, 64>, (const float *)k_sum);
+            else prep(ksum_prep_kernel<float, 128>, (const float *)k_sum);
         }
     }
+    // paged prefill: the scorers read the gathered b_sum
+    if (s.bt) b_sum = ws.bsum;
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // scoring queries

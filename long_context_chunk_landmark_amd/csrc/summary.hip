@@ -23,7 +23,8 @@ template <typename T, typename TS, int D, int S, int GLM>
 __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm,
                                                                TS *__restrict__ k_sum, float *__restrict__ b_sum,
                                                                int H_kv, int N, int C, float scale,
-                                                               int64_t total_units) {
+                                                               int64_t total_units, const int32_t *__restrict__ pages,
+                                                               int num_pages) {
     constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int LPR = D / E;         // lanes covering one key row
     constexpr int RPL = WAVE / LPR;    // key rows per wave-wide load
@@ -37,10 +38,13 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
     const int64_t bg = unit / C;  // b * H_kv + g
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
+    // paged: item b summarises page pb (keys and summary row); else pb = b
+    const int64_t pb = pages ? (int64_t)pages[b] : b;
+    if (pb < 0 || (pages && pb >= num_pages)) return;
     const int col = lane % LPR;
     const int rsub = lane / LPR;
 
-    const T *kb = k + (bg * N + (int64_t)c * S) * D;
+    const T *kb = k + ((pb * H_kv + g) * N + (int64_t)c * S) * D;
     Vec16<T> kr[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) kr[t] = load16(kb + (int64_t)(t * RPL + rsub) * D + col * E);
@@ -50,7 +54,8 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
     // register array
 #pragma unroll 1
     for (int e = 0; e < GLM; ++e) {
-        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;
+        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;   // landmark query
+        const int64_t orow = (pb * H_lm + (int64_t)g * GLM + e) * C + c;  // summary
         const Vec16<T> qv = load16(q_lm + lrow * D + col * E);
         float a[NL];
         float m = -INFINITY;
@@ -88,10 +93,10 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
 #pragma unroll
         for (int x = 0; x < E; ++x) acc[x] = xor_sum<LPR, WAVE / 2>(acc[x]);
         if (rsub == 0) {
-            TS *dst = k_sum + lrow * D + col * E;
+            TS *dst = k_sum + orow * D + col * E;
 #pragma unroll
             for (int x = 0; x < E; ++x) dst[x] = from_f32<TS>(acc[x]);
-            if (col == 0) b_sum[lrow] = ent;
+            if (col == 0) b_sum[orow] = ent;
         }
     }
 }
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
 template <typename TS, int S, int GLM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void landmark_summary_d128_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ q_lm, TS *__restrict__ k_sum, float *__restrict__ b_sum,
-    int H_kv, int N, int C, float scale, int64_t total_units) {
+    int H_kv, int N, int C, float scale, int64_t total_units, const int32_t *__restrict__ pages, int num_pages) {
     constexpr int D = 128, NB = S / 64;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ float p_lds[4][4][S / 4];  // [wave of block][rsub][block * 16 + t]
@@ -118,9 +123,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
     const int64_t bg = unit / C;  // b * H_kv + g
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
+    // paged: item b summarises page pb (keys and summary row); else pb = b
+    const int64_t pb = pages ? (int64_t)pages[b] : b;
+    if (pb < 0 || (pages && pb >= num_pages)) return;
     const int col = lane & 15, rsub = lane >> 4;
     float(*pw)[S / 4] = p_lds[(threadIdx.x / WAVE) & 3];
-    const bf16 *kb = k + (bg * N + (int64_t)c * S) * D + col * 8;
+    const bf16 *kb = k + ((pb * H_kv + g) * N + (int64_t)c * S) * D + col * 8;
     const float sl2 = scale * LOG2E;
     const int H_lm = H_kv * GLM;
 
@@ -136,7 +144,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
     load_block(NB - 1);
 #pragma unroll 1
     for (int e = 0; e < GLM; ++e) {
-        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;
+        const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;   // landmark query
+        const int64_t orow = (pb * H_lm + (int64_t)g * GLM + e) * C + c;  // summary
         const u32x4 qr = *(const u32x4 *)(q_lm + lrow * D + col * 8);
         float lg[NB];
 #pragma unroll
@@ -206,23 +215,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] = rows4_sum(acc[x]);
         if (rsub == 0) {
-            TS *dst = k_sum + lrow * D + col * 8;
+            TS *dst = k_sum + orow * D + col * 8;
 #pragma unroll
             for (int x = 0; x < 8; ++x) dst[x] = from_f32<TS>(acc[x]);
-            if (col == 0) b_sum[lrow] = ent;
+            if (col == 0) b_sum[orow] = ent;
         }
     }
 }
 
 template <typename T, typename TS, int D, int S>
 static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
-                           hipStream_t st) {
+                           const int32_t *pages, int num_pages, hipStream_t st) {
     const int64_t units = (int64_t)s.B * s.H_kv * s.C;
     if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const T *)k, (const T *)q_lm, (TS *)k_sum, b_sum, s.H_kv, s.N,
-                           s.C, s.scale, units);
+                           s.C, s.scale, units, pages, num_pages);
     };
     if constexpr (std::is_same<T, bf16>::value && D == 128) {
         switch (s.GLM) {
@@ -246,21 +255,21 @@ static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void
 
 template <typename T, typename TS>
 static hipError_t launch_t(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
-                           hipStream_t st) {
-    if (s.D == 64 && s.S == 64) return launch_s<T, TS, 64, 64>(s, k, q_lm, k_sum, b_sum, st);
-    if (s.D == 64 && s.S == 128) return launch_s<T, TS, 64, 128>(s, k, q_lm, k_sum, b_sum, st);
-    if (s.D == 128 && s.S == 64) return launch_s<T, TS, 128, 64>(s, k, q_lm, k_sum, b_sum, st);
-    if (s.D == 128 && s.S == 128) return launch_s<T, TS, 128, 128>(s, k, q_lm, k_sum, b_sum, st);
+                           const int32_t *pages, int num_pages, hipStream_t st) {
+    if (s.D == 64 && s.S == 64) return launch_s<T, TS, 64, 64>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
+    if (s.D == 64 && s.S == 128) return launch_s<T, TS, 64, 128>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
+    if (s.D == 128 && s.S == 64) return launch_s<T, TS, 128, 64>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
+    if (s.D == 128 && s.S == 128) return launch_s<T, TS, 128, 128>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_lm, void *k_sum, float *b_sum,
-                                   hipStream_t st) {
+                                   const int32_t *pages, int num_pages, hipStream_t st) {
     if (s.io_bf16)
-        return s.sum_bf16 ? launch_t<bf16, bf16>(s, k, q_lm, k_sum, b_sum, st)
-                          : launch_t<bf16, float>(s, k, q_lm, k_sum, b_sum, st);
-    return s.sum_bf16 ? launch_t<float, bf16>(s, k, q_lm, k_sum, b_sum, st)
-                      : launch_t<float, float>(s, k, q_lm, k_sum, b_sum, st);
+        return s.sum_bf16 ? launch_t<bf16, bf16>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st)
+                          : launch_t<bf16, float>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
+    return s.sum_bf16 ? launch_t<float, bf16>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st)
+                      : launch_t<float, float>(s, k, q_lm, k_sum, b_sum, pages, num_pages, st);
 }
 
 }  // namespace hils

@@ -186,3 +186,25 @@ def make_decode(name_or_params="decode_512k", device="cuda", **overrides):
         w_up = _randn(gen, (cfg.H_q * cfg.d, r), gdev, dt, std=1.0 / math.sqrt(dm))
         out["qcal"] = tuple(x.to(device) for x in (h, w_down, w_up))
     return out
+
+
+def paged_layout(k, v, S, seed, extra_pages=7):
+    """Scatter contiguous [B, H_kv, N, d] keys and values into paged caches
+    [P, H_kv, S, d] at a seeded random page placement: P = B * ceil(N/S) +
+    extra_pages, sequences own disjoint pages, unused pages and the tail of a
+    partial last page are zero.  Returns (k_cache, v_cache, block_table
+    [B, ceil(N/S)] int32) on the device of k."""
+    B, H_kv, N, d = k.shape
+    CA = (N + S - 1) // S
+    P = B * CA + extra_pages
+    bt = torch.randperm(P, generator=_generator(seed, "cpu"))[:B * CA].view(B, CA).to(torch.int32)
+    idx = bt.view(-1).long().to(k.device)
+
+    def scatter(x):
+        xp = torch.zeros((B, H_kv, CA * S, d), dtype=x.dtype, device=x.device)
+        xp[:, :, :N] = x
+        cache = torch.zeros((P, H_kv, S, d), dtype=x.dtype, device=x.device)
+        cache[idx] = xp.view(B, H_kv, CA, S, d).permute(0, 2, 1, 3, 4).reshape(B * CA, H_kv, S, d)
+        return cache
+
+    return scatter(k), scatter(v), bt.to(k.device)

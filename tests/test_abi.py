@@ -164,3 +164,50 @@ def test_fused_shape_beyond_lds_is_unsupported(lib):
     need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
     st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need, None)
     assert st == hb.HILS_ERR_UNSUPPORTED and "LDS" in hb.last_error()
+
+
+def _paged(lib, cfg, q_start=1024, num_pages=200, max_pages=100, bt=A, ws=A2, nbytes=None, h=None, wd=None,
+           wu=None, d_model=0, r=0):
+    if nbytes is None:
+        nbytes = lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), q_start, max_pages, int(h is not None))
+    return lib.hils_prefill_paged(ctypes.byref(cfg), q_start, A, A, A, A, A, num_pages, bt, max_pages, h, wd, wu,
+                                  d_model, r, A, A, A, None, ws, nbytes, None)
+
+
+def test_prefill_paged_argument_checks(lib):
+    cfg = _cfg(N=512)
+    assert _paged(lib, cfg, q_start=1000) == hb.HILS_ERR_INVALID_ARG and "multiple of S" in hb.last_error()
+    assert _paged(lib, cfg, q_start=-64) == hb.HILS_ERR_INVALID_ARG
+    # keys 0 .. q_start + N - 1 need more pages than the block table has
+    assert _paged(lib, cfg, q_start=64 * 95, max_pages=100) == hb.HILS_ERR_INVALID_ARG
+    assert "pages" in hb.last_error()
+    assert _paged(lib, cfg, num_pages=0) == hb.HILS_ERR_INVALID_ARG
+    assert _paged(lib, cfg, num_pages=(1 << 18) + 1) == hb.HILS_ERR_UNSUPPORTED
+    assert _paged(lib, cfg, bt=None) == hb.HILS_ERR_INVALID_ARG and "block_table" in hb.last_error()
+    assert _paged(lib, cfg, ws=None) == hb.HILS_ERR_WORKSPACE
+    need = lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), 1024, 100, 0)
+    assert _paged(lib, cfg, nbytes=need - 1) == hb.HILS_ERR_WORKSPACE
+    assert _paged(lib, cfg, h=A, wd=None, wu=A, d_model=256, r=16) == hb.HILS_ERR_INVALID_ARG
+    assert lib.hils_prefill_paged(ctypes.byref(_cfg(N=0)), 0, None, None, None, None, None, 1, None, 1, None, None,
+                                  None, 0, 0, None, None, None, None, None, 0, None) == hb.HILS_OK
+
+
+def test_prefill_paged_workspace_grows_with_position(lib):
+    cfg = _cfg(N=512)
+    a = lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), 0, 400, 0)
+    b = lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), 64 * 300, 400, 0)
+    c = lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), 64 * 300, 400, 1)
+    assert 0 < a < b < c
+    assert lib.hils_prefill_paged_workspace_size(ctypes.byref(cfg), 64 * 399, 400, 0) == 0  # too few pages
+    assert "pages" in hb.last_error()
+
+
+def test_summarize_pages_argument_checks(lib):
+    cfg = _cfg()
+    f = lib.hils_summarize_pages
+    assert f(ctypes.byref(cfg), -1, A, 100, A, A, A, A, None) == hb.HILS_ERR_INVALID_ARG
+    assert f(ctypes.byref(cfg), 4, A, 100, A, None, A, A, None) == hb.HILS_ERR_INVALID_ARG
+    assert "pages" in hb.last_error()
+    assert f(ctypes.byref(cfg), 4, A, 100, MIS, A, A, A, None) == hb.HILS_ERR_INVALID_ARG
+    assert f(ctypes.byref(_cfg(d=96)), 4, A, 100, A, A, A, A, None) == hb.HILS_ERR_UNSUPPORTED
+    assert f(ctypes.byref(cfg), 0, None, 100, None, None, None, None, None) == hb.HILS_OK
