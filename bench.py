@@ -33,22 +33,24 @@ CSRC = os.path.join(ROOT, "long_context_chunk_landmark_amd", "csrc")
 
 # ---------------------------------------------------------------- algorithmic work
 
-def _chunks(cfg):
-    """Per query chunk: (first query, #queries, #candidates, #selected)."""
+def _chunks(cfg, q0=0):
+    """Per query chunk of positions q0 .. q0 + N - 1 (q0 % S == 0): (first
+    query, #queries, #candidates, #selected)."""
     S, w = cfg.S, cfg.W // cfg.S
     out = []
-    for qc in range((cfg.N + S - 1) // S):
-        n_q = min(S, cfg.N - qc * S)
+    end = q0 + cfg.N
+    for qc in range(q0 // S, (end + S - 1) // S):
+        n_q = min(S, end - qc * S)
         n_c = max(0, qc - w)
         out.append((qc * S, n_q, n_c, min(cfg.K, n_c)))
     return out
 
 
-def attend_flops(cfg):
+def attend_flops(cfg, q0=0):
     """4 d H_q sum_i (selected keys + window keys): QK^T and PV, 2 flops/MAC."""
     S = cfg.S
     keys = 0
-    for i0, n_q, n_c, k in _chunks(cfg):
+    for i0, n_q, n_c, k in _chunks(cfg, q0):
         ws = max(0, i0 - cfg.W)
         # window of query i: keys [ws, i]; sum over the chunk's queries
         win = n_q * (i0 - ws) + n_q * (n_q + 1) // 2
@@ -56,8 +58,8 @@ def attend_flops(cfg):
     return 4.0 * cfg.d * cfg.H_q * keys * cfg.B
 
 
-def score_flops(cfg):
-    return 2.0 * cfg.d * cfg.H_q * cfg.B * sum(n_q * n_c for _, n_q, n_c, _ in _chunks(cfg))
+def score_flops(cfg, q0=0):
+    return 2.0 * cfg.d * cfg.H_q * cfg.B * sum(n_q * n_c for _, n_q, n_c, _ in _chunks(cfg, q0))
 
 
 def summary_bytes(cfg, io_bytes, sum_bytes):
@@ -187,6 +189,66 @@ def bench_decode(args, torch, hb, W):
                 seq_lens=seq_lens)
 
 
+def bench_serving(args, torch, hb, W, pre):
+    """Serving continuity on the prefill workload laid out in a paged cache:
+    (a) summaries of every completed chunk written page by page
+    (hils_summarize_pages); (b) the last args.chunk tokens prefilled as one
+    chunk over the paged cache (hils_prefill_paged)."""
+    dev = torch.device("cuda:0")
+    inp = pre["inp"]
+    cfg = pre["cfg"]
+    kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=17)
+    P, C = kc.shape[0], cfg.C
+    ks = torch.empty((P, cfg.H_lm, cfg.d), dtype=cfg.summary_dtype, device=dev)
+    bs = torch.empty((P, cfg.H_lm), dtype=torch.float32, device=dev)
+    bb = torch.arange(cfg.B, device=dev).repeat_interleave(C)
+    cc = torch.arange(C, device=dev).repeat(cfg.B)
+    pages = bt[bb, cc].contiguous()
+    q_items = inp["q_lm"][bb, :, cc].contiguous()
+    n = min(args.chunk, cfg.N)
+    q_start = (cfg.N - n) // cfg.S * cfg.S
+    n = cfg.N - q_start
+    import dataclasses
+
+    ccfg = dataclasses.replace(cfg, N=n)
+    q = inp["q"][:, :, q_start:].contiguous()
+    qcal = inp.get("qcal")
+    if qcal is not None:
+        qcal = (qcal[0][:, q_start:].contiguous(), qcal[1], qcal[2])
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H_q, n), dtype=torch.float32, device=dev)
+    sel = torch.empty((cfg.B, cfg.H_kv, n, cfg.K), dtype=torch.int32, device=dev)
+    ss = torch.empty((cfg.B, cfg.H_q, n, cfg.K), dtype=torch.float32, device=dev)
+    ws = torch.empty(hb.prefill_paged_workspace_size(ccfg, q_start, bt.shape[1], qcal is not None),
+                     dtype=torch.uint8, device=dev)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step():
+        e = [E() for _ in range(3)]
+        e[0].record()
+        hb.summarize_pages(cfg, kc, q_items, pages, ks, bs)
+        e[1].record()
+        hb.prefill_paged(ccfg, q_start, q, kc, vc, ks, bs, bt, qcal=qcal, out=out, lse=lse, sel_idx=sel,
+                         sel_score=ss, workspace=ws)
+        e[2].record()
+        return {"summarize_pages": (e[0], e[1]), "prefill_paged": (e[1], e[2])}
+
+    _, per = _timed(step, args.steps, args.warmup, torch)
+    io_b = 2 if cfg.io_dtype == torch.bfloat16 else 4
+    sum_b = 2 if cfg.summary_dtype == torch.bfloat16 else 4
+    # the page-by-page summaries move the bytes of the contiguous summary
+    # plus the page ids
+    by = summary_bytes(cfg, io_b, sum_b) + 4 * cfg.B * C
+    ms_s, ms_p = per["summarize_pages"], per["prefill_paged"]
+    fl = attend_flops(ccfg, q_start) + score_flops(ccfg, q_start)
+    del kc, vc, ks, bs, ws
+    return {"workload": f"{args.workload} in a paged cache ({P} pages, random placement)",
+            "summarize_pages": {"items": cfg.B * C, "ms": ms_s, "bound": "hbm", "gbs": by / (ms_s * 1e-3) / 1e9,
+                                "frac": by / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by},
+            "prefill_paged": {"q_start": q_start, "n": n, "ms": ms_p, "tokens_per_s": cfg.B * n / (ms_p * 1e-3),
+                              "tflops": fl / (ms_p * 1e-3) / 1e12, "flops": fl}}
+
+
 def union_overlap(sel, M, sample=4096, seed=0):
     """Mean |union of the selections of M adjacent queries| / K over a sample
     of groups (1 = identical selections, M = disjoint)."""
@@ -247,6 +309,8 @@ def main():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_512k")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-serving", action="store_true")
+    ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -305,6 +369,10 @@ def main():
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }
+    if not args.no_serving:
+        print(f"[bench] serving: paged summaries + chunked prefill of {args.chunk} tokens", file=sys.stderr,
+              flush=True)
+        result["serving"] = bench_serving(args, torch, hb, W, pre)
     if not args.no_decode:
         print(f"[bench] decode {args.decode_workload}", file=sys.stderr, flush=True)
         dec = bench_decode(args, torch, hb, W)
