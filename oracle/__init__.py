@@ -36,13 +36,14 @@ SCORE_MODES = {"landmark": 0, "self_landmark": 1, "exact_mass": 2}
 
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("B", "N", "H_q", "H_kv", "H_lm", "d", "S", "W", "K")] + [
-        ("scale", ctypes.c_double)
+        ("scale", ctypes.c_double), ("agg_mode", ctypes.c_int64)
     ]
 
 
 def build(force: bool = True) -> str:
     """Compile hils_oracle.c into libhils_oracle.so (gcc, -O2, OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC[:-2] + ".h"))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"],
@@ -55,8 +56,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        build(force=False)  # (re)builds when missing or older than its sources
         _lib = ctypes.CDLL(_LIB_PATH)
         for fn in ("hils_ref_summarize", "hils_ref_qcal_rows", "hils_ref_forward_rows", "hils_ref_decode",
                    "hils_ref_dense_causal_rows"):
@@ -125,19 +125,43 @@ def _cfg(cfg: dict) -> _Cfg:
     H_q = int(cfg["H_q"])
     return _Cfg(
         int(cfg.get("B", 1)), int(cfg.get("N", 0)), H_q, int(cfg["H_kv"]), int(cfg.get("H_lm", H_q)), d,
-        int(cfg["S"]), int(cfg["W"]), int(cfg["K"]), float(scale),
+        int(cfg["S"]), int(cfg["W"]), int(cfg["K"]), float(scale), int(cfg.get("agg_mode", 0)),
     )
 
 
-def summarize(cfg: dict, k, q_lm):
+LANDMARK_MODES = ("chunk", "shared", "mean")
+
+
+def landmark_queries(cfg: dict, q_lm, lead, landmark: str = "chunk"):
+    """The landmark query of every chunk, [*lead, H_lm, d] with lead = (B, C)
+    or (items,).  "chunk": q_lm holds them.  "shared" (the landmark-free
+    variant: one query per landmark head for every chunk): q_lm [H_lm, d]
+    repeated.  "mean": q' = 0 (mean-pooled keys)."""
+    c = _cfg(cfg)
+    if landmark == "chunk":
+        return _f32(q_lm)
+    if landmark == "shared":
+        ql = _f32(q_lm)
+        assert ql.shape == (c.H_lm, c.d), ql.shape
+        return np.ascontiguousarray(np.broadcast_to(ql, tuple(lead) + (c.H_lm, c.d)))
+    assert landmark == "mean", landmark
+    return np.zeros(tuple(lead) + (c.H_lm, c.d), np.float32)
+
+
+def summarize(cfg: dict, k, q_lm, landmark: str = "chunk"):
     """Landmark summaries of every completed chunk.
 
-    k: [B, H_kv, N, d]; q_lm: [B, H_lm, C, d] with C = N // S.
+    k: [B, H_kv, N, d]; q_lm: [B, H_lm, C, d] with C = N // S (see
+    ``landmark_queries`` for the other landmark modes).
     Returns (k_sum [B, H_lm, C, d] float64, b_sum [B, H_lm, C] float64).
     """
     c = _cfg(cfg)
     C = c.N // c.S
-    k32, ql32 = _f32(k), _f32(q_lm)
+    k32 = _f32(k)
+    if landmark == "chunk":
+        ql32 = _f32(q_lm)
+    else:  # [B, C, H_lm, d] -> [B, H_lm, C, d]
+        ql32 = np.ascontiguousarray(landmark_queries(cfg, q_lm, (c.B, C), landmark).transpose(0, 2, 1, 3))
     assert k32.shape == (c.B, c.H_kv, c.N, c.d), k32.shape
     assert ql32.shape == (c.B, c.H_lm, C, c.d), ql32.shape
     k_sum = np.zeros((c.B, c.H_lm, C, c.d), np.float64)
@@ -263,7 +287,7 @@ def decode(cfg: dict, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table, 
     return res
 
 
-def summarize_pages(cfg: dict, k_cache, q_lm, pages):
+def summarize_pages(cfg: dict, k_cache, q_lm, pages, landmark: str = "chunk"):
     """Summaries of the chunks held by pages of a paged key cache.
 
     Item i summarises page pages[i] of k_cache [P, H_kv, S, d] (one completed
@@ -273,10 +297,11 @@ def summarize_pages(cfg: dict, k_cache, q_lm, pages):
     Returns (k_sum [n, H_lm, d], b_sum [n, H_lm]) float64.
     """
     c = _cfg(cfg)
-    kc, ql = _f32(k_cache), _f32(q_lm)
+    kc = _f32(k_cache)
     pg = np.asarray(pages, dtype=np.int64).reshape(-1)
     P = kc.shape[0]
     n = len(pg)
+    ql = landmark_queries(cfg, q_lm, (n,), landmark)
     assert kc.shape == (P, c.H_kv, c.S, c.d), kc.shape
     assert ql.shape == (n, c.H_lm, c.d), ql.shape
     k_sum = np.full((n, c.H_lm, c.d), np.nan)

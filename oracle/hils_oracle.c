@@ -435,18 +435,25 @@ static void forward_one(const hils_ref_cfg *cfg, score_ctx *sc, kv_ctx *kv,
     const int64_t nc = num_candidates(cfg, i);
     const int64_t h0 = kv->g * G;
 
-    /* per-head surrogate scores of every candidate chunk, and the group
-     * score (max over the heads of the group) */
+    /* per-head surrogate scores of every candidate chunk */
+    for (int64_t c = 0; c < nc; ++c)
+        for (int64_t e = 0; e < G; ++e)
+            scratch_scores[e * nc + c] = chunk_score(sc, h0 + e, qs_rows + e * d, c);
+    /* group score: the max over the heads of the group of each head's chunk
+     * weight -- its raw s^ (agg_mode 0), or (agg_mode 1) its log-softmax
+     * over the row's candidates, s^ - log sum_c' exp(s^_c').  The fusion
+     * below always uses the raw s^. */
     double *agg = agg_all;
-    for (int64_t c = 0; c < nc; ++c) {
-        double m = -INFINITY;
-        for (int64_t e = 0; e < G; ++e) {
-            const double v = chunk_score(sc, h0 + e, qs_rows + e * d, c);
-            scratch_scores[e * nc + c] = v;
-            if (v > m)
-                m = v;
+    for (int64_t c = 0; c < nc; ++c)
+        agg[c] = -INFINITY;
+    for (int64_t e = 0; e < G; ++e) {
+        const double norm =
+            cfg->agg_mode == 1 ? log_sum_exp(scratch_scores + e * nc, nc) : 0.0;
+        for (int64_t c = 0; c < nc; ++c) {
+            const double v = scratch_scores[e * nc + c] - norm;
+            if (v > agg[c])
+                agg[c] = v;
         }
-        agg[c] = m;
     }
 
     if (given) {
@@ -511,6 +518,8 @@ static int check_cfg(const hils_ref_cfg *cfg)
     if (!(cfg->H_lm == cfg->H_q || cfg->H_lm == cfg->H_kv))
         return -1;
     if (cfg->d > HILS_REF_MAX_D || cfg->K > HILS_REF_MAX_K)
+        return -1;
+    if (cfg->agg_mode != 0 && cfg->agg_mode != 1)
         return -1;
     return 0;
 }

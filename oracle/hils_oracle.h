@@ -21,6 +21,10 @@ enum {
 typedef struct {
     int64_t B, N, H_q, H_kv, H_lm, d, S, W, K;
     double scale;
+    /* 0: a group's chunk score is the max of its heads' s^ (GQA paragraph);
+     * 1: the max of each head's s^ minus its log-sum-exp over the row's
+     *    candidate chunks (per-head normalised weights) */
+    int64_t agg_mode;
 } hils_ref_cfg;
 
 int hils_ref_summarize(const hils_ref_cfg *cfg, const float *k,

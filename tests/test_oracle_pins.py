@@ -666,3 +666,94 @@ def test_prefill_paged_equals_prefill_rows(q_start, n, qcal):
     assert (got["sel_idx"] >= 0).any()  # some rows have candidates
     for key in ("sel_score", "out", "lse", "kth"):
         np.testing.assert_allclose(got[key], pre[key], rtol=0, atol=1e-12, err_msg=key)
+
+
+# ---------------------------------------------------------------- variants
+
+
+def test_mean_landmark_mode_is_mean_pooling():
+    """Landmark mode "mean" (q' = 0): k' is the chunk's mean key and b' = log S."""
+    rng = _rng(151)
+    S, d, N, B = 8, 16, 48, 2
+    cfg = _cfg(B=B, N=N, S=S, d=d, H_q=2, H_kv=1)
+    k = rng.standard_normal((B, 1, N, d)).astype(np.float32)
+    ks, bs = oracle.summarize(cfg, k, None, landmark="mean")
+    mean = k.astype(np.float64).reshape(B, 1, N // S, S, d).mean(3)
+    for l in range(2):  # both landmark heads read kv head 0
+        np.testing.assert_allclose(ks[:, l], mean[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(bs, math.log(S), rtol=0, atol=1e-12)
+
+
+def test_shared_landmark_mode_uses_one_query_per_head():
+    """Landmark-free variant: one landmark query per landmark head, the same
+    for every chunk and sequence; equals per-chunk queries all set to it."""
+    rng = _rng(152)
+    S, d, N, B, H_lm = 8, 16, 40, 2, 4
+    cfg = _cfg(B=B, N=N, S=S, d=d, H_q=H_lm, H_kv=2)
+    k = rng.standard_normal((B, 2, N, d)).astype(np.float32)
+    qs = rng.standard_normal((H_lm, d)).astype(np.float32)
+    ks, bs = oracle.summarize(cfg, k, qs, landmark="shared")
+    tiled = np.tile(qs[None, :, None, :], (B, 1, N // S, 1))
+    ks2, bs2 = oracle.summarize(cfg, k, tiled)
+    np.testing.assert_array_equal(ks, ks2)
+    np.testing.assert_array_equal(bs, bs2)
+    # and a chunk whose keys are all equal to one key gets that key for any query
+    k[:, :, :S] = k[:, :, :1]
+    ks3, _ = oracle.summarize(cfg, k, qs, landmark="shared")
+    np.testing.assert_allclose(ks3[:, :2, 0], k[:, :1, 0].repeat(2, axis=1), rtol=0, atol=1e-12)
+
+
+def _per_head_scores(cfg, q, k, v, ks, bs, rows):
+    """ŝ of each query head separately (a one-head configuration per head)."""
+    out = []
+    for h in range(cfg["H_q"]):
+        c1 = dict(cfg, H_q=1, H_kv=1, H_lm=1, agg_mode=0)
+        g = h // (cfg["H_q"] // cfg["H_kv"])
+        r = oracle.forward_rows(c1, q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], ks[:, h:h + 1], bs[:, h:h + 1],
+                                rows=rows, want_agg=True, attend=False)
+        out.append(r["agg"][0, 0])  # [R, C]
+    return np.stack(out)  # [H_q, R, C]
+
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_normalized_aggregation_is_max_of_log_softmax(K):
+    """agg_mode 1: the group score of chunk c is max over the group's heads of
+    ŝ[h,c] - log Σ_c' exp(ŝ[h,c']) over the row's candidates (numpy
+    log-softmax of the per-head scores); the top-K follows that score by
+    brute-force sort; the fusion still weighs by the raw ŝ."""
+    cfg, q, k, v, ql = _random_case(161 + K, G=4, H_kv=2, K=K)
+    q[:, 1] *= 3.0  # heads with different score spreads: the modes disagree
+    ks, bs = oracle.summarize(cfg, k, ql)
+    rows = np.arange(40, 256, 3)
+    per = _per_head_scores(cfg, q, k, v, ks, bs, rows)
+    cn = dict(cfg, agg_mode=1)
+    res = oracle.forward_rows(cn, q, k, v, ks, bs, rows=rows, want_agg=True)
+    raw = oracle.forward_rows(cfg, q, k, v, ks, bs, rows=rows, want_agg=True)
+    S, W, G = cfg["S"], cfg["W"], 4
+    differ = 0
+    for g in range(cfg["H_kv"]):
+        for r, i in enumerate(rows):
+            n = max(0, i // S - W // S)
+            if n == 0:
+                continue
+            hs = per[g * G:(g + 1) * G, r, :n]
+            want = (hs - logsumexp(hs, axis=1, keepdims=True)).max(0)
+            np.testing.assert_allclose(res["agg"][0, g, r, :n], want, rtol=0, atol=1e-12)
+            order = sorted(range(n), key=lambda c: (-want[c], c))[:K]
+            assert res["sel_idx"][0, g, r].tolist() == sorted(order) + [-1] * (K - len(order))
+            sel = [c for c in res["sel_idx"][0, g, r] if c >= 0]
+            for e in range(G):
+                np.testing.assert_allclose(res["sel_score"][0, g * G + e, r, :len(sel)],
+                                           per[g * G + e, r, sel], rtol=0, atol=1e-12)
+            differ += res["sel_idx"][0, g, r].tolist() != raw["sel_idx"][0, g, r].tolist()
+    assert differ > 0
+
+
+def test_normalized_aggregation_with_one_head_changes_nothing():
+    """With G = 1 the normalisation shifts a row's scores by a constant."""
+    cfg, q, k, v, ql = _random_case(171, G=1, H_kv=2, K=3)
+    ks, bs = oracle.summarize(cfg, k, ql)
+    a = oracle.forward_rows(cfg, q, k, v, ks, bs)
+    b = oracle.forward_rows(dict(cfg, agg_mode=1), q, k, v, ks, bs)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_array_equal(a["out"], b["out"])
