@@ -72,6 +72,25 @@ typedef enum {
 
 typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype_t;
 
+/* Where the landmark query q'_c of a chunk comes from (hyper.ai summary,
+ * 方法: the landmark paragraph, and the landmark-free variant named after the
+ * GQA paragraph). */
+typedef enum {
+    HILS_LM_CHUNK = 0,  /* one landmark query per chunk: q_lm [B, H_lm, C, d]      */
+    HILS_LM_SHARED = 1, /* landmark-free variant: one query per landmark head
+                           shared by every chunk and sequence: q_lm [H_lm, d]   */
+    HILS_LM_MEAN = 2    /* q'_c = 0: mean-pooled keys, b'_c = log S; q_lm unused */
+} hils_landmark_mode_t;
+
+/* How the heads of a GQA group combine their chunk scores before the shared
+ * top-K (hyper.ai summary, 方法, GQA paragraph: per-head chunk weights,
+ * max-aggregated over the group). */
+typedef enum {
+    HILS_AGG_MAX = 0,       /* max over the group's heads of s^[h,c]                   */
+    HILS_AGG_NORMALIZED = 1 /* max over the heads of the per-head normalised weight
+                               s^[h,c] - log sum_{c' candidate} exp(s^[h,c'])          */
+} hils_agg_mode_t;
+
 typedef struct {
     int32_t B;    /* batch (prefill); ignored by hils_decode                 */
     int32_t N;    /* tokens per sequence (prefill); ignored by hils_decode   */
@@ -86,6 +105,8 @@ typedef struct {
     int32_t io_dtype;      /* hils_dtype_t of q, k, v, q_lm, h, W, out, caches */
     int32_t summary_dtype; /* hils_dtype_t of k_sum / ksum_cache; b_sum is fp32 */
     float scale;           /* logit scale; 0 selects 1/sqrt(d)               */
+    int32_t landmark_mode; /* hils_landmark_mode_t; 0 (per-chunk queries) by default */
+    int32_t agg_mode;      /* hils_agg_mode_t; 0 (max of raw scores) by default   */
 } hils_config_t;
 
 /* Workspace kinds for hils_workspace_size(). */
@@ -101,7 +122,8 @@ enum {
  * chunk's S keys, k_sum[l,c] = sum_j p_j k_j, b_sum[l,c] = -sum_j p_j log p_j
  * (hyper.ai summary, 方法: the compressed key and its entropy bias).
  *   k     [B, H_kv, N, d]  io_dtype
- *   q_lm  [B, H_lm, C, d]  io_dtype
+ *   q_lm  [B, H_lm, C, d]  io_dtype ([H_lm, d] with HILS_LM_SHARED; unused,
+ *                          may be NULL, with HILS_LM_MEAN)
  *   k_sum [B, H_lm, C, d]  summary_dtype (written)
  *   b_sum [B, H_lm, C]     fp32          (written)
  * Also usable on a paged cache [P, H_kv, S, d] by passing B = P, N = S. */
@@ -179,7 +201,8 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
  * its entropy bias; the landmark query of a chunk exists once its S tokens
  * have arrived) and writes row pages[i] of the summary caches.
  *   k_cache     [num_pages, H_kv, S, d]   io_dtype; the page must be full
- *   q_lm        [num_items, H_lm, d]      io_dtype
+ *   q_lm        [num_items, H_lm, d]      io_dtype (as in hils_landmark_summarize
+ *               for the other landmark modes)
  *   pages       [num_items] int32 (device); an id outside [0, num_pages)
  *               skips the item (nothing written), so a batch may carry -1
  *               for sequences with no completed chunk this step

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libhils.so")
 
 HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ERR_HIP = range(5)
 HILS_F32, HILS_BF16 = 0, 1
+LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
+AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
 WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE = range(4)
 
 # Every symbol include/hils.h declares.
@@ -46,7 +48,7 @@ class HilsError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "N", "H_q", "H_kv", "H_lm", "d", "S", "W", "K", "M", "io_dtype", "summary_dtype")] + [
-                   ("scale", ctypes.c_float)]
+                   ("scale", ctypes.c_float), ("landmark_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32)]
 
 
 @dataclasses.dataclass
@@ -65,6 +67,8 @@ class Config:
     io_dtype: torch.dtype = torch.bfloat16
     summary_dtype: torch.dtype = torch.float32
     scale: float = 0.0
+    landmark_mode: int = LM_CHUNK
+    agg_mode: int = AGG_MAX
 
     def __post_init__(self):
         if self.H_lm is None:
@@ -87,11 +91,21 @@ class Config:
             raise ValueError(f"unsupported dtype {dt}")
 
         return _CConfig(self.B, self.N, self.H_q, self.H_kv, self.H_lm, self.d, self.S, self.W, self.K, self.M,
-                        code(self.io_dtype), code(self.summary_dtype), float(self.scale))
+                        code(self.io_dtype), code(self.summary_dtype), float(self.scale), int(self.landmark_mode),
+                        int(self.agg_mode))
 
     def oracle_dict(self) -> dict:
         return dict(B=self.B, N=self.N, H_q=self.H_q, H_kv=self.H_kv, H_lm=self.H_lm, d=self.d, S=self.S, W=self.W,
-                    K=self.K, scale=self.scale or 1.0 / math.sqrt(self.d))
+                    K=self.K, scale=self.scale or 1.0 / math.sqrt(self.d), agg_mode=self.agg_mode)
+
+    def q_lm_shape(self, items=None):
+        """Shape of the landmark queries for the landmark mode (None: unused).
+        items: per-item queries of hils_summarize_pages instead of [B, H_lm, C, d]."""
+        if self.landmark_mode == LM_MEAN:
+            return None
+        if self.landmark_mode == LM_SHARED:
+            return (self.H_lm, self.d)
+        return (items, self.H_lm, self.d) if items is not None else (self.B, self.H_lm, self.C, self.d)
 
 
 _lib = None
@@ -179,11 +193,19 @@ def _workspace(cfg: Config, which: int, device, ws: Optional[torch.Tensor], num_
     return torch.empty(need, dtype=torch.uint8, device=device), need
 
 
-def landmark_summarize(cfg: Config, k: torch.Tensor, q_lm: torch.Tensor, k_sum=None, b_sum=None):
-    """k [B,H_kv,N,d], q_lm [B,H_lm,C,d] -> (k_sum [B,H_lm,C,d], b_sum [B,H_lm,C] fp32)."""
+def _want_q_lm(cfg: Config, q_lm, dev, items=None):
+    shape = cfg.q_lm_shape(items)
+    if shape is None:
+        return None  # mean pooling: no landmark queries
+    _want(q_lm, "q_lm", shape, cfg.io_dtype, dev)
+    return q_lm
+
+
+def landmark_summarize(cfg: Config, k: torch.Tensor, q_lm: Optional[torch.Tensor], k_sum=None, b_sum=None):
+    """k [B,H_kv,N,d], q_lm per ``cfg.q_lm_shape()`` -> (k_sum [B,H_lm,C,d], b_sum [B,H_lm,C] fp32)."""
     dev = k.device
     _want(k, "k", (cfg.B, cfg.H_kv, cfg.N, cfg.d), cfg.io_dtype, dev)
-    _want(q_lm, "q_lm", (cfg.B, cfg.H_lm, cfg.C, cfg.d), cfg.io_dtype, dev)
+    q_lm = _want_q_lm(cfg, q_lm, dev)
     if k_sum is None:
         k_sum = torch.empty((cfg.B, cfg.H_lm, cfg.C, cfg.d), dtype=cfg.summary_dtype, device=dev)
     if b_sum is None:
@@ -295,7 +317,7 @@ def summarize_pages(cfg: Config, k_cache, q_lm, pages, ksum_cache, bsum_cache):
     P = k_cache.shape[0]
     n = pages.shape[0]
     _want(k_cache, "k_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
-    _want(q_lm, "q_lm", (n, cfg.H_lm, cfg.d), cfg.io_dtype, dev)
+    q_lm = _want_q_lm(cfg, q_lm, dev, items=n)
     _want(pages, "pages", (n,), torch.int32, dev)
     _want(ksum_cache, "ksum_cache", (P, cfg.H_lm, cfg.d), cfg.summary_dtype, dev)
     _want(bsum_cache, "bsum_cache", (P, cfg.H_lm), torch.float32, dev)

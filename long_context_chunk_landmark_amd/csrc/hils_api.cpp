@@ -68,6 +68,12 @@ hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
     s.C = s.S ? s.N / s.S : 0;
     s.CA = s.S ? (s.N + s.S - 1) / s.S : 0;
     if (need_seq && s.C > 8192) return fail(HILS_ERR_UNSUPPORTED, "N/S=%d chunks: supported up to 8192", s.C);
+    if (cfg->landmark_mode < HILS_LM_CHUNK || cfg->landmark_mode > HILS_LM_MEAN)
+        return fail(HILS_ERR_INVALID_ARG, "landmark_mode=%d unknown", cfg->landmark_mode);
+    if (cfg->agg_mode != HILS_AGG_MAX && cfg->agg_mode != HILS_AGG_NORMALIZED)
+        return fail(HILS_ERR_INVALID_ARG, "agg_mode=%d unknown", cfg->agg_mode);
+    s.lm_mode = cfg->landmark_mode;
+    s.agg_mode = cfg->agg_mode;
     s.io_bf16 = cfg->io_dtype == HILS_BF16;
     s.sum_bf16 = cfg->summary_dtype == HILS_BF16;
     s.scale = cfg->scale > 0.f ? cfg->scale : 1.0f / sqrtf((float)s.D);
@@ -134,7 +140,7 @@ extern "C" {
 
 const char *hils_last_error(void) { return g_err; }
 
-int hils_version(void) { return 10000; }
+int hils_version(void) { return 10100; }
 
 size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs, int32_t max_pages) {
     hils::Shape s;
@@ -160,9 +166,8 @@ hils_status_t hils_landmark_summarize(const hils_config_t *cfg, const void *k, c
     hils_status_t st = resolve(cfg, true, s);
     if (st) return st;
     if ((int64_t)s.B * s.H_lm * s.C == 0) return ok();
-    if ((st = check_ptr(k, "k")) || (st = check_ptr(q_lm, "q_lm")) || (st = check_ptr(k_sum, "k_sum")) ||
-        (st = check_ptr(b_sum, "b_sum")))
-        return st;
+    if ((st = check_ptr(k, "k")) || (st = check_ptr(k_sum, "k_sum")) || (st = check_ptr(b_sum, "b_sum"))) return st;
+    if (s.lm_mode != HILS_LM_MEAN && (st = check_ptr(q_lm, "q_lm"))) return st;
     return hip_status(hils::launch_landmark_summary(s, k, q_lm, k_sum, b_sum, nullptr, 0, stream),
                       "landmark summary launch");
 }
@@ -175,9 +180,10 @@ hils_status_t hils_summarize_pages(const hils_config_t *cfg, int32_t num_items, 
     if (st) return st;
     if (num_items < 0 || num_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_items, num_pages must be >= 0");
     if (num_items == 0 || num_pages == 0) return ok();
-    if ((st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(q_lm, "q_lm")) || (st = check_ptr(pages, "pages")) ||
+    if ((st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(pages, "pages")) ||
         (st = check_ptr(ksum_cache, "ksum_cache")) || (st = check_ptr(bsum_cache, "bsum_cache")))
         return st;
+    if (s.lm_mode != HILS_LM_MEAN && (st = check_ptr(q_lm, "q_lm"))) return st;
     // item b = one "sequence" of a single S-key chunk (page pages[b])
     s.B = num_items;
     s.N = s.S;
@@ -245,6 +251,8 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
     hils_status_t st = resolve(cfg, false, s);
     if (st) return st;
     if (num_seqs < 0 || max_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
+    if (s.agg_mode != HILS_AGG_MAX)
+        return fail(HILS_ERR_UNSUPPORTED, "hils_decode: agg_mode=%d not supported (max aggregation only)", s.agg_mode);
     if (num_seqs == 0) return ok();
     if (max_pages == 0) return fail(HILS_ERR_INVALID_ARG, "max_pages must be >= 1");
     if ((int64_t)max_pages > 65536) return fail(HILS_ERR_UNSUPPORTED, "max_pages=%d: supported up to 65536", max_pages);

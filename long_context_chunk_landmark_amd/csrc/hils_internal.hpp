@@ -20,6 +20,8 @@ struct Shape {
     int CA;     // ceil(N / S) chunks incl. a partial last one
     bool io_bf16, sum_bf16;
     float scale;
+    int lm_mode;   // landmark queries: 0 per chunk, 1 one shared per landmark head, 2 none (q' = 0)
+    int agg_mode;  // group aggregation: 0 max of s^, 1 max of s^ - LSE over the candidates
     // Paged prefill (q0 = 0, Nk = N, bt = null for the contiguous layout):
     // the N query rows are positions q0 .. q0 + N - 1 (q0 % S == 0) of
     // sequences whose keys 0 .. Nk - 1 = q0 + N - 1 live in a paged cache
@@ -51,6 +53,7 @@ struct ScoreWorkspace {
     int64_t per_bg;     // entries per (b, g)
     float *q_s;         // [B,H_q,N,D] Q-Cal scoring queries (fp32) or null
     float *bsum;        // [B,H_lm,C] b_sum gathered from the paged cache (paged prefill) or null
+    float *lse;         // [B,H_q,N] per-head log-sum-exp over the candidates (normalised aggregation) or null
 };
 int64_t score_agg_entries_per_bg(const Shape &s);
 size_t score_workspace_bytes(const Shape &s, bool qcal);

@@ -46,6 +46,7 @@ size_t score_workspace_bytes(const Shape &s, bool qcal) {
     b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
     if (qcal) b += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
     if (s.max_pages > 0) b += align_up((size_t)s.B * s.H_lm * s.C * 4, 256);  // paged: gathered b_sum
+    if (s.agg_mode == 1) b += align_up((size_t)s.B * s.H_q * s.N * 4, 256);    // per-head log-sum-exp
     return b;
 }
 
@@ -66,6 +67,8 @@ void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace
     ws.q_s = qcal ? (float *)p : nullptr;
     if (qcal) p += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
     ws.bsum = s.max_pages > 0 ? (float *)p : nullptr;
+    if (s.max_pages > 0) p += align_up((size_t)s.B * s.H_lm * s.C * 4, 256);
+    ws.lse = s.agg_mode == 1 ? (float *)p : nullptr;
 }
 
 // ------------------------------------------------------------ k' prep
@@ -308,12 +311,19 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 // elementwise, so by Cauchy-Schwarz |exact - approx| <= scale * kappa *
 // ||q_s|| * max_c ||k'_c|| with kappa (set by the launcher) adding those
 // terms to a bound on the fp32 accumulation.
-template <typename TQ, int D, int G, bool KSPLIT>
+//
+// AM selects what the block produces: 0 the group max of the approximate
+// scores; 1 (first pass of the normalised aggregation) each head's
+// log-sum-exp of its approximate scores over the row's candidates, into
+// lse [B, H_q, N]; 2 the group max of the scores minus those log-sum-exps.
+// The subtracted constant is the same in the exact pass, so E still bounds
+// |exact - approximate| of what is ranked.
+template <typename TQ, int D, int G, bool KSPLIT, int AM>
 __global__ __launch_bounds__(128 * G) void score_approx_kernel(
     const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const bf16 *__restrict__ ksb2,
     const float *__restrict__ b_sum, const float *__restrict__ knorm, float *__restrict__ agg_out,
     float *__restrict__ err_out, int N, int H_q, int H_kv, int H_lm, int C, int S, int W, int K, float scale,
-    float kappa, int64_t per_bg, int q0) {
+    float kappa, int64_t per_bg, int q0, float *__restrict__ lse) {
     constexpr bool QSPLIT = std::is_same<TQ, float>::value;
     constexpr int NQT = QSPLIT ? 2 : 1;   // query terms
     constexpr int NKT = KSPLIT ? 2 : 1;   // k' terms
@@ -360,7 +370,14 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
             }
         }
     }
-    if (e == 0) {
+    // normalised aggregation: this wave's head's log-sum-exp of its rows
+    float lsev[2] = {0.f, 0.f};
+    if constexpr (AM == 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) lsev[u] = lse[((int64_t)b * H_q + g * G + e) * N + iqc[u]];
+    }
+    float lm[2] = {-INFINITY, -INFINITY}, lz[2] = {0.f, 0.f};  // AM == 1: running max and sum
+    if (AM != 1 && e == 0) {
         // bound of the group score: the largest per-head bound of the group
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -455,7 +472,28 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) best[u][i] = fmaf(scale, acc[u][i], bt[e][4 * grp + i]);
+            for (int i = 0; i < 4; ++i) best[u][i] = fmaf(scale, acc[u][i], bt[e][4 * grp + i]) - lsev[u];
+        if constexpr (AM == 1) {
+            // running log-sum-exp over this lane's candidates c < n
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float v[4], tm = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = c0 + 4 * grp + i < n ? best[u][i] : -INFINITY;
+                    tm = fmaxf(tm, v[i]);
+                }
+                const float mn = fmaxf(lm[u], tm);
+                if (mn != -INFINITY) {
+                    float z = lz[u] * expf(lm[u] - mn);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z += expf(v[i] - mn);
+                    lz[u] = z;
+                    lm[u] = mn;
+                }
+            }
+            continue;
+        }
         if constexpr (G > 1) {
             if (e > 0) {
                 px[e - 1][qp][0][lane] = best[0];
@@ -477,6 +515,21 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 if (qvalid[u]) *(f32x4 *)(row[u] + c0 + 4 * grp) = best[u];
+        }
+    }
+    if constexpr (AM == 1) {
+        // combine the four lane groups holding a query's candidates
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float m = lm[u], z = lz[u];
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float mo = __shfl_xor(m, off, WAVE), zo = __shfl_xor(z, off, WAVE);
+                const float mn = fmaxf(m, mo);
+                z = (m == -INFINITY ? 0.f : z * expf(m - mn)) + (mo == -INFINITY ? 0.f : zo * expf(mo - mn));
+                m = mn;
+            }
+            if (qvalid[u] && grp == 0) lse[((int64_t)b * H_q + g * G + e) * N + iq[u]] = m + logf(z);
         }
     }
 }
@@ -533,7 +586,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
                                                      const float *__restrict__ err_in, int32_t *__restrict__ sel_idx,
                                                      float *__restrict__ sel_score, int B, int N, int H_q, int H_kv,
                                                      int H_lm, int C, int S, int W, int K, float scale,
-                                                     int64_t per_bg, int q0) {
+                                                     int64_t per_bg, int q0, const float *__restrict__ lse) {
     constexpr int GLM = SHARED ? 1 : G;
     constexpr int EPL = GLM * D / WAVE;   // elements of a survivor row per lane
     constexpr int LR = D / EPL;           // lanes covering one landmark row
@@ -570,6 +623,11 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 #pragma unroll
         for (int x = 0; x < EPL; ++x) qv[e][x] = to_f32(qr[x]);
     }
+    // normalised aggregation: each head's log-sum-exp over the candidates
+    // (from the approximate pass) is subtracted before the group max
+    float lsev[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) lsev[e] = (lse && n > K) ? lse[(b * H_q + (int64_t)g * G + e) * N + i] : 0.f;
     const float *kcm_g = kcm + bg * (int64_t)C * GLM * D;
     const float *bs_g = b_sum + (b * (int64_t)H_lm + (int64_t)g * GLM) * C;  // + e*C + c
 
@@ -662,7 +720,7 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
                         for (int x = 0; x < EPL; ++x) part = fmaf(qv[e][x], kx[u][x], part);
                         const float sc = fmaf(scale, group_sum<WAVE>(part), bb);
                         if (lane == 0) L.sc[slot][e] = sc;
-                        agg = fmaxf(agg, sc);
+                        agg = fmaxf(agg, sc - lsev[e]);
                     }
                 } else {
                     float part = 0.f;
@@ -670,7 +728,10 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
                     for (int x = 0; x < EPL; ++x) part = fmaf(qv[0][x], kx[u][x], part);
                     const float sc = fmaf(scale, group_sum<LR>(part), bs_g[(int64_t)el * C + c]);
                     if (lane % LR == 0) L.sc[slot][el] = sc;
-                    agg = sc;
+                    float sub = lsev[0];
+#pragma unroll
+                    for (int e = 1; e < G; ++e) sub = el == e ? lsev[e] : sub;
+                    agg = sc - sub;
 #pragma unroll
                     for (int m = LR; m < WAVE; m <<= 1) agg = fmaxf(agg, __shfl_xor(agg, m, WAVE));
                 }
@@ -786,17 +847,28 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 
 // ------------------------------------------------------------ launch
 
-template <typename TQ, int D, int G>
-static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
-                      hipStream_t st) {
+template <typename TQ, int D, int G, int AM>
+static void go_approx_m(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
+                        hipStream_t st) {
     const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(128 * G);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const bf16 *)ws.ksb, (const bf16 *)ws.ksb2, b_sum,
                            ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
-                           ws.per_bg, s.q0);
+                           ws.per_bg, s.q0, ws.lse);
     };
-    if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false>);
-    else go(score_approx_kernel<TQ, D, G, true>);
+    if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false, AM>);
+    else go(score_approx_kernel<TQ, D, G, true, AM>);
+}
+
+template <typename TQ, int D, int G>
+static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
+                      hipStream_t st) {
+    if (s.agg_mode == 1) {
+        go_approx_m<TQ, D, G, 1>(s, qv, b_sum, ws, kappa, st);  // per-head log-sum-exp
+        go_approx_m<TQ, D, G, 2>(s, qv, b_sum, ws, kappa, st);  // normalised group max
+    } else {
+        go_approx_m<TQ, D, G, 0>(s, qv, b_sum, ws, kappa, st);
+    }
 }
 
 template <typename TQ>
@@ -821,7 +893,7 @@ static void go_select(const Shape &s, const TQ *qv, const float *b_sum, const Sc
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const float *)ws.kcm, b_sum, (const float *)ws.agg,
                            (const float *)ws.err, sel_idx, sel_score, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W,
-                           s.K, s.scale, ws.per_bg, s.q0);
+                           s.K, s.scale, ws.per_bg, s.q0, (const float *)ws.lse);
     };
     if (s.GLM == 1 && G > 1) go(select_kernel<TQ, D, G, true>);
     else go(select_kernel<TQ, D, G, false>);

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
                                                                TS *__restrict__ k_sum, float *__restrict__ b_sum,
                                                                int H_kv, int N, int C, float scale,
                                                                int64_t total_units, const int32_t *__restrict__ pages,
-                                                               int num_pages) {
+                                                               int num_pages, int lm_mode) {
     constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
     constexpr int LPR = D / E;         // lanes covering one key row
     constexpr int RPL = WAVE / LPR;    // key rows per wave-wide load
@@ -56,7 +56,10 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
     for (int e = 0; e < GLM; ++e) {
         const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;   // landmark query
         const int64_t orow = (pb * H_lm + (int64_t)g * GLM + e) * C + c;  // summary
-        const Vec16<T> qv = load16(q_lm + lrow * D + col * E);
+        // landmark query: per chunk, shared by all chunks of head l, or zero
+        Vec16<T> qv;
+        if (lm_mode == 2) qv = Vec16<T>{};
+        else qv = load16(q_lm + (lm_mode == 1 ? (int64_t)g * GLM + e : lrow) * D + col * E);
         float a[NL];
         float m = -INFINITY;
 #pragma unroll
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
 template <typename TS, int S, int GLM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void landmark_summary_d128_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ q_lm, TS *__restrict__ k_sum, float *__restrict__ b_sum,
-    int H_kv, int N, int C, float scale, int64_t total_units, const int32_t *__restrict__ pages, int num_pages) {
+    int H_kv, int N, int C, float scale, int64_t total_units, const int32_t *__restrict__ pages, int num_pages,
+    int lm_mode) {
     constexpr int D = 128, NB = S / 64;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ float p_lds[4][4][S / 4];  // [wave of block][rsub][block * 16 + t]
@@ -146,7 +150,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
     for (int e = 0; e < GLM; ++e) {
         const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;   // landmark query
         const int64_t orow = (pb * H_lm + (int64_t)g * GLM + e) * C + c;  // summary
-        const u32x4 qr = *(const u32x4 *)(q_lm + lrow * D + col * 8);
+        // landmark query: per chunk, shared by all chunks of head l, or zero
+        const u32x4 qr = lm_mode == 2 ? u32x4{0u, 0u, 0u, 0u}
+                                      : *(const u32x4 *)(q_lm + (lm_mode == 1 ? (int64_t)g * GLM + e : lrow) * D +
+                                                         col * 8);
         float lg[NB];
 #pragma unroll
         for (int blk = NB - 1; blk >= 0; --blk) {
@@ -231,7 +238,7 @@ static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const T *)k, (const T *)q_lm, (TS *)k_sum, b_sum, s.H_kv, s.N,
-                           s.C, s.scale, units, pages, num_pages);
+                           s.C, s.scale, units, pages, num_pages, s.lm_mode);
     };
     if constexpr (std::is_same<T, bf16>::value && D == 128) {
         switch (s.GLM) {

@@ -52,7 +52,8 @@ def config(name_or_params, **overrides) -> Config:
     p.update(overrides)
     return Config(H_q=p["H_q"], H_kv=p["H_kv"], d=p["d"], S=p["S"], W=p["W"], K=p["K"], B=p.get("B", 1),
                   N=p.get("N", 0), H_lm=p.get("H_lm"), M=p.get("M", 4), io_dtype=p.get("io", torch.bfloat16),
-                  summary_dtype=p.get("summary", torch.float32))
+                  summary_dtype=p.get("summary", torch.float32), landmark_mode=p.get("landmark_mode", 0),
+                  agg_mode=p.get("agg_mode", 0))
 
 
 def _randn(gen, shape, device, dtype, std=1.0):
@@ -137,7 +138,13 @@ def make_prefill(name_or_params, device="cuda", **overrides):
         w_down = _randn(gen, (r, dm), gdev, dt, std=1.0 / math.sqrt(dm))
         w_up = _randn(gen, (cfg.H_q * cfg.d, r), gdev, dt, std=1.0 / math.sqrt(dm))
         out["qcal"] = tuple(x.to(device) for x in (h, w_down, w_up))
-    out.update(q=q.to(device), k=k.to(device), v=v.to(device), q_lm=q_lm.to(device))
+    # landmark-free variant: one query per landmark head (the first chunk's
+    # draw); mean pooling: none
+    if cfg.landmark_mode == 1:
+        q_lm = q_lm[0, :, 0].contiguous()
+    elif cfg.landmark_mode == 2:
+        q_lm = None
+    out.update(q=q.to(device), k=k.to(device), v=v.to(device), q_lm=None if q_lm is None else q_lm.to(device))
     return out
 
 

@@ -97,10 +97,11 @@ def oracle_prefill(cfg, inputs, rows=None, k_sum=None, b_sum=None, given_sel=Non
     its summaries as stored (fp64 values rounded to bf16), like the decode
     step reads its cache; res["k_sum_exact"] keeps the unrounded values."""
     oc = cfg.oracle_dict()
-    q, k, v, q_lm = (host(inputs[n]) for n in ("q", "k", "v", "q_lm"))
+    q, k, v = (host(inputs[n]) for n in ("q", "k", "v"))
+    q_lm = None if inputs.get("q_lm") is None else host(inputs["q_lm"])
     exact = None
     if k_sum is None:
-        k_sum, b_sum = oracle.summarize(oc, k, q_lm)
+        k_sum, b_sum = oracle.summarize(oc, k, q_lm, landmark=oracle.LANDMARK_MODES[cfg.landmark_mode])
         exact = k_sum
         if cfg.summary_dtype == torch.bfloat16:
             k_sum = round_to(k_sum, torch.bfloat16).to(torch.float64).numpy()

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert hils.version() == 10000
+    assert hils.version() == 10100
 
 
 def _cfg(**kw):
@@ -211,3 +211,23 @@ def test_summarize_pages_argument_checks(lib):
     assert f(ctypes.byref(cfg), 4, A, 100, MIS, A, A, A, None) == hb.HILS_ERR_INVALID_ARG
     assert f(ctypes.byref(_cfg(d=96)), 4, A, 100, A, A, A, A, None) == hb.HILS_ERR_UNSUPPORTED
     assert f(ctypes.byref(cfg), 0, None, 100, None, None, None, None, None) == hb.HILS_OK
+
+
+def test_variant_modes_are_validated(lib):
+    for field, bad in (("landmark_mode", 3), ("landmark_mode", -1), ("agg_mode", 2)):
+        cfg = _cfg()
+        setattr(cfg, field, bad)
+        assert _summ(lib, cfg) == hb.HILS_ERR_INVALID_ARG and field in hb.last_error()
+    # per-chunk and shared landmark queries need q_lm; mean pooling does not
+    for mode in (hb.LM_CHUNK, hb.LM_SHARED):
+        cfg = _cfg(landmark_mode=mode)
+        assert _summ(lib, cfg, q_lm=None) == hb.HILS_ERR_INVALID_ARG and "q_lm" in hb.last_error()
+    # the decode step ranks by the max aggregation only
+    cfg = _cfg(agg_mode=hb.AGG_NORMALIZED)
+    st = lib.hils_decode(ctypes.byref(cfg), 2, A, A, A, A, A, A, 10, A, None, None, None, 0, 0, A, None, None, A2,
+                         1 << 20, None)
+    assert st == hb.HILS_ERR_UNSUPPORTED and "agg_mode" in hb.last_error()
+    # the normalised aggregation keeps a per-head log-sum-exp in the score workspace
+    a = lib.hils_workspace_size(ctypes.byref(_cfg()), hb.WS_SCORE, 0, 0)
+    b = lib.hils_workspace_size(ctypes.byref(_cfg(agg_mode=hb.AGG_NORMALIZED)), hb.WS_SCORE, 0, 0)
+    assert b == a + 8 * 4096 * 4

@@ -45,6 +45,13 @@ def _empty_summary_cache(cfg, P, dev, fill=0.0):
     return ks, bs
 
 
+def _item_queries(cfg, q_lm, bb, cc):
+    """Landmark queries of the items (b, c) for the configured landmark mode."""
+    if cfg.landmark_mode == hb.LM_CHUNK:
+        return q_lm[bb, :, cc].contiguous()
+    return q_lm  # one shared query per head, or none (mean pooling)
+
+
 def _summarize_all(cfg, inp, dev):
     """GPU summaries of every completed chunk, written at their pages."""
     C = cfg.C
@@ -54,7 +61,7 @@ def _summarize_all(cfg, inp, dev):
         bb = torch.arange(cfg.B, device=dev).repeat_interleave(C)
         cc = torch.arange(C, device=dev).repeat(cfg.B)
         pages = inp["block_table"][bb, cc].contiguous()
-        hb.summarize_pages(cfg, inp["k_cache"], inp["q_lm"][bb, :, cc].contiguous(), pages, ks, bs)
+        hb.summarize_pages(cfg, inp["k_cache"], _item_queries(cfg, inp["q_lm"], bb, cc), pages, ks, bs)
     return ks, bs
 
 
@@ -65,6 +72,8 @@ SUMMARY_CASES = {
     "d128_s128_bf16sum": dict(seed=62, io=BF, B=1, H_q=8, H_kv=2, d=128, N=2048, S=128, W=0, K=0, summary=BF),
     "d64_lmkv": dict(seed=63, io=BF, B=2, H_q=8, H_kv=2, H_lm=2, d=64, N=1024, S=64, W=0, K=0),
     "fp32io_s128": dict(seed=64, io=F32, B=1, H_q=4, H_kv=2, d=64, N=1024, S=128, W=0, K=0),
+    "shared_d128": dict(seed=65, io=BF, B=2, H_q=8, H_kv=2, d=128, N=1024, S=64, W=0, K=0, landmark_mode=1),
+    "mean_d64_s128": dict(seed=66, io=BF, B=1, H_q=4, H_kv=2, d=64, N=1024, S=128, W=0, K=0, landmark_mode=2),
 }
 
 
@@ -82,12 +91,15 @@ def test_summarize_pages_matches_oracle(name, dev):
     order = torch.randperm(cfg.B * C, generator=torch.Generator().manual_seed(p["seed"]))
     bb, cc = order // C, order % C
     pages = torch.cat([bt.cpu()[bb, cc], torch.tensor([-1, P], dtype=torch.int32)]).to(torch.int32)
-    q_items = inp["q_lm"][bb.to(dev), :, cc.to(dev)]
-    q_items = torch.cat([q_items, q_items[:2]]).contiguous()
+    q_items = inp["q_lm"]
+    if cfg.landmark_mode == hb.LM_CHUNK:
+        q_items = inp["q_lm"][bb.to(dev), :, cc.to(dev)]
+        q_items = torch.cat([q_items, q_items[:2]]).contiguous()
     ks, bs = _empty_summary_cache(cfg, P, dev, fill=7.0)
     hb.summarize_pages(cfg, kc, q_items, pages.to(dev), ks, bs)
     torch.cuda.synchronize()
-    rk, rb = oracle.summarize_pages(cfg.oracle_dict(), host(kc), host(q_items), pages.numpy())
+    rk, rb = oracle.summarize_pages(cfg.oracle_dict(), host(kc), None if q_items is None else host(q_items),
+                                    pages.numpy(), landmark=oracle.LANDMARK_MODES[cfg.landmark_mode])
     n = len(order)
     assert np.isnan(rk[n:]).all()
     idx = pages[:n].long()
@@ -129,6 +141,8 @@ PAGED_CASES = {
     "fp32io": (dict(seed=75, io=F32, B=1, H_q=4, H_kv=2, d=64, S=64, W=128, K=4), 640, 500),
     "lmkv": (dict(seed=76, io=BF, B=1, H_q=8, H_kv=2, H_lm=2, d=128, S=64, W=128, K=8), 4096, 333),
     "k0": (dict(seed=77, io=BF, B=1, H_q=4, H_kv=1, d=128, S=64, W=128, K=0), 512, 400),
+    "aggnorm_lmshared": (dict(seed=79, io=BF, B=1, H_q=8, H_kv=2, d=128, S=64, W=256, K=8, agg_mode=1,
+                              landmark_mode=1), 1024, 900),
 }
 
 
@@ -157,7 +171,8 @@ def test_prefill_paged_matches_oracle(name, dev):
     # oracle: its own summaries of the contiguous sequence, stored in the
     # summary dtype at the same pages
     oc_full = cfg_full.oracle_dict()
-    rk, rb = oracle.summarize(oc_full, host(inp["k"]), host(inp["q_lm"]))
+    rk, rb = oracle.summarize(oc_full, host(inp["k"]), None if inp["q_lm"] is None else host(inp["q_lm"]),
+                              landmark=oracle.LANDMARK_MODES[cfg.landmark_mode])
     P = inp["k_cache"].shape[0]
     ksc = np.zeros((P, cfg.H_lm, cfg.d), np.float32)
     bsc = np.zeros((P, cfg.H_lm), np.float32)
@@ -191,7 +206,7 @@ def test_prefill_paged_matches_oracle(name, dev):
     assert_close(host(lse).numpy(), refl, atol, rtol, "lse")
 
 
-@pytest.mark.parametrize("name", ["mid_ragged_b2", "s128_qcal", "g8_bf16sum_d64"])
+@pytest.mark.parametrize("name", ["mid_ragged_b2", "s128_qcal", "g8_bf16sum_d64", "aggnorm_lmshared"])
 def test_prefill_paged_equals_prefill_rows(name, dev):
     """Chunked prefill over the paged cache reproduces rows q_start.. of the
     whole-sequence prefill bitwise (same summaries, selections, outputs)."""

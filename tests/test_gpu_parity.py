@@ -48,6 +48,18 @@ CASES = {
     "s128_g2": dict(seed=34, io=BF, B=1, H_q=4, H_kv=2, d=128, N=6000, S=128, W=128, K=32),
     "g1_k128_s64": dict(seed=39, io=BF, B=1, H_q=2, H_kv=2, d=128, N=9000, S=64, W=128, K=128),
     "g1_k128_s128": dict(seed=40, io=BF, B=1, H_q=1, H_kv=1, d=128, N=20000, S=128, W=256, K=128),
+    # variants: one shared landmark query per head (landmark-free), mean pooling (q' = 0),
+    # normalised-weight group aggregation (both select paths, Q-Cal, fp32, bf16 summaries)
+    "lm_shared_b2": dict(seed=81, io=BF, B=2, H_q=8, H_kv=2, d=128, N=3000, S=64, W=256, K=8, landmark_mode=1),
+    "lm_mean_s128_d64": dict(seed=82, io=BF, B=1, H_q=4, H_kv=2, d=64, N=2600, S=128, W=256, K=6, landmark_mode=2),
+    "lm_shared_fp32": dict(seed=83, io=F32, B=1, H_q=2, H_kv=1, d=64, N=1000, S=64, W=64, K=3, landmark_mode=1),
+    "aggnorm_g4": dict(seed=84, io=BF, B=1, H_q=8, H_kv=2, d=128, N=4096, S=64, W=256, K=8, agg_mode=1),
+    "aggnorm_g8_bf16sum": dict(seed=85, io=BF, B=1, H_q=8, H_kv=1, d=64, N=3000, S=64, W=128, K=6, summary=BF,
+                               agg_mode=1),
+    "aggnorm_lmkv": dict(seed=86, io=BF, B=1, H_q=8, H_kv=2, H_lm=2, d=128, N=3000, S=64, W=128, K=8, agg_mode=1),
+    "aggnorm_qcal": dict(seed=87, io=BF, B=1, H_q=4, H_kv=1, d=128, N=2500, S=128, W=256, K=4, d_model=256, r=16,
+                         agg_mode=1),
+    "aggnorm_fp32": dict(seed=88, io=F32, B=1, H_q=4, H_kv=2, d=64, N=1500, S=64, W=128, K=4, agg_mode=1),
 }
 
 
