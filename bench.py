@@ -249,6 +249,58 @@ def bench_serving(args, torch, hb, W, pre):
                               "tflops": fl / (ms_p * 1e-3) / 1e12, "flops": fl}}
 
 
+def bench_variants(args, torch, hb, W, pre):
+    """The method's variants on the prefill workload: summaries with one
+    shared landmark query per head and with mean pooling (q' = 0), and
+    score/select with the normalised-weight group aggregation."""
+    import dataclasses
+
+    dev = torch.device("cuda:0")
+    inp = pre["inp"]
+    cfg = pre["cfg"]
+    C = cfg.C
+    k_sum = torch.empty((cfg.B, cfg.H_lm, C, cfg.d), dtype=cfg.summary_dtype, device=dev)
+    b_sum = torch.empty((cfg.B, cfg.H_lm, C), dtype=torch.float32, device=dev)
+    shared_q = inp["q_lm"][0, :, 0].contiguous() if inp["q_lm"] is not None else None
+    c_shared = dataclasses.replace(cfg, landmark_mode=hb.LM_SHARED)
+    c_mean = dataclasses.replace(cfg, landmark_mode=hb.LM_MEAN)
+    c_norm = dataclasses.replace(cfg, agg_mode=hb.AGG_NORMALIZED)
+    qcal = inp.get("qcal")
+    sel = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.K), dtype=torch.int32, device=dev)
+    ss = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.K), dtype=torch.float32, device=dev)
+    ws = torch.empty(hb.workspace_size(c_norm, hb.WS_SCORE_QCAL if qcal else hb.WS_SCORE), dtype=torch.uint8,
+                     device=dev)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step():
+        e = [E() for _ in range(4)]
+        e[0].record()
+        hb.landmark_summarize(c_shared, inp["k"], shared_q, k_sum, b_sum)
+        e[1].record()
+        hb.landmark_summarize(c_mean, inp["k"], None, k_sum, b_sum)
+        e[2].record()
+        hb.score_select(c_norm, inp["q"], k_sum, b_sum, qcal=qcal, sel_idx=sel, sel_score=ss, workspace=ws)
+        e[3].record()
+        return {"summary_shared": (e[0], e[1]), "summary_mean": (e[1], e[2]), "score_select_normalized": (e[2], e[3])}
+
+    _, per = _timed(step, max(1, args.steps // 2), 1, torch)
+    io_b = 2 if cfg.io_dtype == torch.bfloat16 else 4
+    sum_b = 2 if cfg.summary_dtype == torch.bfloat16 else 4
+    # shared: the landmark queries shrink to one row per head; mean: none
+    by_shared = summary_bytes(cfg, io_b, sum_b) - cfg.B * cfg.H_lm * C * cfg.d * io_b + cfg.H_lm * cfg.d * io_b
+    by_mean = summary_bytes(cfg, io_b, sum_b) - cfg.B * cfg.H_lm * C * cfg.d * io_b
+    fl = score_flops(cfg)
+    out = {}
+    for name, by in (("summary_shared", by_shared), ("summary_mean", by_mean)):
+        ms = per[name]
+        out[name] = {"ms": ms, "bound": "hbm", "gbs": by / (ms * 1e-3) / 1e9,
+                     "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by}
+    ms = per["score_select_normalized"]
+    out["score_select_normalized"] = {"ms": ms, "bound": "mfma", "tflops": fl / (ms * 1e-3) / 1e12,
+                                      "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl}
+    return out
+
+
 def union_overlap(sel, M, sample=4096, seed=0):
     """Mean |union of the selections of M adjacent queries| / K over a sample
     of groups (1 = identical selections, M = disjoint)."""
@@ -310,6 +362,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_512k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-serving", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -369,6 +422,9 @@ def main():
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }
+    if not args.no_variants:
+        print("[bench] variants: shared / mean landmarks, normalised aggregation", file=sys.stderr, flush=True)
+        result["variants"] = bench_variants(args, torch, hb, W, pre)
     if not args.no_serving:
         print(f"[bench] serving: paged summaries + chunked prefill of {args.chunk} tokens", file=sys.stderr,
               flush=True)
