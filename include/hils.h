@@ -114,7 +114,8 @@ enum {
     HILS_WS_SCORE = 0,      /* hils_score_select without Q-Cal            */
     HILS_WS_SCORE_QCAL = 1, /* hils_score_select with Q-Cal               */
     HILS_WS_FUSED = 2,      /* hils_sparse_attend_fused                   */
-    HILS_WS_DECODE = 3      /* hils_decode                                */
+    HILS_WS_DECODE = 3,     /* hils_decode                                */
+    HILS_WS_BACKWARD = 4    /* hils_sparse_attend_backward                */
 };
 
 /* Landmark summary (compressed keys).  For every completed chunk c and
@@ -253,6 +254,28 @@ hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, cons
  * the configuration is rejected). */
 size_t hils_prefill_paged_workspace_size(const hils_config_t *cfg, int32_t q_start, int32_t max_pages,
                                          int32_t with_qcal);
+
+/* Gradients of the fused forward (hils_landmark_summarize ->
+ * hils_score_select -> hils_sparse_attend_fused) with the selection held
+ * fixed, for the loss sum(dout * out) + sum(dlse * lse) (hyper.ai summary,
+ * 方法: the factorised attention weight makes the chunk scores, and through
+ * them the landmark summaries, differentiable; the top-K choice is not).
+ * The scoring query is q (Q-Cal's parameters get no gradient here).
+ *   q, k, v, dout: as in the forward, io_dtype; lse [B,H_q,N] fp32 and
+ *   sel_idx / sel_score: the forward's outputs (dout.out is formed from
+ *   the recomputed weights, so out itself is not read); k_sum [B,H_lm,C,d] fp32
+ *   (summary_dtype must be F32); q_lm as for hils_landmark_summarize
+ *   (HILS_LM_CHUNK or HILS_LM_MEAN; HILS_LM_SHARED is unsupported);
+ *   dlse [B,H_q,N] fp32 or NULL (zero).
+ *   dq [B,H_q,N,d], dk, dv [B,H_kv,N,d], dq_lm [B,H_lm,C,d]: fp32, written
+ *   (dq_lm unused, may be NULL, with HILS_LM_MEAN).
+ *   workspace: hils_workspace_size(cfg, HILS_WS_BACKWARD, 0, 0) bytes.
+ * G <= 8.  Deterministic (no atomics). */
+hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                          const void *q_lm, const float *k_sum, const int32_t *sel_idx,
+                                          const float *sel_score, const float *lse, const void *dout,
+                                          const float *dlse, float *dq, float *dk, float *dv, float *dq_lm,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace the given call needs (0 if none); 0 with
  * hils_last_error() set when the configuration is rejected.  num_seqs and

@@ -22,7 +22,7 @@ HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ER
 HILS_F32, HILS_BF16 = 0, 1
 LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
 AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
-WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE = range(4)
+WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD = range(5)
 
 # Every symbol include/hils.h declares.
 EXPORTED_SYMBOLS = (
@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "hils_summarize_pages",
     "hils_prefill_paged",
     "hils_prefill_paged_workspace_size",
+    "hils_sparse_attend_backward",
     "hils_workspace_size",
     "hils_last_error",
     "hils_version",
@@ -131,12 +132,13 @@ def load_library(path: str = LIB_PATH):
                                        vp, vp, sz, vp]
     lib.hils_prefill_paged_workspace_size.argtypes = [cfgp, i32, i32, i32]
     lib.hils_prefill_paged_workspace_size.restype = sz
+    lib.hils_sparse_attend_backward.argtypes = [cfgp] + [vp] * 15 + [sz, vp]
     lib.hils_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32]
     lib.hils_workspace_size.restype = sz
     lib.hils_last_error.restype = ctypes.c_char_p
     lib.hils_version.restype = ctypes.c_int
     for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode",
-               "hils_summarize_pages", "hils_prefill_paged"):
+               "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -377,6 +379,34 @@ def prefill_paged(cfg: Config, q_start: int, q, k_cache, v_cache, ksum_cache, bs
                                              _ptr(h), _ptr(wd), _ptr(wu), d_model, r, _ptr(sel_idx), _ptr(sel_score),
                                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
     return out, lse, sel_idx, sel_score
+
+
+def sparse_attend_backward(cfg: Config, q, k, v, q_lm, k_sum, sel_idx, sel_score, lse, dout, dlse=None,
+                           workspace=None):
+    """Gradients of sum(dout*out) + sum(dlse*lse) with the selection fixed -> (dq, dk, dv, dq_lm), fp32."""
+    dev = q.device
+    _want(q, "q", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(k, "k", (cfg.B, cfg.H_kv, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(v, "v", (cfg.B, cfg.H_kv, cfg.N, cfg.d), cfg.io_dtype, dev)
+    q_lm = _want_q_lm(cfg, q_lm, dev)
+    _want(k_sum, "k_sum", (cfg.B, cfg.H_lm, cfg.C, cfg.d), torch.float32, dev)
+    _want(sel_idx, "sel_idx", (cfg.B, cfg.H_kv, cfg.N, cfg.K), torch.int32, dev)
+    _want(sel_score, "sel_score", (cfg.B, cfg.H_q, cfg.N, cfg.K), torch.float32, dev)
+    _want(lse, "lse", (cfg.B, cfg.H_q, cfg.N), torch.float32, dev)
+    _want(dout, "dout", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    if dlse is not None:
+        _want(dlse, "dlse", (cfg.B, cfg.H_q, cfg.N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.d), **f32)
+    dk = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.d), **f32)
+    dv = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.d), **f32)
+    dq_lm = torch.empty((cfg.B, cfg.H_lm, cfg.C, cfg.d), **f32) if cfg.landmark_mode == LM_CHUNK else None
+    ws, nbytes = _workspace(cfg, WS_BACKWARD, dev, workspace)
+    c = cfg.to_c()
+    _check(load_library().hils_sparse_attend_backward(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(q_lm), _ptr(k_sum), _ptr(sel_idx), _ptr(sel_score),
+        _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dq_lm), _ptr(ws), nbytes, _stream()))
+    return dq, dk, dv, dq_lm
 
 
 def prefill(cfg: Config, q, k, v, q_lm, qcal=None):

@@ -150,6 +150,7 @@ size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs
         case HILS_WS_SCORE: return hils::score_workspace_bytes(s, false);
         case HILS_WS_SCORE_QCAL: return hils::score_workspace_bytes(s, true);
         case HILS_WS_FUSED: return hils::fused_workspace_bytes(s);
+        case HILS_WS_BACKWARD: return hils::backward_workspace_bytes(s);
         case HILS_WS_DECODE:
             if (num_seqs < 0 || max_pages < 0) {
                 fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
@@ -277,6 +278,37 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
                                           max_pages, seq_lens, 0, h, w_down, w_up, d_model, r, out, lse, sel_idx,
                                           workspace, stream),
                       "decode launch");
+}
+
+hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                          const void *q_lm, const float *k_sum, const int32_t *sel_idx,
+                                          const float *sel_score, const float *lse, const void *dout,
+                                          const float *dlse, float *dq, float *dk, float *dv, float *dq_lm,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if (s.sum_bf16) return fail(HILS_ERR_UNSUPPORTED, "backward: summary_dtype must be F32");
+    if (s.lm_mode == HILS_LM_SHARED) return fail(HILS_ERR_UNSUPPORTED, "backward: landmark_mode SHARED not supported");
+    if (s.G > 8) return fail(HILS_ERR_UNSUPPORTED, "backward: G=%d, supported up to 8", s.G);
+    if ((int64_t)s.B * s.N == 0) return ok();
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(lse, "lse")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(dq, "dq")) ||
+        (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
+        return st;
+    if (s.K > 0 && ((st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))) return st;
+    if (s.C > 0 && ((st = check_ptr(k_sum, "k_sum")) || (s.lm_mode == HILS_LM_CHUNK && (st = check_ptr(q_lm, "q_lm"))) ||
+                    (s.lm_mode == HILS_LM_CHUNK && (st = check_ptr(dq_lm, "dq_lm")))))
+        return st;
+    if (dlse && !aligned16(dlse)) return fail(HILS_ERR_INVALID_ARG, "dlse is not 16-byte aligned");
+    const size_t need = hils::backward_workspace_bytes(s);
+    if (!workspace || workspace_bytes < need)
+        return fail(HILS_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(hils::launch_backward(s, q, k, v, q_lm, k_sum, sel_idx, sel_score, lse, dout, dlse, dq, dk, dv,
+                                            dq_lm, workspace, stream),
+                      "backward launch");
 }
 
 size_t hils_prefill_paged_workspace_size(const hils_config_t *cfg, int32_t q_start, int32_t max_pages,

@@ -81,6 +81,13 @@ hipError_t launch_decode(const Shape &s, int num_seqs, const void *q, const void
                          const void *w_up, int d_model, int r, void *out, float *lse, int32_t *sel_idx,
                          void *workspace, hipStream_t st);
 
+// ---- backward of the fused attention (fixed selection), incl. the summary
+size_t backward_workspace_bytes(const Shape &s);
+hipError_t launch_backward(const Shape &s, const void *q, const void *k, const void *v, const void *q_lm,
+                           const float *k_sum, const int32_t *sel_idx, const float *sel_score, const float *lse,
+                           const void *dout, const float *dlse, float *dq, float *dk, float *dv, float *dq_lm,
+                           void *workspace, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace hils
