@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 METRIC = "HiLS prefill tokens/s @128K + decode μs/step @512K; % MFMA/HBM peak"
 CSRC = os.path.join(ROOT, "long_context_chunk_landmark_amd", "csrc")
 
@@ -301,6 +302,37 @@ def bench_variants(args, torch, hb, W, pre):
     return out
 
 
+def bench_backward(args, torch, hb, pre):
+    """hils_sparse_attend_backward on the prefill workload (gradients of a
+    random output / log-partition gradient, the forward's selection)."""
+    dev = torch.device("cuda:0")
+    inp = pre["inp"]
+    cfg = pre["cfg"]
+    fw = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    dout = torch.randn(fw["out"].shape, generator=g, device=dev).to(cfg.io_dtype)
+    dlse = torch.randn(fw["lse"].shape, generator=g, device=dev)
+    ws = torch.empty(hb.workspace_size(cfg, hb.WS_BACKWARD), dtype=torch.uint8, device=dev)
+
+    def step():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        hb.sparse_attend_backward(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"], fw["k_sum"], fw["sel_idx"],
+                                  fw["sel_score"], fw["lse"], dout, dlse, workspace=ws)
+        e1.record()
+        return {"backward": (e0, e1)}
+
+    _, per = _timed(step, args.backward_steps, 1, torch)
+    ms = per["backward"]
+    # QK^T recompute, dO V^T, dV, dQ, dK: 2.5x the forward's attention FLOPs
+    fl = 2.5 * attend_flops(cfg)
+    del fw, dout, dlse, ws
+    return {"ms": ms, "bound": "alu", "tflops": fl / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VALU_TFLOPS,
+            "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_VALU_TFLOPS, "flops": fl,
+            "tokens_per_s": cfg.B * cfg.N / (ms * 1e-3)}
+
+
 def union_overlap(sel, M, sample=4096, seed=0):
     """Mean |union of the selections of M adjacent queries| / K over a sample
     of groups (1 = identical selections, M = disjoint)."""
@@ -363,6 +395,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-serving", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=2)
     ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -422,6 +456,9 @@ def main():
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        result["backward"] = bench_backward(args, torch, hb, pre)
     if not args.no_variants:
         print("[bench] variants: shared / mean landmarks, normalised aggregation", file=sys.stderr, flush=True)
         result["variants"] = bench_variants(args, torch, hb, W, pre)

@@ -17,8 +17,9 @@
 //   dq' = scale sum_j da_j k_j, dk_j += p_j dk' + scale da_j q'.
 //
 // Two kernels, deterministic (every sum has one owner, no atomics):
-//   bwd_rows   one wave per (b, query head, row): dq, and per selected slot
-//              ds^, the chunk's log-weight m = s^ - L - lse_c and g = dO.o_c
+//   bwd_rows   one block per (b, kv head, row), a wave per query head of
+//              the group: dq, and per selected slot ds^, the chunk's
+//              log-weight m = s^ - L - lse_c and g = dO.o_c
 //   bwd_keys   one block per (b, kv head, chunk): dk, dv of the chunk's keys
 //              from the window rows and the rows that selected it (found by
 //              a binary search in each later row's ascending selection),
@@ -45,85 +46,126 @@ __device__ __forceinline__ float dot_row(const float *__restrict__ x, const T *_
     return acc;
 }
 
-// One wave per (b, h, i).  D = dO.o is formed in the same pass from the
-// recomputed fp32 weights (D = sum_j P_j dO.v_j), not from the stored
-// output, so the rounding of a bf16 output does not enter the gradients.
-// Every term of dq that carries D is split off: dq = scale (A - D' Bv) with
-// A = sum_window P_j (dO.v_j) k_j + sum_c [sum_j w_c p_j (dO.v_j - g_c) k_j
-// + w_c g_c k'_c] and Bv = sum_window P_j k_j + sum_c w_c k'_c, D' = D - dlse.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_rows_kernel(
+// One block per (b, kv head g, row i), one wave per query head of the
+// group: the G heads share the row's window and selection, so each tile of
+// S keys (and values) is staged in LDS once for all of them.  D = dO.o is
+// formed in the same pass from the recomputed fp32 weights (D = sum_j P_j
+// dO.v_j), not from the stored output, so the rounding of a bf16 output
+// does not enter the gradients.  Every term of dq that carries D is split
+// off: dq = scale (A - D' Bv) with A = sum_window P_j (dO.v_j) k_j +
+// sum_c [sum_j w_c p_j (dO.v_j - g_c) k_j + w_c g_c k'_c] and Bv =
+// sum_window P_j k_j + sum_c w_c k'_c, D' = D - dlse.
+template <typename T, int D, int S, int G>
+__global__ __launch_bounds__(64 * G) void bwd_rows_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ k_sum,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, const float *__restrict__ lse,
     const T *__restrict__ dout, const float *__restrict__ dlse, float *__restrict__ dq, float *__restrict__ dsel,
-    float *__restrict__ mlog, float *__restrict__ gdo, float *__restrict__ dcoef, int B, int N, int H_q, int H_kv,
-    int H_lm, int C, int S, int W, int K, float scale) {
-    constexpr int DPL = D / WAVE;  // dims per lane (1 or 2)
-    __shared__ float q_l[4][D];
-    __shared__ float do_l[4][D];
-    __shared__ float ca_l[4][128];  // per-key coefficient of A
-    __shared__ float cb_l[4][128];  // per-key coefficient of Bv
-    const int wave = threadIdx.x / WAVE, lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;  // (b*H_q + h)*N + i
-    if (row >= (int64_t)B * H_q * N) return;
-    const int i = (int)(row % N);
-    const int64_t bh = row / N;
-    const int h = (int)(bh % H_q);
-    const int64_t b = bh / H_q;
-    const int G = H_q / H_kv, g = h / G, l = h * H_lm / H_q;
-    const T *kb = k + (b * H_kv + g) * (int64_t)N * D;
-    const T *vb = v + (b * H_kv + g) * (int64_t)N * D;
+    float *__restrict__ mlog, float *__restrict__ gdo, float *__restrict__ dcoef, int N, int H_q, int H_kv,
+    int H_lm, int C, int W, int K, float scale) {
+    constexpr int E = 16 / sizeof(T);    // elements per 16-byte piece
+    constexpr int RP = D + E;            // padded LDS row (one extra piece)
+    constexpr int NU = S / WAVE;         // keys per lane in a tile
+    constexpr int DPL = D / WAVE;        // dims per lane in the gathers
+    constexpr int NT = 64 * G;
+    __shared__ T k_t[S][RP];
+    __shared__ T v_t[S][RP];
+    __shared__ float q_l[G][D];
+    __shared__ float do_l[G][D];
+    __shared__ float ca_l[G][S];  // per-key coefficient of A
+    __shared__ float cb_l[G][S];  // per-key coefficient of Bv
+    const int e = threadIdx.x / WAVE, lane = lane_id(), t = threadIdx.x;
+    const int64_t bgi = blockIdx.x;  // (b*H_kv + g)*N + i
+    const int i = (int)(bgi % N);
+    const int64_t bg = bgi / N;
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int h = g * G + e, l = h * H_lm / H_q;
+    const int64_t row = (b * H_q + h) * N + i;
+    const T *kb = k + bg * (int64_t)N * D;
+    const T *vb = v + bg * (int64_t)N * D;
     for (int x = lane; x < D; x += WAVE) {
-        q_l[wave][x] = to_f32(q[row * D + x]);
-        do_l[wave][x] = to_f32(dout[row * D + x]);
+        q_l[e][x] = to_f32(q[row * D + x]);
+        do_l[e][x] = to_f32(dout[row * D + x]);
     }
     const float L = lse[row];
-    wave_sync();
+
+    // stage keys / values j0 .. j0 + n - 1 (n <= S) in LDS
+    auto stage = [&](int64_t j0, int n) {
+        __syncthreads();  // the previous tile is no longer read
+        for (int idx = t; idx < n * (D / E); idx += NT) {
+            const int r = idx / (D / E), cpc = idx % (D / E);
+            *(u32x4 *)&k_t[r][cpc * E] = *(const u32x4 *)(kb + (j0 + r) * D + cpc * E);
+            *(u32x4 *)&v_t[r][cpc * E] = *(const u32x4 *)(vb + (j0 + r) * D + cpc * E);
+        }
+        __syncthreads();
+    };
+    // q.k_r and dO.v_r from the staged tile
+    // (partly unrolled: the query and gradient rows stay in LDS, read as
+    // broadcasts, instead of occupying 2 D registers per lane)
+    auto dots = [&](int r, float &s, float &dpv) {
+        float a = 0.f, c = 0.f;
+#pragma unroll 2
+        for (int x = 0; x < D; x += E) {
+            const Vec16<T> kr = *(const Vec16<T> *)&k_t[r][x];
+            const Vec16<T> vr = *(const Vec16<T> *)&v_t[r][x];
+#pragma unroll
+            for (int y = 0; y < E; y += 4) {
+                const f32x4 qv = *(const f32x4 *)&q_l[e][x + y];
+                const f32x4 dv = *(const f32x4 *)&do_l[e][x + y];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    a = fmaf(qv[z], kr.get(y + z), a);
+                    c = fmaf(dv[z], vr.get(y + z), c);
+                }
+            }
+        }
+        s = scale * a;
+        dpv = c;
+    };
 
     float accA[DPL], accB[DPL];
 #pragma unroll
     for (int y = 0; y < DPL; ++y) accA[y] = accB[y] = 0.f;
-    // accA += sum_j ca_j k_j, accB += sum_j cb_j k_j over keys j0 .. j1 (<= 128)
-    auto gather_keys = [&](int j0, int j1, bool with_b) {
+    // accA += sum_r ca_r k_r, accB += sum_r cb_r k_r over the first n staged keys
+    auto gather = [&](int n, bool with_b) {
         wave_sync();
+#pragma unroll 4
+        for (int r = 0; r < n; ++r) {
+            const float ca = ca_l[e][r], cb = cb_l[e][r];
 #pragma unroll
-        for (int y = 0; y < DPL; ++y) {
-            const int x = lane + y * WAVE;
-            float a = accA[y], bb = accB[y];
-            for (int j = j0; j <= j1; ++j) {
-                const float kx = to_f32(kb[(int64_t)j * D + x]);
-                a = fmaf(ca_l[wave][j - j0], kx, a);
-                if (with_b) bb = fmaf(cb_l[wave][j - j0], kx, bb);
+            for (int y = 0; y < DPL; ++y) {
+                const float kx = to_f32(k_t[r][lane * DPL + y]);
+                accA[y] = fmaf(ca, kx, accA[y]);
+                if (with_b) accB[y] = fmaf(cb, kx, accB[y]);
             }
-            accA[y] = a;
-            accB[y] = bb;
         }
         wave_sync();
     };
 
-    // window: ds_j = P_j (dO.v_j - D')
+    // window [w0, i], in tiles of S keys: ds_j = P_j (dO.v_j - D')
     float dpart = 0.f;  // this lane's share of sum_window P_j dO.v_j
     const int w0 = max(0, (i / S) * S - W);
-    for (int j0 = w0; j0 <= i; j0 += 2 * WAVE) {
-        const int j1 = min(i, j0 + 2 * WAVE - 1);
+    for (int j0 = w0; j0 <= i; j0 += S) {
+        const int n = min(S, i - j0 + 1);
+        stage(j0, n);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = j0 + u * WAVE + lane;
+        for (int u = 0; u < NU; ++u) {
+            const int r = u * WAVE + lane;
             float P = 0.f, dpv = 0.f;
-            if (j <= j1) {
-                const float s = scale * dot_row<T, D>(q_l[wave], kb + (int64_t)j * D);
-                dpv = dot_row<T, D>(do_l[wave], vb + (int64_t)j * D);
+            if (r < n) {
+                float s;
+                dots(r, s, dpv);
                 P = expf(s - L);
             }
             dpart = fmaf(P, dpv, dpart);
-            ca_l[wave][u * WAVE + lane] = P * dpv;
-            cb_l[wave][u * WAVE + lane] = P;
+            ca_l[e][r] = P * dpv;
+            cb_l[e][r] = P;
         }
-        gather_keys(j0, j1, true);
+        gather(n, true);
     }
 
-    // selected chunks
-    const int32_t *sl = sel_idx + ((b * H_kv + g) * N + i) * K;
+    // selected chunks (shared by the group's heads)
+    const int32_t *sl = sel_idx + bgi * K;
     const float *ss = sel_score + row * K;
     float dsel_sum = 0.f;  // sum_c w_c g_c (wave-uniform)
     for (int kk = 0; kk < K; ++kk) {
@@ -132,29 +174,23 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
             if (lane == 0) dsel[row * K + kk] = 0.f, mlog[row * K + kk] = -INFINITY, gdo[row * K + kk] = 0.f;
             continue;
         }
-        float s[2], dpv[2];
+        stage((int64_t)c * S, S);
+        float s[NU], dpv[NU];
         float m = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int jj = u * WAVE + lane;
-            s[u] = -INFINITY;
-            dpv[u] = 0.f;
-            if (jj < S) {
-                const int64_t j = (int64_t)c * S + jj;
-                s[u] = scale * dot_row<T, D>(q_l[wave], kb + j * D);
-                dpv[u] = dot_row<T, D>(do_l[wave], vb + j * D);
-            }
+        for (int u = 0; u < NU; ++u) {
+            dots(u * WAVE + lane, s[u], dpv[u]);
             m = fmaxf(m, s[u]);
         }
         m = wave_max(m);
         float z = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) z += (u * WAVE + lane < S) ? expf(s[u] - m) : 0.f;
+        for (int u = 0; u < NU; ++u) z += expf(s[u] - m);
         const float lse_c = m + logf(wave_sum_f(z));
-        float p[2], gpart = 0.f;
+        float p[NU], gpart = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            p[u] = (u * WAVE + lane < S) ? expf(s[u] - lse_c) : 0.f;
+        for (int u = 0; u < NU; ++u) {
+            p[u] = expf(s[u] - lse_c);
             gpart = fmaf(p[u], dpv[u], gpart);
         }
         const float gc = wave_sum_f(gpart);  // dO.o_c
@@ -162,13 +198,13 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
         const float wc = expf(shat - L);
         dsel_sum = fmaf(wc, gc, dsel_sum);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) ca_l[wave][u * WAVE + lane] = wc * p[u] * (dpv[u] - gc);
-        gather_keys(c * S, c * S + S - 1, false);
+        for (int u = 0; u < NU; ++u) ca_l[e][u * WAVE + lane] = wc * p[u] * (dpv[u] - gc);
+        gather(S, false);
         // score term: ds^_c k'_c = w_c (g_c - D') k'_c
         const float *kp = k_sum + (((int64_t)b * H_lm + l) * C + c) * D;
 #pragma unroll
         for (int y = 0; y < DPL; ++y) {
-            const float kx = kp[lane + y * WAVE];
+            const float kx = kp[lane * DPL + y];
             accA[y] = fmaf(wc * gc, kx, accA[y]);
             accB[y] = fmaf(wc, kx, accB[y]);
         }
@@ -180,7 +216,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
     }
     const float Dp = wave_sum_f(dpart) + dsel_sum - (dlse ? dlse[row] : 0.f);
 #pragma unroll
-    for (int y = 0; y < DPL; ++y) dq[row * D + lane + y * WAVE] = scale * fmaf(-Dp, accB[y], accA[y]);
+    for (int y = 0; y < DPL; ++y) dq[row * D + lane * DPL + y] = scale * fmaf(-Dp, accB[y], accA[y]);
     if (lane == 0) {
         dcoef[row] = Dp;
         for (int kk = 0; kk < K; ++kk)
@@ -201,9 +237,10 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     int H_q, int H_kv, int H_lm, int C, int W, int K, float scale, int lm_mode) {
     constexpr int NT = 4 * S, NQ = 4, DPT = D / NQ, NWV = NT / WAVE;
     constexpr int GMAX = 8;
-    __shared__ float qs_l[GMAX][D];
-    __shared__ float do_l[GMAX][D];
-    __shared__ float sc_l[GMAX][3];
+    constexpr int RB = 4;  // rows staged per barrier round
+    __shared__ float qs_l[RB][GMAX][D];
+    __shared__ float do_l[RB][GMAX][D];
+    __shared__ float sc_l[RB][GMAX][3];
     __shared__ int list_i[NT];
     __shared__ int list_k[NT];
     __shared__ int wcnt[NWV];
@@ -221,68 +258,79 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     const bool valid_j = j < N;
     const int64_t kvrow = ((b * H_kv + g) * N + j) * D;
 
-    float kr[DPT], vr[DPT], dka[DPT], dva[DPT], dkp[DPT];
-    float dbp = 0.f;
+    float kr[DPT], vr[DPT], dka[DPT], dva[DPT];
 #pragma unroll
     for (int x = 0; x < DPT; ++x) {
         kr[x] = valid_j ? to_f32(k[kvrow + x0 + x]) : 0.f;
         vr[x] = valid_j ? to_f32(v[kvrow + x0 + x]) : 0.f;
-        dka[x] = dva[x] = dkp[x] = 0.f;
+        dka[x] = dva[x] = 0.f;
     }
+    // dk', db' of the chunk's landmark heads, accumulated in LDS by their
+    // owner threads (key row jj == landmark index, each its dim slice)
+    for (int idx = t; idx < GLM * D; idx += NT) dkp_l[idx / D][idx % D] = 0.f;
+    if (t < GLM) dbp_l[t] = 0.f;
     auto quad_sum = [&](float a) {
         a += __shfl_xor(a, 1, WAVE);
         a += __shfl_xor(a, 2, WAVE);
         return a;
     };
 
-    // one query row i (all G heads): window row (selected = false) or a row
-    // that selected chunk c in slot kk
-    auto process_row = [&](int i, bool selected, int kk) {
-        __syncthreads();  // the previous row is done with the staged heads
-        for (int idx = t; idx < G * D; idx += NT) {
-            const int e = idx / D, x = idx % D;
+    // up to RB query rows (all G heads each): window rows (selected =
+    // false) or rows that selected chunk c, row_of(rr) -> (i, slot)
+    auto process_rows = [&](int nr, bool selected, auto row_of) {
+        __syncthreads();  // the previous rows are done with the staged heads
+        for (int idx = t; idx < nr * G * D; idx += NT) {
+            const int rr = idx / (G * D), rem = idx % (G * D), e = rem / D, x = rem % D;
+            const int i = row_of(rr).x;
             const int64_t rh = ((b * H_q + (int64_t)g * G + e) * N + i);
-            qs_l[e][x] = to_f32(q[rh * D + x]);
-            do_l[e][x] = to_f32(dout[rh * D + x]);
+            qs_l[rr][e][x] = to_f32(q[rh * D + x]);
+            do_l[rr][e][x] = to_f32(dout[rh * D + x]);
         }
-        if (t < G) {
-            const int64_t rh = ((b * H_q + (int64_t)g * G + t) * N + i);
+        if (t < nr * G) {
+            const int rr = t / G, e = t % G;
+            const int2 ik = row_of(rr);
+            const int64_t rh = ((b * H_q + (int64_t)g * G + e) * N + ik.x);
             if (selected) {
-                sc_l[t][0] = mlog[rh * K + kk];  // log of w_c / e^{lse_c}: P_j = e^{s_j + m}
-                sc_l[t][1] = gdo[rh * K + kk];
-                sc_l[t][2] = dsel[rh * K + kk];
+                sc_l[rr][e][0] = mlog[rh * K + ik.y];  // log of w_c / e^{lse_c}: P_j = e^{s_j + m}
+                sc_l[rr][e][1] = gdo[rh * K + ik.y];
+                sc_l[rr][e][2] = dsel[rh * K + ik.y];
             } else {
-                sc_l[t][0] = -lse[rh];
-                sc_l[t][1] = dcoef[rh];
-                sc_l[t][2] = 0.f;
+                sc_l[rr][e][0] = -lse[rh];
+                sc_l[rr][e][1] = dcoef[rh];
+                sc_l[rr][e][2] = 0.f;
             }
         }
         __syncthreads();
-        const bool live = valid_j && (selected || j <= i);
-        for (int e = 0; e < G; ++e) {
-            float ps = 0.f, pd = 0.f;
+#pragma unroll 1
+        for (int rr = 0; rr < nr; ++rr) {
+            const bool live = valid_j && (selected || j <= row_of(rr).x);
+#pragma unroll 1
+            for (int e = 0; e < G; ++e) {
+                float ps = 0.f, pd = 0.f;
 #pragma unroll
-            for (int x = 0; x < DPT; ++x) {
-                ps = fmaf(qs_l[e][x0 + x], kr[x], ps);
-                pd = fmaf(do_l[e][x0 + x], vr[x], pd);
-            }
-            const float s = scale * quad_sum(ps), dpv = quad_sum(pd);
-            const float P = live ? expf(s + sc_l[e][0]) : 0.f;
-            const float ds = P * (dpv - sc_l[e][1]);
+                for (int x = 0; x < DPT; ++x) {
+                    ps = fmaf(qs_l[rr][e][x0 + x], kr[x], ps);
+                    pd = fmaf(do_l[rr][e][x0 + x], vr[x], pd);
+                }
+                const float s = scale * quad_sum(ps), dpv = quad_sum(pd);
+                const float P = live ? expf(s + sc_l[rr][e][0]) : 0.f;
+                const float ds = P * (dpv - sc_l[rr][e][1]);
 #pragma unroll
-            for (int x = 0; x < DPT; ++x) {
-                dva[x] = fmaf(P, do_l[e][x0 + x], dva[x]);
-                dka[x] = fmaf(scale * ds, qs_l[e][x0 + x], dka[x]);
-            }
-            if (selected) {
-                // landmark head of query head e: its local index le gets the
-                // score gradient (thread rows jj == le hold dk' slices)
-                const int le = (g * G + e) * H_lm / H_q - g * GLM;
-                if (jj == le) {
-                    const float dsh = sc_l[e][2];
+                for (int x = 0; x < DPT; ++x) {
+                    dva[x] = fmaf(P, do_l[rr][e][x0 + x], dva[x]);
+                    dka[x] = fmaf(scale * ds, qs_l[rr][e][x0 + x], dka[x]);
+                }
+                if (selected) {
+                    // landmark head of query head e: its local index le gets
+                    // the score gradient (thread rows jj == le hold dk' slices)
+                    const int le = (g * G + e) * H_lm / H_q - g * GLM;
+                    if (jj == le) {
+                        const float dsh = sc_l[rr][e][2];
 #pragma unroll
-                    for (int x = 0; x < DPT; ++x) dkp[x] = fmaf(scale * dsh, qs_l[e][x0 + x], dkp[x]);
-                    if (qd == 0) dbp += dsh;
+                        for (int x = 0; x < DPT; ++x)
+                            dkp_l[le][x0 + x] = fmaf(scale * dsh, qs_l[rr][e][x0 + x], dkp_l[le][x0 + x]);
+                        if (qd == 0) dbp_l[le] += dsh;
+                    }
                 }
             }
         }
@@ -291,7 +339,8 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     const int wc = W / (S);
     // window rows: query chunks c .. c + W/S
     const int r_end = (int)min((int64_t)N, (int64_t)(c + wc + 1) * S);
-    for (int i = c * S; i < r_end; ++i) process_row(i, false, 0);
+    for (int i0 = c * S; i0 < r_end; i0 += RB)
+        process_rows(min(RB, r_end - i0), false, [&](int rr) { return make_int2(i0 + rr, 0); });
 
     // rows of later query chunks that selected chunk c
     if (K > 0 && c < C) {
@@ -324,20 +373,14 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
                 list_k[pos] = found;
             }
             __syncthreads();
-            for (int r = 0; r < tot; ++r) process_row(list_i[r], true, list_k[r]);
+            for (int r0 = 0; r0 < tot; r0 += RB)
+                process_rows(min(RB, tot - r0), true, [&](int rr) { return make_int2(list_i[r0 + rr], list_k[r0 + rr]); });
         }
     }
 
     // ---- summary backward of the chunk's landmark heads (completed chunks)
     if (c < C) {
-        // dk', db' to LDS (thread rows jj < GLM hold them)
-        __syncthreads();
-        if (jj < GLM) {
-#pragma unroll
-            for (int x = 0; x < DPT; ++x) dkp_l[jj][x0 + x] = dkp[x];
-            if (qd == 0) dbp_l[jj] = dbp;
-        }
-        __syncthreads();
+        __syncthreads();  // dk', db' complete
         for (int e = 0; e < GLM; ++e) {
             const int lh = g * GLM + e;
             const int64_t lrow = ((b * H_lm + lh) * C + c) * D;
@@ -409,9 +452,19 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     float *gdo = (float *)p;
     p += align_up(rows * s.K * 4, 256);
     float *dcoef = (float *)p;
-    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const T *)q,
-                       (const T *)k, (const T *)v, k_sum, sel_idx, sel_score, lse, (const T *)dout, dlse, dq, dsel,
-                       mlog, gdo, dcoef, s.B, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale);
+    const dim3 rgrid((unsigned)((int64_t)s.B * s.H_kv * s.N));
+    auto go_rows = [&](auto kern, int G) {
+        hipLaunchKernelGGL(kern, rgrid, dim3(64 * G), 0, st, (const T *)q, (const T *)k, (const T *)v, k_sum, sel_idx,
+                           sel_score, lse, (const T *)dout, dlse, dq, dsel, mlog, gdo, dcoef, s.N, s.H_q, s.H_kv,
+                           s.H_lm, s.C, s.W, s.K, s.scale);
+    };
+    switch (s.G) {
+        case 1: go_rows(bwd_rows_kernel<T, D, S, 1>, 1); break;
+        case 2: go_rows(bwd_rows_kernel<T, D, S, 2>, 2); break;
+        case 4: go_rows(bwd_rows_kernel<T, D, S, 4>, 4); break;
+        case 8: go_rows(bwd_rows_kernel<T, D, S, 8>, 8); break;
+        default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_keys_kernel<T, D, S>), dim3((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), dim3(4 * S), 0,
