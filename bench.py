@@ -166,6 +166,11 @@ def bench_prefill(args, torch, hb, W):
 
 
 def bench_decode(args, torch, hb, W):
+    """The decode workload's step, then two secondary summary layouts over the
+    same K/V cache: one landmark head per kv head (H_lm = H_kv, bf16 k') and
+    fp32 k' (H_lm = H_q)."""
+    import dataclasses
+
     dev = torch.device("cuda:0")
     inp = W.make_decode(args.decode_workload, device=dev)
     cfg = inp["cfg"]
@@ -174,20 +179,33 @@ def bench_decode(args, torch, hb, W):
     lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device=dev)
     sel = torch.empty((B, cfg.H_kv, cfg.K), dtype=torch.int32, device=dev)
     max_pages = inp["block_table"].shape[1]
-    ws = torch.empty(hb.workspace_size(cfg, hb.WS_DECODE, B, max_pages), dtype=torch.uint8, device=dev)
+    P = inp["k_cache"].shape[0]
 
-    def step():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        hb.decode(cfg, inp["q"], inp["k_cache"], inp["v_cache"], inp["ksum_cache"], inp["bsum_cache"],
-                  inp["block_table"], inp["seq_lens"], out=out, lse=lse, sel_idx=sel, workspace=ws)
-        e1.record()
-        return {"decode": (e0, e1)}
+    def run(c, ksum, bsum, steps, warmup):
+        ws = torch.empty(hb.workspace_size(c, hb.WS_DECODE, B, max_pages), dtype=torch.uint8, device=dev)
 
-    total_ms, per = _timed(step, args.steps, args.warmup, torch)
+        def step():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            hb.decode(c, inp["q"], inp["k_cache"], inp["v_cache"], ksum, bsum, inp["block_table"], inp["seq_lens"],
+                      out=out, lse=lse, sel_idx=sel, workspace=ws)
+            e1.record()
+            return {"decode": (e0, e1)}
+
+        total_ms, per = _timed(step, steps, warmup, torch)
+        return 1000.0 * total_ms / steps, 1000.0 * per["decode"]
+
+    us, call_us = run(cfg, inp["ksum_cache"], inp["bsum_cache"], args.steps, args.warmup)
     seq_lens = inp["seq_lens"].cpu().tolist()
-    return dict(cfg=cfg, us_per_step=1000.0 * total_ms / args.steps, call_us=1000.0 * per["decode"],
-                seq_lens=seq_lens)
+    secondary = {}
+    del inp["ksum_cache"], inp["bsum_cache"]
+    for name, c in (("H_lm=H_kv, bf16 k'", dataclasses.replace(cfg, H_lm=cfg.H_kv)),
+                    ("H_lm=H_q, fp32 k'", dataclasses.replace(cfg, summary_dtype=torch.float32))):
+        ks, bs = W.decode_summary_cache(c, P, seed=41, device=dev)
+        _, cu = run(c, ks, bs, max(2, args.steps // 2), 1)
+        secondary[name] = (c, cu)
+        del ks, bs
+    return dict(cfg=cfg, us_per_step=us, call_us=call_us, seq_lens=seq_lens, secondary=secondary)
 
 
 def bench_serving(args, torch, hb, W, pre):
@@ -352,6 +370,44 @@ def union_overlap(sel, M, sample=4096, seed=0):
     return float(np.mean(vals)) if vals else None
 
 
+def probes(torch):
+    """Practical ceilings measured on this device, for context: a 1 GiB
+    device-to-device copy (HBM read + write) and a bf16 8192^3 matrix product
+    through torch (the vendor GEMM library)."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    out = {}
+    for name, fn, work in (("copy", lambda: dst.copy_(src), 2.0 * src.numel() * 4),
+                           ("gemm_bf16", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / 5
+        out[name] = work / sec / 1e9
+    del src, dst, a, b
+    return {"copy_gbs": out["copy"], "copy_frac": out["copy"] / PEAK_HBM_GBS,
+            "gemm_bf16_tflops": out["gemm_bf16"] / 1e3, "gemm_bf16_frac": out["gemm_bf16"] / 1e3 / PEAK_BF16_TFLOPS}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(pre, budget_s):
     """The fp64 oracle on the host cores: summaries of every chunk plus a
     seeded stratified sample of query rows, extrapolated to tokens/s."""
@@ -379,7 +435,8 @@ def cpu_baseline(pre, budget_s):
     t_rows = time.perf_counter() - t0
     per_row = t_rows / R
     total = t_sum + cfg.N * per_row
-    return {"value": cfg.N / total, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": cfg.N / total, "unit": "tokens/s", "cores": oracle.num_threads(), "cpu_model": _cpu_model(),
+            "kind": "oracle",
             "sample": f"fp64 oracle: summaries of all {cfg.N // cfg.S} chunks x {cfg.H_lm} landmark heads "
                       f"({t_sum:.2f} s) + {R} uniformly sampled query rows, all {cfg.H_q} heads "
                       f"({t_rows:.2f} s); tokens/s extrapolated to {cfg.N} rows"}
@@ -396,6 +453,7 @@ def main():
     ap.add_argument("--no-serving", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=2)
     ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -479,6 +537,14 @@ def main():
                             "roofline": {"kernel": "hils_decode (all phases)", "bound": "hbm", "achieved": gbs,
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "algorithmic_bytes": by}}
+        for name, (c2, cu) in dec["secondary"].items():
+            b2 = decode_bytes(c2, dec["seq_lens"], dio, 2 if c2.summary_dtype == torch.bfloat16 else 4)
+            g2 = b2 / (cu * 1e-6) / 1e9
+            result["decode"].setdefault("secondary", {})[name] = {
+                "us_per_call": cu, "gbs": g2, "frac": g2 / PEAK_HBM_GBS, "algorithmic_bytes": b2}
+    if not args.no_probes:
+        print("[bench] probes: copy and bf16 GEMM ceilings", file=sys.stderr, flush=True)
+        result["probes"] = probes(torch)
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")

@@ -215,3 +215,16 @@ def paged_layout(k, v, S, seed, extra_pages=7):
         return cache
 
     return scatter(k), scatter(v), bt.to(k.device)
+
+
+def decode_summary_cache(cfg, P, seed, device="cuda"):
+    """A summary cache of P pages for the configuration's landmark heads and
+    summary dtype, drawn like the decode workload's (k' ~ N(0, 0.35^2) per
+    component, b' ~ U(1.5, 3.5)).  Returns (ksum_cache [P, H_lm, d],
+    bsum_cache [P, H_lm] fp32)."""
+    gdev = device if torch.cuda.is_available() else "cpu"
+    gen = _generator(seed, gdev)
+    ksum = _randn(gen, (P, cfg.H_lm, cfg.d), gdev, torch.float32, std=DECODE_KSUM_STD).to(cfg.summary_dtype)
+    lo, hi = DECODE_BSUM_RANGE
+    bsum = torch.rand((P, cfg.H_lm), generator=gen, device=gen.device, dtype=torch.float32) * (hi - lo) + lo
+    return ksum.to(device), bsum.to(device)
