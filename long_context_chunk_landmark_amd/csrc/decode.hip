@@ -38,7 +38,7 @@ struct DecodeLayout {
     int np;      // partial (m, l, o) slots per (seq, query head)
     bool fast;   // bf16, d = 128, S = 64: one wave per chunk of the list
     bool pages;  // bf16 summaries, d = 128, H_lm = H_q: page-contiguous scoring
-    size_t off_qs, off_pkey, off_psc, off_sel, off_selsc, off_pm, off_pl, off_po, total;
+    size_t off_qs, off_pkey, off_psc, off_sel, off_selsc, off_pm, off_pl, off_po, off_plse, total;
 };
 
 DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
@@ -48,7 +48,7 @@ DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
     L.fast = s.io_bf16 && s.D == 128 && s.S == 64;
     L.np = L.fast ? s.K + s.W / s.S + 1 : L.nsb;
     L.pages = s.sum_bf16 && s.D == 128 && s.H_lm == s.H_q && (s.H_q == 8 || s.H_q == 16 || s.H_q == 32) &&
-              (max_pages + L.splits - 1) / L.splits <= DECODE_PAGES_CAP;
+              (max_pages + L.splits - 1) / L.splits <= DECODE_PAGES_CAP && s.agg_mode == 0;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -64,6 +64,8 @@ DecodeLayout decode_layout(const Shape &s, int num_seqs, int max_pages) {
     L.off_pm = take(NS * s.H_q * L.np * 4);
     L.off_pl = take(NS * s.H_q * L.np * 4);
     L.off_po = take(NS * s.H_q * L.np * s.D * 4);
+    // normalised aggregation: per (seq, head, split) partial (max, sum) of exp(s^)
+    L.off_plse = take(s.agg_mode == 1 ? NS * s.H_q * L.splits * 2 * 4 : 0);
     L.total = o;
     return L;
 }
@@ -117,17 +119,26 @@ __global__ __launch_bounds__(256) void decode_qprep_kernel(const T *__restrict__
 // Phase A.  LPR lanes cover one landmark row (16-byte loads), CPS = 64/LPR
 // candidates per wave step.  GLM = landmark rows per candidate (G when
 // every query head has its own landmark, 1 when the group shares one).
-template <typename TS, int D, int G, int GLM>
+//
+// AM (aggregation mode): 0 ranks by the group max of s^; 1 (first pass of
+// the normalised aggregation) writes, per head, the split's partial (max,
+// sum of exp) of s^ over its candidates into plse; 2 ranks by the group
+// max of s^ - LSE_h, LSE_h combined from all splits' partials.  psc keeps
+// the raw s^ in every mode.
+template <typename TS, int D, int G, int GLM, int AM = 0>
 __global__ __launch_bounds__(256) void decode_score_kernel(
     const float *__restrict__ qs, const TS *__restrict__ ksum_cache, const float *__restrict__ bsum_cache,
     const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens, uint64_t *pkey,
-    float *psc, int H_q, int H_kv, int H_lm, int S, int W, int K, int splits, float scale) {
+    float *psc, int H_q, int H_kv, int H_lm, int S, int W, int K, int splits, float scale,
+    float *__restrict__ plse) {
     constexpr int E = 16 / sizeof(TS);
     constexpr int LPR = D / E;
     constexpr int CPS = WAVE / LPR;
     constexpr int CAPL = DECODE_SPLIT_CAP;
     __shared__ float agg_l[CAPL];
     __shared__ float sc_l[CAPL][G];
+    __shared__ float lse_l[G];
+    __shared__ float pm_l[4][G], pz_l[4][G];
 
     const int sp = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
     const int wave = threadIdx.x / WAVE, lane = lane_id();
@@ -136,6 +147,25 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int c_lo = (int)((int64_t)sp * n / splits), c_hi = (int)((int64_t)(sp + 1) * n / splits);
     const int cnt = c_hi - c_lo;
     const int col = lane % LPR, cs = lane / LPR;
+    if constexpr (AM == 2) {
+        // each head's log-sum-exp over all candidates, from the splits' partials
+        if (threadIdx.x < G) {
+            const float *pp = plse + ((int64_t)seq * H_q + g * G + threadIdx.x) * splits * 2;
+            float m = -INFINITY, z = 0.f;
+            for (int x = 0; x < splits; ++x) {
+                const float mo = pp[2 * x], zo = pp[2 * x + 1];
+                const float mn = fmaxf(m, mo);
+                if (mn == -INFINITY) continue;
+                z = (m == -INFINITY ? 0.f : z * expf(m - mn)) + (mo == -INFINITY ? 0.f : zo * expf(mo - mn));
+                m = mn;
+            }
+            lse_l[threadIdx.x] = m + logf(z);
+        }
+        __syncthreads();
+    }
+    float lm[G], lz[G];  // AM == 1: this lane's running max / sum per head
+#pragma unroll
+    for (int e = 0; e < G; ++e) lm[e] = -INFINITY, lz[e] = 0.f;
 
     float qv[G][E];
 #pragma unroll
@@ -183,14 +213,52 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
                 for (int x = 0; x < E; ++x) part = fmaf(qv[e][x], kv[u][le].get(x), part);
                 part = seg_sum<LPR>(part);
                 sc[e] = fmaf(scale, part, bias[u][le]);
-                agg = fmaxf(agg, sc[e]);
+                if constexpr (AM == 2) agg = fmaxf(agg, sc[e] - lse_l[e]);
+                else agg = fmaxf(agg, sc[e]);
+                if constexpr (AM == 1) {
+                    if (okv[u] && col == 0) {
+                        const float mn = fmaxf(lm[e], sc[e]);
+                        lz[e] = lz[e] * expf(lm[e] - mn) + expf(sc[e] - mn);
+                        lm[e] = mn;
+                    }
+                }
             }
-            if (okv[u] && col == 0) {
+            if (AM != 1 && okv[u] && col == 0) {
                 agg_l[lc] = agg;
 #pragma unroll
                 for (int e = 0; e < G; ++e) sc_l[lc][e] = sc[e];
             }
         }
+    }
+    if constexpr (AM == 1) {
+        // (max, sum) per head: over the wave's lanes, then the block's waves
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            float m = lm[e], z = lz[e];
+#pragma unroll
+            for (int off = 1; off < WAVE; off <<= 1) {
+                const float mo = __shfl_xor(m, off, WAVE), zo = __shfl_xor(z, off, WAVE);
+                const float mn = fmaxf(m, mo);
+                z = (m == -INFINITY ? 0.f : z * expf(m - mn)) + (mo == -INFINITY ? 0.f : zo * expf(mo - mn));
+                m = mn;
+            }
+            if (lane == 0) pm_l[wave][e] = m, pz_l[wave][e] = z;
+        }
+        __syncthreads();
+        if (threadIdx.x < G) {
+            float m = -INFINITY, z = 0.f;
+            for (int w = 0; w < 4; ++w) {
+                const float mo = pm_l[w][threadIdx.x], zo = pz_l[w][threadIdx.x];
+                const float mn = fmaxf(m, mo);
+                if (mn == -INFINITY) continue;
+                z = (m == -INFINITY ? 0.f : z * expf(m - mn)) + (mo == -INFINITY ? 0.f : zo * expf(mo - mn));
+                m = mn;
+            }
+            float *pp = plse + (((int64_t)seq * H_q + g * G + threadIdx.x) * splits + sp) * 2;
+            pp[0] = m;
+            pp[1] = z;
+        }
+        return;
     }
     __syncthreads();
     if (wave != 0) return;
@@ -758,15 +826,26 @@ static hipError_t go_decode(const Shape &s, const DecodeLayout &L, int num_seqs,
             else sc(decode_score_pages_kernel<32, G>);
         }
     }
+    float *plse = (float *)(ws + L.off_plse);
+    auto gscore = [&](auto kern) {
+        hipLaunchKernelGGL(kern, ga, dim3(256), 0, st, qs, (const TS *)ksum_cache, bsum_cache, block_table, max_pages,
+                           seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W, s.K, L.splits, s.scale, plse);
+    };
     if (pages) {
-    } else if (s.GLM == 1)
-        hipLaunchKernelGGL((decode_score_kernel<TS, D, G, 1>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
-                           bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
-                           s.K, L.splits, s.scale);
-    else
-        hipLaunchKernelGGL((decode_score_kernel<TS, D, G, G>), ga, dim3(256), 0, st, qs, (const TS *)ksum_cache,
-                           bsum_cache, block_table, max_pages, seq_lens, pkey, psc, s.H_q, s.H_kv, s.H_lm, s.S, s.W,
-                           s.K, L.splits, s.scale);
+    } else if (s.agg_mode == 1) {
+        // normalised aggregation: each head's log-sum-exp first, then the ranking pass
+        if (s.GLM == 1) {
+            gscore(decode_score_kernel<TS, D, G, 1, 1>);
+            gscore(decode_score_kernel<TS, D, G, 1, 2>);
+        } else {
+            gscore(decode_score_kernel<TS, D, G, G, 1>);
+            gscore(decode_score_kernel<TS, D, G, G, 2>);
+        }
+    } else if (s.GLM == 1) {
+        gscore(decode_score_kernel<TS, D, G, 1>);
+    } else {
+        gscore(decode_score_kernel<TS, D, G, G>);
+    }
     {
         const int nv = (L.splits * s.K + WAVE - 1) / WAVE;
         auto mg = [&](auto kern) {

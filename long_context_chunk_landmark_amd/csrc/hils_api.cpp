@@ -252,8 +252,6 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
     hils_status_t st = resolve(cfg, false, s);
     if (st) return st;
     if (num_seqs < 0 || max_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
-    if (s.agg_mode != HILS_AGG_MAX)
-        return fail(HILS_ERR_UNSUPPORTED, "hils_decode: agg_mode=%d not supported (max aggregation only)", s.agg_mode);
     if (num_seqs == 0) return ok();
     if (max_pages == 0) return fail(HILS_ERR_INVALID_ARG, "max_pages must be >= 1");
     if ((int64_t)max_pages > 65536) return fail(HILS_ERR_UNSUPPORTED, "max_pages=%d: supported up to 65536", max_pages);

@@ -245,7 +245,7 @@ def _oracle_decode(cfg, inp, seq_lens, given_sel=None):
 
 
 @pytest.mark.parametrize("variant", ["bf16_hq", "bf16_hkv", "fp32sum", "fp32io", "ragged", "g8_s128", "qcal",
-                                     "qcal_fp32io"])
+                                     "qcal_fp32io", "aggnorm_hq", "aggnorm_hkv_fp32io"])
 def test_decode_matches_oracle(variant, dev):
     kw = {
         "bf16_hq": dict(seq_len=3000, seq_lens=[3000, 2113, 64]),
@@ -257,6 +257,10 @@ def test_decode_matches_oracle(variant, dev):
         # Q-Cal calibrates the scoring query only; attention uses the raw q
         "qcal": dict(seq_len=3000, seq_lens=[3000, 1500, 900], d_model=256, r=16),
         "qcal_fp32io": dict(seq_len=2000, io=F32, summary=F32, d=64, seq_lens=[2000, 1111, 700], d_model=128, r=8),
+        # normalised-weight aggregation (two scoring passes)
+        "aggnorm_hq": dict(seq_len=3000, seq_lens=[3000, 2113, 900], agg_mode=1),
+        "aggnorm_hkv_fp32io": dict(seq_len=2500, io=F32, summary=F32, H_lm=2, d=64, seq_lens=[2500, 1700, 64],
+                                   agg_mode=1),
     }[variant]
     inp = W.make_decode(_decode_case(dev, **kw), device=dev)
     cfg = inp["cfg"]
