@@ -200,7 +200,8 @@ def bench_decode(args, torch, hb, W):
     secondary = {}
     del inp["ksum_cache"], inp["bsum_cache"]
     for name, c in (("H_lm=H_kv, bf16 k'", dataclasses.replace(cfg, H_lm=cfg.H_kv)),
-                    ("H_lm=H_q, fp32 k'", dataclasses.replace(cfg, summary_dtype=torch.float32))):
+                    ("H_lm=H_q, fp32 k'", dataclasses.replace(cfg, summary_dtype=torch.float32)),
+                    ("H_lm=H_q, bf16 k', normalised aggregation", dataclasses.replace(cfg, agg_mode=hb.AGG_NORMALIZED))):
         ks, bs = W.decode_summary_cache(c, P, seed=41, device=dev)
         _, cu = run(c, ks, bs, max(2, args.steps // 2), 1)
         secondary[name] = (c, cu)
