@@ -264,10 +264,10 @@ size_t hils_prefill_paged_workspace_size(const hils_config_t *cfg, int32_t q_sta
  *   q, k, v, dout: as in the forward, io_dtype; lse [B,H_q,N] fp32 and
  *   sel_idx / sel_score: the forward's outputs (dout.out is formed from
  *   the recomputed weights, so out itself is not read); k_sum [B,H_lm,C,d] fp32
- *   (summary_dtype must be F32); q_lm as for hils_landmark_summarize
- *   (HILS_LM_CHUNK or HILS_LM_MEAN; HILS_LM_SHARED is unsupported);
+ *   (summary_dtype must be F32); q_lm as for hils_landmark_summarize;
  *   dlse [B,H_q,N] fp32 or NULL (zero).
- *   dq [B,H_q,N,d], dk, dv [B,H_kv,N,d], dq_lm [B,H_lm,C,d]: fp32, written
+ *   dq [B,H_q,N,d], dk, dv [B,H_kv,N,d], dq_lm [B,H_lm,C,d] ([H_lm,d] with
+ *   HILS_LM_SHARED: summed over every sequence and chunk): fp32, written
  *   (dq_lm unused, may be NULL, with HILS_LM_MEAN).
  *   workspace: hils_workspace_size(cfg, HILS_WS_BACKWARD, 0, 0) bytes.
  * G <= 8.  Deterministic (no atomics). */

@@ -400,7 +400,11 @@ def sparse_attend_backward(cfg: Config, q, k, v, q_lm, k_sum, sel_idx, sel_score
     dq = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.d), **f32)
     dk = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.d), **f32)
     dv = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.d), **f32)
-    dq_lm = torch.empty((cfg.B, cfg.H_lm, cfg.C, cfg.d), **f32) if cfg.landmark_mode == LM_CHUNK else None
+    dq_lm = None
+    if cfg.landmark_mode == LM_CHUNK:
+        dq_lm = torch.empty((cfg.B, cfg.H_lm, cfg.C, cfg.d), **f32)
+    elif cfg.landmark_mode == LM_SHARED:
+        dq_lm = torch.empty((cfg.H_lm, cfg.d), **f32)
     ws, nbytes = _workspace(cfg, WS_BACKWARD, dev, workspace)
     c = cfg.to_c()
     _check(load_library().hils_sparse_attend_backward(

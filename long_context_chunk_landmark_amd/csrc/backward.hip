@@ -385,8 +385,10 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
             const int lh = g * GLM + e;
             const int64_t lrow = ((b * H_lm + lh) * C + c) * D;
             float qp[DPT];
+            // landmark query: per chunk, one shared by the chunks of head lh, or zero
+            const int64_t qrow = lm_mode == 1 ? (int64_t)lh * D : lrow;
 #pragma unroll
-            for (int x = 0; x < DPT; ++x) qp[x] = lm_mode == 2 ? 0.f : to_f32(q_lm[lrow + x0 + x]);
+            for (int x = 0; x < DPT; ++x) qp[x] = lm_mode == 2 ? 0.f : to_f32(q_lm[qrow + x0 + x]);
             float pa = 0.f, pk = 0.f;
 #pragma unroll
             for (int x = 0; x < DPT; ++x) {
@@ -433,9 +435,25 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     }
 }
 
+// Shared landmark query: the gradient of the one query of head l is the sum
+// of the per-chunk gradients over every sequence and chunk, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_shared_query_kernel(const float *__restrict__ per_chunk,
+                                                               float *__restrict__ dq_lm, int B, int H_lm, int C,
+                                                               int D) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // l * D + x
+    if (idx >= H_lm * D) return;
+    const int l = idx / D, x = idx % D;
+    float acc = 0.f;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < C; ++c) acc += per_chunk[(((int64_t)b * H_lm + l) * C + c) * D + x];
+    dq_lm[idx] = acc;
+}
+
 size_t backward_workspace_bytes(const Shape &s) {
     const size_t rows = (size_t)s.B * s.H_q * s.N;
-    return 3 * align_up(rows * s.K * 4, 256) + align_up(rows * 4, 256);
+    size_t b = 3 * align_up(rows * s.K * 4, 256) + align_up(rows * 4, 256);
+    if (s.lm_mode == 1) b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // per-chunk dq'
+    return b;
 }
 
 template <typename T, int D, int S>
@@ -452,6 +470,9 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     float *gdo = (float *)p;
     p += align_up(rows * s.K * 4, 256);
     float *dcoef = (float *)p;
+    p += align_up(rows * 4, 256);
+    // shared landmark query: per-chunk gradients first, summed afterwards
+    float *dql_chunks = s.lm_mode == 1 ? (float *)p : dq_lm;
     const dim3 rgrid((unsigned)((int64_t)s.B * s.H_kv * s.N));
     auto go_rows = [&](auto kern, int G) {
         hipLaunchKernelGGL(kern, rgrid, dim3(64 * G), 0, st, (const T *)q, (const T *)k, (const T *)v, k_sum, sel_idx,
@@ -469,8 +490,13 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_keys_kernel<T, D, S>), dim3((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), dim3(4 * S), 0,
                        st, (const T *)q, (const T *)k, (const T *)v, (const T *)q_lm, sel_idx, lse, (const T *)dout,
-                       dcoef, dsel, mlog, gdo, dk, dv, dq_lm, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale,
+                       dcoef, dsel, mlog, gdo, dk, dv, dql_chunks, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale,
                        s.lm_mode);
+    if (s.lm_mode == 1) {
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_shared_query_kernel, dim3((unsigned)((s.H_lm * s.D + 255) / 256)), dim3(256), 0, st,
+                           (const float *)dql_chunks, dq_lm, s.B, s.H_lm, s.C, s.D);
+    }
     return hipGetLastError();
 }
 

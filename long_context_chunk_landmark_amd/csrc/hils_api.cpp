@@ -287,7 +287,6 @@ hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *
     hils_status_t st = resolve(cfg, true, s);
     if (st) return st;
     if (s.sum_bf16) return fail(HILS_ERR_UNSUPPORTED, "backward: summary_dtype must be F32");
-    if (s.lm_mode == HILS_LM_SHARED) return fail(HILS_ERR_UNSUPPORTED, "backward: landmark_mode SHARED not supported");
     if (s.G > 8) return fail(HILS_ERR_UNSUPPORTED, "backward: G=%d, supported up to 8", s.G);
     if ((int64_t)s.B * s.N == 0) return ok();
     if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
@@ -295,8 +294,8 @@ hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *
         (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
         return st;
     if (s.K > 0 && ((st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))) return st;
-    if (s.C > 0 && ((st = check_ptr(k_sum, "k_sum")) || (s.lm_mode == HILS_LM_CHUNK && (st = check_ptr(q_lm, "q_lm"))) ||
-                    (s.lm_mode == HILS_LM_CHUNK && (st = check_ptr(dq_lm, "dq_lm")))))
+    if (s.C > 0 && ((st = check_ptr(k_sum, "k_sum")) || (s.lm_mode != HILS_LM_MEAN && (st = check_ptr(q_lm, "q_lm"))) ||
+                    (s.lm_mode != HILS_LM_MEAN && (st = check_ptr(dq_lm, "dq_lm")))))
         return st;
     if (dlse && !aligned16(dlse)) return fail(HILS_ERR_INVALID_ARG, "dlse is not 16-byte aligned");
     const size_t need = hils::backward_workspace_bytes(s);

@@ -45,11 +45,12 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     """Gradients of sum(dout * out) + sum(dlse * lse) for a prefill with the
     given selection.
 
-    q [B,H_q,N,d]; k, v [B,H_kv,N,d]; q_lm [B,H_lm,C,d] (None for "mean");
+    q [B,H_q,N,d]; k, v [B,H_kv,N,d]; q_lm [B,H_lm,C,d] ([H_lm,d] for
+    "shared": one query per landmark head for every chunk; None for "mean");
     sel_idx [B,H_kv,N,K] (ascending, -1 padded); dout [B,H_q,N,d];
     dlse [B,H_q,N] or None.  Returns dict(dq, dk, dv, dq_lm, out, lse,
-    sel_score, dsel) in float64 (dq_lm None for "mean"; dsel = ds^ per
-    selected slot [B,H_q,N,K], 0 on padding).
+    sel_score, dsel) in float64 (dq_lm None for "mean", [H_lm,d] for
+    "shared"; dsel = ds^ per selected slot [B,H_q,N,K], 0 on padding).
     """
     B, H_q, N, d = np.shape(q)
     H_kv = np.shape(k)[1]
@@ -63,6 +64,8 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     dl = np.zeros((B, H_q, N)) if dlse is None else _f64(dlse)
     if landmark == "chunk":
         ql = _f64(q_lm)
+    elif landmark == "shared":
+        ql = np.broadcast_to(_f64(q_lm)[None, :, None, :], (B, H_lm, C, d)).copy()
     else:
         assert landmark == "mean", landmark
         ql = np.zeros((B, H_lm, C, d))
@@ -154,5 +157,6 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
                 da = p * ((kc - ksum[b, l, c]) @ dks[b, l, c]) - dbs[b, l, c] * p * (a - p @ a)
                 dql[b, l, c] = scale * da @ kc
                 dk[b, g, c * S:(c + 1) * S] += np.outer(p, dks[b, l, c]) + scale * np.outer(da, ql[b, l, c])
-    return dict(dq=dq, dk=dk, dv=dv, dq_lm=dql if landmark == "chunk" else None, out=out, lse=lse,
-                sel_score=sel_score, dsel=dsel)
+    # the shared query's gradient collects every chunk's
+    dq_lm = {"chunk": dql, "shared": dql.sum(axis=(0, 2)), "mean": None}[landmark]
+    return dict(dq=dq, dk=dk, dv=dv, dq_lm=dq_lm, out=out, lse=lse, sel_score=sel_score, dsel=dsel)

@@ -33,6 +33,7 @@ CASES = {
     "mean_g8": dict(seed=94, io=BF, B=1, H_q=8, H_kv=1, d=128, N=800, S=64, W=128, K=3, landmark_mode=2),
     "k0_window_only": dict(seed=95, io=BF, B=1, H_q=2, H_kv=1, d=64, N=700, S=64, W=128, K=0),
     "b2_s128_d128": dict(seed=96, io=BF, B=2, H_q=4, H_kv=2, d=128, N=1000, S=128, W=128, K=2),
+    "shared_b2_g2": dict(seed=97, io=BF, B=2, H_q=4, H_kv=2, d=128, N=900, S=64, W=128, K=4, landmark_mode=1),
 }
 
 
@@ -62,12 +63,12 @@ def _run(name, dev):
 def test_backward_matches_oracle(name, dev):
     print(f"[backward] {name}", flush=True)
     cfg, inp, fw, dout, dlse, (dq, dk, dv, dq_lm) = _run(name, dev)
-    lm = "mean" if cfg.landmark_mode == hb.LM_MEAN else "chunk"
+    lm = {hb.LM_CHUNK: "chunk", hb.LM_SHARED: "shared", hb.LM_MEAN: "mean"}[cfg.landmark_mode]
     ref = oracle_backward(cfg.oracle_dict(), host(inp["q"]), host(inp["k"]), host(inp["v"]),
                           None if inp["q_lm"] is None else host(inp["q_lm"]), host(fw["sel_idx"]), host(dout),
                           host(dlse), landmark=lm)
     a, r = (1e-4, 1e-3) if cfg.io_dtype == BF else (1e-5, 1e-4)
-    pairs = [("dq", dq), ("dk", dk), ("dv", dv)] + ([("dq_lm", dq_lm)] if lm == "chunk" else [])
+    pairs = [("dq", dq), ("dk", dk), ("dv", dv)] + ([("dq_lm", dq_lm)] if lm != "mean" else [])
     for key, got in pairs:
         got = host(got).numpy().astype(np.float64)
         want = ref[key]

@@ -107,3 +107,24 @@ def test_dense_limit_matches_autograd():
     for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
         np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=0, atol=1e-10, err_msg=name)
     assert np.all(g["dq_lm"] == 0)
+
+
+def test_shared_landmark_gradients_match_finite_differences():
+    cfg, q, k, v, _, dout, dlse, _ = _case(8, B=2, N=64)
+    qs = np.random.default_rng(2).standard_normal((cfg["H_lm"], cfg["d"]))
+    ks, bs = oracle.summarize(cfg, k, qs, landmark="shared")
+    sel = oracle.forward_rows(cfg, q, k, v, ks, bs, attend=False)["sel_idx"]
+    g = backward(cfg, q, k, v, qs, sel, dout, dlse, landmark="shared")
+    assert g["dq_lm"].shape == qs.shape
+    eps = 1e-6
+    for name, x in (("q_lm", qs), ("k", k)):
+        u = np.random.default_rng(3).standard_normal(x.shape)
+        if name == "q_lm":
+            fd = (_loss(cfg, q, k, v, qs + eps * u, sel, dout, dlse, "shared") -
+                  _loss(cfg, q, k, v, qs - eps * u, sel, dout, dlse, "shared")) / (2 * eps)
+            an = float((g["dq_lm"] * u).sum())
+        else:
+            fd = (_loss(cfg, q, k + eps * u, v, qs, sel, dout, dlse, "shared") -
+                  _loss(cfg, q, k - eps * u, v, qs, sel, dout, dlse, "shared")) / (2 * eps)
+            an = float((g["dk"] * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
