@@ -73,6 +73,20 @@ void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace
 
 // ------------------------------------------------------------ k' prep
 
+// Copy NB bytes (a multiple of 8; both pointers aligned to min(NB, 16)) with
+// 16-byte (or 8-byte) accesses.
+template <int NB>
+__device__ __forceinline__ void copy_bytes(void *dst, const void *src) {
+    static_assert(NB % 8 == 0, "whole 8-byte pieces");
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) ((u32x4 *)dst)[q] = ((const u32x4 *)src)[q];
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) ((uint2 *)dst)[q] = ((const uint2 *)src)[q];
+    }
+}
+
 __global__ void fill_zero_kernel(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0.f;
@@ -112,15 +126,22 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
         bf16 *dst = ksb + row * D + (lane & 15) * EL;
         bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
         float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
+        // whole-slice vector loads and stores (the slices are 16-byte aligned)
+        TS in[EL];
+        bf16 o1[EL], o2[EL];
+        float o3[EL];
+        copy_bytes<EL * sizeof(TS)>(in, src);
 #pragma unroll
         for (int x = 0; x < EL; ++x) {
-            const float v = to_f32(src[x]);
+            const float v = to_f32(in[x]);
             ss = fmaf(v, v, ss);
-            const bf16 v1 = (bf16)v;
-            dst[x] = v1;
-            if constexpr (std::is_same<TS, float>::value) dst2[x] = (bf16)(v - (float)v1);
-            dcm[x] = v;
+            o1[x] = (bf16)v;
+            o2[x] = (bf16)(v - (float)o1[x]);
+            o3[x] = v;
         }
+        copy_bytes<EL * 2>(dst, o1);
+        if constexpr (std::is_same<TS, float>::value) copy_bytes<EL * 2>(dst2, o2);
+        copy_bytes<EL * 4>(dcm, o3);
     }
     ss = xor_sum<1, 8>(ss);
     // one atomic per wave when its four rows belong to the same (b, l)
