@@ -73,6 +73,8 @@ void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace
 
 // ------------------------------------------------------------ k' prep
 
+constexpr int KPREP_ROWS = 32;  // k' rows per wave in ksum_prep
+
 // Copy NB bytes (a multiple of 8; both pointers aligned to min(NB, 16)) with
 // 16-byte (or 8-byte) accesses.
 template <int NB>
@@ -109,51 +111,71 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
                                                         float *__restrict__ bsum_out) {
     constexpr int EL = D / 16;
     const int lane = lane_id();
-    const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * 4 + (lane >> 4);
-    const bool ok = row < rows;
-    float ss = 0.f;
-    if (ok) {
-        // row = (b * H_lm + l) * C + c with l = g * GLM + e
-        const int64_t c = row % C, bl = row / C;
-        const int64_t e = bl % GLM, bg = bl / GLM;
-        int64_t src_row = row;
-        if (bt) {
-            const int64_t b = bl / H_lm, l = bl % H_lm;
-            src_row = (int64_t)bt[b * max_pages + c] * H_lm + l;
-            if ((lane & 15) == 0) bsum_out[row] = bsum_in[src_row];
-        }
-        const TS *src = k_sum + src_row * D + (lane & 15) * EL;
-        bf16 *dst = ksb + row * D + (lane & 15) * EL;
-        bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
-        float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
-        // whole-slice vector loads and stores (the slices are 16-byte aligned)
-        TS in[EL];
-        bf16 o1[EL], o2[EL];
-        float o3[EL];
-        copy_bytes<EL * sizeof(TS)>(in, src);
+    // each wave: KPREP_ROWS consecutive rows, four per step; the max norm
+    // of its (b, l) run is kept in a register and flushed with one atomic
+    // when the run ends (the knorm words see few atomics)
+    const int64_t wrow0 = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * KPREP_ROWS;
+    int64_t cur_bl = -1;
+    float wmax = 0.f;
+    auto flush = [&]() {
+        if (cur_bl >= 0 && lane == 0) atomicMax((unsigned int *)(knorm + cur_bl), __float_as_uint(wmax));
+    };
+    for (int step = 0; step < KPREP_ROWS / 4; ++step) {
+        const int64_t row0 = wrow0 + step * 4;
+        if (row0 >= rows) break;
+        const int64_t row = row0 + (lane >> 4);
+        const bool ok = row < rows;
+        float ss = 0.f;
+        if (ok) {
+            // row = (b * H_lm + l) * C + c with l = g * GLM + e
+            const int64_t c = row % C, bl = row / C;
+            const int64_t e = bl % GLM, bg = bl / GLM;
+            int64_t src_row = row;
+            if (bt) {
+                const int64_t b = bl / H_lm, l = bl % H_lm;
+                src_row = (int64_t)bt[b * max_pages + c] * H_lm + l;
+                if ((lane & 15) == 0) bsum_out[row] = bsum_in[src_row];
+            }
+            const TS *src = k_sum + src_row * D + (lane & 15) * EL;
+            bf16 *dst = ksb + row * D + (lane & 15) * EL;
+            bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
+            float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
+            // whole-slice vector loads and stores (the slices are 16-byte aligned)
+            TS in[EL];
+            bf16 o1[EL], o2[EL];
+            float o3[EL];
+            copy_bytes<EL * sizeof(TS)>(in, src);
 #pragma unroll
-        for (int x = 0; x < EL; ++x) {
-            const float v = to_f32(in[x]);
-            ss = fmaf(v, v, ss);
-            o1[x] = (bf16)v;
-            o2[x] = (bf16)(v - (float)o1[x]);
-            o3[x] = v;
+            for (int x = 0; x < EL; ++x) {
+                const float v = to_f32(in[x]);
+                ss = fmaf(v, v, ss);
+                o1[x] = (bf16)v;
+                o2[x] = (bf16)(v - (float)o1[x]);
+                o3[x] = v;
+            }
+            copy_bytes<EL * 2>(dst, o1);
+            if constexpr (std::is_same<TS, float>::value) copy_bytes<EL * 2>(dst2, o2);
+            copy_bytes<EL * 4>(dcm, o3);
         }
-        copy_bytes<EL * 2>(dst, o1);
-        if constexpr (std::is_same<TS, float>::value) copy_bytes<EL * 2>(dst2, o2);
-        copy_bytes<EL * 4>(dcm, o3);
+        ss = xor_sum<1, 8>(ss);
+        const float nrm = ok ? sqrtf(ss) : 0.f;
+        const int64_t last = min(row0 + 3, rows - 1);
+        if (row0 / C == last / C) {  // the four rows share (b, l)
+            const float m = xor_max<16, 32>(nrm);
+            if (row0 / C != cur_bl) {
+                flush();
+                cur_bl = row0 / C;
+                wmax = m;
+            } else {
+                wmax = fmaxf(wmax, m);
+            }
+        } else {  // a run boundary inside the step: per-row atomics
+            flush();
+            cur_bl = -1;
+            if (ok && (lane & 15) == 0) atomicMax((unsigned int *)(knorm + row / C), __float_as_uint(nrm));
+        }
     }
-    ss = xor_sum<1, 8>(ss);
-    // one atomic per wave when its four rows belong to the same (b, l)
-    const float nrm = ok ? sqrtf(ss) : 0.f;
-    const int64_t row0 = row - (lane >> 4);
-    const int64_t last = min(row0 + 3, rows - 1);
-    if (row0 / C == last / C) {
-        const float m = xor_max<16, 32>(nrm);
-        if (lane == 0) atomicMax((unsigned int *)(knorm + row0 / C), __float_as_uint(m));
-    } else if (ok && (lane & 15) == 0) {
-        atomicMax((unsigned int *)(knorm + row / C), __float_as_uint(nrm));
-    }
+    flush();
 }
 
 // ------------------------------------------------------------ Q-Cal
@@ -944,7 +966,7 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, ws.knorm, nl);
     const int64_t krows = (int64_t)s.B * s.H_lm * s.C;
     if (krows > 0) {
-        const dim3 grid((unsigned)((krows + 15) / 16)), block(256);
+        const dim3 grid((unsigned)((krows + 4 * KPREP_ROWS - 1) / (4 * KPREP_ROWS))), block(256);
         auto prep = [&](auto kern, auto *src) {
             hipLaunchKernelGGL(kern, grid, block, 0, st, src, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C,
                                s.GLM, krows, s.bt, s.max_pages, s.H_lm, b_sum, ws.bsum);
