@@ -337,9 +337,12 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 
 // ------------------------------------------------------------ approximate scores (MFMA)
 
-// One block = 64 consecutive queries of one query chunk (S is a multiple of
-// 64) for one (b, g): 2G waves, wave (qp, e) owns query tiles 2qp, 2qp+1
-// (16 queries each) of head e of the group.  The B operands of the
+// One block = 64 NQP consecutive queries (NQP = 1 or 2; 64 queries lie in
+// one query chunk, S being a multiple of 64) for one (b, g): 2 NQP G waves,
+// wave (qp, e) owns query tiles 2qp, 2qp+1 (16 queries each) of head e of
+// the group.  Query chunks are nested in their candidates (chunk qc has
+// candidates 0 .. n(qc) - 1), so two chunks share every k' tile up to the
+// smaller count: the block walks the larger one and each row keeps its own.  The B operands of the
 // 16x16x32 MFMAs are q^T of those 32 queries (bf16 terms, in registers);
 // the A operand is a 16-candidate k' tile staged in LDS, each fragment read
 // feeding both query tiles.  D: lane l holds candidates 4*(l/16)+i of query
@@ -361,8 +364,8 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 // lse [B, H_q, N]; 2 the group max of the scores minus those log-sum-exps.
 // The subtracted constant is the same in the exact pass, so E still bounds
 // |exact - approximate| of what is ranked.
-template <typename TQ, int D, int G, bool KSPLIT, int AM>
-__global__ __launch_bounds__(128 * G) void score_approx_kernel(
+template <typename TQ, int D, int G, bool KSPLIT, int AM, int NQP>
+__global__ __launch_bounds__(128 * G * NQP) void score_approx_kernel(
     const TQ *__restrict__ q, const bf16 *__restrict__ ksb, const bf16 *__restrict__ ksb2,
     const float *__restrict__ b_sum, const float *__restrict__ knorm, float *__restrict__ agg_out,
     float *__restrict__ err_out, int N, int H_q, int H_kv, int H_lm, int C, int S, int W, int K, float scale,
@@ -370,24 +373,26 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
     constexpr bool QSPLIT = std::is_same<TQ, float>::value;
     constexpr int NQT = QSPLIT ? 2 : 1;   // query terms
     constexpr int NKT = KSPLIT ? 2 : 1;   // k' terms
-    constexpr int NT = 128 * G;
+    constexpr int NT = 128 * G * NQP;
+    constexpr int NPAIR = 2 * NQP;        // 32-query pairs per head
     constexpr int KS = D / 32;            // MFMA k-steps over the head dim
     constexpr int NB = D / 8;             // 16-byte blocks per k' row
     __shared__ u32x4 kt[NKT][G][16][NB];
     __shared__ float bt[G][16];
-    __shared__ f32x4 px[G > 1 ? G - 1 : 1][2][2][WAVE];
+    __shared__ f32x4 px[G > 1 ? G - 1 : 1][NPAIR][2][WAVE];
 
     const int g = blockIdx.y;
     const int64_t b = blockIdx.z;
-    const int i0 = blockIdx.x * 64;  // local row; position q0 + i0 (q0 % S == 0)
+    const int i0 = blockIdx.x * 64 * NQP;  // local row; position q0 + i0 (q0 % S == 0)
     const int w = W / S;
-    const int qc = (q0 + i0) / S;
-    const int n = max(0, qc - w);
+    // candidates of the block's last row (the most of its rows)
+    const int n = max(0, (q0 + min(N - 1, i0 + 64 * NQP - 1)) / S - w);
     if (n <= K) return;  // every candidate is selected; nothing to rank
 
     const int wave = threadIdx.x / WAVE, lane = lane_id();
-    const int qp = wave % 2, e = wave / 2;
+    const int qp = wave % NPAIR, e = wave / NPAIR;
     const int grp = lane >> 4;
+    const int n_row = max(0, (q0 + i0 + 32 * qp) / S - w);  // candidates of this wave's rows
     int iq[2], iqc[2];
     bool qvalid[2];
 #pragma unroll
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
 
     // k' tiles are staged through registers one tile ahead: the loads of
     // tile c0 + 16 are in flight while tile c0 is multiplied
-    constexpr int NPRE = NKT * NB / 8;  // 16-byte pieces per thread and tile
+    constexpr int NPRE = NKT * G * 16 * NB / NT;  // 16-byte pieces per thread and tile
     static_assert(NKT * G * 16 * NB == NPRE * NT, "staging pieces");
     u32x4 pre[NPRE];
     float bpre = 0.f;
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
                 float v[4], tm = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    v[i] = c0 + 4 * grp + i < n ? best[u][i] : -INFINITY;
+                    v[i] = c0 + 4 * grp + i < n_row ? best[u][i] : -INFINITY;
                     tm = fmaxf(tm, v[i]);
                 }
                 const float mn = fmaxf(lm[u], tm);
@@ -554,7 +559,7 @@ __global__ __launch_bounds__(128 * G) void score_approx_kernel(
                     }
             }
         }
-        if (e == 0) {
+        if (e == 0 && c0 < n_row) {  // (c0 < n_row keeps the store inside the row's pad16(n_row))
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 if (qvalid[u]) *(f32x4 *)(row[u] + c0 + 4 * grp) = best[u];
@@ -893,14 +898,18 @@ __global__ __launch_bounds__(256) void select_kernel(const TQ *__restrict__ q, c
 template <typename TQ, int D, int G, int AM>
 static void go_approx_m(const Shape &s, const TQ *qv, const float *b_sum, const ScoreWorkspace &ws, float kappa,
                         hipStream_t st) {
-    const dim3 grid((unsigned)((s.N + 63) / 64), (unsigned)s.H_kv, (unsigned)s.B), block(128 * G);
+    // 128-query blocks while they fit 1024 threads and the k' tile still
+    // gives every thread whole 16-byte pieces to stage
+    constexpr int NQP = (G <= 4 && D == 128) ? 2 : 1;
+    const dim3 grid((unsigned)((s.N + 64 * NQP - 1) / (64 * NQP)), (unsigned)s.H_kv, (unsigned)s.B),
+        block(128 * G * NQP);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, qv, (const bf16 *)ws.ksb, (const bf16 *)ws.ksb2, b_sum,
                            ws.knorm, ws.agg, ws.err, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.S, s.W, s.K, s.scale, kappa,
                            ws.per_bg, s.q0, ws.lse);
     };
-    if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false, AM>);
-    else go(score_approx_kernel<TQ, D, G, true, AM>);
+    if (s.sum_bf16) go(score_approx_kernel<TQ, D, G, false, AM, NQP>);
+    else go(score_approx_kernel<TQ, D, G, true, AM, NQP>);
 }
 
 template <typename TQ, int D, int G>
