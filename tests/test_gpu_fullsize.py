@@ -121,3 +121,36 @@ def test_decode_full_size(dev):
     atol, rtol = tol_for(cfg.io_dtype)
     assert_close(host(out).float().numpy(), refo, atol, rtol, "out")
     assert_close(host(lse).numpy(), refl, atol, rtol, "lse")
+
+
+def test_paged_prefill_full_size(dev):
+    """prefill_128k laid out in a paged cache at a random page placement:
+    page-by-page summaries equal the whole-sequence summaries, and the last
+    8192 tokens prefilled as one chunk over the paged cache (the bench's
+    serving call) equal the whole-sequence prefill's rows, bit for bit."""
+    import dataclasses
+
+    inp = W.make_prefill("prefill_128k", device=dev)
+    cfg = inp["cfg"]
+    print(f"[fullsize] paged prefill: whole-sequence prefill N={cfg.N}", flush=True)
+    full = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
+    kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=17)
+    P, C = kc.shape[0], cfg.C
+    ks = torch.empty((P, cfg.H_lm, cfg.d), dtype=cfg.summary_dtype, device=dev)
+    bs = torch.empty((P, cfg.H_lm), dtype=torch.float32, device=dev)
+    bb = torch.arange(cfg.B, device=dev).repeat_interleave(C)
+    cc = torch.arange(C, device=dev).repeat(cfg.B)
+    hb.summarize_pages(cfg, kc, inp["q_lm"][bb, :, cc].contiguous(), bt[bb, cc].contiguous(), ks, bs)
+    n = 8192
+    q_start = cfg.N - n
+    print(f"[fullsize] paged prefill: rows {q_start}..{cfg.N - 1}", flush=True)
+    out, lse, sel, ssc = hb.prefill_paged(dataclasses.replace(cfg, N=n), q_start,
+                                          inp["q"][:, :, q_start:].contiguous(), kc, vc, ks, bs, bt)
+    torch.cuda.synchronize()
+    pg = bt[0, :C].long()
+    assert torch.equal(ks[pg], full["k_sum"][0].permute(1, 0, 2))
+    assert torch.equal(bs[pg], full["b_sum"][0].permute(1, 0))
+    assert torch.equal(sel, full["sel_idx"][:, :, q_start:])
+    assert torch.equal(ssc, full["sel_score"][:, :, q_start:])
+    assert torch.equal(out, full["out"][:, :, q_start:])
+    assert torch.equal(lse, full["lse"][:, :, q_start:])
