@@ -230,3 +230,35 @@ def test_variant_modes_are_validated(lib):
     a = lib.hils_workspace_size(ctypes.byref(_cfg()), hb.WS_SCORE, 0, 0)
     b = lib.hils_workspace_size(ctypes.byref(_cfg(agg_mode=hb.AGG_NORMALIZED)), hb.WS_SCORE, 0, 0)
     assert b == a + 8 * 4096 * 4
+
+
+def _bwd(lib, cfg, ws=A2, nbytes=None, **ptr):
+    p = dict(q=A, k=A, v=A, q_lm=A, k_sum=A, sel_idx=A, sel_score=A, lse=A, dout=A, dlse=None, dq=A, dk=A, dv=A,
+             dq_lm=A)
+    p.update(ptr)
+    if nbytes is None:
+        nbytes = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_BACKWARD, 0, 0)
+    return lib.hils_sparse_attend_backward(ctypes.byref(cfg), p["q"], p["k"], p["v"], p["q_lm"], p["k_sum"],
+                                           p["sel_idx"], p["sel_score"], p["lse"], p["dout"], p["dlse"], p["dq"],
+                                           p["dk"], p["dv"], p["dq_lm"], ws, nbytes, None)
+
+
+def test_backward_argument_checks(lib):
+    cfg = _cfg()
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_BACKWARD, 0, 0)
+    assert need > 0
+    bf16sum = _cfg()
+    bf16sum.summary_dtype = hb.HILS_BF16
+    assert _bwd(lib, bf16sum) == hb.HILS_ERR_UNSUPPORTED and "summary_dtype" in hb.last_error()
+    for name in ("q", "k", "v", "lse", "dout", "dq", "dk", "dv", "sel_idx", "sel_score", "k_sum", "q_lm", "dq_lm"):
+        assert _bwd(lib, cfg, **{name: None}) == hb.HILS_ERR_INVALID_ARG, name
+        assert f"{name} is NULL" in hb.last_error()
+    # K = 0 reads no selection; mean pooling has no landmark query and no gradient for one
+    assert _bwd(lib, _cfg(K=0), sel_idx=None, sel_score=None, ws=None, nbytes=0) == hb.HILS_ERR_WORKSPACE
+    mean = _cfg(landmark_mode=hb.LM_MEAN)
+    assert _bwd(lib, mean, q_lm=None, dq_lm=None, ws=None, nbytes=0) == hb.HILS_ERR_WORKSPACE
+    assert _bwd(lib, cfg, dlse=MIS) == hb.HILS_ERR_INVALID_ARG and "dlse" in hb.last_error()
+    assert _bwd(lib, cfg, nbytes=need - 1) == hb.HILS_ERR_WORKSPACE
+    assert _bwd(lib, cfg, ws=MIS, nbytes=need) == hb.HILS_ERR_INVALID_ARG and "workspace" in hb.last_error()
+    empty = _cfg(N=0)
+    assert lib.hils_sparse_attend_backward(ctypes.byref(empty), *([None] * 15), 0, None) == hb.HILS_OK
