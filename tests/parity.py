@@ -1,6 +1,6 @@
 """Comparison helpers shared by the GPU parity tests and the smoke check.
 
-Tolerances (benchmark spec of the benchmark):
+Tolerances (the parity bar of the benchmark workloads):
   * bf16 inputs: |gpu - ref| <= 2e-3 + 1e-2 * |ref| elementwise;
   * fp32 inputs: |gpu - ref| <= 1e-5 + 1e-5 * |ref|;
   * selected chunk ids: identical sets, except rows where the oracle's K-th

@@ -3,7 +3,7 @@
 Stage tests feed the GPU and the oracle the same inputs (the oracle's own
 summaries / selection rounded to the GPU input dtype); end-to-end tests run
 both pipelines independently and compare selections with the near-tie rule
-and outputs to the benchmark spec's tolerance.
+and outputs to the output tolerance of tests/parity.py.
 """
 import math
 

@@ -118,7 +118,7 @@ def test_worked_prefill_s2(K):
 
 
 def test_taylor_identity_landmark_equals_query():
-    """Spec invariant (a): with q'_c = q_i, s^_ic = log sum_{j in c} exp(s_ij)."""
+    """Invariant (a): with q'_c = q_i, s^_ic = log sum_{j in c} exp(s_ij)."""
     rng = _rng(11)
     S, d, N = 16, 32, 256
     C = N // S
@@ -258,7 +258,7 @@ def _random_case(seed, S=8, d=16, N=256, G=2, H_kv=2, H_lm=None, W_chunks=1, K=3
 
 @pytest.mark.parametrize("seed", [21, 22, 23])
 def test_k1_selection_is_brute_force_argmax(seed):
-    """Spec invariant (c): K = 1 selects the argmax of the group score."""
+    """Invariant (c): K = 1 selects the argmax of the group score."""
     cfg, q, k, v, ql = _random_case(seed, K=1)
     ks, bs = oracle.summarize(cfg, k, ql)
     rows = np.arange(cfg["N"])
@@ -394,7 +394,7 @@ def test_s1_topk_tokens_plus_window():
 
 @pytest.mark.parametrize("G,H_kv", [(1, 1), (2, 2), (4, 1)])
 def test_self_landmark_all_chunks_is_dense(G, H_kv):
-    """Spec invariant (b): landmark = query and K >= n_cand give dense
+    """Invariant (b): landmark = query and K >= n_cand give dense
     causal attention."""
     rng = _rng(71 + G)
     S, d, N = 8, 16, 96
