@@ -462,6 +462,20 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                 __builtin_amdgcn_s_sleep(NSTAGE >= 4 ? 8 : 1);
             }
         }
+        // A stage is refilled only when its last wave leaves it, so the
+        // waves that at least half of the block has already passed are on
+        // the refill's critical path: they take issue priority over the
+        // waves running ahead for this chunk.  (rel[buf] holds
+        // NWAVE * lap + the waves that have left this lap's chunk; read in
+        // asm for the same reason as the flag.)
+        {
+            int left;
+            const uint32_t raddr = (uint32_t)(uintptr_t)&rel[buf];
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(left) : "v"(raddr) : "memory");
+            left = __builtin_amdgcn_readfirstlane(left) - NWAVE * (it / NSTAGE);
+            if (left >= NWAVE / 2) __builtin_amdgcn_s_setprio(3);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         if (__ballot(any) != 0ull) {
             f32x4 acc[TPW][KT];
             if (!window) {
