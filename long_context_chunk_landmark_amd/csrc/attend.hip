@@ -27,7 +27,9 @@
 //     the chunks its tiles compute (a flag the DMA writes behind the data),
 //     counts itself out of each stage, and the last wave out refills the
 //     stage NSTAGE chunks ahead, so waves drift up to NSTAGE - 1 chunks
-//     apart and the uneven per-chunk work of the tiles evens out.  A
+//     apart and the uneven per-chunk work of the tiles evens out.  The
+//     waves behind (those most of the block has passed) take issue priority,
+//     since the last of them gates the next refill.  A
 //     16-byte-block XOR swizzle by
 //     row (applied through the per-lane source address, since the DMA
 //     writes lane-contiguous LDS) keeps the MFMA operand reads free of
@@ -448,14 +450,21 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         // (LDS operations of a wave execute in order, so a plain flag read
         // orders the flag before the data reads, and those before the
         // release below; the asm statements are compiler barriers.)
+        int rel_seen = 0;  // rel[buf] read just after the flag
         {
             const int want = (it / NSTAGE) & 1;
-            const uint32_t faddr = (uint32_t)(uintptr_t)&flag[buf];  // LDS offset
+            const uint32_t faddr = (uint32_t)(uintptr_t)&flag[buf];  // LDS offsets
+            const uint32_t raddr = (uint32_t)(uintptr_t)&rel[buf];
             for (int spin = 0; spin < (1 << 18); ++spin) {
                 // read in asm: the compiler would otherwise first wait for
-                // all of this wave's DMA in flight (the flag is a DMA target)
-                int fv;
-                asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(fv) : "v"(faddr) : "memory");
+                // all of this wave's DMA in flight (the flag is a DMA target).
+                // The stage's leave counter comes in the same round trip.
+                int fv, rv;
+                asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(fv), "=v"(rv)
+                             : "v"(faddr), "v"(raddr)
+                             : "memory");
+                rel_seen = rv;
                 if (fv == want) break;
                 // a waiting wave yields its SIMD to the working ones (the
                 // longer pause suits the deeper ring: its waits are longer)
@@ -465,14 +474,12 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         // A stage is refilled only when its last wave leaves it, so the
         // waves that at least half of the block has already passed are on
         // the refill's critical path: they take issue priority over the
-        // waves running ahead for this chunk.  (rel[buf] holds
-        // NWAVE * lap + the waves that have left this lap's chunk; read in
-        // asm for the same reason as the flag.)
+        // waves running ahead for this chunk.  rel[buf] holds NWAVE * lap +
+        // the waves that have left this lap's chunk; read after this lap's
+        // flag, it is at least NWAVE * lap (the lap's DMA was issued once
+        // the previous lap's last wave left).
         {
-            int left;
-            const uint32_t raddr = (uint32_t)(uintptr_t)&rel[buf];
-            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(left) : "v"(raddr) : "memory");
-            left = __builtin_amdgcn_readfirstlane(left) - NWAVE * (it / NSTAGE);
+            const int left = __builtin_amdgcn_readfirstlane(rel_seen) - NWAVE * (it / NSTAGE);
             if (left >= NWAVE / 2) __builtin_amdgcn_s_setprio(3);
             else __builtin_amdgcn_s_setprio(0);
         }
