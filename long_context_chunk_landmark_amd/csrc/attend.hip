@@ -458,10 +458,12 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             for (int spin = 0; spin < (1 << 18); ++spin) {
                 // read in asm: the compiler would otherwise first wait for
                 // all of this wave's DMA in flight (the flag is a DMA target).
-                // The stage's leave counter comes in the same round trip.
+                // The stage's leave counter comes in the same round trip
+                // (early-clobber outputs: the first load's destination must
+                // not be the second load's address register).
                 int fv, rv;
                 asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                             : "=v"(fv), "=v"(rv)
+                             : "=&v"(fv), "=&v"(rv)
                              : "v"(faddr), "v"(raddr)
                              : "memory");
                 rel_seen = rv;
