@@ -107,6 +107,12 @@ typedef struct {
     float scale;           /* logit scale; 0 selects 1/sqrt(d)               */
     int32_t landmark_mode; /* hils_landmark_mode_t; 0 (per-chunk queries) by default */
     int32_t agg_mode;      /* hils_agg_mode_t; 0 (max of raw scores) by default   */
+    int32_t wait_spins;    /* bound on each internal wait of the bf16 fused-attention
+                              kernel, in pauses of the waiting wave; 0 selects the
+                              default (2^18).  A wait that reaches it gives up, and
+                              the call reports it in its status word (see
+                              hils_sparse_attend_fused).  Smaller values only serve
+                              to exercise that report. */
 } hils_config_t;
 
 /* Workspace kinds for hils_workspace_size(). */
@@ -163,10 +169,17 @@ hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const v
  *   q [B,H_q,N,d], k, v [B,H_kv,N,d] io_dtype; sel_idx / sel_score as
  *   written by hils_score_select; out [B,H_q,N,d] io_dtype (written);
  *   lse [B,H_q,N] fp32 (written, may be NULL).
- *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes (a
- *   transposed fp16 copy of v; 0 for fp32 I/O).  bf16 path: values of v
- *   must have magnitude below 65504 (v enters the probability-weighted sum
- *   as fp16). */
+ *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes (0 for
+ *   fp32 I/O).  bf16 I/O: bytes 0..255 are a status block, followed by a
+ *   transposed fp16 copy of v.  Word 0 of the status block (uint32) is
+ *   written by the call: 0 when every internal wait of the kernel completed,
+ *   nonzero when one gave up after cfg->wait_spins pauses; the outputs of
+ *   that call are then unreliable, and the rows of the waves that gave up
+ *   hold NaN in out and lse.  Read it once the stream is synchronised.
+ *   bf16 path: values of v must have magnitude below 65504 (v enters the
+ *   probability-weighted sum as fp16, which keeps 11 significant bits for
+ *   |v| >= 2^-14 and is subnormal below: a value under 2^-24 in magnitude
+ *   becomes 0). */
 hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, const void *k, const void *v,
                                        const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
                                        void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -241,7 +254,8 @@ hils_status_t hils_summarize_pages(const hils_config_t *cfg, int32_t num_items, 
  *   out         [B, H_q, N, d] io_dtype (written); lse [B, H_q, N] fp32
  *               (written, may be NULL)
  *   workspace   hils_prefill_paged_workspace_size(cfg, q_start, max_pages,
- *               h != NULL) bytes.
+ *               h != NULL) bytes; with bf16 I/O its word 0 is the status
+ *               word of hils_sparse_attend_fused.
  * num_pages <= 262144; q_start + N <= 8192 * S. */
 hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, const void *q, const void *k_cache,
                                  const void *v_cache, const void *ksum_cache, const float *bsum_cache,

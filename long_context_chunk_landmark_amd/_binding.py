@@ -49,7 +49,8 @@ class HilsError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "N", "H_q", "H_kv", "H_lm", "d", "S", "W", "K", "M", "io_dtype", "summary_dtype")] + [
-                   ("scale", ctypes.c_float), ("landmark_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32)]
+                   ("scale", ctypes.c_float), ("landmark_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32),
+                   ("wait_spins", ctypes.c_int32)]
 
 
 @dataclasses.dataclass
@@ -70,6 +71,7 @@ class Config:
     scale: float = 0.0
     landmark_mode: int = LM_CHUNK
     agg_mode: int = AGG_MAX
+    wait_spins: int = 0
 
     def __post_init__(self):
         if self.H_lm is None:
@@ -93,7 +95,7 @@ class Config:
 
         return _CConfig(self.B, self.N, self.H_q, self.H_kv, self.H_lm, self.d, self.S, self.W, self.K, self.M,
                         code(self.io_dtype), code(self.summary_dtype), float(self.scale), int(self.landmark_mode),
-                        int(self.agg_mode))
+                        int(self.agg_mode), int(self.wait_spins))
 
     def oracle_dict(self) -> dict:
         return dict(B=self.B, N=self.N, H_q=self.H_q, H_kv=self.H_kv, H_lm=self.H_lm, d=self.d, S=self.S, W=self.W,
@@ -201,6 +203,14 @@ def _want_q_lm(cfg: Config, q_lm, dev, items=None):
         return None  # mean pooling: no landmark queries
     _want(q_lm, "q_lm", shape, cfg.io_dtype, dev)
     return q_lm
+
+
+def status_word(workspace: torch.Tensor) -> int:
+    """Word 0 of a fused-attention (or chunked-prefill) workspace after the
+    call: 0 when every bounded wait of the kernel completed.  Synchronises
+    the current stream."""
+    torch.cuda.current_stream().synchronize()
+    return int(workspace[:4].view(torch.int32).item())
 
 
 def landmark_summarize(cfg: Config, k: torch.Tensor, q_lm: Optional[torch.Tensor], k_sum=None, b_sum=None):

@@ -41,9 +41,12 @@
 //     32-key group in the order the S^T accumulators deliver them.
 //   * Q K^T runs on bf16 operands (exact products of the bf16 inputs).  P
 //     lies in [0, 1] and is rounded to fp16 (8x finer than bf16), V^T is
-//     fp16 (exact for bf16 values below 65504), so V^T P^T runs on fp16
-//     MFMA: bf16 rounding of P alone can miss a 2e-3 absolute bound on rows
-//     with few keys whose values cancel.
+//     fp16, so V^T P^T runs on fp16 MFMA: bf16 rounding of P alone can miss
+//     a 2e-3 absolute bound on rows with few keys whose values cancel.  A
+//     bf16 value of v converts to fp16 exactly when 2^-14 <= |v| < 65504
+//     (fp16 normals keep 11 significant bits); below 2^-14 it rounds to the
+//     fp16 subnormal grid (absolute error <= 2^-25), so a value under 2^-25
+//     becomes 0.
 //   * Selected chunk c of a row: exact softmax over its S keys, scaled by
 //     exp(s^_c - m^) where m^ = max of the row's selected s^ (known up
 //     front); the window then continues as an online softmax from running
@@ -80,12 +83,15 @@ __host__ __device__ __forceinline__ int vt_slot_key(int p) {
 // vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]), 0 past
 // key Nk.  With a block table, chunk c of sequence b is page
 // bt[b * max_pages + c] of a paged cache [P, H_kv, S, D].
+// The first block also clears the call's status word (it runs before the
+// fused kernel on the same stream).
 template <int D, int S>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int Nk,
                                                           int CA, int H_kv, const int32_t *__restrict__ bt,
-                                                          int max_pages) {
+                                                          int max_pages, uint32_t *__restrict__ status) {
     __shared__ bf16 tile[S][D + 8];
     const int c = blockIdx.x;
+    if (c == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0u;
     const int64_t bg = (int64_t)blockIdx.z * H_kv + blockIdx.y;
     const bf16 *src = bt ? v + ((int64_t)bt[(int64_t)blockIdx.z * max_pages + c] * H_kv + blockIdx.y) * S * D
                          : v + (bg * Nk + (int64_t)c * S) * D;
@@ -159,7 +165,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, bf16 *__restrict__ out,
     float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP,
-    int nqb, int64_t n_items, int64_t per_xcd, int q0, int Nk, const int32_t *__restrict__ bt, int max_pages) {
+    int nqb, int64_t n_items, int64_t per_xcd, int q0, int Nk, const int32_t *__restrict__ bt, int max_pages,
+    int wait_spins, uint32_t *__restrict__ status) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
     constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, NP = Cf::NP;
@@ -430,6 +437,10 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     // tiles that a chunk activates spreads over several chunks' time.
     // Every wait is bounded, and the slowest wave never waits on another
     // wave: its chunk was issued when it left that chunk's stage.
+    // A wait that runs out of pauses gives up: the wave goes on, marks its
+    // rows NaN and sets the call's status word (the protocol's counters stay
+    // exact, so every wave still reaches the end).
+    bool expired = false;
     for (int j = wave; j < NSTAGE && j < T; j += NWAVE) issue(j);
     for (int it = 0; it < T; ++it) {
         const int buf = it % NSTAGE;
@@ -455,7 +466,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             const int want = (it / NSTAGE) & 1;
             const uint32_t faddr = (uint32_t)(uintptr_t)&flag[buf];  // LDS offsets
             const uint32_t raddr = (uint32_t)(uintptr_t)&rel[buf];
-            for (int spin = 0; spin < (1 << 18); ++spin) {
+            bool landed = false;
+            for (int spin = 0; spin < wait_spins; ++spin) {
                 // read in asm: the compiler would otherwise first wait for
                 // all of this wave's DMA in flight (the flag is a DMA target).
                 // The stage's leave counter comes in the same round trip
@@ -467,11 +479,15 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                              : "v"(faddr), "v"(raddr)
                              : "memory");
                 rel_seen = rv;
-                if (fv == want) break;
+                if (fv == want) {
+                    landed = true;
+                    break;
+                }
                 // a waiting wave yields its SIMD to the working ones (the
                 // longer pause suits the deeper ring: its waits are longer)
                 __builtin_amdgcn_s_sleep(NSTAGE >= 4 ? 8 : 1);
             }
+            expired |= !landed;
         }
         // A stage is refilled only when its last wave leaves it, so the
         // waves that at least half of the block has already passed are on
@@ -587,13 +603,14 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         if (old == NWAVE * (it / NSTAGE + 1) - 1 && it + NSTAGE < T) issue(it + NSTAGE);
     }
     wait_vmcnt<0>();  // no DMA outstanding when the wave retires
+    if (expired && lane == 0) atomicOr(status, 1u);
 
     // ---- epilogue
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int iq = i0 + qrow[t];
         if (iq >= N) continue;
-        const float inv = 1.f / lrun[t];
+        const float inv = expired ? __builtin_nanf("") : 1.f / lrun[t];
         bf16 *orow = out + ((b * H_q + hrow[t]) * N + iq) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -602,7 +619,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
             for (int i = 0; i < 4; ++i) y[i] = (bf16)(O[t][dt][i] * inv);
             *(bf16x4 *)(orow + 16 * dt + 4 * grp) = y;
         }
-        if (lse && grp == 0) lse[(b * H_q + hrow[t]) * N + iq] = (mrun[t] + log2f(lrun[t])) * LN2;
+        if (lse && grp == 0)
+            lse[(b * H_q + hrow[t]) * N + iq] = expired ? __builtin_nanf("") : (mrun[t] + log2f(lrun[t])) * LN2;
     }
 }
 
@@ -724,7 +742,7 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
 
 size_t fused_workspace_bytes(const Shape &s) {
     if (!s.io_bf16) return 0;
-    return align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
+    return FUSED_STATUS_BYTES + align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
 }
 
 // Block shapes: NWAVE waves of one 16-row tile each (QB = NWAVE * 16/G
@@ -755,7 +773,7 @@ static size_t attend_dyn_lds(const Shape &s) {
 
 template <int D, int S, int G, int NWAVE, int TPW>
 static hipError_t go_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                            const float *sel_score, void *out, float *lse, hipStream_t st) {
+                            const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
     using P = AttendPlan<D, S, G, NWAVE, TPW>;
     const int QB = P::QB;
     const int NW = (s.C + 31) / 32 + 1;
@@ -770,7 +788,7 @@ static hipError_t go_attend(const Shape &s, const void *q, const void *k, const 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
                        sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP,
-                       nqb, n_items, per_xcd, s.q0, s.Nk, s.bt, s.max_pages);
+                       nqb, n_items, per_xcd, s.q0, s.Nk, s.bt, s.max_pages, s.wait_spins, status);
     return hipGetLastError();
 }
 
@@ -786,24 +804,25 @@ static bool fits(const Shape &s) {
 // Largest block whose LDS (chunk ring + selections + union) fits.
 template <int D, int S, int G, int NWAVE, int TPW>
 static bool try_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                       const float *sel_score, void *out, float *lse, hipStream_t st, hipError_t &err) {
+                       const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st,
+                       hipError_t &err) {
     if constexpr (!AttendPlan<D, S, G, NWAVE, TPW>::valid) {
         return false;
     } else {
         if (!fits<D, S, G, NWAVE, TPW>(s)) return false;
-        err = go_attend<D, S, G, NWAVE, TPW>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        err = go_attend<D, S, G, NWAVE, TPW>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
         return true;
     }
 }
 
 template <int D, int S, int G>
 static hipError_t dispatch_w(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                             const float *sel_score, void *out, float *lse, hipStream_t st) {
+                             const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
     hipError_t err = hipErrorInvalidValue;
-    if (try_attend<D, S, G, 16, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
-    if (try_attend<D, S, G, 8, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
-    if (try_attend<D, S, G, 4, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
-    if (try_attend<D, S, G, 2, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st, err)) return err;
+    if (try_attend<D, S, G, 16, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
+    if (try_attend<D, S, G, 8, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
+    if (try_attend<D, S, G, 4, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
+    if (try_attend<D, S, G, 2, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
     return hipErrorInvalidValue;
 }
 
@@ -835,18 +854,19 @@ bool sparse_attend_supported(const Shape &s) {
 
 template <int D, int S>
 static hipError_t dispatch_g(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                             const float *sel_score, void *out, float *lse, hipStream_t st) {
+                             const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
     switch (s.G) {
-        case 1: return dispatch_w<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 2: return dispatch_w<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 4: return dispatch_w<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-        case 8: return dispatch_w<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+        case 1: return dispatch_w<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+        case 2: return dispatch_w<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+        case 4: return dispatch_w<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+        case 8: return dispatch_w<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
-                                const float *sel_score, void *out, float *lse, void *workspace, hipStream_t st) {
+                                const float *sel_score, void *out, float *lse, uint32_t *status, void *vt_ws,
+                                hipStream_t st) {
     if ((int64_t)s.B * s.N == 0) return hipSuccess;
     if (!s.io_bf16) {
         const int64_t rows = (int64_t)s.B * s.H_q * s.N;
@@ -862,11 +882,12 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
         return hipGetLastError();
     }
     // V^T pre-pass (fp16, slot order) into the workspace
-    f16 *vt = (f16 *)workspace;
+    f16 *vt = (f16 *)vt_ws;
     {
         const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
         auto vtr = [&](auto kern) {
-            hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16 *)v, vt, s.Nk, s.CA, s.H_kv, s.bt, s.max_pages);
+            hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16 *)v, vt, s.Nk, s.CA, s.H_kv, s.bt, s.max_pages,
+                               status);
         };
         if (s.D == 64 && s.S == 64) vtr(v_transpose_kernel<64, 64>);
         else if (s.D == 64) vtr(v_transpose_kernel<64, 128>);
@@ -875,10 +896,10 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (s.D == 64 && s.S == 64) return dispatch_g<64, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-    if (s.D == 64 && s.S == 128) return dispatch_g<64, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-    if (s.D == 128 && s.S == 64) return dispatch_g<128, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
-    if (s.D == 128 && s.S == 128) return dispatch_g<128, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, st);
+    if (s.D == 64 && s.S == 64) return dispatch_g<64, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+    if (s.D == 64 && s.S == 128) return dispatch_g<64, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+    if (s.D == 128 && s.S == 64) return dispatch_g<128, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+    if (s.D == 128 && s.S == 128) return dispatch_g<128, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
     return hipErrorInvalidValue;
 }
 

@@ -72,8 +72,10 @@ hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
         return fail(HILS_ERR_INVALID_ARG, "landmark_mode=%d unknown", cfg->landmark_mode);
     if (cfg->agg_mode != HILS_AGG_MAX && cfg->agg_mode != HILS_AGG_NORMALIZED)
         return fail(HILS_ERR_INVALID_ARG, "agg_mode=%d unknown", cfg->agg_mode);
+    if (cfg->wait_spins < 0) return fail(HILS_ERR_INVALID_ARG, "wait_spins=%d must be >= 0", cfg->wait_spins);
     s.lm_mode = cfg->landmark_mode;
     s.agg_mode = cfg->agg_mode;
+    s.wait_spins = cfg->wait_spins > 0 ? cfg->wait_spins : (1 << 18);
     s.io_bf16 = cfg->io_dtype == HILS_BF16;
     s.sum_bf16 = cfg->summary_dtype == HILS_BF16;
     s.scale = cfg->scale > 0.f ? cfg->scale : 1.0f / sqrtf((float)s.D);
@@ -115,8 +117,11 @@ hils_status_t resolve_paged(const hils_config_t *cfg, int32_t q_start, int32_t n
     return ok();
 }
 
+// [fused status block][score workspace][transposed v]: the status word sits
+// at offset 0 as in the fused entry point's workspace.
 size_t paged_workspace_bytes(const hils::Shape &s, bool qcal) {
-    return hils::align_up(hils::score_workspace_bytes(s, qcal), 256) + hils::fused_workspace_bytes(s);
+    return hils::align_up(hils::score_workspace_bytes(s, qcal), 256) + hils::fused_workspace_bytes(s) +
+           (s.io_bf16 ? 0 : hils::FUSED_STATUS_BYTES);
 }
 
 hils_status_t check_ptr(const void *p, const char *name) {
@@ -239,7 +244,9 @@ hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, 
         return fail(HILS_ERR_WORKSPACE, "sparse_attend_fused needs %zu workspace bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (need > 0 && !aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-    return hip_status(hils::launch_sparse_attend(s, q, k, v, sel_idx, sel_score, out, lse, workspace, stream),
+    uint32_t *status = s.io_bf16 ? (uint32_t *)workspace : nullptr;
+    void *vt_ws = s.io_bf16 ? (char *)workspace + hils::FUSED_STATUS_BYTES : nullptr;
+    return hip_status(hils::launch_sparse_attend(s, q, k, v, sel_idx, sel_score, out, lse, status, vt_ws, stream),
                       "sparse attention launch");
 }
 
@@ -344,16 +351,17 @@ hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, cons
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
     const size_t score_bytes = hils::align_up(hils::score_workspace_bytes(s, qcal), 256);
+    char *score_ws = (char *)workspace + hils::FUSED_STATUS_BYTES;
     if (s.K > 0) {
         hils::ScoreWorkspace ws;
-        hils::score_workspace_carve(s, qcal, workspace, ws);
+        hils::score_workspace_carve(s, qcal, score_ws, ws);
         if ((st = hip_status(hils::launch_score_select(s, q, ksum_cache, bsum_cache, h, w_down, w_up, d_model, r,
                                                        sel_idx, sel_score, ws, stream),
                              "paged score/select launch")))
             return st;
     }
     return hip_status(hils::launch_sparse_attend(s, q, k_cache, v_cache, sel_idx, sel_score, out, lse,
-                                                 (char *)workspace + score_bytes, stream),
+                                                 (uint32_t *)workspace, score_ws + score_bytes, stream),
                       "paged sparse attention launch");
 }
 

@@ -22,6 +22,7 @@ struct Shape {
     float scale;
     int lm_mode;   // landmark queries: 0 per chunk, 1 one shared per landmark head, 2 none (q' = 0)
     int agg_mode;  // group aggregation: 0 max of s^, 1 max of s^ - LSE over the candidates
+    int wait_spins;  // bound on each wait of the fused kernel (pauses)
     // Paged prefill (q0 = 0, Nk = N, bt = null for the contiguous layout):
     // the N query rows are positions q0 .. q0 + N - 1 (q0 % S == 0) of
     // sequences whose keys 0 .. Nk - 1 = q0 + N - 1 live in a paged cache
@@ -63,12 +64,18 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
                                float *sel_score, const ScoreWorkspace &ws, hipStream_t st);
 
 // ---- kernel 3: fused sparse attention
+// bf16 I/O: a 256-byte status block (word 0: nonzero when a bounded wait of
+// the kernel gave up) followed by the transposed fp16 copy of v; fp32: none.
+constexpr size_t FUSED_STATUS_BYTES = 256;
 size_t fused_workspace_bytes(const Shape &s);
 // Whether the fused kernel has a block shape whose LDS fits this shape
 // (every combination with K <= 32 does; large K with G = 1 at S = 128 may not).
 bool sparse_attend_supported(const Shape &s);
+// status: word zeroed by the launch and set when a wait gives up (bf16 I/O);
+// vt_ws: room for the transposed copy of v.
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
-                                const float *sel_score, void *out, float *lse, void *workspace, hipStream_t st);
+                                const float *sel_score, void *out, float *lse, uint32_t *status, void *vt_ws,
+                                hipStream_t st);
 
 // ---- kernel 4: decode
 size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages);

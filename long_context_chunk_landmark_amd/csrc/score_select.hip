@@ -9,8 +9,8 @@
 // scores the same candidate set), so it runs on bf16 MFMA.  fp32 operands
 // (k', a Q-Cal or fp32 query) enter as two-term bf16 splits, so the MFMA
 // scores are approximate within a rigorous bound E on |approx - exact|
-// (two-term residuals <= 2^-18 |x|, fp32 accumulation, Cauchy-Schwarz:
-// E = scale * kappa * ||q|| * max_c ||k'_c||).  The select kernel then
+// (a two-term split is within 2^-16 |x| of x, fp32 accumulation,
+// Cauchy-Schwarz: E = scale * kappa * ||q|| * max_c ||k'_c||).  The select kernel then
 // takes a lower bound tau' of the K-th largest approximate group score,
 // keeps every candidate whose approximate score is >= tau' - 2E (a superset
 // of the exact top-K, about K + 1 candidates), recomputes those in fp32 on
@@ -352,9 +352,10 @@ __global__ __launch_bounds__(256) void qcal_mfma_kernel(const bf16 *__restrict__
 // Split products: the scoring query q_s = t1 + t2 and k' = k1 + k2 with
 // t1 = bf16(q_s), t2 = bf16(q_s - t1) (k likewise); the MFMAs sum
 // t1 k1 + t1 k2 + t2 k1.  Terms that are exactly zero are skipped: bf16
-// queries have t2 = 0, bf16 summaries k2 = 0.  Each two-term split is
-// within 2^-18 |x| of x, the dropped t2 k2 term within 2^-18 |q||k|
-// elementwise, so by Cauchy-Schwarz |exact - approx| <= scale * kappa *
+// queries have t2 = 0, bf16 summaries k2 = 0.  A bf16 rounding is within
+// 2^-8 of its argument, so each two-term split is within 2^-16 |x| of x
+// and the dropped t2 k2 term within 2^-16 (1 + 2^-8)^2 |q_j||k_j|
+// elementwise; by Cauchy-Schwarz |exact - approx| <= scale * kappa *
 // ||q_s|| * max_c ||k'_c|| with kappa (set by the launcher) adding those
 // terms to a bound on the fp32 accumulation.
 //
@@ -1013,12 +1014,14 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    // kappa, relative to ||q_s|| ||k'||: fp32 accumulation (at most 2^9
-    // roundings of unit 2^-24 over d <= 128 products and three split terms,
-    // bounded by 2^-14), plus 2^-18 for each two-term split (fp32 queries,
-    // fp32 summaries) and 2^-18 for the dropped t2 k2 term, doubled.
+    // kappa, relative to ||q_s|| ||k'||.  Accumulation: the products of
+    // bf16 terms are exact in fp32 and at most 3 d <= 384 of them are summed,
+    // so fp32 rounding stays within gamma_384 (1 + 2^-7) < 2.4e-5, bounded
+    // here by 2^-14 whatever order the MFMA sums in.  Representation: each
+    // two-term split (fp32 queries, fp32 summaries) and the dropped t2 k2
+    // term add at most 2^-16 (1 + 2^-7) each.
     const int nq = (qcal || !s.io_bf16) ? 1 : 0, nk = s.sum_bf16 ? 0 : 1;
-    const float kappa = 1.0f / 16384.f + 2.f * (float)(nq + nk + nq * nk) / 262144.f;
+    const float kappa = 1.0f / 16384.f + (float)(nq + nk + nq * nk) * (1.f + 1.f / 128.f) / 65536.f;
 
     if (qcal || !s.io_bf16) {
         const float *qv = qcal ? ws.q_s : (const float *)q;

@@ -1,0 +1,160 @@
+"""Exact ties in the chunk ranking, on the GPU through the C ABI.
+
+The top-K keeps chunks by (group score descending, chunk index ascending), so
+of two chunks whose scores are equal the lower index wins (hyper.ai HiLS
+summary, 方法: chunks are ranked by the surrogate score and the top K kept;
+the group ranks by the max over its heads).  These workloads make the tie
+exact on both sides: chunk 2a+1 is a copy of chunk 2a (keys and landmark
+query for the prefill, summary-cache rows for the decode step), so both
+chunks get bitwise the same summary and the same score for every query, in
+the oracle's fp64 and in the kernels' fp32.  With K odd the K-th and
+(K+1)-th ranked chunks are then usually such twins, and the selection is
+decided by the tie-break alone.  The GPU selection must equal the oracle's
+exactly: no near-tie exemption applies here.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_chunk_landmark_amd import _binding as hb
+from long_context_chunk_landmark_amd import workloads as W
+from tests.parity import assert_close, host, oracle_prefill, tol_for
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+F32 = torch.float32
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hb.load_library()
+    return torch.device("cuda:0")
+
+
+def _twin_chunks(inp, S):
+    """Chunk 2a+1 := chunk 2a (keys and landmark queries), in place."""
+    k, q_lm = inp["k"], inp["q_lm"]
+    C = k.shape[2] // S
+    for a in range(C // 2):
+        lo, hi = 2 * a * S, (2 * a + 1) * S
+        k[:, :, hi:hi + S] = k[:, :, lo:lo + S]
+        if q_lm is not None and q_lm.dim() == 4:
+            q_lm[:, :, 2 * a + 1] = q_lm[:, :, 2 * a]
+
+
+def _tie_rows(ref, K):
+    """Rows whose oracle K-th and (K+1)-th group scores are exactly equal."""
+    kth = ref["kth"]
+    return np.isfinite(kth[..., 0]) & (kth[..., 0] == kth[..., 1])
+
+
+PREFILL_TIES = {
+    "g4_fp32sum": dict(seed=91, io=BF, B=1, H_q=8, H_kv=2, d=128, N=4096, S=64, W=256, K=7),
+    "g1_bf16sum_s128": dict(seed=92, io=BF, B=1, H_q=2, H_kv=2, d=128, N=8192, S=128, W=256, K=5, summary=BF),
+    "g8_d64_lmkv": dict(seed=93, io=BF, B=2, H_q=8, H_kv=1, H_lm=1, d=64, N=3000, S=64, W=128, K=9),
+    "qcal": dict(seed=94, io=BF, B=1, H_q=4, H_kv=1, d=128, N=4096, S=64, W=128, K=11, d_model=256, r=16),
+    "fp32io": dict(seed=95, io=F32, B=1, H_q=4, H_kv=2, d=64, N=2048, S=64, W=128, K=3),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_TIES))
+def test_prefill_exact_ties_take_lower_index(name, dev):
+    p = PREFILL_TIES[name]
+    inp = W.make_prefill(p, device=dev)
+    cfg = inp["cfg"]
+    _twin_chunks(inp, cfg.S)
+    print(f"[ties prefill] {name}", flush=True)
+    res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"], qcal=inp.get("qcal"))
+    torch.cuda.synchronize()
+    # the twins' summaries are bitwise equal on the GPU as well
+    ks, bs = host(res["k_sum"]), host(res["b_sum"])
+    C = cfg.C
+    for a in range(C // 2):
+        assert torch.equal(ks[:, :, 2 * a], ks[:, :, 2 * a + 1]), f"k_sum twin {a}"
+        assert torch.equal(bs[:, :, 2 * a], bs[:, :, 2 * a + 1]), f"b_sum twin {a}"
+    ref = oracle_prefill(cfg, inp)
+    gsel = host(res["sel_idx"]).numpy()
+    ties = _tie_rows(ref, cfg.K)
+    # the construction puts a tie at the boundary of most ranked rows
+    n_cand = np.array([max(0, i // cfg.S - cfg.W // cfg.S) for i in range(cfg.N)])
+    ranked = np.broadcast_to(n_cand > cfg.K, ties.shape)
+    assert ties.sum() >= 0.5 * ranked.sum() > 0, (int(ties.sum()), int(ranked.sum()))
+    bad = np.argwhere(np.any(gsel != ref["sel_idx"], axis=-1))
+    assert len(bad) == 0, (f"{len(bad)} rows differ from the oracle, e.g. {bad[:3].tolist()}: gpu "
+                           f"{gsel[tuple(bad[0])].tolist()} oracle {ref['sel_idx'][tuple(bad[0])].tolist()}")
+    # on every tie row the boundary pair splits: its lower twin is kept
+    b, g, i = np.argwhere(ties)[0]
+    kept = set(gsel[b, g, i].tolist())
+    assert any(c % 2 == 0 and c + 1 not in kept for c in kept), "no split twin pair on a tie row"
+    atol, rtol = tol_for(cfg.io_dtype)
+    assert_close(host(res["out"]).float().numpy(), ref["out"], atol, rtol, "out")
+    assert_close(host(res["lse"]).numpy(), ref["lse"], atol, rtol, "lse")
+
+
+# Sequence lengths give every sequence an even number of candidates, so every
+# candidate has its twin and, with K odd, every row ranks a tie at its boundary.
+DECODE_TIES = {
+    # bf16 summaries, H_lm = H_q, d = 128: the page-contiguous scorer
+    "pages_scorer": dict(seed=96, io=BF, num_seqs=4, seq_len=4000, H_q=8, H_kv=2, d=128, S=64, W=256, K=7,
+                         pages=300, summary=BF, seq_lens=[4000, 3333, 2049, 1600]),
+    # one landmark head per kv head: the per-group scorer
+    "group_scorer": dict(seed=97, io=BF, num_seqs=3, seq_len=3000, H_q=8, H_kv=2, H_lm=2, d=128, S=64, W=128,
+                         K=9, pages=200, summary=BF, seq_lens=[3000, 2600, 1200]),
+    "fp32": dict(seed=98, io=F32, num_seqs=2, seq_len=2600, H_q=4, H_kv=1, d=64, S=64, W=128, K=5, pages=100,
+                 summary=F32, seq_lens=[2600, 1950]),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_TIES))
+def test_decode_exact_ties_take_lower_index(name, dev):
+    inp = W.make_decode(DECODE_TIES[name], device=dev)
+    cfg = inp["cfg"]
+    bt = host(inp["block_table"]).long()
+    ks, bs = inp["ksum_cache"], inp["bsum_cache"]
+    for b in range(bt.shape[0]):
+        for a in range(bt.shape[1] // 2):
+            ks[bt[b, 2 * a + 1]] = ks[bt[b, 2 * a]]
+            bs[bt[b, 2 * a + 1]] = bs[bt[b, 2 * a]]
+    print(f"[ties decode] {name}", flush=True)
+    out, lse, sel = hb.decode(cfg, inp["q"], inp["k_cache"], inp["v_cache"], ks, bs, inp["block_table"],
+                              inp["seq_lens"])
+    torch.cuda.synchronize()
+    sl = host(inp["seq_lens"]).numpy()
+    ref = oracle.decode(cfg.oracle_dict(), host(inp["q"]), host(inp["k_cache"]), host(inp["v_cache"]), host(ks),
+                        host(bs), host(inp["block_table"]), sl)
+    ties = _tie_rows(ref, cfg.K)
+    assert ties.all(), (int(ties.sum()), ties.size)
+    np.testing.assert_array_equal(host(sel).numpy(), ref["sel_idx"])
+    atol, rtol = tol_for(cfg.io_dtype)
+    assert_close(host(out).float().numpy(), ref["out"], atol, rtol, "out")
+    assert_close(host(lse).numpy(), ref["lse"], atol, rtol, "lse")
+
+
+def test_prefill_ties_paged_equals_contiguous(dev):
+    """The chunked prefill over a paged cache breaks the same ties the same
+    way (its selection passes the same ranking)."""
+    p = dict(PREFILL_TIES["g4_fp32sum"])
+    inp = W.make_prefill(p, device=dev)
+    cfg = inp["cfg"]
+    _twin_chunks(inp, cfg.S)
+    res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
+    kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=5)
+    P = kc.shape[0]
+    ksc = torch.zeros((P, cfg.H_lm, cfg.d), dtype=cfg.summary_dtype, device=dev)
+    bsc = torch.zeros((P, cfg.H_lm), dtype=F32, device=dev)
+    C = cfg.C
+    pages = bt[0, :C].long()
+    ksc[pages] = res["k_sum"][0].permute(1, 0, 2)
+    bsc[pages] = res["b_sum"][0].permute(1, 0)
+    q_start = cfg.N // 2 // cfg.S * cfg.S
+    cc = dataclasses.replace(cfg, N=cfg.N - q_start)
+    out, lse, sel, _ = hb.prefill_paged(cc, q_start, inp["q"][:, :, q_start:].contiguous(), kc, vc, ksc, bsc, bt)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, res["sel_idx"][:, :, q_start:])
+    assert torch.equal(out, res["out"][:, :, q_start:])

@@ -437,6 +437,34 @@ def test_rows_without_candidates_are_dense():
     np.testing.assert_allclose(res["lse"], l[:, :, rows], atol=1e-12)
 
 
+def test_dense_causal_rows_is_textbook_attention():
+    """The oracle's dense causal attention equals the numpy/scipy textbook
+    softmax attention under GQA (query head h reads kv head h // G), on all
+    rows and on a row subset; with every key equal, each row's output is the
+    mean of the values 0..i and its log-mass is s + log(i + 1)."""
+    rng = _rng(97)
+    B, H_q, H_kv, N, d = 2, 4, 2, 40, 16
+    cfg = _cfg(B=B, H_q=H_q, H_kv=H_kv, N=N, S=8, d=d)
+    q = rng.standard_normal((B, H_q, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, H_kv, N, d)).astype(np.float32)
+    v = rng.standard_normal((B, H_kv, N, d)).astype(np.float32)
+    o_ref, l_ref = _dense_textbook(q, k, v, 1 / math.sqrt(d))
+    o, l = oracle.dense_causal_rows(cfg, q, k, v)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    np.testing.assert_allclose(l, l_ref, atol=1e-12)
+    rows = np.array([0, 7, 8, 39])
+    o2, l2 = oracle.dense_causal_rows(cfg, q, k, v, rows=rows)
+    np.testing.assert_allclose(o2, o_ref[:, :, rows], atol=1e-12)
+    np.testing.assert_allclose(l2, l_ref[:, :, rows], atol=1e-12)
+    ke = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    o3, l3 = oracle.dense_causal_rows(cfg, q, ke, v)
+    cnt = np.arange(1, N + 1, dtype=np.float64)
+    mean_v = np.cumsum(v.astype(np.float64), axis=2) / cnt[None, None, :, None]
+    s = np.einsum("bhid,bhd->bhi", q.astype(np.float64), np.repeat(ke[:, :, 0].astype(np.float64), 2, axis=1))
+    np.testing.assert_allclose(o3, np.repeat(mean_v, 2, axis=1), atol=1e-12)
+    np.testing.assert_allclose(l3, s / math.sqrt(d) + np.log(cnt)[None, None, :], atol=1e-12)
+
+
 def test_fusion_weights_are_convex_and_output_linear_in_v():
     cfg, q, k, v, ql = _random_case(92, K=2)
     ks, bs = oracle.summarize(cfg, k, ql)
