@@ -208,6 +208,25 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
                           const void *w_down, const void *w_up, int32_t d_model, int32_t r, void *out, float *lse,
                           int32_t *sel_idx, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hils_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, layouts and results are
+ * those of hils_decode.  Its scratch is a static device array of
+ * HILS_DECODE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; its address is looked up on the first call on
+ * each device.  A call whose scratch need (hils_workspace_size(cfg,
+ * HILS_WS_DECODE, num_seqs, max_pages)) exceeds that size returns
+ * HILS_ERR_UNSUPPORTED.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  The
+ * stream must belong to the current device. */
+#define HILS_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+hils_status_t hils_decode_noalloc(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,
+                                  const void *v_cache, const void *ksum_cache, const float *bsum_cache,
+                                  const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                                  const void *h, const void *w_down, const void *w_up, int32_t d_model, int32_t r,
+                                  void *out, float *lse, int32_t *sel_idx, hipStream_t stream);
+
 /* Landmark summaries of chunks that complete while a sequence is served:
  * item i summarises the S keys held by page pages[i] of the paged key cache
  * with the landmark queries q_lm[i] (the summary definition of

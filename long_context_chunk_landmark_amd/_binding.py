@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "hils_score_select",
     "hils_sparse_attend_fused",
     "hils_decode",
+    "hils_decode_noalloc",
     "hils_summarize_pages",
     "hils_prefill_paged",
     "hils_prefill_paged_workspace_size",
@@ -129,6 +130,8 @@ def load_library(path: str = LIB_PATH):
     lib.hils_sparse_attend_fused.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_decode.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz,
                                 vp]
+    lib.hils_decode_noalloc.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                        vp]
     lib.hils_summarize_pages.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, vp]
     lib.hils_prefill_paged.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp,
                                        vp, vp, sz, vp]
@@ -140,6 +143,7 @@ def load_library(path: str = LIB_PATH):
     lib.hils_last_error.restype = ctypes.c_char_p
     lib.hils_version.restype = ctypes.c_int
     for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode",
+               "hils_decode_noalloc",
                "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -320,6 +324,39 @@ def decode(cfg: Config, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table
                                       _ptr(ksum_cache), _ptr(bsum_cache), _ptr(block_table), max_pages,
                                       _ptr(seq_lens), _ptr(h), _ptr(wd), _ptr(wu), d_model, r, _ptr(out), _ptr(lse),
                                       _ptr(sel_idx), _ptr(ws), nbytes, _stream()))
+    return out, lse, sel_idx
+
+
+def decode_noalloc(cfg: Config, q, k_cache, v_cache, ksum_cache, bsum_cache, block_table, seq_lens, out, lse,
+                   sel_idx, qcal=None):
+    """hils_decode_noalloc: the decode step with the library's static scratch
+    instead of a workspace.  The outputs are the caller's (no tensor is
+    created here)."""
+    dev = q.device
+    num_seqs = q.shape[0]
+    P = k_cache.shape[0]
+    max_pages = block_table.shape[1]
+    _want(q, "q", (num_seqs, cfg.H_q, cfg.d), cfg.io_dtype, dev)
+    _want(k_cache, "k_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(v_cache, "v_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(ksum_cache, "ksum_cache", (ksum_cache.shape[0], cfg.H_lm, cfg.d), cfg.summary_dtype, dev)
+    _want(bsum_cache, "bsum_cache", (ksum_cache.shape[0], cfg.H_lm), torch.float32, dev)
+    _want(block_table, "block_table", (num_seqs, max_pages), torch.int32, dev)
+    _want(seq_lens, "seq_lens", (num_seqs,), torch.int32, dev)
+    _want(out, "out", (num_seqs, cfg.H_q, cfg.d), cfg.io_dtype, dev)
+    _want(lse, "lse", (num_seqs, cfg.H_q), torch.float32, dev)
+    if sel_idx is not None:
+        _want(sel_idx, "sel_idx", (num_seqs, cfg.H_kv, cfg.K), torch.int32, dev)
+    h = wd = wu = None
+    d_model = r = 0
+    if qcal is not None:
+        h, wd, wu = qcal
+        r, d_model = wd.shape
+    c = cfg.to_c()
+    _check(load_library().hils_decode_noalloc(ctypes.byref(c), num_seqs, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(ksum_cache), _ptr(bsum_cache), _ptr(block_table), max_pages,
+                                              _ptr(seq_lens), _ptr(h), _ptr(wd), _ptr(wu), d_model, r, _ptr(out),
+                                              _ptr(lse), _ptr(sel_idx), _stream()))
     return out, lse, sel_idx
 
 

@@ -141,6 +141,13 @@ hils_status_t check_qcal(const void *h, const void *w_down, const void *w_up, in
 
 }  // namespace
 
+namespace hils {
+int report_error(int status, const char *msg) {
+    snprintf(g_err, sizeof(g_err), "%s", msg);
+    return status;
+}
+}  // namespace hils
+
 extern "C" {
 
 const char *hils_last_error(void) { return g_err; }

@@ -97,4 +97,8 @@ hipError_t launch_backward(const Shape &s, const void *q, const void *k, const v
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Record msg as the calling thread's last error (hils_last_error) and
+// return status.
+int report_error(int status, const char *msg);
+
 }  // namespace hils
