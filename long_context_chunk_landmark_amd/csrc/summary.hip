@@ -104,95 +104,103 @@ __global__ __launch_bounds__(256) void landmark_summary_kernel(const T *__restri
     }
 }
 
-// Fast path for bf16 keys at d = 128 (16 lanes per key row).  Keys go in
-// blocks of 64 rows: lane (col, rsub) holds rows 4t + rsub of the block,
-// t < 16, as packed bf16.  Per landmark head, the partial dots (packed
-// bf16 dot2 instructions, fp32 accumulation) are transpose-reduced over the
-// 16 lanes of the DPP row, after which the lane holds the logit of block
-// row 4*col + rsub (base-2 scaled).  p goes through LDS, transposed per
-// rsub, to every lane for the weighted key sum.  A 128-key chunk keeps one
-// block in registers and re-reads the other (from L2) when it needs it.
+// Fast path for bf16 keys at d = 128 (16 lanes per key row).  A chunk's keys
+// go in blocks of 64 rows, one block per wave (S / 64 waves per chunk, in
+// one workgroup of 4 waves), loaded once: lane (col, rsub) holds rows
+// 4t + rsub of its block, t < 16, as packed bf16.  Per landmark head, the
+// partial dots (packed bf16 dot2 instructions, fp32 accumulation) are
+// transpose-reduced over the 16 lanes of the DPP row, after which the lane
+// holds the logit of block row 4*col + rsub (base-2 scaled).  The waves of a
+// 128-key chunk combine their softmax statistics (max, mass, mass-weighted
+// logit) through LDS.  p goes through LDS, transposed per rsub, to every
+// lane of its wave for the weighted key sum; the second wave's partial k'
+// is added by the first, which writes the summary.
 template <typename TS, int S, int GLM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void landmark_summary_d128_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ q_lm, TS *__restrict__ k_sum, float *__restrict__ b_sum,
     int H_kv, int N, int C, float scale, int64_t total_units, const int32_t *__restrict__ pages, int num_pages,
     int lm_mode) {
-    constexpr int D = 128, NB = S / 64;
+    constexpr int D = 128, NB = S / 64, CPB = 4 / NB;  // waves per chunk, chunks per workgroup
+    static_assert(NB == 1 || NB == 2, "64- or 128-key chunks");
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    __shared__ float p_lds[4][4][S / 4];  // [wave of block][rsub][block * 16 + t]
-    const int lane = lane_id();
-    const int64_t unit = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-    if (unit >= total_units) return;
-    const int c = (int)(unit % C);
-    const int64_t bg = unit / C;  // b * H_kv + g
+    __shared__ float p_lds[4][4][16];  // [wave][rsub][t]: p of block row 4t + rsub
+    __shared__ float stat[4][4];       // [wave]: max, mass, mass-weighted logit (base 2)
+    __shared__ float part[4][D];       // [wave]: partial k' of a chunk's second block
+    const int lane = lane_id(), wv = threadIdx.x / WAVE, half = wv % NB;
+    const int64_t unit = (int64_t)blockIdx.x * CPB + wv / NB;
+    bool live = unit < total_units;
+    const int c = live ? (int)(unit % C) : 0;
+    const int64_t bg = live ? unit / C : 0;  // b * H_kv + g
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
     // paged: item b summarises page pb (keys and summary row); else pb = b
-    const int64_t pb = pages ? (int64_t)pages[b] : b;
-    if (pb < 0 || (pages && pb >= num_pages)) return;
+    const int64_t pb = (pages && live) ? (int64_t)pages[b] : b;
+    live = live && pb >= 0 && !(pages && pb >= num_pages);
+    // a dead wave of a 128-key chunk still takes part in the barriers
+    if (NB == 1 && !live) return;
     const int col = lane & 15, rsub = lane >> 4;
-    float(*pw)[S / 4] = p_lds[(threadIdx.x / WAVE) & 3];
-    const bf16 *kb = k + ((pb * H_kv + g) * N + (int64_t)c * S) * D + col * 8;
+    float(*pw)[16] = p_lds[wv];
+    const bf16 *kb = k + ((pb * H_kv + g) * N + (int64_t)c * S + 64 * half) * D + col * 8;
     const float sl2 = scale * LOG2E;
     const int H_lm = H_kv * GLM;
 
     u32x4 kx[16];
-    auto load_block = [&](int blk) {
-        // an opaque block offset keeps the reloads inside the head loop
-        // (hoisted, both blocks would stay live in registers)
-        int off = 64 * blk * D;
-        asm volatile("" : "+s"(off));
 #pragma unroll
-        for (int t = 0; t < 16; ++t) kx[t] = *(const u32x4 *)(kb + off + (t * 4 + rsub) * D);
-    };
-    load_block(NB - 1);
+    for (int t = 0; t < 16; ++t) kx[t] = u32x4{0u, 0u, 0u, 0u};
+    if (live) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) kx[t] = *(const u32x4 *)(kb + (t * 4 + rsub) * D);
+    }
 #pragma unroll 1
     for (int e = 0; e < GLM; ++e) {
         const int64_t lrow = (b * H_lm + (int64_t)g * GLM + e) * C + c;   // landmark query
         const int64_t orow = (pb * H_lm + (int64_t)g * GLM + e) * C + c;  // summary
         // landmark query: per chunk, shared by all chunks of head l, or zero
-        const u32x4 qr = lm_mode == 2 ? u32x4{0u, 0u, 0u, 0u}
-                                      : *(const u32x4 *)(q_lm + (lm_mode == 1 ? (int64_t)g * GLM + e : lrow) * D +
-                                                         col * 8);
-        float lg[NB];
+        u32x4 qr = u32x4{0u, 0u, 0u, 0u};
+        if (live && lm_mode != 2)
+            qr = *(const u32x4 *)(q_lm + (lm_mode == 1 ? (int64_t)g * GLM + e : lrow) * D + col * 8);
+        float prt[16];
 #pragma unroll
-        for (int blk = NB - 1; blk >= 0; --blk) {
-            if (blk != NB - 1) load_block(blk);
-            float part[16];
+        for (int t = 0; t < 16; ++t) {
+            float acc = 0.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = 0.f;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const uint32_t qa = qr[x], kb2 = kx[t][x];
-                    bf16x2 a2, b2;
-                    __builtin_memcpy(&a2, &qa, 4);
-                    __builtin_memcpy(&b2, &kb2, 4);
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, acc, false);
-                }
-                part[t] = acc;
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t qa = qr[x], kb2 = kx[t][x];
+                bf16x2 a2, b2;
+                __builtin_memcpy(&a2, &qa, 4);
+                __builtin_memcpy(&b2, &kb2, 4);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, acc, false);
             }
-            lg[blk] = transpose_sum16(part, col) * sl2;
+            prt[t] = acc;
         }
-        float m = lg[0];
-#pragma unroll
-        for (int h = 1; h < NB; ++h) m = fmaxf(m, lg[h]);
-        m = wave_max_f(m);
-        float ex[NB], z = 0.f, ez = 0.f;
-#pragma unroll
-        for (int h = 0; h < NB; ++h) {
-            ex[h] = exp2f(lg[h] - m);
-            z += ex[h];
-            ez = fmaf(ex[h], lg[h] - m, ez);
+        const float lg = transpose_sum16(prt, col) * sl2;
+        float m = wave_max_f(lg);
+        float ex = exp2f(lg - m);
+        float z = wave_sum_f(ex);
+        float ez = wave_sum_f(ex * (lg - m));
+        if constexpr (NB == 2) {
+            // both waves combine the two blocks' statistics in the same order
+            if (lane == 0) {
+                stat[wv][0] = m;
+                stat[wv][1] = z;
+                stat[wv][2] = ez;
+            }
+            __syncthreads();
+            const int w0 = wv & ~1;
+            const float m0 = stat[w0][0], z0 = stat[w0][1], ez0 = stat[w0][2];
+            const float m1 = stat[w0 + 1][0], z1 = stat[w0 + 1][1], ez1 = stat[w0 + 1][2];
+            const float mn = fmaxf(m0, m1);
+            const float a0 = exp2f(m0 - mn), a1 = exp2f(m1 - mn);
+            // sum_j 2^(lg_j - mn) (lg_j - mn) = a (ez + (m - mn) z) per block
+            ez = a0 * fmaf(m0 - mn, z0, ez0) + a1 * fmaf(m1 - mn, z1, ez1);
+            z = a0 * z0 + a1 * z1;
+            ex *= half ? a1 : a0;
         }
-        z = wave_sum_f(z);
-        ez = wave_sum_f(ez);
         const float inv_z = 1.f / z;
         // entropy = ln 2 * (log2 Z - sum_j p_j (a2_j - m)), a2 = base-2 logits
         const float ent = LN2 * (log2f(z) - ez * inv_z);
         wave_sync();
-#pragma unroll
-        for (int h = 0; h < NB; ++h) pw[rsub][16 * h + col] = ex[h] * inv_z;
+        pw[rsub][col] = ex * inv_z;
         wave_sync();
         float acc[8];
 #pragma unroll
@@ -203,25 +211,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void l
         uint32_t sh = 16, mk = 0xffff0000u;
         asm volatile("" : "+v"(sh), "+v"(mk));
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            if (NB > 1) load_block(blk);
+        for (int t0 = 0; t0 < 16; t0 += 4) {
+            const f32x4 p4 = *(const f32x4 *)&pw[rsub][t0];
 #pragma unroll
-            for (int t0 = 0; t0 < 16; t0 += 4) {
-                const f32x4 p4 = *(const f32x4 *)&pw[rsub][16 * blk + t0];
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const uint32_t w = kx[t0 + u][x];
-                        acc[2 * x] = fmaf(p4[u], __uint_as_float(w << sh), acc[2 * x]);
-                        acc[2 * x + 1] = fmaf(p4[u], __uint_as_float(w & mk), acc[2 * x + 1]);
-                    }
-            }
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t w = kx[t0 + u][x];
+                    acc[2 * x] = fmaf(p4[u], __uint_as_float(w << sh), acc[2 * x]);
+                    acc[2 * x + 1] = fmaf(p4[u], __uint_as_float(w & mk), acc[2 * x + 1]);
+                }
         }
-        if (NB > 1) load_block(NB - 1);
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] = rows4_sum(acc[x]);
-        if (rsub == 0) {
+        if constexpr (NB == 2) {
+            if (half == 1 && rsub == 0) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) part[wv][col * 8 + x] = acc[x];
+            }
+            __syncthreads();
+            if (half == 0) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc[x] += part[wv + 1][col * 8 + x];
+            }
+        }
+        if (live && half == 0 && rsub == 0) {
             TS *dst = k_sum + orow * D + col * 8;
 #pragma unroll
             for (int x = 0; x < 8; ++x) dst[x] = from_f32<TS>(acc[x]);
@@ -235,7 +249,10 @@ static hipError_t launch_s(const Shape &s, const void *k, const void *q_lm, void
                            const int32_t *pages, int num_pages, hipStream_t st) {
     const int64_t units = (int64_t)s.B * s.H_kv * s.C;
     if (units == 0) return hipSuccess;
-    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+    // four waves per workgroup: one chunk each, or, on the bf16 d = 128 path,
+    // S / 64 waves per chunk
+    const int cpb = (std::is_same<T, bf16>::value && D == 128) ? 4 / (S / 64) : 4;
+    const dim3 grid((unsigned)((units + cpb - 1) / cpb)), block(256);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const T *)k, (const T *)q_lm, (TS *)k_sum, b_sum, s.H_kv, s.N,
                            s.C, s.scale, units, pages, num_pages, s.lm_mode);
