@@ -172,14 +172,17 @@ hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const v
  *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes (0 for
  *   fp32 I/O).  bf16 I/O: bytes 0..255 are a status block, followed by a
  *   transposed fp16 copy of v.  Word 0 of the status block (uint32) is
- *   written by the call: 0 when every internal wait of the kernel completed,
- *   nonzero when one gave up after cfg->wait_spins pauses; the outputs of
- *   that call are then unreliable, and the rows of the waves that gave up
- *   hold NaN in out and lse.  Read it once the stream is synchronised.
- *   bf16 path: values of v must have magnitude below 65504 (v enters the
- *   probability-weighted sum as fp16, which keeps 11 significant bits for
- *   |v| >= 2^-14 and is subnormal below: a value under 2^-24 in magnitude
- *   becomes 0). */
+ *   written by the call; read it once the stream is synchronised.  0: the
+ *   call completed normally.  Bit 0: an internal wait of the kernel gave up
+ *   after cfg->wait_spins pauses; the rows of the waves that gave up hold
+ *   NaN in out and lse.  Bit 1: some value of v is not finite or has
+ *   magnitude >= 65520, beyond fp16's range.  With either bit set the
+ *   outputs of the call are unreliable.
+ *   bf16 path: v enters the probability-weighted sum as fp16.  A bf16 value
+ *   converts exactly when 2^-14 <= |v| <= 65280 (the largest bf16 value
+ *   below fp16's maximum 65504).  Below 2^-14 it rounds to fp16's subnormal
+ *   grid, an absolute error of at most 2^-25, and a magnitude of at most
+ *   2^-25 becomes 0. */
 hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, const void *k, const void *v,
                                        const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
                                        void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -211,8 +211,9 @@ def _want_q_lm(cfg: Config, q_lm, dev, items=None):
 
 def status_word(workspace: torch.Tensor) -> int:
     """Word 0 of a fused-attention (or chunked-prefill) workspace after the
-    call: 0 when every bounded wait of the kernel completed.  Synchronises
-    the current stream."""
+    call: 0 when the call completed normally; bit 0 when a bounded wait of
+    the kernel gave up, bit 1 when a value of v is beyond fp16's range.
+    Synchronises the current stream."""
     torch.cuda.current_stream().synchronize()
     return int(workspace[:4].view(torch.int32).item())
 

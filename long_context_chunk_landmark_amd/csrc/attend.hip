@@ -45,8 +45,9 @@
 //     a 2e-3 absolute bound on rows with few keys whose values cancel.  A
 //     bf16 value of v converts to fp16 exactly when 2^-14 <= |v| < 65504
 //     (fp16 normals keep 11 significant bits); below 2^-14 it rounds to the
-//     fp16 subnormal grid (absolute error <= 2^-25), so a value under 2^-25
-//     becomes 0.
+//     fp16 subnormal grid (absolute error <= 2^-25), so a magnitude of at most
+//     2^-25 becomes 0.  A value beyond fp16's range sets bit 1 of the
+//     call's status word (V^T pre-pass).
 //   * Selected chunk c of a row: exact softmax over its S keys, scaled by
 //     exp(s^_c - m^) where m^ = max of the row's selected s^ (known up
 //     front); the window then continues as an online softmax from running
@@ -83,18 +84,19 @@ __host__ __device__ __forceinline__ int vt_slot_key(int p) {
 // vt[b, g, c, d, slot] = fp16(v[b, g, c*S + vt_slot_key(slot), d]), 0 past
 // key Nk.  With a block table, chunk c of sequence b is page
 // bt[b * max_pages + c] of a paged cache [P, H_kv, S, D].
-// The first block also clears the call's status word (it runs before the
-// fused kernel on the same stream).
+// A value of v that fp16 cannot hold (|v| >= 65520, or not finite) sets bit
+// 1 of the call's status word: the probability-weighted sum would then be
+// wrong.
 template <int D, int S>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict__ v, f16 *__restrict__ vt, int Nk,
                                                           int CA, int H_kv, const int32_t *__restrict__ bt,
                                                           int max_pages, uint32_t *__restrict__ status) {
     __shared__ bf16 tile[S][D + 8];
     const int c = blockIdx.x;
-    if (c == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0u;
     const int64_t bg = (int64_t)blockIdx.z * H_kv + blockIdx.y;
     const bf16 *src = bt ? v + ((int64_t)bt[(int64_t)blockIdx.z * max_pages + c] * H_kv + blockIdx.y) * S * D
                          : v + (bg * Nk + (int64_t)c * S) * D;
+    bool range_bad = false;
     for (int idx = threadIdx.x; idx < S * (D / 8); idx += blockDim.x) {
         const int j = idx / (D / 8), cb = idx % (D / 8);
         u32x4 val = {0u, 0u, 0u, 0u};
@@ -102,8 +104,12 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
         bf16x8 x;
         __builtin_memcpy(&x, &val, 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tile[j][cb * 8 + e] = x[e];
+        for (int e = 0; e < 8; ++e) {
+            tile[j][cb * 8 + e] = x[e];
+            range_bad |= !(fabsf((float)x[e]) < 65520.f);
+        }
     }
+    if (__ballot(range_bad) != 0ull && lane_id() == 0) atomicOr(status, 2u);
     __syncthreads();
     f16 *dst = vt + (bg * CA + c) * (int64_t)D * S;
     for (int idx = threadIdx.x; idx < D * (S / 8); idx += blockDim.x) {
@@ -113,6 +119,11 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const bf16 *__restrict
         for (int e = 0; e < 8; ++e) x[e] = (f16)(float)tile[vt_slot_key(blk * 8 + e)][d];
         *(f16x8 *)(dst + (int64_t)d * S + blk * 8) = x;
     }
+}
+
+// Zeroes the status word of a call (the first kernel of the call).
+__global__ void status_clear_kernel(uint32_t *status) {
+    if (threadIdx.x == 0) *status = 0u;
 }
 
 // s_waitcnt with vmcnt = n (expcnt / lgkmcnt not waited).
@@ -881,7 +892,9 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
                                s.W, s.K, s.scale, s.q0, s.Nk, s.bt, s.max_pages);
         return hipGetLastError();
     }
-    // V^T pre-pass (fp16, slot order) into the workspace
+    // clear the call's status word, then the V^T pre-pass (fp16, slot
+    // order) into the workspace
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, st, status);
     f16 *vt = (f16 *)vt_ws;
     {
         const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);

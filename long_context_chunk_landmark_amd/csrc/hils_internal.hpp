@@ -64,8 +64,9 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
                                float *sel_score, const ScoreWorkspace &ws, hipStream_t st);
 
 // ---- kernel 3: fused sparse attention
-// bf16 I/O: a 256-byte status block (word 0: nonzero when a bounded wait of
-// the kernel gave up) followed by the transposed fp16 copy of v; fp32: none.
+// bf16 I/O: a 256-byte status block (word 0: bit 0 set when a bounded wait
+// of the kernel gave up, bit 1 when a value of v is beyond fp16's range)
+// followed by the transposed fp16 copy of v; fp32: none.
 constexpr size_t FUSED_STATUS_BYTES = 256;
 size_t fused_workspace_bytes(const Shape &s);
 // Whether the fused kernel has a block shape whose LDS fits this shape

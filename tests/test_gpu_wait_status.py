@@ -72,3 +72,29 @@ def test_paged_prefill_status_word_is_clear(dev):
                                         workspace=ws)
     assert hb.status_word(ws) == 0
     assert torch.equal(out, res["out"][:, :, q_start:])
+
+
+def test_v_beyond_fp16_range_sets_status_bit(dev):
+    """v enters the probability-weighted sum as fp16: a value fp16 cannot hold
+    (|v| >= 65520) sets bit 1 of the status word, and a normal call clears it."""
+    inp = W.make_prefill(dict(seed=72, io=torch.bfloat16, B=1, H_q=4, H_kv=1, d=128, N=1024, S=64, W=128, K=4),
+                         device=dev)
+    cfg = inp["cfg"]
+    ref = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
+    ws = torch.empty(hb.workspace_size(cfg, hb.WS_FUSED), dtype=torch.uint8, device=dev)
+    ws.fill_(0xFF)
+    v_big = inp["v"].clone()
+    v_big[0, 0, 517, 3] = 1.0e5  # bf16 99840
+    print("[status] v beyond fp16 range", flush=True)
+    hb.sparse_attend_fused(cfg, inp["q"], inp["k"], v_big, ref["sel_idx"], ref["sel_score"], workspace=ws)
+    assert hb.status_word(ws) & 2
+    v_edge = inp["v"].clone()
+    v_edge[0, 0, 517, 3] = 65280.0  # the largest bf16 value fp16 holds: no report
+    print("[status] v at the edge of fp16 range", flush=True)
+    hb.sparse_attend_fused(cfg, inp["q"], inp["k"], v_edge, ref["sel_idx"], ref["sel_score"], workspace=ws)
+    assert hb.status_word(ws) == 0
+    print("[status] normal v", flush=True)
+    out, lse = hb.sparse_attend_fused(cfg, inp["q"], inp["k"], inp["v"], ref["sel_idx"], ref["sel_score"],
+                                      workspace=ws)
+    assert hb.status_word(ws) == 0
+    assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
