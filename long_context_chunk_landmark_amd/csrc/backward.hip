@@ -27,6 +27,8 @@
 //              summary backward into dk and dq'.
 // fp32 VALU throughout: a first, exact backward; the forward's MFMA
 // schedule is not carried over.
+#include <type_traits>
+
 #include "hils_device.hpp"
 #include "hils_internal.hpp"
 
@@ -435,6 +437,364 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     }
 }
 
+// ---------------------------------------------------------------- MFMA key pass (bf16 I/O)
+//
+// The key-side pass on the matrix cores.  Block (chunk c, kv head g, batch
+// b) of S / 16 waves; wave w owns keys c*S + 16w .. +15 and keeps their K
+// and V slices in registers as B operands, with dK^T and dV^T of those keys
+// as fp32 accumulators (lane l: key 16w + l%16, dims 16dt + 4(l/16) + i).
+// The rows that attend chunk c (the window rows, then the later rows that
+// selected it) go in tiles of 32 (row, head) pairs staged in LDS, row-major
+// (A operand of S = Q K^T and dP = dO V^T) and transposed (A operand of
+// dK^T += Q^T dS and dV^T += dO^T P).  The accumulators of S for pairs 0-15
+// and 16-31 hold, in lane group gq, pairs 4gq + i and 16 + 4gq + i of key
+// l%16: as the B operand of the second products they are k-slots 8gq + i
+// and 8gq + 4 + i, the order the transposed tiles are written in.  P and
+// dS enter those products as two bf16 terms each (hi + lo, within 2^-16 of
+// the fp32 value); q, k, v and dO are bf16 inputs, so every product is
+// exact and the sums are fp32.
+
+namespace {
+
+// 16-byte block swizzle of an LDS row of NB blocks, by row, so the 16 rows
+// of one MFMA operand read fall in distinct bank groups
+template <int NB>
+__device__ __forceinline__ int bswz(int row) {
+    return NB == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+
+}  // namespace
+
+template <int D, int S, int G>
+__global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void bwd_keys_mfma_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ q_lm, const int32_t *__restrict__ sel_idx, const uint64_t *__restrict__ selbits,
+    const float *__restrict__ lse, const bf16 *__restrict__ dout, const float *__restrict__ dcoef,
+    const float *__restrict__ dsel, const float *__restrict__ mlog, const float *__restrict__ gdo,
+    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dq_lm, int N, int H_q, int H_kv, int H_lm,
+    int C, int W, int K, float scale, int lm_mode) {
+    constexpr int NT = 4 * S;                     // one wave per 16 keys
+    constexpr int BW = 16, LCAP = BW * 64 + 32;  // bitmap words per batch; row list capacity
+    constexpr int KS = D / 32, DT = D / 16, NB = D / 8;
+    constexpr int RT = 32, RPT = RT / G;  // pairs and rows per row tile
+    constexpr int NQ = 4, DPT = D / NQ;   // summary backward: four threads per key
+    __shared__ u32x4 q_t[RT][NB];         // tile rows of q (bf16, swizzled by pair)
+    __shared__ u32x4 do_t[RT][NB];        // and of dO
+    __shared__ u32x4 qT[D][4];            // q transposed: [dim][k-slot], 32 bf16 per dim
+    __shared__ u32x4 doT[D][4];           // dO transposed
+    __shared__ float pbias[RT];           // per pair: log-weight added to the scaled logit
+    __shared__ float pdc[RT];             // the term subtracted from dO.v (D' or dO.o_c)
+    __shared__ float pdsh[RT];            // ds^_c of a selecting pair (0 for window pairs)
+    __shared__ int prow[RT];              // last key the pair may see (its row; selected: all)
+    __shared__ int list_i[LCAP];
+    __shared__ int list_k[LCAP];
+    __shared__ int nlist;
+    __shared__ float red[S][D + 1];  // summary backward: per-key partial rows
+    __shared__ float a_l[S], p_l[S], kd_l[S], da_l[S];
+    __shared__ float dkp_l[G][D];
+    __shared__ float dbp_l[G];
+    __shared__ float qp_l[D];
+
+    const int c = blockIdx.x, g = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int GLM = H_lm / H_kv;
+    const int t = threadIdx.x, wave = t / WAVE, lane = lane_id(), grp = lane >> 4, r16 = lane & 15;
+    const int64_t kvb = (b * H_kv + g) * (int64_t)N;  // first key row of (b, g)
+    const int keyl = 16 * wave + r16;                  // the lane's key within the chunk
+    const int key = c * S + keyl;
+    const bool key_ok = key < N;
+
+    bf16x8 kf[KS], vf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+        if (key_ok) {
+            kr = *(const u32x4 *)(k + (kvb + key) * D + 32 * s + 8 * grp);
+            vr = *(const u32x4 *)(v + (kvb + key) * D + 32 * s + 8 * grp);
+        }
+        __builtin_memcpy(&kf[s], &kr, 16);
+        __builtin_memcpy(&vf[s], &vr, 16);
+    }
+    f32x4 accK[DT], accV[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) accK[dt] = accV[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int idx = t; idx < G * D; idx += NT) dkp_l[idx / D][idx % D] = 0.f;
+    if (t < G) dbp_l[t] = 0.f;
+
+    // one tile: nrows rows x G heads; pair p is row p / G, head p % G;
+    // row_of(rr) -> (row, selection slot)
+    auto run_tile = [&](int nrows, bool selected, auto row_of) {
+        __syncthreads();  // the previous tile is no longer read
+        const int np = nrows * G;
+        for (int idx = t; idx < 2 * RT * NB; idx += NT) {
+            const int which = idx / (RT * NB), rem = idx % (RT * NB), p = rem / NB, cb = rem % NB;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (p < np) {
+                const int64_t rh = (b * H_q + (int64_t)g * G + p % G) * N + row_of(p / G).x;
+                val = *(const u32x4 *)((which ? dout : q) + rh * D + cb * 8);
+            }
+            (which ? do_t : q_t)[p][cb ^ bswz<NB>(p)] = val;
+        }
+        if (t < RT) {
+            float bias = -INFINITY, dc = 0.f, dsh = 0.f;
+            int lim = -1;
+            if (t < np) {
+                const int2 ik = row_of(t / G);
+                const int64_t rh = (b * H_q + (int64_t)g * G + t % G) * N + ik.x;
+                if (selected) {
+                    bias = mlog[rh * K + ik.y];  // P_j = e^{s_j + m}, m = s^_c - L - lse_c
+                    dc = gdo[rh * K + ik.y];
+                    dsh = dsel[rh * K + ik.y];
+                    lim = 0x7fffffff;
+                } else {
+                    bias = -lse[rh];
+                    dc = dcoef[rh];
+                    lim = ik.x;
+                }
+            }
+            pbias[t] = bias;
+            pdc[t] = dc;
+            pdsh[t] = dsh;
+            prow[t] = lim;
+        }
+        __syncthreads();
+        // the transposed tiles, 8 k-slots (16 bytes) of one dim per item
+        for (int idx = t; idx < 2 * D * 4; idx += NT) {
+            const int which = idx / (D * 4), x = (idx / 4) % D, jb = idx % 4;
+            const u32x4(*src)[NB] = which ? do_t : q_t;
+            bf16x8 e8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int p = j < 4 ? 4 * jb + j : 16 + 4 * jb + (j - 4);  // pair of k-slot 8 jb + j
+                e8[j] = ((const bf16 *)&src[p][(x >> 3) ^ bswz<NB>(p)])[x & 7];
+            }
+            __builtin_memcpy(&(which ? doT : qT)[x][jb], &e8, 16);
+        }
+        __syncthreads();
+        f32x4 sacc[2], dacc[2];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+            sacc[rg] = dacc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int pr = 16 * rg + r16;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int blk = (4 * s + grp) ^ bswz<NB>(pr);
+                bf16x8 qa, da;
+                const u32x4 rq = q_t[pr][blk], rd = do_t[pr][blk];
+                __builtin_memcpy(&qa, &rq, 16);
+                __builtin_memcpy(&da, &rd, 16);
+                sacc[rg] = mfma16(qa, kf[s], sacc[rg]);
+                dacc[rg] = mfma16(da, vf[s], dacc[rg]);
+            }
+        }
+        bf16x8 ph, pl, sh, sl;
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = 16 * rg + 4 * grp + i;
+                float P = 0.f;
+                if (key_ok && key <= prow[p]) P = expf(fmaf(sacc[rg][i], scale, pbias[p]));
+                const float ds = scale * P * (dacc[rg][i] - pdc[p]);
+                const bf16 p1 = (bf16)P, d1 = (bf16)ds;
+                ph[4 * rg + i] = p1;
+                pl[4 * rg + i] = (bf16)(P - (float)p1);
+                sh[4 * rg + i] = d1;
+                sl[4 * rg + i] = (bf16)(ds - (float)d1);
+            }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            bf16x8 ad, aq;
+            const u32x4 rd = doT[16 * dt + r16][grp], rq = qT[16 * dt + r16][grp];
+            __builtin_memcpy(&ad, &rd, 16);
+            __builtin_memcpy(&aq, &rq, 16);
+            accV[dt] = mfma16(ad, ph, accV[dt]);
+            accV[dt] = mfma16(ad, pl, accV[dt]);
+            accK[dt] = mfma16(aq, sh, accK[dt]);
+            accK[dt] = mfma16(aq, sl, accK[dt]);
+        }
+        if (selected) {
+            // dk' += scale ds^ q and db' += ds^ of each landmark head, by
+            // owner threads (dim t % D of heads t / D, + NT / D, ...)
+            const int x = t % D;
+            for (int lm = t / D; lm < GLM; lm += NT / D) {
+                float acc = dkp_l[lm][x], accb = 0.f;
+                for (int p = 0; p < np; ++p) {
+                    if ((GLM == G ? p % G : 0) != lm) continue;
+                    const bf16 qx = ((const bf16 *)&q_t[p][(x >> 3) ^ bswz<NB>(p)])[x & 7];
+                    acc = fmaf(scale * pdsh[p], (float)qx, acc);
+                    accb += pdsh[p];
+                }
+                dkp_l[lm][x] = acc;
+                if (x == 0) dbp_l[lm] += accb;
+            }
+        }
+    };
+
+    // window rows: query chunks c .. c + W/S
+    const int r_end = (int)min((int64_t)N, (int64_t)(c + W / S + 1) * S);
+    for (int i0 = c * S; i0 < r_end; i0 += RPT)
+        run_tile(min(RPT, r_end - i0), false, [&](int rr) { return make_int2(i0 + rr, 0); });
+
+    // rows of later query chunks that selected chunk c, in row order, from
+    // the chunk's row bitmap: BW words per batch go to the row list (wave
+    // 0); each listed row finds the chunk's slot in its selection (the count
+    // of its entries below c: the lists are ascending); full tiles run, and
+    // the rows of a partial tile carry over to the next batch
+    if (K > 0 && c < C) {
+        const int NWB = (N + 63) / 64;
+        const uint64_t *bw = selbits + ((b * H_kv + g) * (int64_t)C + c) * NWB;
+        if (t == 0) nlist = 0;
+        for (int w0 = r_end / 64; w0 < NWB; w0 += BW) {
+            __syncthreads();  // nlist and the carried rows are in place
+            const int carry = nlist;
+            if (wave == 0) {
+                uint64_t word = 0ull;
+                if (lane < BW && w0 + lane < NWB) {
+                    word = bw[w0 + lane];
+                    if (w0 + lane == r_end / 64) word &= ~0ull << (r_end & 63);  // rows >= r_end only
+                }
+                const int cnt = __popcll(word);
+                int incl = cnt;
+#pragma unroll
+                for (int o = 1; o < WAVE; o <<= 1) {
+                    const int y = __shfl_up(incl, o, WAVE);
+                    if (lane >= o) incl += y;
+                }
+                int pos = carry + incl - cnt;
+                while (word) {
+                    const int bit = __builtin_ffsll((long long)word) - 1;
+                    word &= word - 1;
+                    list_i[pos++] = (w0 + lane) * 64 + bit;
+                }
+                if (lane == WAVE - 1) nlist = carry + incl;
+            }
+            __syncthreads();
+            const int tot = nlist;
+            for (int x = carry + t; x < tot; x += NT) {
+                const int32_t *sr = sel_idx + ((b * H_kv + g) * N + list_i[x]) * K;
+                int below = 0;
+#pragma unroll 8
+                for (int kk = 0; kk < K; ++kk) {
+                    const int y = sr[kk];
+                    below += (y >= 0 && y < c) ? 1 : 0;
+                }
+                list_k[x] = below;
+            }
+            __syncthreads();
+            const bool last = w0 + BW >= NWB;
+            const int nfull = last ? tot : tot / RPT * RPT;
+            for (int r0 = 0; r0 < nfull; r0 += RPT)
+                run_tile(min(RPT, nfull - r0), true,
+                         [&](int rr) { return make_int2(list_i[r0 + rr], list_k[r0 + rr]); });
+            __syncthreads();  // the tiles are done with the list
+            const bool mv = t < tot - nfull;
+            int li = 0, lk = 0;
+            if (mv) li = list_i[nfull + t], lk = list_k[nfull + t];
+            __syncthreads();
+            if (mv) list_i[t] = li, list_k[t] = lk;
+            if (t == 0) nlist = tot - nfull;
+        }
+    }
+
+    // dv is final (the summary does not involve v)
+    if (key_ok) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4 *)(dv + (kvb + key) * D + 16 * dt + 4 * grp) = accV[dt];
+    }
+
+    // ---- summary backward of the chunk's landmark heads (completed chunks):
+    // a_j = scale q'.k_j, p = softmax a; da_j = p_j dk'.(k_j - k') -
+    // db' p_j (a_j - p.a); dk_j += p_j dk' + scale da_j q'; dq' = scale sum_j da_j k_j
+    if (c < C) {
+        __syncthreads();  // dk', db' complete
+        const int jj = t / NQ, qd = t % NQ, x0 = qd * DPT;
+        const int64_t jrow = (int64_t)c * S + jj;  // completed chunk: jrow < N
+        float kr[DPT];
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) kr[x] = (float)k[(kvb + jrow) * D + x0 + x];
+        auto quad_sum = [&](float a) {
+            a += __shfl_xor(a, 1, WAVE);
+            a += __shfl_xor(a, 2, WAVE);
+            return a;
+        };
+        for (int e = 0; e < GLM; ++e) {
+            const int lh = g * GLM + e;
+            const int64_t lrow = ((b * H_lm + lh) * C + c) * D;
+            // landmark query: per chunk, one shared by the chunks of head lh, or zero
+            const int64_t qrow = lm_mode == 1 ? (int64_t)lh * D : lrow;
+            float pa = 0.f, pk = 0.f;
+#pragma unroll
+            for (int x = 0; x < DPT; ++x) {
+                const float qx = lm_mode == 2 ? 0.f : (float)q_lm[qrow + x0 + x];
+                pa = fmaf(qx, kr[x], pa);
+                pk = fmaf(dkp_l[e][x0 + x], kr[x], pk);
+            }
+            const float a = scale * quad_sum(pa), kdk = quad_sum(pk);  // a_j, dk'.k_j
+            __syncthreads();  // the previous head is done with the LDS rows
+            if (qd == 0) a_l[jj] = a, kd_l[jj] = kdk;
+            if (t < D) qp_l[t] = lm_mode == 2 ? 0.f : (float)q_lm[qrow + t];
+            __syncthreads();
+            float mx = -INFINITY;
+            for (int r = 0; r < S; ++r) mx = fmaxf(mx, a_l[r]);
+            float z = 0.f, za = 0.f, zk = 0.f;
+            for (int r = 0; r < S; ++r) {
+                const float ex = expf(a_l[r] - mx);
+                z += ex;
+                za = fmaf(ex, a_l[r], za);
+                zk = fmaf(ex, kd_l[r], zk);
+            }
+            const float p = expf(a - mx) / z;
+            const float abar = za / z, kpdk = zk / z;  // p.a, dk'.k'
+            const float da = p * (kdk - kpdk) - dbp_l[e] * p * (a - abar);
+            if (qd == 0) p_l[jj] = p, da_l[jj] = da;
+#pragma unroll
+            for (int x = 0; x < DPT; ++x) red[jj][x0 + x] = da * kr[x];
+            __syncthreads();
+            // dk_j += p_j dk' + scale da_j q' in the accumulator layout
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = 16 * dt + 4 * grp + i;
+                    accK[dt][i] = fmaf(p_l[keyl], dkp_l[e][x], accK[dt][i]);
+                    accK[dt][i] = fmaf(scale * da_l[keyl], qp_l[x], accK[dt][i]);
+                }
+            if (lm_mode != 2 && t < D) {
+                float sum = 0.f;
+                for (int r = 0; r < S; ++r) sum += red[r][t];
+                dq_lm[lrow + t] = scale * sum;
+            }
+        }
+    }
+
+    if (key_ok) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4 *)(dk + (kvb + key) * D + 16 * dt + 4 * grp) = accK[dt];
+    }
+}
+
+// Row bitmap of each chunk's selecting rows: bit i of row c of (b, g) is
+// set when row i selected chunk c (order-free ORs, so the map is
+// deterministic).  Thread per row.
+__global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t *__restrict__ sel_idx,
+                                                          uint64_t *__restrict__ selbits, int N, int H_kv, int C,
+                                                          int K) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int64_t bg = (int64_t)blockIdx.z * H_kv + blockIdx.y;
+    if (i >= N) return;
+    const int NWB = (N + 63) / 64;
+    const int32_t *sr = sel_idx + (bg * N + i) * K;
+    for (int kk = 0; kk < K; ++kk) {
+        const int c = sr[kk];
+        if (c >= 0 && c < C) atomicOr((unsigned long long *)&selbits[(bg * C + c) * NWB + i / 64], 1ull << (i & 63));
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_u64_kernel(uint64_t *__restrict__ p, int64_t n) {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) p[x] = 0ull;
+}
+
 // Shared landmark query: the gradient of the one query of head l is the sum
 // of the per-chunk gradients over every sequence and chunk, in a fixed order.
 __global__ __launch_bounds__(256) void bwd_shared_query_kernel(const float *__restrict__ per_chunk,
@@ -449,10 +809,17 @@ __global__ __launch_bounds__(256) void bwd_shared_query_kernel(const float *__re
     dq_lm[idx] = acc;
 }
 
+// bf16 I/O: one bit per (chunk, row) of each (b, kv head)
+static size_t selbits_bytes(const Shape &s) {
+    if (!s.io_bf16 || s.K == 0) return 0;
+    return (size_t)s.B * s.H_kv * s.C * ((s.N + 63) / 64) * 8;
+}
+
 size_t backward_workspace_bytes(const Shape &s) {
     const size_t rows = (size_t)s.B * s.H_q * s.N;
     size_t b = 3 * align_up(rows * s.K * 4, 256) + align_up(rows * 4, 256);
     if (s.lm_mode == 1) b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // per-chunk dq'
+    b += align_up(selbits_bytes(s), 256);
     return b;
 }
 
@@ -473,6 +840,9 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     p += align_up(rows * 4, 256);
     // shared landmark query: per-chunk gradients first, summed afterwards
     float *dql_chunks = s.lm_mode == 1 ? (float *)p : dq_lm;
+    if (s.lm_mode == 1) p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
+    uint64_t *selbits = (uint64_t *)p;  // bf16 I/O with K > 0
+    const int64_t nbits = (int64_t)(selbits_bytes(s) / 8);
     const dim3 rgrid((unsigned)((int64_t)s.B * s.H_kv * s.N));
     auto go_rows = [&](auto kern, int G) {
         hipLaunchKernelGGL(kern, rgrid, dim3(64 * G), 0, st, (const T *)q, (const T *)k, (const T *)v, k_sum, sel_idx,
@@ -488,10 +858,31 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_keys_kernel<T, D, S>), dim3((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), dim3(4 * S), 0,
-                       st, (const T *)q, (const T *)k, (const T *)v, (const T *)q_lm, sel_idx, lse, (const T *)dout,
-                       dcoef, dsel, mlog, gdo, dk, dv, dql_chunks, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale,
-                       s.lm_mode);
+    const dim3 kgrid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B);
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (nbits > 0) {
+            hipLaunchKernelGGL(bwd_zero_u64_kernel, dim3((unsigned)std::min<int64_t>(4096, (nbits + 255) / 256)),
+                               dim3(256), 0, st, selbits, nbits);
+            hipLaunchKernelGGL(bwd_selbits_kernel, dim3((unsigned)((s.N + 255) / 256), (unsigned)s.H_kv, (unsigned)s.B),
+                               dim3(256), 0, st, sel_idx, selbits, s.N, s.H_kv, s.C, s.K);
+        }
+        auto go_keys = [&](auto kern) {
+            hipLaunchKernelGGL(kern, kgrid, dim3(4 * S), 0, st, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
+                               (const bf16 *)q_lm, sel_idx, (const uint64_t *)selbits, lse, (const bf16 *)dout, dcoef,
+                               dsel, mlog, gdo, dk, dv, dql_chunks, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale,
+                               s.lm_mode);
+        };
+        switch (s.G) {
+            case 1: go_keys(bwd_keys_mfma_kernel<D, S, 1>); break;
+            case 2: go_keys(bwd_keys_mfma_kernel<D, S, 2>); break;
+            case 4: go_keys(bwd_keys_mfma_kernel<D, S, 4>); break;
+            default: go_keys(bwd_keys_mfma_kernel<D, S, 8>); break;
+        }
+    } else {
+        hipLaunchKernelGGL((bwd_keys_kernel<T, D, S>), kgrid, dim3(4 * S), 0, st, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)q_lm, sel_idx, lse, (const T *)dout, dcoef, dsel, mlog, gdo, dk,
+                           dv, dql_chunks, s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale, s.lm_mode);
+    }
     if (s.lm_mode == 1) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_shared_query_kernel, dim3((unsigned)((s.H_lm * s.D + 255) / 256)), dim3(256), 0, st,
