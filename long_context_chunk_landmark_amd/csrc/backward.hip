@@ -32,6 +32,11 @@
 #include "hils_device.hpp"
 #include "hils_internal.hpp"
 
+#define BWD_LPTR(p) ((void __attribute__((address_space(3))) *)(p))
+// Word 3 of a raw buffer resource on CDNA: 32-bit data format (untyped
+// dword loads), no swizzle, no index stride.
+#define BWD_RSRC_WORD3 0x00020000
+
 namespace hils {
 
 // dot of an fp32 vector in LDS with a row of T in global memory (16-byte loads)
@@ -774,6 +779,355 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     }
 }
 
+// ---------------------------------------------------------------- MFMA row pass (bf16 I/O)
+//
+// Key of k-slot p of a chunk: in the S^T accumulators of 16-key tiles 2s
+// and 2s+1, lane group gq holds keys 32s + 4gq + {0..3} and 32s + 16 + 4gq +
+// {0..3}; as the B operand of a 32-key step they are slots 8gq .. 8gq + 7.
+__device__ __forceinline__ int bwd_slot_key(int p) {
+    const int s = p >> 5, qd = p & 31, gq = qd >> 3, j = qd & 7;
+    return 32 * s + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
+}
+
+// kt[(bg * CA + c) * D * S + x * S + p] = k[bg, c * S + bwd_slot_key(p), x]
+// (bf16, zero past key N): the A operand of dq^T += K^T dS^T.
+template <int D, int S>
+__global__ __launch_bounds__(256) void bwd_kslot_kernel(const bf16 *__restrict__ k, bf16 *__restrict__ kt, int N,
+                                                        int CA) {
+    __shared__ bf16 tile[S][D + 8];
+    const int c = blockIdx.x;
+    const int64_t bg = blockIdx.y;
+    const bf16 *src = k + (bg * N + (int64_t)c * S) * D;
+    for (int idx = threadIdx.x; idx < S * (D / 8); idx += blockDim.x) {
+        const int j = idx / (D / 8), cb = idx % (D / 8);
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if ((int64_t)c * S + j < N) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
+        bf16x8 x;
+        __builtin_memcpy(&x, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[j][cb * 8 + e] = x[e];
+    }
+    __syncthreads();
+    bf16 *dst = kt + (bg * CA + c) * (int64_t)D * S;
+    for (int idx = threadIdx.x; idx < D * (S / 8); idx += blockDim.x) {
+        const int d = idx / (S / 8), blk = idx % (S / 8);
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = tile[bwd_slot_key(blk * 8 + e)][d];
+        *(bf16x8 *)(dst + (int64_t)d * S + blk * 8) = x;
+    }
+}
+
+// Block (query block, kv head g, batch b): NWAVE waves, each one MFMA tile
+// of 16 (row, head) pairs (16/G consecutive rows x the G heads; lane l is
+// pair l%16).  The block walks the ascending union of its rows' selections,
+// then the window chunks.  Per chunk it stages K and V (row-major: A
+// operands of S^T = K Q^T and dP^T = V dO^T) and K^T in k-slot order (A
+// operand of dq^T += K^T dS^T), the next chunk's loads in flight while the
+// current one is used.  A wave computes the chunk when one of its pairs
+// selected it (window: always).  The accumulators A^T and Bv^T hold, in
+// lane l, dims 16dt + 4(l/16) + i of pair l%16:
+//   window key j:       A += P_j (dO.v_j) k_j,  Bv += P_j k_j
+//   key j of chunk c:   A += w_c p_cj (dO.v_j - g_c) k_j
+// and, once the walk is done, A += sum_c w_c g_c k'_c, Bv += sum_c w_c k'_c,
+// D' = sum_window P_j dO.v_j + sum_c w_c g_c - dlse, dq = scale (A - D' Bv).
+// P and the ds operands enter as two bf16 terms each.
+template <int D, int S, int G, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ kt, const float *__restrict__ k_sum, const int32_t *__restrict__ sel_idx,
+    const float *__restrict__ sel_score, const float *__restrict__ lse, const bf16 *__restrict__ dout,
+    const float *__restrict__ dlse, float *__restrict__ dq, float *__restrict__ dsel, float *__restrict__ mlog,
+    float *__restrict__ gdo, float *__restrict__ dcoef, int N, int H_q, int H_kv, int H_lm, int C, int CA, int W,
+    int K, float scale, int NW, int UCAP) {
+    constexpr int QPT = 16 / G, QB = NWAVE * QPT, NT = NWAVE * 64;
+    constexpr int KS = D / 32, KT = S / 16, PS = S / 32, DT = D / 16, NB = D / 8, NBS = S / 8;
+    constexpr int TK = S * NB, TV = S * NB, TT = D * NBS, STAGE = TK + TV + TT;  // 16-byte units
+    constexpr int PK = TK / 64, NPC = STAGE / 64;  // 1 KB DMA pieces: of a K (or V) tile, of a chunk
+    __shared__ u32x4 stg[2][STAGE];
+    extern __shared__ int dyn[];
+    int16_t *sel_l = (int16_t *)dyn;                                      // [QB][K]
+    float *sc_l = (float *)(dyn + (QB * K + 1) / 2);                       // [QB * G][K] s^ of each pair's slots
+    uint32_t *bitmap = (uint32_t *)(sc_l + QB * G * K);                    // [NW]
+    int *ulist = (int *)(bitmap + NW);                                     // [UCAP + W/S + 1]
+    int *scan = ulist + UCAP + W / S + 1;                                  // [16]
+
+    const int qb = blockIdx.x, g = blockIdx.y;
+    const int64_t b = blockIdx.z, bg = b * H_kv + g;
+    const int i0 = qb * QB, qc = i0 / S, n = max(0, qc - W / S);
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4, r = lane & 15;
+    const int GLM = H_lm / H_kv;
+
+    // ---- setup: selections, scores, union of the block's selections
+    for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
+    for (int t = tid; t < QB * K; t += NT) {
+        const int iq = i0 + t / K;
+        sel_l[t] = (int16_t)(iq < N ? sel_idx[(bg * N + iq) * K + t % K] : -1);
+    }
+    for (int t = tid; t < QB * G * K; t += NT) {
+        const int m = t / (G * K), rem = t % (G * K), e = rem / K, iq = i0 + m;
+        sc_l[t] = iq < N ? sel_score[((b * H_q + g * G + e) * N + iq) * K + rem % K] : -INFINITY;
+    }
+    __syncthreads();
+    for (int t = tid; t < QB * K; t += NT) {
+        const int c = sel_l[t];
+        if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    int U = 0;
+    {
+        int base = 0;
+        for (int w0 = 0; w0 < NW; w0 += NT) {
+            const int wi = w0 + tid;
+            const uint32_t word = wi < NW ? bitmap[wi] : 0u;
+            const int cnt = __popc(word);
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int y = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += y;
+            }
+            if (lane == WAVE - 1) scan[wave] = incl;
+            __syncthreads();
+            int wbase = 0, tot = 0;
+            for (int x = 0; x < NWAVE; ++x) {
+                if (x < wave) wbase += scan[x];
+                tot += scan[x];
+            }
+            int pos = base + wbase + incl - cnt;
+            uint32_t wv = word;
+            while (wv) {
+                const int bit = __ffs(wv) - 1;
+                wv &= wv - 1;
+                if (pos < UCAP) ulist[pos] = wi * 32 + bit;
+                ++pos;
+            }
+            base += tot;
+            __syncthreads();
+        }
+        U = min(base, UCAP);
+    }
+    const int wc0 = max(0, qc - W / S);
+    const int T = U + (qc - wc0 + 1);
+    for (int t = tid; t < T - U; t += NT) ulist[U + t] = wc0 + t;
+
+    // ---- per-pair state
+    const int m = wave * QPT + r / G, e = r % G, iq = i0 + m, h = g * G + e;
+    const bool rv = iq < N;
+    const int64_t row = (b * H_q + h) * N + min(iq, N - 1);
+    bf16x8 qf[KS], df[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const u32x4 a = *(const u32x4 *)(q + row * D + 32 * s + 8 * grp);
+        const u32x4 c2 = *(const u32x4 *)(dout + row * D + 32 * s + 8 * grp);
+        __builtin_memcpy(&qf[s], &a, 16);
+        __builtin_memcpy(&df[s], &c2, 16);
+    }
+    const float L = lse[row];
+    f32x4 accA[DT], accB[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) accA[dt] = accB[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dpart = 0.f;
+    __syncthreads();  // sel_l, sc_l, ulist complete
+    const int16_t *sl = sel_l + m * K;
+    const float *scp = sc_l + (m * G + e) * K;
+    int cur = 0, nsel = 0;
+    for (int kk = 0; kk < K; ++kk) nsel += sl[kk] >= 0;
+    int nch = (rv && nsel > 0) ? sl[0] : 0x7fffffff;
+
+    const bf16 *kb = k + bg * (int64_t)N * D, *vb = v + bg * (int64_t)N * D;
+    const bf16 *ktb = kt + bg * (int64_t)CA * D * S;
+    // DMA of chunk ulist[it] into buffer buf: 1 KB pieces, 16 bytes per
+    // lane into lane-contiguous LDS, the XOR swizzle applied through the
+    // per-lane source offset; K and V resources end at key N (rows past it
+    // read as zeros), K^T is zero-padded by its pre-pass
+    auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+        const int c = __builtin_amdgcn_readfirstlane(ulist[it]);
+        const int kbytes = max(0, min(S, N - c * S)) * D * 2;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kb + (int64_t)c * S * D), (short)0, kbytes, BWD_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vb + (int64_t)c * S * D), (short)0, kbytes, BWD_RSRC_WORD3);
+        const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(ktb + (int64_t)c * D * S), (short)0, D * S * 2, BWD_RSRC_WORD3);
+        for (int pc = wave; pc < NPC; pc += NWAVE) {
+            if (pc < 2 * PK) {
+                constexpr int RPP = 1024 / (D * 2);  // key rows per piece
+                const int pp = pc % PK, row = pp * RPP + lane / NB, blk = lane % NB;
+                const int off = (row * D + (blk ^ bswz<NB>(row)) * 8) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(pc < PK ? kr : vr, BWD_LPTR(&stg[buf][pc * 64]), 16, off, 0, 0,
+                                                         0);
+            } else {
+                constexpr int RPP = 1024 / (S * 2);  // K^T rows (dims) per piece
+                const int pp = pc - 2 * PK, row = pp * RPP + lane / NBS, blk = lane % NBS;
+                const int off = (row * S + (blk ^ bswz<NBS>(row)) * 8) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, BWD_LPTR(&stg[buf][pc * 64]), 16, off, 0, 0, 0);
+            }
+        }
+    };
+    // ds (or P) operand of a 32-key step from two 16-key accumulator tiles,
+    // as hi and lo bf16 terms
+    auto split_op = [&](const f32x4 &a0, const f32x4 &a1, bf16x8 &hi, bf16x8 &lo) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16 h0 = (bf16)a0[i], h1 = (bf16)a1[i];
+            hi[i] = h0;
+            hi[4 + i] = h1;
+            lo[i] = (bf16)(a0[i] - (float)h0);
+            lo[4 + i] = (bf16)(a1[i] - (float)h1);
+        }
+    };
+    // acc^T += K^T X^T over the chunk, X given per 16-key tile in the S^T layout
+    auto ktx = [&](const f32x4 (&x)[KT], f32x4 (&acc)[DT], const u32x4 (*t_l)[NBS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps) {
+            bf16x8 hi, lo;
+            split_op(x[2 * ps], x[2 * ps + 1], hi, lo);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int xr = 16 * dt + r;
+                const u32x4 raw = t_l[xr][(4 * ps + grp) ^ bswz<NBS>(xr)];
+                bf16x8 a;
+                __builtin_memcpy(&a, &raw, 16);
+                acc[dt] = mfma16(a, hi, acc[dt]);
+                acc[dt] = mfma16(a, lo, acc[dt]);
+            }
+        }
+    };
+
+    __syncthreads();  // the walk list is complete
+    if (T > 0) issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int it = 0; it < T; ++it) {
+        // the next chunk's DMA runs while this one is used; the buffer it
+        // fills was released by every wave at the end of the last step
+        if (it + 1 < T) issue(it + 1, (it + 1) & 1);
+        const u32x4(*k_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it & 1][0]);
+        const u32x4(*v_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it & 1][TK]);
+        const u32x4(*t_l)[NBS] = reinterpret_cast<const u32x4(*)[NBS]>(&stg[it & 1][TK + TV]);
+        const int c = ulist[it];
+        const bool window = it >= U;
+        const bool act = rv && (window || nch == c);
+        if (__ballot(act) != 0ull) {
+        f32x4 sacc[KT], dacc[KT];
+#pragma unroll
+        for (int kt2 = 0; kt2 < KT; ++kt2) sacc[kt2] = dacc[kt2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2) {
+                const int kr = 16 * kt2 + r, blk = (4 * s + grp) ^ bswz<NB>(kr);
+                const u32x4 rk = k_l[kr][blk], rvv = v_l[kr][blk];
+                bf16x8 ak, av;
+                __builtin_memcpy(&ak, &rk, 16);
+                __builtin_memcpy(&av, &rvv, 16);
+                sacc[kt2] = mfma16(ak, qf[s], sacc[kt2]);
+                dacc[kt2] = mfma16(av, df[s], dacc[kt2]);
+            }
+        if (!window) {
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sacc[kt2][i] *= scale;
+                    cmax = fmaxf(cmax, sacc[kt2][i]);
+                }
+            cmax = rows4_max(cmax);
+            float z = 0.f;
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z += expf(sacc[kt2][i] - cmax);
+            const float lse_c = cmax + logf(rows4_sum(z));
+            float gp = 0.f;
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sacc[kt2][i] = expf(sacc[kt2][i] - lse_c);  // p_cj
+                    gp = fmaf(sacc[kt2][i], dacc[kt2][i], gp);
+                }
+            const float gc = rows4_sum(gp);  // dO.o_c
+            const float shat = act ? scp[cur] : 0.f;
+            const float wc = act ? expf(shat - L) : 0.f;
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sacc[kt2][i] = wc * sacc[kt2][i] * (dacc[kt2][i] - gc);
+            ktx(sacc, accA, t_l);
+            if (act) {
+                if (grp == 0) {
+                    mlog[row * K + cur] = shat - L - lse_c;
+                    gdo[row * K + cur] = gc;
+                }
+                ++cur;
+                nch = cur < nsel ? (int)sl[cur] : 0x7fffffff;
+            }
+        } else {
+            const bool diag = c == qc;
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = c * S + 16 * kt2 + 4 * grp + i;
+                    const bool ok = rv && j < N && !(diag && j > iq);
+                    const float P = ok ? expf(fmaf(sacc[kt2][i], scale, -L)) : 0.f;
+                    sacc[kt2][i] = P;
+                    dpart = fmaf(P, dacc[kt2][i], dpart);
+                    dacc[kt2][i] *= P;
+                }
+            ktx(dacc, accA, t_l);
+            ktx(sacc, accB, t_l);
+        }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the next chunk has landed
+        __syncthreads();
+    }
+
+    // ---- epilogue: the summary terms, D', dq, ds^ of each slot
+    __syncthreads();  // this wave's gdo writes are visible to its other lanes
+    const int lh = GLM == G ? h : g;  // landmark head of the pair
+    float dsum = 0.f;
+    for (int kk = 0; kk < nsel; ++kk) {
+        const int c = sl[kk];
+        const float wc = expf(scp[kk] - L), gc = gdo[row * K + kk];
+        dsum = fmaf(wc, gc, dsum);
+        const float *kp = k_sum + ((b * H_lm + lh) * (int64_t)C + c) * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 kv = *(const f32x4 *)(kp + 16 * dt);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                accA[dt][i] = fmaf(wc * gc, kv[i], accA[dt][i]);
+                accB[dt][i] = fmaf(wc, kv[i], accB[dt][i]);
+            }
+        }
+    }
+    if (!rv) return;
+    const float Dp = rows4_sum(dpart) + dsum - (dlse ? dlse[row] : 0.f);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = scale * fmaf(-Dp, accB[dt][i], accA[dt][i]);
+        *(f32x4 *)(dq + row * D + 16 * dt + 4 * grp) = o;
+    }
+    if (grp == 0) {
+        dcoef[row] = Dp;
+        for (int kk = 0; kk < K; ++kk) {
+            if (kk < nsel) {
+                dsel[row * K + kk] = expf(scp[kk] - L) * (gdo[row * K + kk] - Dp);
+            } else {
+                dsel[row * K + kk] = 0.f;
+                mlog[row * K + kk] = -INFINITY;
+                gdo[row * K + kk] = 0.f;
+            }
+        }
+    }
+}
+
 // Row bitmap of each chunk's selecting rows: bit i of row c of (b, g) is
 // set when row i selected chunk c (order-free ORs, so the map is
 // deterministic).  Thread per row.
@@ -820,7 +1174,38 @@ size_t backward_workspace_bytes(const Shape &s) {
     size_t b = 3 * align_up(rows * s.K * 4, 256) + align_up(rows * 4, 256);
     if (s.lm_mode == 1) b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // per-chunk dq'
     b += align_up(selbits_bytes(s), 256);
+    if (s.io_bf16) b += align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);  // K^T in k-slot order
     return b;
+}
+
+// The MFMA row pass when its LDS fits the shape (false: not launched).
+// 64-key chunks only: two stages of a 128-key chunk (96 KB each) do not fit.
+template <int D, int S, int G>
+static bool try_rows_mfma(const Shape &s, const void *q, const void *k, const void *v, const bf16 *ktw,
+                          const float *k_sum, const int32_t *sel_idx, const float *sel_score, const float *lse,
+                          const void *dout, const float *dlse, float *dq, float *dsel, float *mlog, float *gdo,
+                          float *dcoef, hipStream_t st) {
+    if constexpr (S != 64) {
+        return false;
+    } else {
+        constexpr int NWAVE = S * G / 16 < 8 ? S * G / 16 : 8;
+        constexpr int QB = NWAVE * (16 / G);
+        constexpr size_t stage = 2 * ((size_t)2 * S * (D / 8) + (size_t)D * (S / 8)) * 16;
+        const int NW = (s.C + 31) / 32 + 1;
+        const int UCAP = std::min(s.C + 1, QB * s.K + 1);
+        const size_t dyn = (size_t)((QB * s.K + 1) / 2) * 4 + (size_t)QB * G * s.K * 4 + (size_t)NW * 4 +
+                           (size_t)(UCAP + s.W / s.S + 1) * 4 + 16 * 4;
+        if (stage + dyn > 160 * 1024) return false;
+        auto kern = bwd_rows_mfma_kernel<D, S, G, NWAVE>;
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
+            hipSuccess)
+            return false;
+        const dim3 grid((unsigned)((s.N + QB - 1) / QB), (unsigned)s.H_kv, (unsigned)s.B);
+        hipLaunchKernelGGL(kern, grid, dim3(NWAVE * 64), dyn, st, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
+                           ktw, k_sum, sel_idx, sel_score, lse, (const bf16 *)dout, dlse, dq, dsel, mlog, gdo, dcoef,
+                           s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.CA, s.W, s.K, s.scale, NW, UCAP);
+        return true;
+    }
 }
 
 template <typename T, int D, int S>
@@ -843,18 +1228,37 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     if (s.lm_mode == 1) p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
     uint64_t *selbits = (uint64_t *)p;  // bf16 I/O with K > 0
     const int64_t nbits = (int64_t)(selbits_bytes(s) / 8);
-    const dim3 rgrid((unsigned)((int64_t)s.B * s.H_kv * s.N));
-    auto go_rows = [&](auto kern, int G) {
-        hipLaunchKernelGGL(kern, rgrid, dim3(64 * G), 0, st, (const T *)q, (const T *)k, (const T *)v, k_sum, sel_idx,
-                           sel_score, lse, (const T *)dout, dlse, dq, dsel, mlog, gdo, dcoef, s.N, s.H_q, s.H_kv,
-                           s.H_lm, s.C, s.W, s.K, s.scale);
-    };
-    switch (s.G) {
-        case 1: go_rows(bwd_rows_kernel<T, D, S, 1>, 1); break;
-        case 2: go_rows(bwd_rows_kernel<T, D, S, 2>, 2); break;
-        case 4: go_rows(bwd_rows_kernel<T, D, S, 4>, 4); break;
-        case 8: go_rows(bwd_rows_kernel<T, D, S, 8>, 8); break;
-        default: return hipErrorInvalidValue;
+    p += align_up(selbits_bytes(s), 256);
+    bf16 *ktw = (bf16 *)p;  // bf16 I/O: K^T in k-slot order
+    bool rows_done = false;
+    if constexpr (std::is_same<T, bf16>::value) {
+        hipLaunchKernelGGL((bwd_kslot_kernel<D, S>), dim3((unsigned)s.CA, (unsigned)(s.B * s.H_kv)), dim3(256), 0, st,
+                           (const bf16 *)k, ktw, s.N, s.CA);
+        switch (s.G) {
+            case 1: rows_done = try_rows_mfma<D, S, 1>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+                                                        dsel, mlog, gdo, dcoef, st); break;
+            case 2: rows_done = try_rows_mfma<D, S, 2>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+                                                        dsel, mlog, gdo, dcoef, st); break;
+            case 4: rows_done = try_rows_mfma<D, S, 4>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+                                                        dsel, mlog, gdo, dcoef, st); break;
+            default: rows_done = try_rows_mfma<D, S, 8>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+                                                         dsel, mlog, gdo, dcoef, st); break;
+        }
+    }
+    if (!rows_done) {
+        const dim3 rgrid((unsigned)((int64_t)s.B * s.H_kv * s.N));
+        auto go_rows = [&](auto kern, int G) {
+            hipLaunchKernelGGL(kern, rgrid, dim3(64 * G), 0, st, (const T *)q, (const T *)k, (const T *)v, k_sum,
+                               sel_idx, sel_score, lse, (const T *)dout, dlse, dq, dsel, mlog, gdo, dcoef, s.N, s.H_q,
+                               s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale);
+        };
+        switch (s.G) {
+            case 1: go_rows(bwd_rows_kernel<T, D, S, 1>, 1); break;
+            case 2: go_rows(bwd_rows_kernel<T, D, S, 2>, 2); break;
+            case 4: go_rows(bwd_rows_kernel<T, D, S, 4>, 4); break;
+            case 8: go_rows(bwd_rows_kernel<T, D, S, 8>, 8); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
