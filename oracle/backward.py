@@ -41,7 +41,7 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str = "chunk"):
+def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str = "chunk", rows=None):
     """Gradients of sum(dout * out) + sum(dlse * lse) for a prefill with the
     given selection.
 
@@ -51,6 +51,11 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     dlse [B,H_q,N] or None.  Returns dict(dq, dk, dv, dq_lm, out, lse,
     sel_score, dsel) in float64 (dq_lm None for "mean", [H_lm,d] for
     "shared"; dsel = ds^ per selected slot [B,H_q,N,K], 0 on padding).
+    rows: optional query positions to visit (default all).  The loss is
+    linear in dout and dlse, so a row whose dout and dlse vanish contributes
+    nothing to any gradient: with dout = dlse = 0 outside ``rows`` the
+    gradients are exactly those of the full loop (out, lse and sel_score are
+    then filled for the visited rows only).
     """
     B, H_q, N, d = np.shape(q)
     H_kv = np.shape(k)[1]
@@ -104,7 +109,7 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     for b in range(B):
         for h in range(H_q):
             g, l = h // G, lm_of(h)
-            for i in range(N):
+            for i in (range(N) if rows is None else rows):
                 qi, doi = q[b, h, i], do[b, h, i]
                 w0 = max(0, (i // S) * S - W)
                 # forward: the effective logits of every attended key

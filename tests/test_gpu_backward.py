@@ -88,3 +88,45 @@ def test_backward_is_deterministic(dev):
     torch.cuda.synchronize()
     for x, y in zip(first, again):
         assert torch.equal(x, y)
+
+
+def test_backward_8k_k16_sampled_rows(dev):
+    """The 8K GQA workload (N = 8192, K = 16, G = 4, d = 128, S = 64: the MFMA
+    row and key passes, several walk tiles and bitmap batches per block).
+    The output gradient is nonzero on 96 sampled rows only, so the oracle
+    visits just those rows (the gradients are linear in dout and dlse; its
+    row-subset pin).  dq of every other row must be exactly zero."""
+    p = dict(W.PRESETS["gqa_8k"])
+    print("[backward] gqa_8k sampled rows", flush=True)
+    inp = W.make_prefill(p, device=dev)
+    cfg = inp["cfg"]
+    fw = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
+    rng = np.random.default_rng(123)
+    rows = np.sort(np.concatenate([rng.choice(np.arange(0, 2048), 24, replace=False),
+                                   rng.choice(np.arange(2048, cfg.N - 1024), 40, replace=False),
+                                   rng.choice(np.arange(cfg.N - 1024, cfg.N), 32, replace=False)]))
+    g = torch.Generator().manual_seed(321)
+    dout = torch.zeros(fw["out"].shape, dtype=torch.float32)
+    dlse = torch.zeros(fw["lse"].shape, dtype=torch.float32)
+    dout[:, :, rows] = torch.randn((cfg.B, cfg.H_q, len(rows), cfg.d), generator=g)
+    dlse[:, :, rows] = torch.randn((cfg.B, cfg.H_q, len(rows)), generator=g)
+    dout = dout.to(cfg.io_dtype).to(dev)
+    dlse = dlse.to(dev)
+    dq, dk, dv, dq_lm = hb.sparse_attend_backward(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"], fw["k_sum"],
+                                                  fw["sel_idx"], fw["sel_score"], fw["lse"], dout, dlse)
+    torch.cuda.synchronize()
+    print("[backward] oracle on the sampled rows", flush=True)
+    ref = oracle_backward(cfg.oracle_dict(), host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["q_lm"]),
+                          host(fw["sel_idx"]), host(dout), host(dlse), landmark="chunk", rows=rows)
+    others = np.ones(cfg.N, bool)
+    others[rows] = False
+    got_dq = host(dq).numpy().astype(np.float64)
+    assert np.all(got_dq[:, :, others] == 0.0)
+    for key, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dq_lm", dq_lm)):
+        got = host(got).numpy().astype(np.float64)
+        want = ref[key]
+        bound = 1e-4 * np.abs(want).max() + 1e-3 * np.abs(want)
+        bad = np.abs(got - want) > bound
+        print(f"  {key}: max err {np.abs(got - want).max():.3g} (max |ref| {np.abs(want).max():.3g})", flush=True)
+        assert not bad.any(), (f"{key}: {bad.sum()} of {bad.size} outside; max err "
+                               f"{np.abs(got - want).max():.3g}, max |ref| {np.abs(want).max():.3g}")

@@ -128,3 +128,19 @@ def test_shared_landmark_gradients_match_finite_differences():
                   _loss(cfg, q, k - eps * u, v, qs, sel, dout, dlse, "shared")) / (2 * eps)
             an = float((g["dk"] * u).sum())
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_row_subset_is_the_full_loop_when_other_rows_carry_no_gradient():
+    """The loss is linear in dout and dlse: zeroing them outside a row set and
+    visiting only those rows gives the full loop's gradients."""
+    cfg, q, k, v, ql, dout, dlse, sel = _case(31)
+    rows = np.array([5, 40, 41, 77, 95])
+    mask = np.zeros(cfg["N"], bool)
+    mask[rows] = True
+    dout0 = np.where(mask[None, None, :, None], dout, 0.0)
+    dlse0 = np.where(mask[None, None, :], dlse, 0.0)
+    full = backward(cfg, q, k, v, ql, sel, dout0, dlse0)
+    part = backward(cfg, q, k, v, ql, sel, dout0, dlse0, rows=rows)
+    for key in ("dq", "dk", "dv", "dq_lm"):
+        np.testing.assert_allclose(part[key], full[key], rtol=0, atol=1e-12)
+    assert np.abs(full["dk"]).max() > 0 and np.abs(full["dq"][:, :, ~mask]).max() == 0
