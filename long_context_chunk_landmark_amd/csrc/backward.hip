@@ -526,41 +526,56 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int idx = t; idx < G * D; idx += NT) dkp_l[idx / D][idx % D] = 0.f;
     if (t < G) dbp_l[t] = 0.f;
 
-    // one tile: nrows rows x G heads; pair p is row p / G, head p % G;
-    // row_of(rr) -> (row, selection slot)
-    auto run_tile = [&](int nrows, bool selected, auto row_of) {
-        __syncthreads();  // the previous tile is no longer read
+    // A tile: nrows rows x G heads; pair p is row p / G, head p % G;
+    // row_of(rr) -> (row, selection slot).  fetch loads a tile's rows and
+    // per-pair values into registers, commit stores them (and the
+    // transposed rows) in LDS, compute runs the products; the next tile is
+    // fetched while the current one computes.
+    constexpr int NPT = (2 * RT * NB + NT - 1) / NT;  // 16-byte row pieces per thread
+    u32x4 tv[NPT];
+    float tbias = -INFINITY, tdc = 0.f, tdsh = 0.f;
+    int tlim = -1;
+    auto fetch = [&](int nrows, bool selected, auto row_of) __attribute__((always_inline)) {
         const int np = nrows * G;
-        for (int idx = t; idx < 2 * RT * NB; idx += NT) {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int idx = t + j * NT;
             const int which = idx / (RT * NB), rem = idx % (RT * NB), p = rem / NB, cb = rem % NB;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (p < np) {
+            tv[j] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < 2 * RT * NB && p < np) {
                 const int64_t rh = (b * H_q + (int64_t)g * G + p % G) * N + row_of(p / G).x;
-                val = *(const u32x4 *)((which ? dout : q) + rh * D + cb * 8);
+                tv[j] = *(const u32x4 *)((which ? dout : q) + rh * D + cb * 8);
             }
-            (which ? do_t : q_t)[p][cb ^ bswz<NB>(p)] = val;
+        }
+        tbias = -INFINITY, tdc = 0.f, tdsh = 0.f, tlim = -1;
+        if (t < np) {
+            const int2 ik = row_of(t / G);
+            const int64_t rh = (b * H_q + (int64_t)g * G + t % G) * N + ik.x;
+            if (selected) {
+                tbias = mlog[rh * K + ik.y];  // P_j = e^{s_j + m}, m = s^_c - L - lse_c
+                tdc = gdo[rh * K + ik.y];
+                tdsh = dsel[rh * K + ik.y];
+                tlim = 0x7fffffff;
+            } else {
+                tbias = -lse[rh];
+                tdc = dcoef[rh];
+                tlim = ik.x;
+            }
+        }
+    };
+    auto commit = [&]() __attribute__((always_inline)) {
+        __syncthreads();  // the previous tile is no longer read
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int idx = t + j * NT;
+            const int which = idx / (RT * NB), rem = idx % (RT * NB), p = rem / NB, cb = rem % NB;
+            if (idx < 2 * RT * NB) (which ? do_t : q_t)[p][cb ^ bswz<NB>(p)] = tv[j];
         }
         if (t < RT) {
-            float bias = -INFINITY, dc = 0.f, dsh = 0.f;
-            int lim = -1;
-            if (t < np) {
-                const int2 ik = row_of(t / G);
-                const int64_t rh = (b * H_q + (int64_t)g * G + t % G) * N + ik.x;
-                if (selected) {
-                    bias = mlog[rh * K + ik.y];  // P_j = e^{s_j + m}, m = s^_c - L - lse_c
-                    dc = gdo[rh * K + ik.y];
-                    dsh = dsel[rh * K + ik.y];
-                    lim = 0x7fffffff;
-                } else {
-                    bias = -lse[rh];
-                    dc = dcoef[rh];
-                    lim = ik.x;
-                }
-            }
-            pbias[t] = bias;
-            pdc[t] = dc;
-            pdsh[t] = dsh;
-            prow[t] = lim;
+            pbias[t] = tbias;
+            pdc[t] = tdc;
+            pdsh[t] = tdsh;
+            prow[t] = tlim;
         }
         __syncthreads();
         // the transposed tiles, 8 k-slots (16 bytes) of one dim per item
@@ -576,6 +591,9 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             __builtin_memcpy(&(which ? doT : qT)[x][jb], &e8, 16);
         }
         __syncthreads();
+    };
+    auto compute = [&](int nrows, bool selected) __attribute__((always_inline)) {
+        const int np = nrows * G;
         f32x4 sacc[2], dacc[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
@@ -636,10 +654,21 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
         }
     };
 
+    // ntile tiles: tile j has nrows_of(j) rows, row_of(j, rr)
+    auto run_tiles = [&](int ntile, bool selected, auto nrows_of, auto row_of) __attribute__((always_inline)) {
+        if (ntile <= 0) return;
+        fetch(nrows_of(0), selected, [&](int rr) { return row_of(0, rr); });
+        for (int j = 0; j < ntile; ++j) {
+            commit();
+            if (j + 1 < ntile) fetch(nrows_of(j + 1), selected, [&](int rr) { return row_of(j + 1, rr); });
+            compute(nrows_of(j), selected);
+        }
+    };
+
     // window rows: query chunks c .. c + W/S
     const int r_end = (int)min((int64_t)N, (int64_t)(c + W / S + 1) * S);
-    for (int i0 = c * S; i0 < r_end; i0 += RPT)
-        run_tile(min(RPT, r_end - i0), false, [&](int rr) { return make_int2(i0 + rr, 0); });
+    run_tiles((r_end - c * S + RPT - 1) / RPT, false, [&](int j) { return min(RPT, r_end - c * S - j * RPT); },
+              [&](int j, int rr) { return make_int2(c * S + j * RPT + rr, 0); });
 
     // rows of later query chunks that selected chunk c, in row order, from
     // the chunk's row bitmap: BW words per batch go to the row list (wave
@@ -689,9 +718,8 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             __syncthreads();
             const bool last = w0 + BW >= NWB;
             const int nfull = last ? tot : tot / RPT * RPT;
-            for (int r0 = 0; r0 < nfull; r0 += RPT)
-                run_tile(min(RPT, nfull - r0), true,
-                         [&](int rr) { return make_int2(list_i[r0 + rr], list_k[r0 + rr]); });
+            run_tiles((nfull + RPT - 1) / RPT, true, [&](int j) { return min(RPT, nfull - j * RPT); },
+                      [&](int j, int rr) { return make_int2(list_i[j * RPT + rr], list_k[j * RPT + rr]); });
             __syncthreads();  // the tiles are done with the list
             const bool mv = t < tot - nfull;
             int li = 0, lk = 0;
