@@ -345,11 +345,14 @@ def bench_backward(args, torch, hb, pre):
 
     _, per = _timed(step, args.backward_steps, 1, torch)
     ms = per["backward"]
-    # QK^T recompute, dO V^T, dV, dQ, dK: 2.5x the forward's attention FLOPs
+    # QK^T recompute, dO V^T, dV, dQ, dK: 2.5x the forward's attention FLOPs.
+    # bf16 I/O runs them on bf16 MFMA (fp32 I/O: fp32 VALU)
     fl = 2.5 * attend_flops(cfg)
+    mfma = cfg.io_dtype == torch.bfloat16
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
     del fw, dout, dlse, ws
-    return {"ms": ms, "bound": "alu", "tflops": fl / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VALU_TFLOPS,
-            "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_VALU_TFLOPS, "flops": fl,
+    return {"ms": ms, "bound": "mfma" if mfma else "alu", "tflops": fl / (ms * 1e-3) / 1e12, "peak": peak,
+            "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / peak, "flops": fl,
             "tokens_per_s": cfg.B * cfg.N / (ms * 1e-3)}
 
 
