@@ -809,50 +809,18 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
 
 // ---------------------------------------------------------------- MFMA row pass (bf16 I/O)
 //
-// Key of k-slot p of a chunk: in the S^T accumulators of 16-key tiles 2s
-// and 2s+1, lane group gq holds keys 32s + 4gq + {0..3} and 32s + 16 + 4gq +
-// {0..3}; as the B operand of a 32-key step they are slots 8gq .. 8gq + 7.
-__device__ __forceinline__ int bwd_slot_key(int p) {
-    const int s = p >> 5, qd = p & 31, gq = qd >> 3, j = qd & 7;
-    return 32 * s + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// kt[(bg * CA + c) * D * S + x * S + p] = k[bg, c * S + bwd_slot_key(p), x]
-// (bf16, zero past key N): the A operand of dq^T += K^T dS^T.
-template <int D, int S>
-__global__ __launch_bounds__(256) void bwd_kslot_kernel(const bf16 *__restrict__ k, bf16 *__restrict__ kt, int N,
-                                                        int CA) {
-    __shared__ bf16 tile[S][D + 8];
-    const int c = blockIdx.x;
-    const int64_t bg = blockIdx.y;
-    const bf16 *src = k + (bg * N + (int64_t)c * S) * D;
-    for (int idx = threadIdx.x; idx < S * (D / 8); idx += blockDim.x) {
-        const int j = idx / (D / 8), cb = idx % (D / 8);
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if ((int64_t)c * S + j < N) val = *(const u32x4 *)(src + (int64_t)j * D + cb * 8);
-        bf16x8 x;
-        __builtin_memcpy(&x, &val, 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tile[j][cb * 8 + e] = x[e];
-    }
-    __syncthreads();
-    bf16 *dst = kt + (bg * CA + c) * (int64_t)D * S;
-    for (int idx = threadIdx.x; idx < D * (S / 8); idx += blockDim.x) {
-        const int d = idx / (S / 8), blk = idx % (S / 8);
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = tile[bwd_slot_key(blk * 8 + e)][d];
-        *(bf16x8 *)(dst + (int64_t)d * S + blk * 8) = x;
-    }
-}
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding)
+constexpr int bwd_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Block (query block, kv head g, batch b): NWAVE waves, each one MFMA tile
 // of 16 (row, head) pairs (16/G consecutive rows x the G heads; lane l is
 // pair l%16).  The block walks the ascending union of its rows' selections,
-// then the window chunks.  Per chunk it stages K and V (row-major: A
-// operands of S^T = K Q^T and dP^T = V dO^T) and K^T in k-slot order (A
-// operand of dq^T += K^T dS^T), the next chunk's loads in flight while the
-// current one is used.  A wave computes the chunk when one of its pairs
+// then the window chunks.  Per chunk it stages K and V row-major (A operands
+// of S^T = K Q^T and dP^T = V dO^T; the A operand K^T of dq^T += K^T dS^T
+// is read from the K tile with transposing LDS reads) through a ring of
+// NSTG stages, so several chunks' loads are in flight while one is used.  A wave computes the chunk when one of its pairs
 // selected it (window: always).  The accumulators A^T and Bv^T hold, in
 // lane l, dims 16dt + 4(l/16) + i of pair l%16:
 //   window key j:       A += P_j (dO.v_j) k_j,  Bv += P_j k_j
@@ -860,19 +828,21 @@ __global__ __launch_bounds__(256) void bwd_kslot_kernel(const bf16 *__restrict__
 // and, once the walk is done, A += sum_c w_c g_c k'_c, Bv += sum_c w_c k'_c,
 // D' = sum_window P_j dO.v_j + sum_c w_c g_c - dlse, dq = scale (A - D' Bv).
 // P and the ds operands enter as two bf16 terms each.
-template <int D, int S, int G, int NWAVE>
+template <int D, int S, int G, int NWAVE, int NSTG>
 __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ kt, const float *__restrict__ k_sum, const int32_t *__restrict__ sel_idx,
+    const float *__restrict__ k_sum, const int32_t *__restrict__ sel_idx,
     const float *__restrict__ sel_score, const float *__restrict__ lse, const bf16 *__restrict__ dout,
     const float *__restrict__ dlse, float *__restrict__ dq, float *__restrict__ dsel, float *__restrict__ mlog,
-    float *__restrict__ gdo, float *__restrict__ dcoef, int N, int H_q, int H_kv, int H_lm, int C, int CA, int W,
-    int K, float scale, int NW, int UCAP) {
+    float *__restrict__ gdo, float *__restrict__ dcoef, int N, int H_q, int H_kv, int H_lm, int C, int W, int K,
+    float scale, int NW, int UCAP) {
     constexpr int QPT = 16 / G, QB = NWAVE * QPT, NT = NWAVE * 64;
-    constexpr int KS = D / 32, KT = S / 16, PS = S / 32, DT = D / 16, NB = D / 8, NBS = S / 8;
-    constexpr int TK = S * NB, TV = S * NB, TT = D * NBS, STAGE = TK + TV + TT;  // 16-byte units
+    constexpr int KS = D / 32, KT = S / 16, PS = S / 32, DT = D / 16, NB = D / 8;
+    constexpr int TK = S * NB, TV = S * NB, STAGE = TK + TV;  // 16-byte units
     constexpr int PK = TK / 64, NPC = STAGE / 64;  // 1 KB DMA pieces: of a K (or V) tile, of a chunk
-    __shared__ u32x4 stg[2][STAGE];
+    constexpr int PPW = NPC / NWAVE;               // pieces per wave and chunk
+    static_assert(NPC % NWAVE == 0, "every wave issues the same number of pieces");
+    __shared__ u32x4 stg[NSTG][STAGE];
     extern __shared__ int dyn[];
     int16_t *sel_l = (int16_t *)dyn;                                      // [QB][K]
     float *sc_l = (float *)(dyn + (QB * K + 1) / 2);                       // [QB * G][K] s^ of each pair's slots
@@ -964,11 +934,10 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
     int nch = (rv && nsel > 0) ? sl[0] : 0x7fffffff;
 
     const bf16 *kb = k + bg * (int64_t)N * D, *vb = v + bg * (int64_t)N * D;
-    const bf16 *ktb = kt + bg * (int64_t)CA * D * S;
-    // DMA of chunk ulist[it] into buffer buf: 1 KB pieces, 16 bytes per
-    // lane into lane-contiguous LDS, the XOR swizzle applied through the
-    // per-lane source offset; K and V resources end at key N (rows past it
-    // read as zeros), K^T is zero-padded by its pre-pass
+    // DMA of chunk ulist[it] into ring stage buf: 1 KB pieces, 16 bytes
+    // per lane into lane-contiguous LDS, the XOR swizzle applied through the
+    // per-lane source offset; the resources end at key N (rows past it read
+    // as zeros).  Every wave issues PPW pieces per chunk.
     auto issue = [&](int it, int buf) __attribute__((always_inline)) {
         const int c = __builtin_amdgcn_readfirstlane(ulist[it]);
         const int kbytes = max(0, min(S, N - c * S)) * D * 2;
@@ -976,22 +945,20 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
             (void *)(kb + (int64_t)c * S * D), (short)0, kbytes, BWD_RSRC_WORD3);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vb + (int64_t)c * S * D), (short)0, kbytes, BWD_RSRC_WORD3);
-        const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(ktb + (int64_t)c * D * S), (short)0, D * S * 2, BWD_RSRC_WORD3);
-        for (int pc = wave; pc < NPC; pc += NWAVE) {
-            if (pc < 2 * PK) {
-                constexpr int RPP = 1024 / (D * 2);  // key rows per piece
-                const int pp = pc % PK, row = pp * RPP + lane / NB, blk = lane % NB;
-                const int off = (row * D + (blk ^ bswz<NB>(row)) * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(pc < PK ? kr : vr, BWD_LPTR(&stg[buf][pc * 64]), 16, off, 0, 0,
-                                                         0);
-            } else {
-                constexpr int RPP = 1024 / (S * 2);  // K^T rows (dims) per piece
-                const int pp = pc - 2 * PK, row = pp * RPP + lane / NBS, blk = lane % NBS;
-                const int off = (row * S + (blk ^ bswz<NBS>(row)) * 8) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, BWD_LPTR(&stg[buf][pc * 64]), 16, off, 0, 0, 0);
-            }
+        constexpr int RPP = 1024 / (D * 2);  // key rows per piece
+#pragma unroll
+        for (int x = 0; x < PPW; ++x) {
+            const int pc = wave + x * NWAVE;
+            const int pp = pc % PK, row = pp * RPP + lane / NB, blk = lane % NB;
+            const int off = (row * D + (blk ^ bswz<NB>(row)) * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pc < PK ? kr : vr, BWD_LPTR(&stg[buf][pc * 64]), 16, off, 0, 0, 0);
         }
+    };
+    // wait until at most n pieces groups (PPW each) of this wave are in flight
+    auto wait_groups = [&](int n) __attribute__((always_inline)) {
+        if (n <= 0) __builtin_amdgcn_s_waitcnt(bwd_vmcnt(0));
+        else if (n == 1) __builtin_amdgcn_s_waitcnt(bwd_vmcnt(PPW));
+        else __builtin_amdgcn_s_waitcnt(bwd_vmcnt(2 * PPW));
     };
     // ds (or P) operand of a 32-key step from two 16-key accumulator tiles,
     // as hi and lo bf16 terms
@@ -1006,34 +973,53 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
         }
     };
     // acc^T += K^T X^T over the chunk, X given per 16-key tile in the S^T layout
-    auto ktx = [&](const f32x4 (&x)[KT], f32x4 (&acc)[DT], const u32x4 (*t_l)[NBS]) __attribute__((always_inline)) {
+    // The A operand K^T (dims 16 dt + l%16 x k-slots 8 grp .. +7 of step
+    // ps) read transposed from the row-major K tile: in each 16-lane group,
+    // the transpose read gives lane i element i of the 16 values that lanes
+    // 4r .. 4r+3 address, r = 0..3; lane 4r + sub addresses 4 dims of key
+    // row r, so lane i gets dim 16 dt + i of four consecutive keys.  Slots
+    // 8grp .. 8grp+3 are keys 32ps + 4grp + r, slots 8grp+4 .. +7 keys
+    // 32ps + 16 + 4grp + r.
+    const int tsub = r & 3, trow = r >> 2;
+    auto kt_frag = [&](const u32x4 (*k_l)[NB], int ps, int dt) __attribute__((always_inline)) {
+        const int x0 = 16 * dt + 4 * tsub;  // the 4 dims this lane addresses
+        bf16x8 a;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 32 * ps + 16 * h + 4 * grp + trow;
+            const short *src = (const short *)&k_l[key][(x0 >> 3) ^ bswz<NB>(key)] + (x0 & 7);
+            const v4i16 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)src);
+            __builtin_memcpy((char *)&a + 8 * h, &v4, 8);
+        }
+        return a;
+    };
+    auto ktx = [&](const f32x4 (&x)[KT], f32x4 (&acc)[DT], const u32x4 (*k_l)[NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps) {
             bf16x8 hi, lo;
             split_op(x[2 * ps], x[2 * ps + 1], hi, lo);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int xr = 16 * dt + r;
-                const u32x4 raw = t_l[xr][(4 * ps + grp) ^ bswz<NBS>(xr)];
-                bf16x8 a;
-                __builtin_memcpy(&a, &raw, 16);
+                const bf16x8 a = kt_frag(k_l, ps, dt);
                 acc[dt] = mfma16(a, hi, acc[dt]);
                 acc[dt] = mfma16(a, lo, acc[dt]);
             }
         }
     };
 
+    // ---- the walk, through a ring of NSTG stages: chunk it + NSTG - 1 is
+    // issued at the start of step it, into the stage every wave released at
+    // the end of step it - 1; a step ends once chunk it + 1 has landed (this
+    // wave's later pieces may stay in flight; other vector-memory operations
+    // issued after them only make the wait longer)
     __syncthreads();  // the walk list is complete
-    if (T > 0) issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int j = 0; j < NSTG - 1 && j < T; ++j) issue(j, j);
+    wait_groups(min(NSTG - 2, T - 1));
     __syncthreads();
     for (int it = 0; it < T; ++it) {
-        // the next chunk's DMA runs while this one is used; the buffer it
-        // fills was released by every wave at the end of the last step
-        if (it + 1 < T) issue(it + 1, (it + 1) & 1);
-        const u32x4(*k_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it & 1][0]);
-        const u32x4(*v_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it & 1][TK]);
-        const u32x4(*t_l)[NBS] = reinterpret_cast<const u32x4(*)[NBS]>(&stg[it & 1][TK + TV]);
+        if (it + NSTG - 1 < T) issue(it + NSTG - 1, (it + NSTG - 1) % NSTG);
+        const u32x4(*k_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it % NSTG][0]);
+        const u32x4(*v_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it % NSTG][TK]);
         const int c = ulist[it];
         const bool window = it >= U;
         const bool act = rv && (window || nch == c);
@@ -1084,7 +1070,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
             for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sacc[kt2][i] = wc * sacc[kt2][i] * (dacc[kt2][i] - gc);
-            ktx(sacc, accA, t_l);
+            ktx(sacc, accA, k_l);
             if (act) {
                 if (grp == 0) {
                     mlog[row * K + cur] = shat - L - lse_c;
@@ -1106,11 +1092,13 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
                     dpart = fmaf(P, dacc[kt2][i], dpart);
                     dacc[kt2][i] *= P;
                 }
-            ktx(dacc, accA, t_l);
-            ktx(sacc, accB, t_l);
+            ktx(dacc, accA, k_l);
+            ktx(sacc, accB, k_l);
         }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the next chunk has landed
+        // chunk it + 1 has landed once at most the groups issued after it
+        // (chunks it + 2 .. min(it + NSTG - 1, T - 1)) are in flight
+        wait_groups(min(NSTG - 2, T - 2 - it));
         __syncthreads();
     }
 
@@ -1202,37 +1190,56 @@ size_t backward_workspace_bytes(const Shape &s) {
     size_t b = 3 * align_up(rows * s.K * 4, 256) + align_up(rows * 4, 256);
     if (s.lm_mode == 1) b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // per-chunk dq'
     b += align_up(selbits_bytes(s), 256);
-    if (s.io_bf16) b += align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);  // K^T in k-slot order
     return b;
 }
 
-// The MFMA row pass when its LDS fits the shape (false: not launched).
-// 64-key chunks only: two stages of a 128-key chunk (96 KB each) do not fit.
-template <int D, int S, int G>
-static bool try_rows_mfma(const Shape &s, const void *q, const void *k, const void *v, const bf16 *ktw,
-                          const float *k_sum, const int32_t *sel_idx, const float *sel_score, const float *lse,
-                          const void *dout, const float *dlse, float *dq, float *dsel, float *mlog, float *gdo,
-                          float *dcoef, hipStream_t st) {
-    if constexpr (S != 64) {
+// The MFMA row pass when its LDS fits the shape (false: not launched): the
+// deepest ring (4, 3 or 2 stages of K and V) that fits beside the block's
+// selections, scores and walk list.  64-key chunks; 128-key chunks take the
+// fp32 VALU row pass.
+template <int D, int S, int G, int NWAVE, int NSTG>
+static bool go_rows_mfma(const Shape &s, const void *q, const void *k, const void *v, const float *k_sum,
+                         const int32_t *sel_idx, const float *sel_score, const float *lse, const void *dout,
+                         const float *dlse, float *dq, float *dsel, float *mlog, float *gdo, float *dcoef,
+                         size_t dyn, int NW, int UCAP, hipStream_t st) {
+    constexpr int QB = NWAVE * (16 / G);
+    constexpr size_t stage = (size_t)NSTG * 2 * S * (D / 8) * 16;
+    if constexpr (stage > 160 * 1024) {
         return false;
     } else {
-        constexpr int NWAVE = S * G / 16 < 8 ? S * G / 16 : 8;
-        constexpr int QB = NWAVE * (16 / G);
-        constexpr size_t stage = 2 * ((size_t)2 * S * (D / 8) + (size_t)D * (S / 8)) * 16;
-        const int NW = (s.C + 31) / 32 + 1;
-        const int UCAP = std::min(s.C + 1, QB * s.K + 1);
-        const size_t dyn = (size_t)((QB * s.K + 1) / 2) * 4 + (size_t)QB * G * s.K * 4 + (size_t)NW * 4 +
-                           (size_t)(UCAP + s.W / s.S + 1) * 4 + 16 * 4;
         if (stage + dyn > 160 * 1024) return false;
-        auto kern = bwd_rows_mfma_kernel<D, S, G, NWAVE>;
+        auto kern = bwd_rows_mfma_kernel<D, S, G, NWAVE, NSTG>;
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) !=
             hipSuccess)
             return false;
         const dim3 grid((unsigned)((s.N + QB - 1) / QB), (unsigned)s.H_kv, (unsigned)s.B);
         hipLaunchKernelGGL(kern, grid, dim3(NWAVE * 64), dyn, st, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                           ktw, k_sum, sel_idx, sel_score, lse, (const bf16 *)dout, dlse, dq, dsel, mlog, gdo, dcoef,
-                           s.N, s.H_q, s.H_kv, s.H_lm, s.C, s.CA, s.W, s.K, s.scale, NW, UCAP);
+                           k_sum, sel_idx, sel_score, lse, (const bf16 *)dout, dlse, dq, dsel, mlog, gdo, dcoef, s.N,
+                           s.H_q, s.H_kv, s.H_lm, s.C, s.W, s.K, s.scale, NW, UCAP);
         return true;
+    }
+}
+
+template <int D, int S, int G>
+static bool try_rows_mfma(const Shape &s, const void *q, const void *k, const void *v, const float *k_sum,
+                          const int32_t *sel_idx, const float *sel_score, const float *lse, const void *dout,
+                          const float *dlse, float *dq, float *dsel, float *mlog, float *gdo, float *dcoef,
+                          hipStream_t st) {
+    if constexpr (S != 64) {
+        return false;
+    } else {
+        constexpr int NWAVE = S * G / 16 < 8 ? S * G / 16 : 8;
+        constexpr int QB = NWAVE * (16 / G);
+        const int NW = (s.C + 31) / 32 + 1;
+        const int UCAP = std::min(s.C + 1, QB * s.K + 1);
+        const size_t dyn = (size_t)((QB * s.K + 1) / 2) * 4 + (size_t)QB * G * s.K * 4 + (size_t)NW * 4 +
+                           (size_t)(UCAP + s.W / s.S + 1) * 4 + 16 * 4;
+        return go_rows_mfma<D, S, G, NWAVE, 4>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq, dsel,
+                                               mlog, gdo, dcoef, dyn, NW, UCAP, st) ||
+               go_rows_mfma<D, S, G, NWAVE, 3>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq, dsel,
+                                               mlog, gdo, dcoef, dyn, NW, UCAP, st) ||
+               go_rows_mfma<D, S, G, NWAVE, 2>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq, dsel,
+                                               mlog, gdo, dcoef, dyn, NW, UCAP, st);
     }
 }
 
@@ -1257,19 +1264,16 @@ static hipError_t go_backward(const Shape &s, const void *q, const void *k, cons
     uint64_t *selbits = (uint64_t *)p;  // bf16 I/O with K > 0
     const int64_t nbits = (int64_t)(selbits_bytes(s) / 8);
     p += align_up(selbits_bytes(s), 256);
-    bf16 *ktw = (bf16 *)p;  // bf16 I/O: K^T in k-slot order
     bool rows_done = false;
     if constexpr (std::is_same<T, bf16>::value) {
-        hipLaunchKernelGGL((bwd_kslot_kernel<D, S>), dim3((unsigned)s.CA, (unsigned)(s.B * s.H_kv)), dim3(256), 0, st,
-                           (const bf16 *)k, ktw, s.N, s.CA);
         switch (s.G) {
-            case 1: rows_done = try_rows_mfma<D, S, 1>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+            case 1: rows_done = try_rows_mfma<D, S, 1>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
                                                         dsel, mlog, gdo, dcoef, st); break;
-            case 2: rows_done = try_rows_mfma<D, S, 2>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+            case 2: rows_done = try_rows_mfma<D, S, 2>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
                                                         dsel, mlog, gdo, dcoef, st); break;
-            case 4: rows_done = try_rows_mfma<D, S, 4>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+            case 4: rows_done = try_rows_mfma<D, S, 4>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
                                                         dsel, mlog, gdo, dcoef, st); break;
-            default: rows_done = try_rows_mfma<D, S, 8>(s, q, k, v, ktw, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
+            default: rows_done = try_rows_mfma<D, S, 8>(s, q, k, v, k_sum, sel_idx, sel_score, lse, dout, dlse, dq,
                                                          dsel, mlog, gdo, dcoef, st); break;
         }
     }
