@@ -625,6 +625,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
                 sh[4 * rg + i] = d1;
                 sl[4 * rg + i] = (bf16)(ds - (float)d1);
             }
+        // V and K alternate, so consecutive MFMAs write different accumulators
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             bf16x8 ad, aq;
@@ -632,8 +633,8 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             __builtin_memcpy(&ad, &rd, 16);
             __builtin_memcpy(&aq, &rq, 16);
             accV[dt] = mfma16(ad, ph, accV[dt]);
-            accV[dt] = mfma16(ad, pl, accV[dt]);
             accK[dt] = mfma16(aq, sh, accK[dt]);
+            accV[dt] = mfma16(ad, pl, accV[dt]);
             accK[dt] = mfma16(aq, sl, accK[dt]);
         }
         if (selected) {
@@ -998,12 +999,16 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
         for (int ps = 0; ps < PS; ++ps) {
             bf16x8 hi, lo;
             split_op(x[2 * ps], x[2 * ps + 1], hi, lo);
+            // the hi terms of every dim tile, then the lo terms: consecutive
+            // MFMAs write different accumulators
+            bf16x8 a[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 a = kt_frag(k_l, ps, dt);
-                acc[dt] = mfma16(a, hi, acc[dt]);
-                acc[dt] = mfma16(a, lo, acc[dt]);
+                a[dt] = kt_frag(k_l, ps, dt);
+                acc[dt] = mfma16(a[dt], hi, acc[dt]);
             }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16(a[dt], lo, acc[dt]);
         }
     };
 
