@@ -272,8 +272,9 @@ def bench_serving(args, torch, hb, W, pre):
 
 def bench_variants(args, torch, hb, W, pre):
     """The method's variants on the prefill workload: summaries with one
-    shared landmark query per head and with mean pooling (q' = 0), and
-    score/select with the normalised-weight group aggregation."""
+    shared landmark query per head and with mean pooling (q' = 0),
+    score/select with the normalised-weight group aggregation, and the
+    streaming form of score/select (O(N K) workspace)."""
     import dataclasses
 
     dev = torch.device("cuda:0")
@@ -286,15 +287,17 @@ def bench_variants(args, torch, hb, W, pre):
     c_shared = dataclasses.replace(cfg, landmark_mode=hb.LM_SHARED)
     c_mean = dataclasses.replace(cfg, landmark_mode=hb.LM_MEAN)
     c_norm = dataclasses.replace(cfg, agg_mode=hb.AGG_NORMALIZED)
+    c_stream = dataclasses.replace(cfg, score_mode=hb.SCORE_STREAMING)
     qcal = inp.get("qcal")
     sel = torch.empty((cfg.B, cfg.H_kv, cfg.N, cfg.K), dtype=torch.int32, device=dev)
     ss = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.K), dtype=torch.float32, device=dev)
-    ws = torch.empty(hb.workspace_size(c_norm, hb.WS_SCORE_QCAL if qcal else hb.WS_SCORE), dtype=torch.uint8,
-                     device=dev)
+    wk = hb.WS_SCORE_QCAL if qcal else hb.WS_SCORE
+    ws = torch.empty(hb.workspace_size(c_norm, wk), dtype=torch.uint8, device=dev)
+    ws_stream = torch.empty(hb.workspace_size(c_stream, wk), dtype=torch.uint8, device=dev)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step():
-        e = [E() for _ in range(4)]
+        e = [E() for _ in range(5)]
         e[0].record()
         hb.landmark_summarize(c_shared, inp["k"], shared_q, k_sum, b_sum)
         e[1].record()
@@ -302,7 +305,10 @@ def bench_variants(args, torch, hb, W, pre):
         e[2].record()
         hb.score_select(c_norm, inp["q"], k_sum, b_sum, qcal=qcal, sel_idx=sel, sel_score=ss, workspace=ws)
         e[3].record()
-        return {"summary_shared": (e[0], e[1]), "summary_mean": (e[1], e[2]), "score_select_normalized": (e[2], e[3])}
+        hb.score_select(c_stream, inp["q"], k_sum, b_sum, qcal=qcal, sel_idx=sel, sel_score=ss, workspace=ws_stream)
+        e[4].record()
+        return {"summary_shared": (e[0], e[1]), "summary_mean": (e[1], e[2]), "score_select_normalized": (e[2], e[3]),
+                "score_select_streaming": (e[3], e[4])}
 
     _, per = _timed(step, max(1, args.steps // 2), 1, torch)
     io_b = 2 if cfg.io_dtype == torch.bfloat16 else 4
@@ -316,9 +322,14 @@ def bench_variants(args, torch, hb, W, pre):
         ms = per[name]
         out[name] = {"ms": ms, "bound": "hbm", "gbs": by / (ms * 1e-3) / 1e9,
                      "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by}
-    ms = per["score_select_normalized"]
-    out["score_select_normalized"] = {"ms": ms, "bound": "mfma", "tflops": fl / (ms * 1e-3) / 1e12,
-                                      "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl}
+    for name in ("score_select_normalized", "score_select_streaming"):
+        ms = per[name]
+        out[name] = {"ms": ms, "bound": "mfma", "tflops": fl / (ms * 1e-3) / 1e12,
+                     "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl}
+    out["score_select_streaming"]["workspace_bytes"] = ws_stream.numel()
+    out["score_select_streaming"]["two_pass_workspace_bytes"] = hb.workspace_size(
+        dataclasses.replace(cfg, score_mode=hb.SCORE_TWO_PASS), wk)
+    del ws, ws_stream
     return out
 
 

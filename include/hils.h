@@ -113,7 +113,24 @@ typedef struct {
                               the call reports it in its status word (see
                               hils_sparse_attend_fused).  Smaller values only serve
                               to exercise that report. */
+    int32_t score_mode;    /* hils_score_mode_t: how hils_score_select (and the
+                              paged prefill) ranks the candidates; 0 (auto) by
+                              default */
 } hils_config_t;
+
+/* Score-and-select forms (same selection, same scores up to fp32 rounding
+ * order).  TWO_PASS writes approximate scores of every candidate (a ragged
+ * array of about B * H_kv * N * C / 2 floats) and selects from them; it is
+ * the faster form.  STREAMING keeps per-row candidate lists on chip and
+ * O(B * H_kv * N * K) workspace; it covers every shape except d = 128 with
+ * G = 8, fp32 summaries and K > 32, whose per-block working set exceeds the
+ * LDS (HILS_ERR_UNSUPPORTED).  AUTO takes TWO_PASS unless its score array
+ * would exceed 32 GiB and STREAMING covers the shape. */
+typedef enum {
+    HILS_SCORE_AUTO = 0,
+    HILS_SCORE_TWO_PASS = 1,
+    HILS_SCORE_STREAMING = 2
+} hils_score_mode_t;
 
 /* Workspace kinds for hils_workspace_size(). */
 enum {

@@ -22,6 +22,7 @@ HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ER
 HILS_F32, HILS_BF16 = 0, 1
 LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
 AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
+SCORE_AUTO, SCORE_TWO_PASS, SCORE_STREAMING = 0, 1, 2  # hils_score_mode_t
 WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD = range(5)
 
 # Every symbol include/hils.h declares.
@@ -51,7 +52,7 @@ class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "N", "H_q", "H_kv", "H_lm", "d", "S", "W", "K", "M", "io_dtype", "summary_dtype")] + [
                    ("scale", ctypes.c_float), ("landmark_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32),
-                   ("wait_spins", ctypes.c_int32)]
+                   ("wait_spins", ctypes.c_int32), ("score_mode", ctypes.c_int32)]
 
 
 @dataclasses.dataclass
@@ -73,6 +74,7 @@ class Config:
     landmark_mode: int = LM_CHUNK
     agg_mode: int = AGG_MAX
     wait_spins: int = 0
+    score_mode: int = 0
 
     def __post_init__(self):
         if self.H_lm is None:
@@ -96,7 +98,7 @@ class Config:
 
         return _CConfig(self.B, self.N, self.H_q, self.H_kv, self.H_lm, self.d, self.S, self.W, self.K, self.M,
                         code(self.io_dtype), code(self.summary_dtype), float(self.scale), int(self.landmark_mode),
-                        int(self.agg_mode), int(self.wait_spins))
+                        int(self.agg_mode), int(self.wait_spins), int(self.score_mode))
 
     def oracle_dict(self) -> dict:
         return dict(B=self.B, N=self.N, H_q=self.H_q, H_kv=self.H_kv, H_lm=self.H_lm, d=self.d, S=self.S, W=self.W,

@@ -73,6 +73,9 @@ hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
     if (cfg->agg_mode != HILS_AGG_MAX && cfg->agg_mode != HILS_AGG_NORMALIZED)
         return fail(HILS_ERR_INVALID_ARG, "agg_mode=%d unknown", cfg->agg_mode);
     if (cfg->wait_spins < 0) return fail(HILS_ERR_INVALID_ARG, "wait_spins=%d must be >= 0", cfg->wait_spins);
+    if (cfg->score_mode < HILS_SCORE_AUTO || cfg->score_mode > HILS_SCORE_STREAMING)
+        return fail(HILS_ERR_INVALID_ARG, "score_mode=%d unknown", cfg->score_mode);
+    s.score_mode = cfg->score_mode;
     s.lm_mode = cfg->landmark_mode;
     s.agg_mode = cfg->agg_mode;
     s.wait_spins = cfg->wait_spins > 0 ? cfg->wait_spins : (1 << 18);
@@ -122,6 +125,13 @@ hils_status_t resolve_paged(const hils_config_t *cfg, int32_t q_start, int32_t n
 size_t paged_workspace_bytes(const hils::Shape &s, bool qcal) {
     return hils::align_up(hils::score_workspace_bytes(s, qcal), 256) + hils::fused_workspace_bytes(s) +
            (s.io_bf16 ? 0 : hils::FUSED_STATUS_BYTES);
+}
+
+// An explicit streaming score/select on a shape its kernel does not cover.
+hils_status_t check_score_mode(const hils::Shape &s) {
+    if (s.score_mode == HILS_SCORE_STREAMING && !hils::score_topk_supported(s))
+        return fail(HILS_ERR_UNSUPPORTED, "streaming score/select does not cover d=%d, G=%d, K=%d", s.D, s.G, s.K);
+    return HILS_OK;
 }
 
 hils_status_t check_ptr(const void *p, const char *name) {
@@ -214,6 +224,7 @@ hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const v
     hils_status_t st = resolve(cfg, true, s);
     if (st) return st;
     if ((int64_t)s.B * s.N == 0 || s.K == 0) return ok();
+    if ((st = check_score_mode(s))) return st;
     if ((st = check_ptr(q, "q")) || (st = check_ptr(sel_idx, "sel_idx")) || (st = check_ptr(sel_score, "sel_score")))
         return st;
     if (s.C > 0 && ((st = check_ptr(k_sum, "k_sum")) || (st = check_ptr(b_sum, "b_sum")))) return st;
@@ -347,6 +358,7 @@ hils_status_t hils_prefill_paged(const hils_config_t *cfg, int32_t q_start, cons
         return st;
     if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
     if ((st = check_qcal(h, w_down, w_up, d_model, r))) return st;
+    if (s.K > 0 && (st = check_score_mode(s))) return st;
     s.bt = block_table;
     if (!hils::sparse_attend_supported(s))
         return fail(HILS_ERR_UNSUPPORTED, "no fused-attention block shape fits LDS for G=%d, S=%d, d=%d, K=%d", s.G, s.S,

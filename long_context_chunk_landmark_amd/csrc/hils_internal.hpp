@@ -23,6 +23,7 @@ struct Shape {
     int lm_mode;   // landmark queries: 0 per chunk, 1 one shared per landmark head, 2 none (q' = 0)
     int agg_mode;  // group aggregation: 0 max of s^, 1 max of s^ - LSE over the candidates
     int wait_spins;  // bound on each wait of the fused kernel (pauses)
+    int score_mode;  // score/select form: 0 auto, 1 two-pass, 2 streaming
     // Paged prefill (q0 = 0, Nk = N, bt = null for the contiguous layout):
     // the N query rows are positions q0 .. q0 + N - 1 (q0 % S == 0) of
     // sequences whose keys 0 .. Nk - 1 = q0 + N - 1 live in a paged cache
@@ -45,9 +46,12 @@ hipError_t launch_landmark_summary(const Shape &s, const void *k, const void *q_
 
 // ---- kernel 2: score + select
 struct ScoreWorkspace {
+    bool topk;          // streaming top-K kernel (no per-candidate scores in memory)
     void *ksb;          // [B,H_lm,C,D] bf16 k1 = bf16(k_sum)
     void *ksb2;         // [B,H_lm,C,D] bf16 k2 = bf16(k_sum - k1) (fp32 summaries)
-    float *kcm;         // [B,H_kv,C,GLM,D] fp32 chunk-major copy of k_sum
+    void *ksb3;         // [B,H_lm,C,D] bf16 k3 = bf16(k_sum - k1 - k2) (fp32 summaries, streaming kernel)
+    float *heads;       // [B,H_kv,N,CAP,G] per-head scores of each row's listed chunks (streaming kernel)
+    float *kcm;         // [B,H_kv,C,GLM,D] fp32 chunk-major copy of k_sum (two-kernel path)
     float *knorm;       // [B,H_lm] max_c ||k'_c||
     float *err;         // [B,H_kv,N] per-row bound of the approximate group score
     float *agg;         // ragged approximate group scores, per (b,g): per_bg entries
@@ -57,6 +61,15 @@ struct ScoreWorkspace {
     float *lse;         // [B,H_q,N] per-head log-sum-exp over the candidates (normalised aggregation) or null
 };
 int64_t score_agg_entries_per_bg(const Shape &s);
+// streaming top-K kernel (score_topk.hip): whether its LDS fits the shape,
+// its per-row list capacity, and the launch (qv: bf16 q or fp32 scoring
+// queries)
+bool score_topk_supported(const Shape &s);
+int score_topk_capacity(const Shape &s);
+// whether score/select runs the streaming kernel for this shape and mode
+bool score_use_topk(const Shape &s);
+hipError_t launch_score_topk(const Shape &s, const void *qv, bool q_fp32, const ScoreWorkspace &ws,
+                             const float *b_sum, int32_t *sel_idx, float *sel_score, hipStream_t st);
 size_t score_workspace_bytes(const Shape &s, bool qcal);
 void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace &ws);
 hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum, const float *b_sum, const void *h,

@@ -37,13 +37,34 @@ int64_t score_agg_entries_per_bg(const Shape &s) {
     return cand_row_offset((int64_t)s.q0 + s.N, w, s.S) - cand_row_offset(s.q0, w, s.S);
 }
 
+// Two-pass form (faster): two bf16 split terms of k', a chunk-major fp32
+// copy of k', per-row bounds and the ragged approximate scores of every
+// candidate (O(N^2 / S) per kv head).  Streaming form: the split terms of k'
+// (three for fp32 summaries), max ||k'|| and the per-head scores of each
+// row's listed chunks (O(N K) per head).  Auto takes the two-pass form
+// unless its score array would exceed 32 GiB.
+constexpr size_t SCORE_TWO_PASS_BUDGET = (size_t)32 << 30;
+
+bool score_use_topk(const Shape &s) {
+    if (s.score_mode == 1 || !score_topk_supported(s)) return false;
+    if (s.score_mode == 2) return true;
+    return (size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4 > SCORE_TWO_PASS_BUDGET;
+}
+
 size_t score_workspace_bytes(const Shape &s, bool qcal) {
+    const size_t kr = (size_t)s.B * s.H_lm * s.C * s.D * 2;  // one bf16 term
     size_t b = 0;
-    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // ksb: two bf16 terms
-    b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // kcm
-    b += align_up((size_t)s.B * s.H_lm * 4, 256);               // knorm
-    b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
-    b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
+    if (score_use_topk(s)) {
+        b += align_up(kr * (s.sum_bf16 ? 1 : 3), 256);
+        b += align_up((size_t)s.B * s.H_lm * 4, 256);  // knorm
+        b += align_up((size_t)s.B * s.H_kv * s.N * score_topk_capacity(s) * s.G * 4, 256);  // heads
+    } else {
+        b += align_up(kr * 2, 256);                                  // ksb: two bf16 terms
+        b += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);  // kcm
+        b += align_up((size_t)s.B * s.H_lm * 4, 256);               // knorm
+        b += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);         // err
+        b += align_up((size_t)s.B * s.H_kv * score_agg_entries_per_bg(s) * 4, 256);
+    }
     if (qcal) b += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
     if (s.max_pages > 0) b += align_up((size_t)s.B * s.H_lm * s.C * 4, 256);  // paged: gathered b_sum
     if (s.agg_mode == 1) b += align_up((size_t)s.B * s.H_q * s.N * 4, 256);    // per-head log-sum-exp
@@ -52,18 +73,36 @@ size_t score_workspace_bytes(const Shape &s, bool qcal) {
 
 void score_workspace_carve(const Shape &s, bool qcal, void *base, ScoreWorkspace &ws) {
     char *p = (char *)base;
+    const size_t kr = (size_t)s.B * s.H_lm * s.C * s.D * 2;
+    ws.topk = score_use_topk(s);
     ws.ksb = p;
-    ws.ksb2 = p + (size_t)s.B * s.H_lm * s.C * s.D * 2;
-    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
-    ws.kcm = (float *)p;
-    p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
-    ws.knorm = (float *)p;
-    p += align_up((size_t)s.B * s.H_lm * 4, 256);
-    ws.err = (float *)p;
-    p += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);
-    ws.per_bg = score_agg_entries_per_bg(s);
-    ws.agg = (float *)p;
-    p += align_up((size_t)s.B * s.H_kv * ws.per_bg * 4, 256);
+    ws.ksb2 = s.sum_bf16 ? nullptr : p + kr;
+    ws.ksb3 = nullptr;
+    ws.heads = nullptr;
+    ws.kcm = nullptr;
+    ws.err = nullptr;
+    ws.agg = nullptr;
+    ws.per_bg = 0;
+    if (ws.topk) {
+        ws.ksb3 = s.sum_bf16 ? nullptr : p + 2 * kr;
+        p += align_up(kr * (s.sum_bf16 ? 1 : 3), 256);
+        ws.knorm = (float *)p;
+        p += align_up((size_t)s.B * s.H_lm * 4, 256);
+        ws.heads = (float *)p;
+        p += align_up((size_t)s.B * s.H_kv * s.N * score_topk_capacity(s) * s.G * 4, 256);
+    } else {
+        ws.ksb2 = p + kr;
+        p += align_up(kr * 2, 256);
+        ws.kcm = (float *)p;
+        p += align_up((size_t)s.B * s.H_lm * s.C * s.D * 4, 256);
+        ws.knorm = (float *)p;
+        p += align_up((size_t)s.B * s.H_lm * 4, 256);
+        ws.err = (float *)p;
+        p += align_up((size_t)s.B * s.H_kv * s.N * 4, 256);
+        ws.per_bg = score_agg_entries_per_bg(s);
+        ws.agg = (float *)p;
+        p += align_up((size_t)s.B * s.H_kv * ws.per_bg * 4, 256);
+    }
     ws.q_s = qcal ? (float *)p : nullptr;
     if (qcal) p += align_up((size_t)s.B * s.H_q * s.N * s.D * 4, 256);
     ws.bsum = s.max_pages > 0 ? (float *)p : nullptr;
@@ -104,7 +143,8 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
 // b_sum [P, H_lm] is gathered into bsum_out [B, H_lm, C] as well.
 template <typename TS, int D>
 __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k_sum, bf16 *__restrict__ ksb,
-                                                        bf16 *__restrict__ ksb2, float *__restrict__ kcm,
+                                                        bf16 *__restrict__ ksb2, bf16 *__restrict__ ksb3,
+                                                        float *__restrict__ kcm,
                                                         float *__restrict__ knorm, int C, int GLM, int64_t rows,
                                                         const int32_t *__restrict__ bt, int max_pages, int H_lm,
                                                         const float *__restrict__ bsum_in,
@@ -138,11 +178,9 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
             }
             const TS *src = k_sum + src_row * D + (lane & 15) * EL;
             bf16 *dst = ksb + row * D + (lane & 15) * EL;
-            bf16 *dst2 = ksb2 + row * D + (lane & 15) * EL;
-            float *dcm = kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL;
             // whole-slice vector loads and stores (the slices are 16-byte aligned)
             TS in[EL];
-            bf16 o1[EL], o2[EL];
+            bf16 o1[EL], o2[EL], o4[EL];
             float o3[EL];
             copy_bytes<EL * sizeof(TS)>(in, src);
 #pragma unroll
@@ -150,12 +188,17 @@ __global__ __launch_bounds__(256) void ksum_prep_kernel(const TS *__restrict__ k
                 const float v = to_f32(in[x]);
                 ss = fmaf(v, v, ss);
                 o1[x] = (bf16)v;
-                o2[x] = (bf16)(v - (float)o1[x]);
+                const float r1 = v - (float)o1[x];  // exact
+                o2[x] = (bf16)r1;
+                o4[x] = (bf16)(r1 - (float)o2[x]);
                 o3[x] = v;
             }
             copy_bytes<EL * 2>(dst, o1);
-            if constexpr (std::is_same<TS, float>::value) copy_bytes<EL * 2>(dst2, o2);
-            copy_bytes<EL * 4>(dcm, o3);
+            if constexpr (std::is_same<TS, float>::value) {
+                copy_bytes<EL * 2>(ksb2 + row * D + (lane & 15) * EL, o2);
+                if (ksb3) copy_bytes<EL * 2>(ksb3 + row * D + (lane & 15) * EL, o4);
+            }
+            if (kcm) copy_bytes<EL * 4>(kcm + ((bg * C + c) * GLM + e) * D + (lane & 15) * EL, o3);
         }
         ss = xor_sum<1, 8>(ss);
         const float nrm = ok ? sqrtf(ss) : 0.f;
@@ -918,7 +961,8 @@ static void go_approx(const Shape &s, const TQ *qv, const float *b_sum, const Sc
                       hipStream_t st) {
     if (s.agg_mode == 1) {
         go_approx_m<TQ, D, G, 1>(s, qv, b_sum, ws, kappa, st);  // per-head log-sum-exp
-        go_approx_m<TQ, D, G, 2>(s, qv, b_sum, ws, kappa, st);  // normalised group max
+        // normalised group max (the streaming kernel ranks by it itself)
+        if (!ws.topk) go_approx_m<TQ, D, G, 2>(s, qv, b_sum, ws, kappa, st);
     } else {
         go_approx_m<TQ, D, G, 0>(s, qv, b_sum, ws, kappa, st);
     }
@@ -978,8 +1022,8 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     if (krows > 0) {
         const dim3 grid((unsigned)((krows + 4 * KPREP_ROWS - 1) / (4 * KPREP_ROWS))), block(256);
         auto prep = [&](auto kern, auto *src) {
-            hipLaunchKernelGGL(kern, grid, block, 0, st, src, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, ws.kcm, ws.knorm, s.C,
-                               s.GLM, krows, s.bt, s.max_pages, s.H_lm, b_sum, ws.bsum);
+            hipLaunchKernelGGL(kern, grid, block, 0, st, src, (bf16 *)ws.ksb, (bf16 *)ws.ksb2, (bf16 *)ws.ksb3,
+                               ws.kcm, ws.knorm, s.C, s.GLM, krows, s.bt, s.max_pages, s.H_lm, b_sum, ws.bsum);
         };
         if (s.sum_bf16) {
             if (s.D == 64) prep(ksum_prep_kernel<bf16, 64>, (const bf16 *)k_sum);
@@ -1023,6 +1067,17 @@ hipError_t launch_score_select(const Shape &s, const void *q, const void *k_sum,
     const int nq = (qcal || !s.io_bf16) ? 1 : 0, nk = s.sum_bf16 ? 0 : 1;
     const float kappa = 1.0f / 16384.f + (float)(nq + nk + nq * nk) * (1.f + 1.f / 128.f) / 65536.f;
 
+    if (ws.topk) {
+        // normalised aggregation: each head's log-sum-exp over the candidates first
+        const bool qf32 = qcal || !s.io_bf16;
+        const void *qv = qcal ? (const void *)ws.q_s : q;
+        if (s.agg_mode == 1) {
+            if (qf32) e = dispatch_approx<float>(s, (const float *)qv, b_sum, ws, kappa, st);
+            else e = dispatch_approx<bf16>(s, (const bf16 *)qv, b_sum, ws, kappa, st);
+            if (e != hipSuccess) return e;
+        }
+        return launch_score_topk(s, qv, qf32, ws, b_sum, sel_idx, sel_score, st);
+    }
     if (qcal || !s.io_bf16) {
         const float *qv = qcal ? ws.q_s : (const float *)q;
         if ((e = dispatch_approx<float>(s, qv, b_sum, ws, kappa, st)) != hipSuccess) return e;

@@ -6,6 +6,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import long_context_chunk_landmark_amd as hils
 from long_context_chunk_landmark_amd import _binding as hb
@@ -262,3 +263,39 @@ def test_backward_argument_checks(lib):
     assert _bwd(lib, cfg, ws=MIS, nbytes=need) == hb.HILS_ERR_INVALID_ARG and "workspace" in hb.last_error()
     empty = _cfg(N=0)
     assert lib.hils_sparse_attend_backward(ctypes.byref(empty), *([None] * 15), 0, None) == hb.HILS_OK
+
+
+def test_score_modes_and_their_workspaces(lib):
+    """Two-pass form: workspace grows with N^2 / S (the ragged score array);
+    streaming form: with N K.  Auto keeps the two-pass form while its score
+    array stays within 32 GiB and streams beyond.  An unknown mode is refused."""
+    def ws(mode, N, B=1):
+        c = hb.Config(H_q=32, H_kv=8, d=128, S=64, W=1024, K=32, B=B, N=N, score_mode=mode).to_c()
+        return lib.hils_workspace_size(ctypes.byref(c), hb.WS_SCORE, 0, 0)
+    two_small, two_big = ws(hb.SCORE_TWO_PASS, 65536), ws(hb.SCORE_TWO_PASS, 131072)
+    st_small, st_big = ws(hb.SCORE_STREAMING, 65536), ws(hb.SCORE_STREAMING, 131072)
+    assert two_big > 3.5 * two_small  # quadratic term dominates
+    assert 1.9 * st_small < st_big < 2.1 * st_small  # linear in N
+    assert st_big < two_big / 4
+    assert ws(hb.SCORE_AUTO, 131072) == two_big  # 4.3 GB of scores: the two-pass form
+    big2 = ws(hb.SCORE_AUTO, 524288, B=2)  # 137 GB of scores: streaming
+    assert big2 == ws(hb.SCORE_STREAMING, 524288, B=2) < ws(hb.SCORE_TWO_PASS, 524288, B=2) / 10
+    c = hb.Config(H_q=8, H_kv=2, d=128, S=64, W=128, K=4, N=1024, score_mode=3).to_c()
+    assert lib.hils_score_select(ctypes.byref(c), None, None, None, None, None, None, 0, 0, None, None, None, 0,
+                                 None) == hb.HILS_ERR_INVALID_ARG
+
+
+def test_streaming_coverage_is_checked_before_pointers(lib):
+    """The streaming form is refused for d = 128, G = 8, fp32 summaries and
+    K > 32 (its per-block working set exceeds the LDS) and accepted otherwise:
+    an accepted shape gets as far as the pointer checks."""
+    def st(**kw):
+        c = hb.Config(**dict(dict(H_q=8, H_kv=1, d=128, S=64, W=128, K=40, N=4096,
+                                  score_mode=hb.SCORE_STREAMING), **kw)).to_c()
+        return lib.hils_score_select(ctypes.byref(c), None, None, None, None, None, None, 0, 0, None, None, None, 0,
+                                     None)
+    assert st() == hb.HILS_ERR_UNSUPPORTED
+    assert st(K=32) == hb.HILS_ERR_INVALID_ARG  # covered: fails on the NULL q
+    assert st(summary_dtype=torch.bfloat16) == hb.HILS_ERR_INVALID_ARG
+    assert st(H_q=4) == hb.HILS_ERR_INVALID_ARG
+    assert st(score_mode=hb.SCORE_TWO_PASS) == hb.HILS_ERR_INVALID_ARG
