@@ -442,6 +442,8 @@ __global__ __launch_bounds__(4 * S) void bwd_keys_kernel(
     }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------- MFMA key pass (bf16 I/O)
 //
 // The key-side pass on the matrix cores.  Block (chunk c, kv head g, batch
@@ -485,8 +487,6 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     constexpr int NQ = 4, DPT = D / NQ;   // summary backward: four threads per key
     __shared__ u32x4 q_t[RT][NB];         // tile rows of q (bf16, swizzled by pair)
     __shared__ u32x4 do_t[RT][NB];        // and of dO
-    __shared__ u32x4 qT[D][4];            // q transposed: [dim][k-slot], 32 bf16 per dim
-    __shared__ u32x4 doT[D][4];           // dO transposed
     __shared__ float pbias[RT];           // per pair: log-weight added to the scaled logit
     __shared__ float pdc[RT];             // the term subtracted from dO.v (D' or dO.o_c)
     __shared__ float pdsh[RT];            // ds^_c of a selecting pair (0 for window pairs)
@@ -578,19 +578,25 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             prow[t] = tlim;
         }
         __syncthreads();
-        // the transposed tiles, 8 k-slots (16 bytes) of one dim per item
-        for (int idx = t; idx < 2 * D * 4; idx += NT) {
-            const int which = idx / (D * 4), x = (idx / 4) % D, jb = idx % 4;
-            const u32x4(*src)[NB] = which ? do_t : q_t;
-            bf16x8 e8;
+    };
+    // The A operands Q^T and dO^T (dims 16 dt + l%16 x k-slots 8 grp .. +7)
+    // read transposed from the row-major tiles: in each 16-lane group, the
+    // transpose read gives lane i element i of the 16 values that lanes
+    // 4r .. 4r+3 address; lane 4r + sub addresses 4 dims of pair row r.
+    // Slots 8grp .. 8grp+3 are pairs 4grp + r, slots 8grp+4 .. +7 pairs
+    // 16 + 4grp + r.
+    const int tsub = r16 & 3, trow = r16 >> 2;
+    auto t_frag = [&](const u32x4 (*src)[NB], int dt) __attribute__((always_inline)) {
+        const int x0 = 16 * dt + 4 * tsub;
+        bf16x8 a;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int p = j < 4 ? 4 * jb + j : 16 + 4 * jb + (j - 4);  // pair of k-slot 8 jb + j
-                e8[j] = ((const bf16 *)&src[p][(x >> 3) ^ bswz<NB>(p)])[x & 7];
-            }
-            __builtin_memcpy(&(which ? doT : qT)[x][jb], &e8, 16);
+        for (int h = 0; h < 2; ++h) {
+            const int p = 16 * h + 4 * grp + trow;
+            const short *at = (const short *)&src[p][(x0 >> 3) ^ bswz<NB>(p)] + (x0 & 7);
+            const v4i16 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)at);
+            __builtin_memcpy((char *)&a + 8 * h, &v4, 8);
         }
-        __syncthreads();
+        return a;
     };
     auto compute = [&](int nrows, bool selected) __attribute__((always_inline)) {
         const int np = nrows * G;
@@ -628,10 +634,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
         // V and K alternate, so consecutive MFMAs write different accumulators
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            bf16x8 ad, aq;
-            const u32x4 rd = doT[16 * dt + r16][grp], rq = qT[16 * dt + r16][grp];
-            __builtin_memcpy(&ad, &rd, 16);
-            __builtin_memcpy(&aq, &rq, 16);
+            const bf16x8 ad = t_frag(do_t, dt), aq = t_frag(q_t, dt);
             accV[dt] = mfma16(ad, ph, accV[dt]);
             accK[dt] = mfma16(aq, sh, accK[dt]);
             accV[dt] = mfma16(ad, pl, accV[dt]);
@@ -810,8 +813,6 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
 
 // ---------------------------------------------------------------- MFMA row pass (bf16 I/O)
 //
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding)
 constexpr int bwd_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
