@@ -487,7 +487,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     constexpr int NQ = 4, DPT = D / NQ;   // summary backward: four threads per key
     __shared__ u32x4 q_t[RT][NB];         // tile rows of q (bf16, swizzled by pair)
     __shared__ u32x4 do_t[RT][NB];        // and of dO
-    __shared__ float pbias[RT];           // per pair: log-weight added to the scaled logit
+    __shared__ float pbias[RT];           // per pair: log-weight (base 2) added to the scaled logit
     __shared__ float pdc[RT];             // the term subtracted from dO.v (D' or dO.o_c)
     __shared__ float pdsh[RT];            // ds^_c of a selecting pair (0 for window pairs)
     __shared__ int prow[RT];              // last key the pair may see (its row; selected: all)
@@ -508,6 +508,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     const int keyl = 16 * wave + r16;                  // the lane's key within the chunk
     const int key = c * S + keyl;
     const bool key_ok = key < N;
+    const float scale2 = scale * LOG2E;
 
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -552,12 +553,12 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             const int2 ik = row_of(t / G);
             const int64_t rh = (b * H_q + (int64_t)g * G + t % G) * N + ik.x;
             if (selected) {
-                tbias = mlog[rh * K + ik.y];  // P_j = e^{s_j + m}, m = s^_c - L - lse_c
+                tbias = mlog[rh * K + ik.y] * LOG2E;  // P_j = e^{s_j + m}, m = s^_c - L - lse_c
                 tdc = gdo[rh * K + ik.y];
                 tdsh = dsel[rh * K + ik.y];
                 tlim = 0x7fffffff;
             } else {
-                tbias = -lse[rh];
+                tbias = -lse[rh] * LOG2E;
                 tdc = dcoef[rh];
                 tlim = ik.x;
             }
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int i = 0; i < 4; ++i) {
                 const int p = 16 * rg + 4 * grp + i;
                 float P = 0.f;
-                if (key_ok && key <= prow[p]) P = expf(fmaf(sacc[rg][i], scale, pbias[p]));
+                if (key_ok && key <= prow[p]) P = exp2_hw(fmaf(sacc[rg][i], scale2, pbias[p]));
                 const float ds = scale * P * (dacc[rg][i] - pdc[p]);
                 const bf16 p1 = (bf16)P, d1 = (bf16)ds;
                 ph[4 * rg + i] = p1;
@@ -924,6 +925,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
         __builtin_memcpy(&df[s], &c2, 16);
     }
     const float L = lse[row];
+    const float scale2 = scale * LOG2E, L2 = rv ? L * LOG2E : INFINITY;
     f32x4 accA[DT], accB[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) accA[dt] = accB[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1046,36 +1048,37 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
                 dacc[kt2] = mfma16(av, df[s], dacc[kt2]);
             }
         if (!window) {
+            // the chunk's softmax in base 2: e_j = 2^(x_j - max x), x = s log2 e,
+            // p_cj = e_j / z, lse_c = (max x + log2 z) ln 2
             float cmax = -INFINITY;
 #pragma unroll
             for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sacc[kt2][i] *= scale;
+                    sacc[kt2][i] *= scale2;
                     cmax = fmaxf(cmax, sacc[kt2][i]);
                 }
             cmax = rows4_max(cmax);
-            float z = 0.f;
-#pragma unroll
-            for (int kt2 = 0; kt2 < KT; ++kt2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) z += expf(sacc[kt2][i] - cmax);
-            const float lse_c = cmax + logf(rows4_sum(z));
-            float gp = 0.f;
+            float z = 0.f, gp = 0.f;
 #pragma unroll
             for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sacc[kt2][i] = expf(sacc[kt2][i] - lse_c);  // p_cj
-                    gp = fmaf(sacc[kt2][i], dacc[kt2][i], gp);
+                    const float ex = exp2_hw(sacc[kt2][i] - cmax);
+                    sacc[kt2][i] = ex;
+                    z += ex;
+                    gp = fmaf(ex, dacc[kt2][i], gp);
                 }
-            const float gc = rows4_sum(gp);  // dO.o_c
+            z = rows4_sum(z);  // >= 1: the largest key contributes 2^0
+            const float rz = __builtin_amdgcn_rcpf(z);
+            const float lse_c = (cmax + log2f(z)) * LN2;
+            const float gc = rows4_sum(gp) * rz;  // dO.o_c
             const float shat = act ? scp[cur] : 0.f;
-            const float wc = act ? expf(shat - L) : 0.f;
+            const float f = act ? expf(shat - L) * rz : 0.f;  // w_c / z
 #pragma unroll
             for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sacc[kt2][i] = wc * sacc[kt2][i] * (dacc[kt2][i] - gc);
+                for (int i = 0; i < 4; ++i) sacc[kt2][i] = f * sacc[kt2][i] * (dacc[kt2][i] - gc);
             ktx(sacc, accA, k_l);
             if (act) {
                 if (grp == 0) {
@@ -1086,17 +1089,26 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
                 nch = cur < nsel ? (int)sl[cur] : 0x7fffffff;
             }
         } else {
-            const bool diag = c == qc;
+            // P = 2^(s scale log2 e - L log2 e); a row past N has L2 = +inf (P = 0).
+            // Keys of a window chunk below the query chunk all precede the
+            // row; in the query's own chunk, keys after the row are masked.
+#pragma unroll
+            for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sacc[kt2][i] = exp2_hw(fmaf(sacc[kt2][i], scale2, -L2));
+            if (c == qc) {
+#pragma unroll
+                for (int kt2 = 0; kt2 < KT; ++kt2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (c * S + 16 * kt2 + 4 * grp + i > iq) sacc[kt2][i] = 0.f;
+            }
 #pragma unroll
             for (int kt2 = 0; kt2 < KT; ++kt2)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = c * S + 16 * kt2 + 4 * grp + i;
-                    const bool ok = rv && j < N && !(diag && j > iq);
-                    const float P = ok ? expf(fmaf(sacc[kt2][i], scale, -L)) : 0.f;
-                    sacc[kt2][i] = P;
-                    dpart = fmaf(P, dacc[kt2][i], dpart);
-                    dacc[kt2][i] *= P;
+                    dpart = fmaf(sacc[kt2][i], dacc[kt2][i], dpart);
+                    dacc[kt2][i] *= sacc[kt2][i];
                 }
             ktx(dacc, accA, k_l);
             ktx(sacc, accB, k_l);

@@ -71,6 +71,11 @@ __device__ __forceinline__ int xor_sum_i(int v) {
     return v;
 }
 
+// 2^x by the hardware instruction alone (v_exp_f32, about 1 ulp).  Unlike
+// exp2f it skips the rescaling that keeps results below 2^-126 denormal
+// instead of zero: softmax weights that small change no sum they enter.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48) with the gfx950 lane-swap instructions, which stay in the VALU
 // instead of a ds_bpermute round trip.  Swapping a register with itself
