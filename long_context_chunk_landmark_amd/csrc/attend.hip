@@ -537,7 +537,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                acc[t][kt][i] = exp2f(fmaf(acc[t][kt][i], scale_log2, -cmax));
+                                acc[t][kt][i] = exp2_hw(fmaf(acc[t][kt][i], scale_log2, -cmax));
                                 lc += acc[t][kt][i];
                             }
                         lc = rows4_sum(lc);
@@ -583,13 +583,13 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                         }
                     cmax = rows4_max(cmax);
                     const float mnew = fmaxf(mrun[t], cmax);
-                    const float alpha = exp2f(mrun[t] - mnew);
+                    const float alpha = exp2_hw(mrun[t] - mnew);
                     float ls = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            acc[t][kt][i] = exp2f(acc[t][kt][i] - mnew);
+                            acc[t][kt][i] = exp2_hw(acc[t][kt][i] - mnew);
                             ls += acc[t][kt][i];
                         }
                     ls = rows4_sum(ls);
