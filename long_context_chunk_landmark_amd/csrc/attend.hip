@@ -337,7 +337,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         const int ent = __builtin_amdgcn_readfirstlane(ulist[it]);
         const int c = ent & 0x3fff;
         const bf16 *kc = btb ? k + ((int64_t)((uint32_t)ent >> 14) * H_kv + g) * S * D : kbase + (int64_t)c * S * D;
-        const int buf = it % NSTAGE;
+        const int buf = __builtin_amdgcn_readfirstlane(it % NSTAGE);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vtbase + (int64_t)c * D * S), (short)0, D * S * 2, BUF_RSRC_WORD3);
         // The swizzle repeats every 16 rows, so the lane part of a piece's
@@ -540,8 +540,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                                 acc[t][kt][i] = exp2_hw(fmaf(acc[t][kt][i], scale_log2, -cmax));
                                 lc += acc[t][kt][i];
                             }
-                        lc = rows4_sum(lc);
-                        const float f = act[t] ? nwt[t] / lc : 0.f;
+                        lc = rows4_sum(lc);  // >= 1: the largest key contributes 2^0
+                        const float f = act[t] ? nwt[t] * __builtin_amdgcn_rcpf(lc) : 0.f;
 #pragma unroll
                         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -571,19 +571,22 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const int iq = i0 + qrow[t];
+                    // only the query's own chunk holds keys after the row: lim is
+                    // the last key offset (from the lane's first) the row sees
+                    const int lim = diag ? q0 + iq - c * S - 4 * grp : S;
                     float cmax = -INFINITY;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int j = c * S + 16 * kt + 4 * grp + i;
-                            const float x = (diag && j > q0 + iq) ? -INFINITY : acc[t][kt][i] * scale_log2;
+                            const float x = 16 * kt + i > lim ? -INFINITY : acc[t][kt][i] * scale_log2;
                             acc[t][kt][i] = x;
                             cmax = fmaxf(cmax, x);
                         }
                     cmax = rows4_max(cmax);
                     const float mnew = fmaxf(mrun[t], cmax);
                     const float alpha = exp2_hw(mrun[t] - mnew);
+                    const bool rescale = __ballot(mnew > mrun[t]) != 0ull;
                     float ls = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
@@ -595,8 +598,11 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                     ls = rows4_sum(ls);
                     lrun[t] = lrun[t] * alpha + ls;
                     mrun[t] = mnew;
+                    // alpha = 1 exactly in every lane whose max held
+                    if (rescale) {
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
+                        for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
+                    }
                 }
                 pv(std::integral_constant<int, ALL>{}, v_tile(buf), acc);
             }
