@@ -487,10 +487,11 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     constexpr int NQ = 4, DPT = D / NQ;   // summary backward: four threads per key
     __shared__ u32x4 q_t[RT][NB];         // tile rows of q (bf16, swizzled by pair)
     __shared__ u32x4 do_t[RT][NB];        // and of dO
-    __shared__ float pbias[RT];           // per pair: log-weight (base 2) added to the scaled logit
-    __shared__ float pdc[RT];             // the term subtracted from dO.v (D' or dO.o_c)
-    __shared__ float pdsh[RT];            // ds^_c of a selecting pair (0 for window pairs)
-    __shared__ int prow[RT];              // last key the pair may see (its row; selected: all)
+    // per pair (16-byte aligned: a lane reads four consecutive pairs at once)
+    __shared__ __attribute__((aligned(16))) float pbias[RT];  // log-weight (base 2) added to the scaled logit
+    __shared__ __attribute__((aligned(16))) float pdc[RT];    // the term subtracted from dO.v (D' or dO.o_c)
+    __shared__ __attribute__((aligned(16))) float pdsh[RT];   // ds^_c of a selecting pair (0 for window pairs)
+    __shared__ __attribute__((aligned(16))) int prow[RT];     // last key the pair may see (its row; selected: all)
     __shared__ int list_i[LCAP];
     __shared__ int list_k[LCAP];
     __shared__ int nlist;
@@ -524,8 +525,13 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
     f32x4 accK[DT], accV[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) accK[dt] = accV[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int idx = t; idx < G * D; idx += NT) dkp_l[idx / D][idx % D] = 0.f;
-    if (t < G) dbp_l[t] = 0.f;
+    // dk'^T of the chunk's landmark heads (dims x heads, head = MFMA column):
+    // wave w accumulates the dim tiles dt = w, w + NWV, ...; db' as a sum
+    constexpr int NWV = S / 16, KPN = (DT + NWV - 1) / NWV;
+    f32x4 accKP[KPN];
+#pragma unroll
+    for (int j = 0; j < KPN; ++j) accKP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dbacc = 0.f;
 
     // A tile: nrows rows x G heads; pair p is row p / G, head p % G;
     // row_of(rr) -> (row, selection slot).  fetch loads a tile's rows and
@@ -599,8 +605,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
         }
         return a;
     };
-    auto compute = [&](int nrows, bool selected) __attribute__((always_inline)) {
-        const int np = nrows * G;
+    auto compute = [&](bool selected) __attribute__((always_inline)) {
         f32x4 sacc[2], dacc[2];
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg) {
@@ -617,21 +622,26 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
                 dacc[rg] = mfma16(da, vf[s], dacc[rg]);
             }
         }
+        // the lane's k-slots 4 rg + i are pairs 16 rg + 4 grp + i
         bf16x8 ph, pl, sh, sl;
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
+        for (int rg = 0; rg < 2; ++rg) {
+            const int p0 = 16 * rg + 4 * grp;
+            const f32x4 pb = *(const f32x4 *)&pbias[p0], pc = *(const f32x4 *)&pdc[p0];
+            const int4 pr = *(const int4 *)&prow[p0];
+            const int lim[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int p = 16 * rg + 4 * grp + i;
-                float P = 0.f;
-                if (key_ok && key <= prow[p]) P = exp2_hw(fmaf(sacc[rg][i], scale2, pbias[p]));
-                const float ds = scale * P * (dacc[rg][i] - pdc[p]);
+                const float ex = exp2_hw(fmaf(sacc[rg][i], scale2, pb[i]));
+                const float P = (key_ok && key <= lim[i]) ? ex : 0.f;
+                const float ds = scale * P * (dacc[rg][i] - pc[i]);
                 const bf16 p1 = (bf16)P, d1 = (bf16)ds;
                 ph[4 * rg + i] = p1;
                 pl[4 * rg + i] = (bf16)(P - (float)p1);
                 sh[4 * rg + i] = d1;
                 sl[4 * rg + i] = (bf16)(ds - (float)d1);
             }
+        }
         // V and K alternate, so consecutive MFMAs write different accumulators
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -642,20 +652,35 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             accK[dt] = mfma16(aq, sl, accK[dt]);
         }
         if (selected) {
-            // dk' += scale ds^ q and db' += ds^ of each landmark head, by
-            // owner threads (dim t % D of heads t / D, + NT / D, ...)
-            const int x = t % D;
-            for (int lm = t / D; lm < GLM; lm += NT / D) {
-                float acc = dkp_l[lm][x], accb = 0.f;
-                for (int p = 0; p < np; ++p) {
-                    if ((GLM == G ? p % G : 0) != lm) continue;
-                    const bf16 qx = ((const bf16 *)&q_t[p][(x >> 3) ^ bswz<NB>(p)])[x & 7];
-                    acc = fmaf(scale * pdsh[p], (float)qx, acc);
-                    accb += pdsh[p];
+            // dk'^T += Q^T X with X[pair][head] = scale ds^ when the pair's
+            // query head feeds landmark head `head` (all pairs when there is
+            // one landmark head per kv head); column r16 is head r16
+            bf16x8 kh, kl;
+            float dbs = 0.f;
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg) {
+                const f32x4 pd = *(const f32x4 *)&pdsh[16 * rg + 4 * grp];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lm = GLM == G ? (4 * grp + i) % G : 0;
+                    const float x = lm == r16 ? pd[i] : 0.f;
+                    dbs += x;
+                    const float xs = scale * x;
+                    const bf16 x1 = (bf16)xs;
+                    kh[4 * rg + i] = x1;
+                    kl[4 * rg + i] = (bf16)(xs - (float)x1);
                 }
-                dkp_l[lm][x] = acc;
-                if (x == 0) dbp_l[lm] += accb;
             }
+#pragma unroll
+            for (int j = 0; j < KPN; ++j) {
+                const int dt = wave + NWV * j;
+                if (dt < DT) {
+                    const bf16x8 aq = t_frag(q_t, dt);
+                    accKP[j] = mfma16(aq, kh, accKP[j]);
+                    accKP[j] = mfma16(aq, kl, accKP[j]);
+                }
+            }
+            dbacc += rows4_sum(dbs);  // this tile's ds^ of head r16
         }
     };
 
@@ -666,7 +691,7 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int j = 0; j < ntile; ++j) {
             commit();
             if (j + 1 < ntile) fetch(nrows_of(j + 1), selected, [&](int rr) { return row_of(j + 1, rr); });
-            compute(nrows_of(j), selected);
+            compute(selected);
         }
     };
 
@@ -733,6 +758,20 @@ __global__ __launch_bounds__(4 * S) __attribute__((amdgpu_waves_per_eu(2))) void
             if (mv) list_i[t] = li, list_k[t] = lk;
             if (t == 0) nlist = tot - nfull;
         }
+    }
+
+    // dk' and db' of the landmark heads: lane l holds dims 16 dt + 4 grp + i
+    // of head l % 16
+    if (r16 < GLM) {
+#pragma unroll
+        for (int j = 0; j < KPN; ++j) {
+            const int dt = wave + NWV * j;
+            if (dt < DT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dkp_l[r16][16 * dt + 4 * grp + i] = accKP[j][i];
+            }
+        }
+        if (wave == 0 && grp == 0) dbp_l[r16] = dbacc;
     }
 
     // dv is final (the summary does not involve v)
