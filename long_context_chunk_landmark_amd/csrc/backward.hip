@@ -1036,6 +1036,25 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
         }
         return a;
     };
+    // acc1^T += K^T X1^T and acc2^T += K^T X2^T from one read of each K^T
+    // fragment (the window: X1 = P o dP, X2 = P)
+    auto ktx2 = [&](const f32x4 (&x1)[KT], f32x4 (&acc1)[DT], const f32x4 (&x2)[KT], f32x4 (&acc2)[DT],
+                    const u32x4 (*k_l)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps) {
+            bf16x8 hi1, lo1, hi2, lo2;
+            split_op(x1[2 * ps], x1[2 * ps + 1], hi1, lo1);
+            split_op(x2[2 * ps], x2[2 * ps + 1], hi2, lo2);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 a = kt_frag(k_l, ps, dt);
+                acc1[dt] = mfma16(a, hi1, acc1[dt]);
+                acc2[dt] = mfma16(a, hi2, acc2[dt]);
+                acc1[dt] = mfma16(a, lo1, acc1[dt]);
+                acc2[dt] = mfma16(a, lo2, acc2[dt]);
+            }
+        }
+    };
     auto ktx = [&](const f32x4 (&x)[KT], f32x4 (&acc)[DT], const u32x4 (*k_l)[NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps) {
@@ -1149,8 +1168,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
                     dpart = fmaf(sacc[kt2][i], dacc[kt2][i], dpart);
                     dacc[kt2][i] *= sacc[kt2][i];
                 }
-            ktx(dacc, accA, k_l);
-            ktx(sacc, accB, k_l);
+            ktx2(dacc, accA, sacc, accB, k_l);
         }
         }
         // chunk it + 1 has landed once at most the groups issued after it
