@@ -16,17 +16,20 @@
 //   da_j = p_j dk'.(k_j - k') - db' p_j (a_j - p.a)
 //   dq' = scale sum_j da_j k_j, dk_j += p_j dk' + scale da_j q'.
 //
-// Two kernels, deterministic (every sum has one owner, no atomics):
-//   bwd_rows   one block per (b, kv head, row), a wave per query head of
-//              the group: dq, and per selected slot ds^, the chunk's
-//              log-weight m = s^ - L - lse_c and g = dO.o_c
-//   bwd_keys   one block per (b, kv head, chunk): dk, dv of the chunk's keys
-//              from the window rows and the rows that selected it (found by
-//              a binary search in each later row's ascending selection),
-//              the chunk's dk', db' of its landmark heads, and then the
-//              summary backward into dk and dq'.
-// fp32 VALU throughout: a first, exact backward; the forward's MFMA
-// schedule is not carried over.
+// Two passes, deterministic (every sum has one owner; the only atomics
+// are the order-free ORs of the selection bitmap):
+//   rows   dq, and per selected slot ds^, the chunk's log-weight
+//          m = s^ - L - lse_c and g = dO.o_c
+//   keys   dk, dv of a chunk's keys from the window rows and the rows that
+//          selected it, the chunk's dk', db' of its landmark heads, and then
+//          the summary backward into dk and dq'.
+// bf16 I/O runs them on MFMA (bwd_rows_mfma_kernel: a block per 32 queries
+// walking the union of their selections through an LDS ring;
+// bwd_selbits_kernel: a bitmap of each chunk's selecting rows;
+// bwd_keys_mfma_kernel: a block per chunk, rows in tiles of 32 pairs), with
+// P and dS entering their products as two bf16 terms each.  fp32 I/O runs
+// the first, fp32 VALU kernels (bwd_rows_kernel, bwd_keys_kernel: selecting
+// rows found by a binary search in each later row's ascending selection).
 #include <type_traits>
 
 #include "hils_device.hpp"
