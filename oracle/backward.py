@@ -55,7 +55,9 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     linear in dout and dlse, so a row whose dout and dlse vanish contributes
     nothing to any gradient: with dout = dlse = 0 outside ``rows`` the
     gradients are exactly those of the full loop (out, lse and sel_score are
-    then filled for the visited rows only).
+    then filled for the visited rows only).  Then, too, only the chunks that
+    a visited row selected get their summaries and summary backward: every
+    other chunk's dk' and db' are zero, so its summary backward adds nothing.
     """
     B, H_q, N, d = np.shape(q)
     H_kv = np.shape(k)[1]
@@ -81,6 +83,16 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
     def lm_of(h):
         return h * H_lm // H_q
 
+    # chunks whose summaries enter the visited rows (all of them without rows)
+    used = np.ones((B, H_kv, C), bool)
+    if rows is not None:
+        used[:] = False
+        for b in range(B):
+            for g in range(H_kv):
+                for i in rows:
+                    cs = sel[b, g, i]
+                    used[b, g, cs[cs >= 0]] = True
+
     # summaries (forward), kept with their softmax for the summary backward
     ksum = np.zeros((B, H_lm, C, d))
     bsum = np.zeros((B, H_lm, C))
@@ -90,6 +102,8 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
         for l in range(H_lm):
             g = kv_of_lm(l)
             for c in range(C):
+                if not used[b, g, c]:
+                    continue
                 kc = k[b, g, c * S:(c + 1) * S]
                 a = scale * kc @ ql[b, l, c]
                 p = np.exp(a - logsumexp(a))
@@ -157,6 +171,8 @@ def backward(cfg: dict, q, k, v, q_lm, sel_idx, dout, dlse=None, landmark: str =
         for l in range(H_lm):
             g = kv_of_lm(l)
             for c in range(C):
+                if not used[b, g, c]:
+                    continue
                 kc = k[b, g, c * S:(c + 1) * S]
                 p, a = pl[b, l, c], al[b, l, c]
                 da = p * ((kc - ksum[b, l, c]) @ dks[b, l, c]) - dbs[b, l, c] * p * (a - p @ a)

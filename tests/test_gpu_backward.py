@@ -90,22 +90,15 @@ def test_backward_is_deterministic(dev):
         assert torch.equal(x, y)
 
 
-def test_backward_8k_k16_sampled_rows(dev):
-    """The 8K GQA workload (N = 8192, K = 16, G = 4, d = 128, S = 64: the MFMA
-    row and key passes, several walk tiles and bitmap batches per block).
-    The output gradient is nonzero on 96 sampled rows only, so the oracle
-    visits just those rows (the gradients are linear in dout and dlse; its
-    row-subset pin).  dq of every other row must be exactly zero."""
-    p = dict(W.PRESETS["gqa_8k"])
-    print("[backward] gqa_8k sampled rows", flush=True)
+def _sampled_rows_backward(dev, p, rows, seed):
+    """GPU backward against the oracle with the output gradient nonzero on
+    the given rows only: the oracle visits just those rows (the gradients
+    are linear in dout and dlse; its row-subset pin).  dq of every other row
+    must be exactly zero."""
     inp = W.make_prefill(p, device=dev)
     cfg = inp["cfg"]
     fw = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
-    rng = np.random.default_rng(123)
-    rows = np.sort(np.concatenate([rng.choice(np.arange(0, 2048), 24, replace=False),
-                                   rng.choice(np.arange(2048, cfg.N - 1024), 40, replace=False),
-                                   rng.choice(np.arange(cfg.N - 1024, cfg.N), 32, replace=False)]))
-    g = torch.Generator().manual_seed(321)
+    g = torch.Generator().manual_seed(seed)
     dout = torch.zeros(fw["out"].shape, dtype=torch.float32)
     dlse = torch.zeros(fw["lse"].shape, dtype=torch.float32)
     dout[:, :, rows] = torch.randn((cfg.B, cfg.H_q, len(rows), cfg.d), generator=g)
@@ -120,8 +113,9 @@ def test_backward_8k_k16_sampled_rows(dev):
                           host(fw["sel_idx"]), host(dout), host(dlse), landmark="chunk", rows=rows)
     others = np.ones(cfg.N, bool)
     others[rows] = False
-    got_dq = host(dq).numpy().astype(np.float64)
+    got_dq = host(dq).numpy()
     assert np.all(got_dq[:, :, others] == 0.0)
+    del got_dq
     for key, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dq_lm", dq_lm)):
         got = host(got).numpy().astype(np.float64)
         want = ref[key]
@@ -130,3 +124,32 @@ def test_backward_8k_k16_sampled_rows(dev):
         print(f"  {key}: max err {np.abs(got - want).max():.3g} (max |ref| {np.abs(want).max():.3g})", flush=True)
         assert not bad.any(), (f"{key}: {bad.sum()} of {bad.size} outside; max err "
                                f"{np.abs(got - want).max():.3g}, max |ref| {np.abs(want).max():.3g}")
+
+
+def test_backward_8k_k16_sampled_rows(dev):
+    """The 8K GQA workload (N = 8192, K = 16, G = 4, d = 128, S = 64: the MFMA
+    row and key passes, several walk tiles and bitmap batches per block), the
+    output gradient on 96 sampled rows."""
+    p = dict(W.PRESETS["gqa_8k"])
+    print("[backward] gqa_8k sampled rows", flush=True)
+    N = p["N"]
+    rng = np.random.default_rng(123)
+    rows = np.sort(np.concatenate([rng.choice(np.arange(0, 2048), 24, replace=False),
+                                   rng.choice(np.arange(2048, N - 1024), 40, replace=False),
+                                   rng.choice(np.arange(N - 1024, N), 32, replace=False)]))
+    _sampled_rows_backward(dev, p, rows, 321)
+
+
+def test_backward_128k_k32_sampled_rows(dev):
+    """The 128K prefill workload the bench times (N = 131072, H_q = 32,
+    H_kv = 8, d = 128, S = 64, W = 1024, K = 32, drifting inputs), the output
+    gradient on 32 sampled rows: early rows with fewer candidates than K,
+    rows across the sequence and the last rows (the longest walks)."""
+    p = dict(W.PRESETS["prefill_128k"])
+    print("[backward] prefill_128k sampled rows", flush=True)
+    N = p["N"]
+    rng = np.random.default_rng(124)
+    rows = np.sort(np.concatenate([rng.choice(np.arange(0, 4096), 8, replace=False),
+                                   rng.choice(np.arange(4096, N - 2048), 16, replace=False),
+                                   rng.choice(np.arange(N - 2048, N), 8, replace=False)]))
+    _sampled_rows_backward(dev, p, rows, 322)
