@@ -1081,12 +1081,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
     // the end of step it - 1; a step ends once chunk it + 1 has landed (this
     // wave's later pieces may stay in flight; other vector-memory operations
     // issued after them only make the wait longer)
-    __syncthreads();  // the walk list is complete
-    for (int j = 0; j < NSTG - 1 && j < T; ++j) issue(j, j);
-    wait_groups(min(NSTG - 2, T - 1));
-    __syncthreads();
-    for (int it = 0; it < T; ++it) {
-        if (it + NSTG - 1 < T) issue(it + NSTG - 1, (it + NSTG - 1) % NSTG);
+    // one step of the walk: chunk it, staged in ring stage it % NSTG
+    auto step = [&](int it) __attribute__((always_inline)) {
         const u32x4(*k_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it % NSTG][0]);
         const u32x4(*v_l)[NB] = reinterpret_cast<const u32x4(*)[NB]>(&stg[it % NSTG][TK]);
         const int c = ulist[it];
@@ -1174,10 +1170,34 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_rows_mfma_kernel(
             ktx2(dacc, accA, sacc, accB, k_l);
         }
         }
-        // chunk it + 1 has landed once at most the groups issued after it
-        // (chunks it + 2 .. min(it + NSTG - 1, T - 1)) are in flight
-        wait_groups(min(NSTG - 2, T - 2 - it));
+    };
+    __syncthreads();  // the walk list is complete
+    if constexpr (NSTG == 4) {
+        // steps in pairs, one barrier per pair: chunks it + 2 and it + 3 are
+        // issued at the start of the pair into the stages the previous
+        // barrier released, and have landed at its end
+        for (int j = 0; j < 2 && j < T; ++j) issue(j, j);
+        wait_groups(0);
         __syncthreads();
+        for (int it = 0; it < T; it += 2) {
+            for (int j = it + 2; j < it + 4 && j < T; ++j) issue(j, j % NSTG);
+            step(it);
+            if (it + 1 < T) step(it + 1);
+            wait_groups(0);
+            __syncthreads();
+        }
+    } else {
+        for (int j = 0; j < NSTG - 1 && j < T; ++j) issue(j, j);
+        wait_groups(min(NSTG - 2, T - 1));
+        __syncthreads();
+        for (int it = 0; it < T; ++it) {
+            if (it + NSTG - 1 < T) issue(it + NSTG - 1, (it + NSTG - 1) % NSTG);
+            step(it);
+            // chunk it + 1 has landed once at most the groups issued after it
+            // (chunks it + 2 .. min(it + NSTG - 1, T - 1)) are in flight
+            wait_groups(min(NSTG - 2, T - 2 - it));
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: the summary terms, D', dq, ds^ of each slot
