@@ -138,7 +138,8 @@ enum {
     HILS_WS_SCORE_QCAL = 1, /* hils_score_select with Q-Cal               */
     HILS_WS_FUSED = 2,      /* hils_sparse_attend_fused                   */
     HILS_WS_DECODE = 3,     /* hils_decode                                */
-    HILS_WS_BACKWARD = 4    /* hils_sparse_attend_backward                */
+    HILS_WS_BACKWARD = 4,   /* hils_sparse_attend_backward                */
+    HILS_WS_DENSE = 5       /* hils_dense_causal_attend                   */
 };
 
 /* Landmark summary (compressed keys).  For every completed chunk c and
@@ -329,6 +330,26 @@ hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *
                                           const float *sel_score, const float *lse, const void *dout,
                                           const float *dlse, float *dq, float *dk, float *dv, float *dq_lm,
                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense causal attention, the full-attention baseline that the pages quote
+ * HiLS's prefill speed against (wmrh.cn article on HiLS-Attention, results
+ * table: prefill at a 512K context; hyper.ai summary, experiments paragraph
+ * on inference efficiency).  For every query head h (kv head h / G):
+ *   out[b,h,i] = sum_{j<=i} softmax_j(scale q[b,h,i] . k[b,g,j]) v[b,g,j]
+ *   lse[b,h,i] = log sum_{j<=i} exp(scale q[b,h,i] . k[b,g,j])
+ * i.e. the hyper.ai summary's block-sparse attention (方法, naive block-sparse
+ * paragraph) with every key kept.
+ *   q [B,H_q,N,d], k, v [B,H_kv,N,d]  bf16 (io_dtype must be BF16)
+ *   out [B,H_q,N,d] bf16 (written); lse [B,H_q,N] fp32 (written, may be NULL)
+ *   workspace: hils_workspace_size(cfg, HILS_WS_DENSE, 0, 0) bytes; word 0
+ *   is the call's status word, as for hils_sparse_attend_fused (bit 1: a
+ *   value of v beyond fp16's range; v enters the weighted sum as fp16).
+ * d must be 64 or 128 (else HILS_ERR_UNSUPPORTED).  cfg's S, W, K, H_lm and
+ * the landmark, aggregation and score modes are validated as for every call
+ * and otherwise ignored. */
+hils_status_t hils_dense_causal_attend(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                       void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 /* Bytes of workspace the given call needs (0 if none); 0 with
  * hils_last_error() set when the configuration is rejected.  num_seqs and

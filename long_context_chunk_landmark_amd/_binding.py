@@ -23,13 +23,14 @@ HILS_F32, HILS_BF16 = 0, 1
 LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
 AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
 SCORE_AUTO, SCORE_TWO_PASS, SCORE_STREAMING = 0, 1, 2  # hils_score_mode_t
-WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD = range(5)
+WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD, WS_DENSE = range(6)
 
 # Every symbol include/hils.h declares.
 EXPORTED_SYMBOLS = (
     "hils_landmark_summarize",
     "hils_score_select",
     "hils_sparse_attend_fused",
+    "hils_dense_causal_attend",
     "hils_decode",
     "hils_decode_noalloc",
     "hils_summarize_pages",
@@ -140,13 +141,14 @@ def load_library(path: str = LIB_PATH):
     lib.hils_prefill_paged_workspace_size.argtypes = [cfgp, i32, i32, i32]
     lib.hils_prefill_paged_workspace_size.restype = sz
     lib.hils_sparse_attend_backward.argtypes = [cfgp] + [vp] * 15 + [sz, vp]
+    lib.hils_dense_causal_attend.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hils_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32]
     lib.hils_workspace_size.restype = sz
     lib.hils_last_error.restype = ctypes.c_char_p
     lib.hils_version.restype = ctypes.c_int
     for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode",
                "hils_decode_noalloc",
-               "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward"):
+               "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward", "hils_dense_causal_attend"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -290,6 +292,26 @@ def sparse_attend_fused(cfg: Config, q, k, v, sel_idx, sel_score, out=None, lse=
     _check(load_library().hils_sparse_attend_fused(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx),
                                                    _ptr(sel_score), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
                                                    _stream()))
+    return out, lse
+
+
+def dense_causal_attend(cfg: Config, q, k, v, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Dense causal attention over every key (the full-attention baseline) -> (out, lse)."""
+    dev = q.device
+    _want(q, "q", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(k, "k", (cfg.B, cfg.H_kv, cfg.N, cfg.d), cfg.io_dtype, dev)
+    _want(v, "v", (cfg.B, cfg.H_kv, cfg.N, cfg.d), cfg.io_dtype, dev)
+    if out is None:
+        out = torch.empty((cfg.B, cfg.H_q, cfg.N, cfg.d), dtype=cfg.io_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((cfg.B, cfg.H_q, cfg.N), dtype=torch.float32, device=dev)
+    _want(out, "out", (cfg.B, cfg.H_q, cfg.N, cfg.d), cfg.io_dtype, dev)
+    if lse is not None:
+        _want(lse, "lse", (cfg.B, cfg.H_q, cfg.N), torch.float32, dev)
+    ws, nbytes = _workspace(cfg, WS_DENSE, dev, workspace)
+    c = cfg.to_c()
+    _check(load_library().hils_dense_causal_attend(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                   _ptr(ws), nbytes, _stream()))
     return out, lse
 
 

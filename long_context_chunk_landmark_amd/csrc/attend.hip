@@ -881,6 +881,21 @@ static hipError_t dispatch_g(const Shape &s, const void *q, const void *k, const
     }
 }
 
+hipError_t launch_vt_prepass(const Shape &s, const void *v, void *vt, uint32_t *status, hipStream_t st) {
+    // clear the call's status word, then the V^T pre-pass (fp16, slot order)
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, st, status);
+    const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
+    auto vtr = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16 *)v, (f16 *)vt, s.Nk, s.CA, s.H_kv, s.bt,
+                           s.max_pages, status);
+    };
+    if (s.D == 64 && s.S == 64) vtr(v_transpose_kernel<64, 64>);
+    else if (s.D == 64) vtr(v_transpose_kernel<64, 128>);
+    else if (s.S == 64) vtr(v_transpose_kernel<128, 64>);
+    else vtr(v_transpose_kernel<128, 128>);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
                                 const float *sel_score, void *out, float *lse, uint32_t *status, void *vt_ws,
                                 hipStream_t st) {
@@ -898,21 +913,9 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
                                s.W, s.K, s.scale, s.q0, s.Nk, s.bt, s.max_pages);
         return hipGetLastError();
     }
-    // clear the call's status word, then the V^T pre-pass (fp16, slot
-    // order) into the workspace
-    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, st, status);
     f16 *vt = (f16 *)vt_ws;
     {
-        const dim3 grid((unsigned)s.CA, (unsigned)s.H_kv, (unsigned)s.B), block(256);
-        auto vtr = [&](auto kern) {
-            hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16 *)v, vt, s.Nk, s.CA, s.H_kv, s.bt, s.max_pages,
-                               status);
-        };
-        if (s.D == 64 && s.S == 64) vtr(v_transpose_kernel<64, 64>);
-        else if (s.D == 64) vtr(v_transpose_kernel<64, 128>);
-        else if (s.S == 64) vtr(v_transpose_kernel<128, 64>);
-        else vtr(v_transpose_kernel<128, 128>);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_vt_prepass(s, v, vt, status, st);
         if (e != hipSuccess) return e;
     }
     if (s.D == 64 && s.S == 64) return dispatch_g<64, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);

@@ -173,6 +173,7 @@ size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs
         case HILS_WS_SCORE_QCAL: return hils::score_workspace_bytes(s, true);
         case HILS_WS_FUSED: return hils::fused_workspace_bytes(s);
         case HILS_WS_BACKWARD: return hils::backward_workspace_bytes(s);
+        case HILS_WS_DENSE: return hils::dense_workspace_bytes(s);
         case HILS_WS_DECODE:
             if (num_seqs < 0 || max_pages < 0) {
                 fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
@@ -266,6 +267,28 @@ hils_status_t hils_sparse_attend_fused(const hils_config_t *cfg, const void *q, 
     void *vt_ws = s.io_bf16 ? (char *)workspace + hils::FUSED_STATUS_BYTES : nullptr;
     return hip_status(hils::launch_sparse_attend(s, q, k, v, sel_idx, sel_score, out, lse, status, vt_ws, stream),
                       "sparse attention launch");
+}
+
+hils_status_t hils_dense_causal_attend(const hils_config_t *cfg, const void *q, const void *k, const void *v,
+                                       void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, true, s);
+    if (st) return st;
+    if (!hils::dense_attend_supported(s))
+        return fail(HILS_ERR_UNSUPPORTED, "dense attention covers bf16 I/O with d = 64 or 128 (io_dtype=%d, d=%d)",
+                    cfg->io_dtype, s.D);
+    if ((int64_t)s.B * s.N == 0) return ok();
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+        (st = check_ptr(out, "out")))
+        return st;
+    if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    const size_t need = hils::dense_workspace_bytes(s);
+    if (!workspace || workspace_bytes < need)
+        return fail(HILS_ERR_WORKSPACE, "dense_causal_attend needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(hils::launch_dense_attend(s, q, k, v, out, lse, workspace, stream), "dense attention launch");
 }
 
 hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,

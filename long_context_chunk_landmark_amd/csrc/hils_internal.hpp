@@ -91,6 +91,20 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
                                 const float *sel_score, void *out, float *lse, uint32_t *status, void *vt_ws,
                                 hipStream_t st);
 
+// Status word cleared, then v [B, H_kv, Nk, D] (or the paged cache with
+// s.bt) copied to vt as fp16 [B, H_kv, CA, D, S] with the keys of each 32-key
+// step in MFMA accumulator order; bit 1 of *status is set for a value beyond
+// fp16's range.
+hipError_t launch_vt_prepass(const Shape &s, const void *v, void *vt, uint32_t *status, hipStream_t st);
+
+// ---- dense causal attention (bf16, d = 64 or 128): the full-attention
+// point of comparison.  Workspace: the status block, then the fp16 V^T copy
+// in 64-key tiles.
+bool dense_attend_supported(const Shape &s);
+size_t dense_workspace_bytes(const Shape &s);
+hipError_t launch_dense_attend(const Shape &s, const void *q, const void *k, const void *v, void *out, float *lse,
+                               void *workspace, hipStream_t st);
+
 // ---- kernel 4: decode
 size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages);
 // Largest candidate range one phase-A block may own (LDS capacity).

@@ -299,3 +299,21 @@ def test_streaming_coverage_is_checked_before_pointers(lib):
     assert st(summary_dtype=torch.bfloat16) == hb.HILS_ERR_INVALID_ARG
     assert st(H_q=4) == hb.HILS_ERR_INVALID_ARG
     assert st(score_mode=hb.SCORE_TWO_PASS) == hb.HILS_ERR_INVALID_ARG
+
+
+def test_dense_attention_arguments_are_checked(lib):
+    """The dense causal attention entry: empty problems need no pointers,
+    the workspace is sized and checked, and fp32 I/O is refused."""
+    assert lib.hils_dense_causal_attend(ctypes.byref(_cfg(N=0)), None, None, None, None, None, None, 0,
+                                        None) == hb.HILS_OK
+    cfg = _cfg()
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DENSE, 0, 0)
+    assert need > lib.hils_workspace_size(ctypes.byref(_cfg(N=cfg.N // 2)), hb.WS_DENSE, 0, 0) > 0
+    st = lib.hils_dense_causal_attend(ctypes.byref(cfg), A, A, A, A, None, A2, need - 16, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+    st = lib.hils_dense_causal_attend(ctypes.byref(cfg), A, None, A, A, None, A2, need, None)
+    assert st == hb.HILS_ERR_INVALID_ARG
+    f32 = _cfg()
+    f32.io_dtype = hb.HILS_F32
+    assert lib.hils_dense_causal_attend(ctypes.byref(f32), A, A, A, A, None, A2, need, None) == hb.HILS_ERR_UNSUPPORTED
+    assert lib.hils_workspace_size(ctypes.byref(f32), hb.WS_DENSE, 0, 0) == 0
