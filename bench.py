@@ -4,9 +4,10 @@
 One step = one prefill pass over the 128K-token workload (landmark summary ->
 score/select -> fused sparse attention, inputs resident in HBM), timed with
 HIP events on the stream the kernels run on.  The same run times one decode
-step over the 512K-token paged-cache workload (16 sequences) and the fp64
-CPU oracle on a bounded sample of the prefill workload.  Prints one JSON
-line.
+step over the 512K-token paged-cache workload (16 sequences), the dense
+causal attention baselines of both (the full attention that the pages quote
+HiLS's speedups against), and the fp64 CPU oracle on a bounded sample of the
+prefill workload.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -198,6 +199,22 @@ def bench_decode(args, torch, hb, W):
 
     us, call_us = run(cfg, inp["ksum_cache"], inp["bsum_cache"], args.steps, args.warmup)
     seq_lens = inp["seq_lens"].cpu().tolist()
+    dense_us = None
+    if not args.no_dense:
+        # the full-attention baseline: every key of each sequence
+        wsd = torch.empty(hb.workspace_size(cfg, hb.WS_DENSE_DECODE, B, max_pages), dtype=torch.uint8, device=dev)
+
+        def dstep():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            hb.dense_decode(cfg, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"], inp["seq_lens"],
+                            out=out, lse=lse, workspace=wsd)
+            e1.record()
+            return {"dense": (e0, e1)}
+
+        _, dper = _timed(dstep, max(2, args.steps // 2), 1, torch)
+        dense_us = 1000.0 * dper["dense"]
+        del wsd
     secondary = {}
     del inp["ksum_cache"], inp["bsum_cache"]
     for name, c in (("H_lm=H_kv, bf16 k'", dataclasses.replace(cfg, H_lm=cfg.H_kv)),
@@ -207,7 +224,7 @@ def bench_decode(args, torch, hb, W):
         _, cu = run(c, ks, bs, max(2, args.steps // 2), 1)
         secondary[name] = (c, cu)
         del ks, bs
-    return dict(cfg=cfg, us_per_step=us, call_us=call_us, seq_lens=seq_lens, secondary=secondary)
+    return dict(cfg=cfg, us_per_step=us, call_us=call_us, seq_lens=seq_lens, secondary=secondary, dense_us=dense_us)
 
 
 def bench_serving(args, torch, hb, W, pre):
@@ -367,6 +384,38 @@ def bench_backward(args, torch, hb, pre):
             "tokens_per_s": cfg.B * cfg.N / (ms * 1e-3)}
 
 
+def dense_flops(cfg):
+    """Dense causal attention: 4 d FLOPs per (query head, query, visible key)."""
+    return 4.0 * cfg.d * cfg.H_q * cfg.B * (cfg.N * (cfg.N + 1) / 2)
+
+
+def bench_dense(torch, hb, pre, steps, hils_ms):
+    """hils_dense_causal_attend on the prefill workload's inputs: the
+    full-attention baseline of the pages' prefill speed comparison."""
+    dev = torch.device("cuda:0")
+    inp = pre["inp"]
+    cfg = pre["cfg"]
+    ws = torch.empty(hb.workspace_size(cfg, hb.WS_DENSE), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+    lse = torch.empty((cfg.B, cfg.H_q, cfg.N), dtype=torch.float32, device=dev)
+
+    def step():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        hb.dense_causal_attend(cfg, inp["q"], inp["k"], inp["v"], out=out, lse=lse, workspace=ws)
+        e1.record()
+        return {"dense": (e0, e1)}
+
+    _, per = _timed(step, steps, 1, torch)
+    ms = per["dense"]
+    fl = dense_flops(cfg)
+    tfl = fl / (ms * 1e-3) / 1e12
+    del ws, out, lse
+    return {"kernel": "dense_attend_kernel (hils_dense_causal_attend)", "steps": steps, "ms": ms, "bound": "mfma",
+            "tflops": tfl, "frac": tfl / PEAK_BF16_TFLOPS, "flops": fl,
+            "tokens_per_s": cfg.B * cfg.N / (ms * 1e-3), "hils_speedup": ms / hils_ms}
+
+
 def union_overlap(sel, M, sample=4096, seed=0):
     """Mean |union of the selections of M adjacent queries| / K over a sample
     of groups (1 = identical selections, M = disjoint)."""
@@ -520,6 +569,9 @@ def bench_stress(args, torch, hb, W):
                                           "flops": fl_score},
                "fused": {"ms": per["fused"], "bound": "mfma", "tflops": tfl, "frac": tfl / PEAK_BF16_TFLOPS,
                          "flops": fl_att}}}
+    if not args.no_dense:
+        print("[bench] stress: dense causal attention baseline", file=sys.stderr, flush=True)
+        out["dense"] = bench_dense(torch, hb, pre, 1, pre["ms_per_step"])
     if not args.no_cpu_baseline:
         print("[bench] stress: oracle parity sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(pre, min(args.cpu_seconds, 10.0), max_rows=256)
@@ -542,6 +594,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention baselines")
     ap.add_argument("--stress-workload", default="prefill_512k_qcal")
     ap.add_argument("--no-stress", action="store_true", help="skip the 512K Q-Cal stress prefill leg")
     ap.add_argument("--backward-steps", type=int, default=2)
@@ -604,6 +657,9 @@ def main():
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }
+    if not args.no_dense:
+        print("[bench] dense causal attention baseline", file=sys.stderr, flush=True)
+        result["dense"] = bench_dense(torch, hb, pre, max(2, args.steps // 3), pre["ms_per_step"])
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
         result["backward"] = bench_backward(args, torch, hb, pre)
@@ -627,6 +683,15 @@ def main():
                             "roofline": {"kernel": "hils_decode (all phases)", "bound": "hbm", "achieved": gbs,
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "algorithmic_bytes": by}}
+        if dec["dense_us"] is not None:
+            # K and V of every token of every sequence, the queries and the outputs
+            dby = sum(dcfg.H_kv * n * dcfg.d * dio * 2 for n in dec["seq_lens"])
+            dby += 2 * len(dec["seq_lens"]) * dcfg.H_q * dcfg.d * dio
+            dg = dby / (dec["dense_us"] * 1e-6) / 1e9
+            result["decode"]["dense"] = {"kernel": "dense_decode_kernel (hils_dense_decode)",
+                                         "us_per_call": dec["dense_us"], "bound": "hbm", "gbs": dg,
+                                         "frac": dg / PEAK_HBM_GBS, "algorithmic_bytes": dby,
+                                         "hils_speedup": dec["dense_us"] / dec["us_per_step"]}
         for name, (c2, cu) in dec["secondary"].items():
             b2 = decode_bytes(c2, dec["seq_lens"], dio, 2 if c2.summary_dtype == torch.bfloat16 else 4)
             g2 = b2 / (cu * 1e-6) / 1e9

@@ -139,7 +139,8 @@ enum {
     HILS_WS_FUSED = 2,      /* hils_sparse_attend_fused                   */
     HILS_WS_DECODE = 3,     /* hils_decode                                */
     HILS_WS_BACKWARD = 4,   /* hils_sparse_attend_backward                */
-    HILS_WS_DENSE = 5       /* hils_dense_causal_attend                   */
+    HILS_WS_DENSE = 5,      /* hils_dense_causal_attend                   */
+    HILS_WS_DENSE_DECODE = 6 /* hils_dense_decode                         */
 };
 
 /* Landmark summary (compressed keys).  For every completed chunk c and
@@ -350,6 +351,26 @@ hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *
 hils_status_t hils_dense_causal_attend(const hils_config_t *cfg, const void *q, const void *k, const void *v,
                                        void *out, float *lse, void *workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+
+/* Dense decode step, the full-attention baseline of the pages' decode speed
+ * comparison (wmrh.cn article on HiLS-Attention, results table: decode at a
+ * 512K context): the query at t = seq_lens[b] - 1 attends every key 0 .. t
+ * of its sequence in the paged cache,
+ *   out[b,h] = sum_{j<=t} softmax_j(scale q[b,h] . k_j) v_j over kv head h / G,
+ *   lse[b,h] = log sum_{j<=t} exp(scale q[b,h] . k_j).
+ *   q [num_seqs,H_q,d], k_cache, v_cache [P,H_kv,S,d], block_table
+ *   [num_seqs,max_pages], seq_lens [num_seqs]: as for hils_decode (bf16)
+ *   out [num_seqs,H_q,d] bf16 (written); lse [num_seqs,H_q] fp32 (written, may
+ *   be NULL)
+ *   workspace: hils_workspace_size(cfg, HILS_WS_DENSE_DECODE, num_seqs,
+ *   max_pages) bytes.
+ * Requires bf16 I/O, d = 128 and S = 64 (else HILS_ERR_UNSUPPORTED).  Page
+ * ids are not checked on the device; seq_lens are clamped to [1, max_pages *
+ * S].  cfg->B, N, W, K and the summary fields are ignored. */
+hils_status_t hils_dense_decode(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table, int32_t max_pages,
+                                const int32_t *seq_lens, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace the given call needs (0 if none); 0 with
  * hils_last_error() set when the configuration is rejected.  num_seqs and

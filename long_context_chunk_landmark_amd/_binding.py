@@ -23,7 +23,7 @@ HILS_F32, HILS_BF16 = 0, 1
 LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
 AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
 SCORE_AUTO, SCORE_TWO_PASS, SCORE_STREAMING = 0, 1, 2  # hils_score_mode_t
-WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD, WS_DENSE = range(6)
+WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD, WS_DENSE, WS_DENSE_DECODE = range(7)
 
 # Every symbol include/hils.h declares.
 EXPORTED_SYMBOLS = (
@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "hils_score_select",
     "hils_sparse_attend_fused",
     "hils_dense_causal_attend",
+    "hils_dense_decode",
     "hils_decode",
     "hils_decode_noalloc",
     "hils_summarize_pages",
@@ -142,13 +143,15 @@ def load_library(path: str = LIB_PATH):
     lib.hils_prefill_paged_workspace_size.restype = sz
     lib.hils_sparse_attend_backward.argtypes = [cfgp] + [vp] * 15 + [sz, vp]
     lib.hils_dense_causal_attend.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hils_dense_decode.argtypes = [cfgp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.hils_workspace_size.argtypes = [cfgp, ctypes.c_int, i32, i32]
     lib.hils_workspace_size.restype = sz
     lib.hils_last_error.restype = ctypes.c_char_p
     lib.hils_version.restype = ctypes.c_int
     for fn in ("hils_landmark_summarize", "hils_score_select", "hils_sparse_attend_fused", "hils_decode",
                "hils_decode_noalloc",
-               "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward", "hils_dense_causal_attend"):
+               "hils_summarize_pages", "hils_prefill_paged", "hils_sparse_attend_backward", "hils_dense_causal_attend",
+               "hils_dense_decode"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -312,6 +315,30 @@ def dense_causal_attend(cfg: Config, q, k, v, out=None, lse=None, workspace=None
     c = cfg.to_c()
     _check(load_library().hils_dense_causal_attend(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                                    _ptr(ws), nbytes, _stream()))
+    return out, lse
+
+
+def dense_decode(cfg: Config, q, k_cache, v_cache, block_table, seq_lens, out=None, lse=None, workspace=None,
+                 want_lse: bool = True):
+    """One dense decode step over the paged cache (every key of each sequence) -> (out, lse)."""
+    dev = q.device
+    num_seqs = q.shape[0]
+    max_pages = block_table.shape[1]
+    P = k_cache.shape[0]
+    _want(q, "q", (num_seqs, cfg.H_q, cfg.d), cfg.io_dtype, dev)
+    _want(k_cache, "k_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(v_cache, "v_cache", (P, cfg.H_kv, cfg.S, cfg.d), cfg.io_dtype, dev)
+    _want(block_table, "block_table", (num_seqs, max_pages), torch.int32, dev)
+    _want(seq_lens, "seq_lens", (num_seqs,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((num_seqs, cfg.H_q, cfg.d), dtype=cfg.io_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((num_seqs, cfg.H_q), dtype=torch.float32, device=dev)
+    ws, nbytes = _workspace(cfg, WS_DENSE_DECODE, dev, workspace, num_seqs, max_pages)
+    c = cfg.to_c()
+    _check(load_library().hils_dense_decode(ctypes.byref(c), num_seqs, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(block_table), max_pages, _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                            _ptr(ws), nbytes, _stream()))
     return out, lse
 
 

@@ -792,6 +792,202 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *__rest
     }
 }
 
+// Dense decode, the full-attention point of comparison for one decode step:
+// the query at t = seq_len - 1 attends every key 0 .. t of its sequence.
+// Grid (splits, H_kv, num_seqs) of 4-wave blocks; block x owns chunks
+// [x cps, (x + 1) cps) of its (seq, group), its waves take every fourth
+// chunk and carry one running softmax state per query head of the group
+// (base-2 max, mass, and output sums left unreduced over the lane's four
+// key rows until the end).  The block joins its four wave states into one
+// partial (max, mass, sum) per head, and decode_combine_kernel merges the
+// splits.  The per-chunk arithmetic is the fast attend path's: packed bf16
+// dot2 logits, fp16 dot2 products of p and V.
+template <int G>
+__global__ __launch_bounds__(256) void dense_decode_kernel(
+    const bf16 *__restrict__ q_raw, const bf16 *__restrict__ k_cache, const bf16 *__restrict__ v_cache,
+    const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens, float *pm,
+    float *pl, float *po, int H_q, int H_kv, int splits, int cps, float scale) {
+    constexpr int D = 128, S = 64;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    __shared__ float p_l[4][G][4][16];  // [wave][head][rsub][t]
+    __shared__ float st_m[4][G], st_l[4][G];
+    __shared__ float st_o[4][G][D];
+    const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    const int col = lane & 15, rsub = lane >> 4;
+    const int t_last = clamp_len(seq_lens[seq], max_pages, S) - 1;
+    const int c0 = split * cps, c1 = min(t_last / S + 1, c0 + cps);
+    const int64_t hrow0 = (int64_t)seq * H_q + g * G;  // first query head of the group
+    const float sl2 = scale * LOG2E;
+    const int j = 4 * col + rsub;  // key of this lane after the transpose-reduce
+
+    u32x4 qr[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) qr[e] = *(const u32x4 *)(q_raw + (hrow0 + e) * D + col * 8);
+    float m[G], l[G], oacc[G][8];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+        m[e] = -INFINITY;
+        l[e] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) oacc[e][d] = 0.f;
+    }
+    float (*pw)[4][16] = p_l[wave];
+    for (int c = c0 + wave; c < c1; c += 4) {
+        const int64_t page = block_table[(int64_t)seq * max_pages + c];
+        const bf16 *kp = k_cache + (page * H_kv + g) * (int64_t)S * D + col * 8;
+        const bf16 *vp = v_cache + (page * H_kv + g) * (int64_t)S * D + col * 8;
+        u32x4 kx[16], vx[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) kx[t] = *(const u32x4 *)(kp + (t * 4 + rsub) * D);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) vx[t] = *(const u32x4 *)(vp + (t * 4 + rsub) * D);
+        const bool masked = c * S + j > t_last;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            float part[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float acc = 0.f;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t qa = qr[e][x], kb2 = kx[t][x];
+                    bf16x2 a2, b2;
+                    __builtin_memcpy(&a2, &qa, 4);
+                    __builtin_memcpy(&b2, &kb2, 4);
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, acc, false);
+                }
+                part[t] = acc;
+            }
+            // the cross-lane reduction runs on every lane; masking comes after
+            const float tr = transpose_sum16(part, col);
+            const float lg = masked ? -INFINITY : tr * sl2;
+            // key c S is visible, so the chunk's maximum is finite
+            const float mnew = fmaxf(m[e], wave_max_f(lg));
+            const float alpha = exp2_hw(m[e] - mnew);
+            const float ex = exp2_hw(lg - mnew);
+            l[e] = fmaf(l[e], alpha, wave_sum_f(ex));
+            m[e] = mnew;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) oacc[e][d] *= alpha;
+            pw[e][rsub][col] = ex;
+        }
+        wave_sync();
+        // V as fp16 pairs of consecutive rows: vh[tp][d] = (v[2tp][d], v[2tp+1][d])
+        f16x2 vh[8][8];
+#pragma unroll
+        for (int tp = 0; tp < 8; ++tp)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t a = vx[2 * tp][x], b = vx[2 * tp + 1][x];
+                vh[tp][2 * x] = f16x2{(_Float16)__uint_as_float(a << 16), (_Float16)__uint_as_float(b << 16)};
+                vh[tp][2 * x + 1] =
+                    f16x2{(_Float16)__uint_as_float(a & 0xffff0000u), (_Float16)__uint_as_float(b & 0xffff0000u)};
+            }
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            f16x2 bp[8];
+#pragma unroll
+            for (int t0 = 0; t0 < 16; t0 += 4) {
+                const f32x4 p4 = *(const f32x4 *)&pw[e][rsub][t0];
+                bp[t0 / 2] = f16x2{(_Float16)p4[0], (_Float16)p4[1]};
+                bp[t0 / 2 + 1] = f16x2{(_Float16)p4[2], (_Float16)p4[3]};
+            }
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+#pragma unroll
+                for (int tp = 0; tp < 8; ++tp) oacc[e][d] = __builtin_amdgcn_fdot2(vh[tp][d], bp[tp], oacc[e][d], false);
+        }
+        wave_sync();  // the next chunk's p overwrites this one's
+    }
+    // the wave's state: lane (col, 0) holds dims 8 col .. +7 of each head
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const float o = rows4_sum(oacc[e][d]);
+            if (rsub == 0) st_o[wave][e][col * 8 + d] = o;
+        }
+        if (lane == 0) {
+            st_m[wave][e] = m[e];
+            st_l[wave][e] = l[e];
+        }
+    }
+    __syncthreads();
+    // join the four wave states: thread (e, dim) pairs, base-2 maxima
+    for (int x = threadIdx.x; x < G * D; x += 256) {
+        const int e = x / D, dim = x % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, st_m[w][e]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float a = st_m[w][e] == -INFINITY ? 0.f : exp2_hw(st_m[w][e] - M);
+                L = fmaf(st_l[w][e], a, L);
+                O = fmaf(st_o[w][e][dim], a, O);
+            }
+        }
+        const int64_t hb = (hrow0 + e) * splits + split;
+        po[hb * D + dim] = O;
+        if (dim == 0) {
+            pm[hb] = M == -INFINITY ? -INFINITY : M * LN2;
+            pl[hb] = L;
+        }
+    }
+}
+
+// Splits of the dense decode: about 8192 blocks in all, at least 4 chunks each.
+static void dense_decode_split(int num_seqs, int H_kv, int max_pages, int &splits, int &cps) {
+    const int units = std::max(1, num_seqs * H_kv);
+    splits = std::max(1, std::min((max_pages + 3) / 4, (8192 + units - 1) / units));
+    cps = (max_pages + splits - 1) / splits;
+    splits = (max_pages + cps - 1) / cps;
+}
+
+size_t dense_decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages) {
+    if (!dense_decode_supported(s)) return 0;
+    int splits, cps;
+    dense_decode_split(num_seqs, s.H_kv, max_pages, splits, cps);
+    const size_t rows = (size_t)num_seqs * s.H_q * splits;
+    return align_up(rows * 4, 256) * 2 + align_up(rows * s.D * 4, 256);
+}
+
+bool dense_decode_supported(const Shape &s) {
+    return s.io_bf16 && s.D == 128 && s.S == 64 && (s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8);
+}
+
+hipError_t launch_dense_decode(const Shape &s, int num_seqs, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table, int max_pages,
+                               const int32_t *seq_lens, void *out, float *lse, void *workspace, hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    int splits, cps;
+    dense_decode_split(num_seqs, s.H_kv, max_pages, splits, cps);
+    const size_t rows = (size_t)num_seqs * s.H_q * splits;
+    char *ws = (char *)workspace;
+    float *pm = (float *)ws, *pl = (float *)(ws + align_up(rows * 4, 256));
+    float *po = (float *)(ws + 2 * align_up(rows * 4, 256));
+    const dim3 grid((unsigned)splits, (unsigned)s.H_kv, (unsigned)num_seqs);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const bf16 *)q, (const bf16 *)k_cache,
+                           (const bf16 *)v_cache, block_table, max_pages, seq_lens, pm, pl, po, s.H_q, s.H_kv, splits,
+                           cps, s.scale);
+    };
+    switch (s.G) {
+        case 1: go(dense_decode_kernel<1>); break;
+        case 2: go(dense_decode_kernel<2>); break;
+        case 4: go(dense_decode_kernel<4>); break;
+        case 8: go(dense_decode_kernel<8>); break;
+        default: return hipErrorInvalidValue;
+    }
+    const int64_t hrows = (int64_t)num_seqs * s.H_q;
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, 128>), dim3((unsigned)((hrows + 3) / 4)), dim3(256), 0, st, pm, pl,
+                       po, (bf16 *)out, lse, hrows, splits);
+    return hipGetLastError();
+}
+
 size_t decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages) {
     return decode_layout(s, num_seqs, max_pages).total;
 }

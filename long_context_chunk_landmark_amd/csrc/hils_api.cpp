@@ -166,7 +166,7 @@ int hils_version(void) { return 10100; }
 
 size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs, int32_t max_pages) {
     hils::Shape s;
-    const bool seq = which != HILS_WS_DECODE;
+    const bool seq = which != HILS_WS_DECODE && which != HILS_WS_DENSE_DECODE;
     if (resolve(cfg, seq, s) != HILS_OK) return 0;
     switch (which) {
         case HILS_WS_SCORE: return hils::score_workspace_bytes(s, false);
@@ -174,6 +174,12 @@ size_t hils_workspace_size(const hils_config_t *cfg, int which, int32_t num_seqs
         case HILS_WS_FUSED: return hils::fused_workspace_bytes(s);
         case HILS_WS_BACKWARD: return hils::backward_workspace_bytes(s);
         case HILS_WS_DENSE: return hils::dense_workspace_bytes(s);
+        case HILS_WS_DENSE_DECODE:
+            if (num_seqs < 0 || max_pages < 1) {
+                fail(HILS_ERR_INVALID_ARG, "num_seqs must be >= 0 and max_pages >= 1");
+                return 0;
+            }
+            return hils::dense_decode_workspace_bytes(s, num_seqs, max_pages);
         case HILS_WS_DECODE:
             if (num_seqs < 0 || max_pages < 0) {
                 fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
@@ -324,6 +330,35 @@ hils_status_t hils_decode(const hils_config_t *cfg, int32_t num_seqs, const void
                                           max_pages, seq_lens, 0, h, w_down, w_up, d_model, r, out, lse, sel_idx,
                                           workspace, stream),
                       "decode launch");
+}
+
+hils_status_t hils_dense_decode(const hils_config_t *cfg, int32_t num_seqs, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_table, int32_t max_pages,
+                                const int32_t *seq_lens, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    hils::Shape s;
+    hils_status_t st = resolve(cfg, false, s);
+    if (st) return st;
+    if (!hils::dense_decode_supported(s))
+        return fail(HILS_ERR_UNSUPPORTED, "dense decode covers bf16 I/O with d = 128 and S = 64 (io_dtype=%d, d=%d, S=%d)",
+                    cfg->io_dtype, s.D, s.S);
+    if (num_seqs < 0 || max_pages < 0) return fail(HILS_ERR_INVALID_ARG, "num_seqs, max_pages must be >= 0");
+    if (num_seqs == 0) return ok();
+    if (max_pages == 0) return fail(HILS_ERR_INVALID_ARG, "max_pages must be >= 1");
+    if (num_seqs > 65535) return fail(HILS_ERR_UNSUPPORTED, "num_seqs=%d: supported up to 65535", num_seqs);
+    if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
+        (st = check_ptr(block_table, "block_table")) || (st = check_ptr(seq_lens, "seq_lens")) ||
+        (st = check_ptr(out, "out")))
+        return st;
+    if (lse && !aligned16(lse)) return fail(HILS_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+    const size_t need = hils::dense_decode_workspace_bytes(s, num_seqs, max_pages);
+    if (!workspace || workspace_bytes < need)
+        return fail(HILS_ERR_WORKSPACE, "dense decode needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    return hip_status(hils::launch_dense_decode(s, num_seqs, q, k_cache, v_cache, block_table, max_pages, seq_lens,
+                                                out, lse, workspace, stream),
+                      "dense decode launch");
 }
 
 hils_status_t hils_sparse_attend_backward(const hils_config_t *cfg, const void *q, const void *k, const void *v,

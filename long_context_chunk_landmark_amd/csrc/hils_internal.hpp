@@ -116,6 +116,15 @@ hipError_t launch_decode(const Shape &s, int num_seqs, const void *q, const void
                          const void *w_up, int d_model, int r, void *out, float *lse, int32_t *sel_idx,
                          void *workspace, hipStream_t st);
 
+// Dense decode (bf16, d = 128, S = 64 pages): the query at seq_len - 1 over
+// every key of its sequence; the full-attention point of comparison for a
+// decode step.  Workspace: per-split partial states.
+bool dense_decode_supported(const Shape &s);
+size_t dense_decode_workspace_bytes(const Shape &s, int num_seqs, int max_pages);
+hipError_t launch_dense_decode(const Shape &s, int num_seqs, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table, int max_pages,
+                               const int32_t *seq_lens, void *out, float *lse, void *workspace, hipStream_t st);
+
 // ---- backward of the fused attention (fixed selection), incl. the summary
 size_t backward_workspace_bytes(const Shape &s);
 hipError_t launch_backward(const Shape &s, const void *q, const void *k, const void *v, const void *q_lm,

@@ -317,3 +317,18 @@ def test_dense_attention_arguments_are_checked(lib):
     f32.io_dtype = hb.HILS_F32
     assert lib.hils_dense_causal_attend(ctypes.byref(f32), A, A, A, A, None, A2, need, None) == hb.HILS_ERR_UNSUPPORTED
     assert lib.hils_workspace_size(ctypes.byref(f32), hb.WS_DENSE, 0, 0) == 0
+
+
+def test_dense_decode_arguments_are_checked(lib):
+    cfg = _cfg()
+    assert lib.hils_dense_decode(ctypes.byref(cfg), 0, None, None, None, None, 1, None, None, None, None, 0,
+                                 None) == hb.HILS_OK
+    need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DENSE_DECODE, 4, 100)
+    assert need > lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_DENSE_DECODE, 2, 100) > 0
+    st = lib.hils_dense_decode(ctypes.byref(cfg), 4, A, A, A, A, 100, A, A, None, A2, need - 1, None)
+    assert st == hb.HILS_ERR_WORKSPACE
+    st = lib.hils_dense_decode(ctypes.byref(cfg), 4, A, A, A, A, 0, A, A, None, A2, need, None)
+    assert st == hb.HILS_ERR_INVALID_ARG
+    s128 = _cfg(S=128, W=128)
+    assert lib.hils_dense_decode(ctypes.byref(s128), 4, A, A, A, A, 100, A, A, None, A2, need,
+                                 None) == hb.HILS_ERR_UNSUPPORTED
