@@ -67,6 +67,13 @@ __device__ __forceinline__ int dswz(int row) {
 // keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void dense_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+#ifndef DENSE_NSTAGE
+#define DENSE_NSTAGE 4  // ring stages (tiles in flight + the one in use)
+#endif
+#ifndef DENSE_LA
+#define DENSE_LA 4  // LDS fragment reads issued ahead of their MFMAs
+#endif
+
 template <int D, int G>
 struct DenseCfg {
     static constexpr int KB = 64;                     // keys per tile (one V^T pre-pass chunk)
@@ -77,7 +84,7 @@ struct DenseCfg {
     static constexpr int NBK = D / 8, NBV = KB / 8;   // 16-byte blocks per K row, per V^T row
     static constexpr int PK = KB * D * 2 / 1024, PV = D * KB * 2 / 1024, NP = PK + PV;  // 1 KB pieces
     static constexpr int PPW = NP / NWAVE;            // pieces per wave per tile
-    static constexpr int NSTAGE = 4;
+    static constexpr int NSTAGE = DENSE_NSTAGE;
     static_assert(QB % 32 == 0 && NP % NWAVE == 0, "block shape");
 };
 
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(512) void dense_attend_kernel(const bf16 *__restric
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) acc[t][kt] = mfma16(a, qf[t][s], acc[t][kt]);
             }
-        pipeline(std::integral_constant<int, KS * KT>{}, std::integral_constant<int, 4>{});
+        pipeline(std::integral_constant<int, KS * KT>{}, std::integral_constant<int, DENSE_LA>{});
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(512) void dense_attend_kernel(const bf16 *__restric
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) O[t][dt] = mfma16h(a, bp[t][ps], O[t][dt]);
             }
-        pipeline(std::integral_constant<int, PS * DT>{}, std::integral_constant<int, 4>{});
+        pipeline(std::integral_constant<int, PS * DT>{}, std::integral_constant<int, DENSE_LA>{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -279,7 +286,9 @@ __global__ __launch_bounds__(512) void dense_attend_kernel(const bf16 *__restric
         // this wave's pieces of tile it have landed once at most the later
         // tiles' pieces are outstanding
         const int later = min(NSTAGE - 2, T - 1 - it);
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(dense_vmcnt(2 * PPW));
+        static_assert(NSTAGE <= 5, "the waits below cover up to 3 later tiles");
+        if (later >= 3) __builtin_amdgcn_s_waitcnt(dense_vmcnt(3 * PPW));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(dense_vmcnt(2 * PPW));
         else if (later == 1) __builtin_amdgcn_s_waitcnt(dense_vmcnt(PPW));
         else __builtin_amdgcn_s_waitcnt(dense_vmcnt(0));
         // every wave's pieces of tile it are in; every wave is done with tile
