@@ -116,7 +116,29 @@ typedef struct {
     int32_t score_mode;    /* hils_score_mode_t: how hils_score_select (and the
                               paged prefill) ranks the candidates; 0 (auto) by
                               default */
+    int32_t attend_mode;   /* hils_attend_mode_t: how hils_sparse_attend_fused
+                              visits the selected chunks; 0 (auto) by default */
+    int32_t attend_slab;   /* chunk-major form: query rows per slab, rounded up to
+                              a multiple of S; 0 bounds the slab's partial buffer
+                              by 16 GiB.  Results do not depend on it. */
 } hils_config_t;
+
+/* Forms of the selected-chunk attention of hils_sparse_attend_fused (bf16
+ * I/O; same definition, outputs equal up to fp32 rounding order and the fp16
+ * rounding of each chunk's weighted output).  WALK: a block of adjacent
+ * queries stages the union of their selected chunks once and walks it, then
+ * the window.  CHUNK_MAJOR: the selections are inverted into per-chunk lists
+ * of (query, slot); each chunk is staged once per list segment for every
+ * query that selected it, its weighted output exp(s^_c - m^) o_c goes to an
+ * fp16 partial buffer, and the window pass starts each row from the sum of
+ * its partials; it pays when adjacent queries select different chunks.
+ * Workspace grows by about B * H_q * min(N, slab) * K * d * 2 bytes.  The
+ * paged prefill always walks.  AUTO takes the walk. */
+typedef enum {
+    HILS_ATTEND_AUTO = 0,
+    HILS_ATTEND_WALK = 1,
+    HILS_ATTEND_CHUNK_MAJOR = 2
+} hils_attend_mode_t;
 
 /* Score-and-select forms (same selection, same scores up to fp32 rounding
  * order).  TWO_PASS writes approximate scores of every candidate (a ragged

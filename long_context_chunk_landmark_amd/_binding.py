@@ -23,6 +23,7 @@ HILS_F32, HILS_BF16 = 0, 1
 LM_CHUNK, LM_SHARED, LM_MEAN = 0, 1, 2   # hils_landmark_mode_t
 AGG_MAX, AGG_NORMALIZED = 0, 1           # hils_agg_mode_t
 SCORE_AUTO, SCORE_TWO_PASS, SCORE_STREAMING = 0, 1, 2  # hils_score_mode_t
+ATTEND_AUTO, ATTEND_WALK, ATTEND_CHUNK_MAJOR = 0, 1, 2  # hils_attend_mode_t
 WS_SCORE, WS_SCORE_QCAL, WS_FUSED, WS_DECODE, WS_BACKWARD, WS_DENSE, WS_DENSE_DECODE = range(7)
 
 # Every symbol include/hils.h declares.
@@ -54,7 +55,8 @@ class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "N", "H_q", "H_kv", "H_lm", "d", "S", "W", "K", "M", "io_dtype", "summary_dtype")] + [
                    ("scale", ctypes.c_float), ("landmark_mode", ctypes.c_int32), ("agg_mode", ctypes.c_int32),
-                   ("wait_spins", ctypes.c_int32), ("score_mode", ctypes.c_int32)]
+                   ("wait_spins", ctypes.c_int32), ("score_mode", ctypes.c_int32),
+                   ("attend_mode", ctypes.c_int32), ("attend_slab", ctypes.c_int32)]
 
 
 @dataclasses.dataclass
@@ -77,6 +79,8 @@ class Config:
     agg_mode: int = AGG_MAX
     wait_spins: int = 0
     score_mode: int = 0
+    attend_mode: int = 0
+    attend_slab: int = 0
 
     def __post_init__(self):
         if self.H_lm is None:
@@ -100,7 +104,8 @@ class Config:
 
         return _CConfig(self.B, self.N, self.H_q, self.H_kv, self.H_lm, self.d, self.S, self.W, self.K, self.M,
                         code(self.io_dtype), code(self.summary_dtype), float(self.scale), int(self.landmark_mode),
-                        int(self.agg_mode), int(self.wait_spins), int(self.score_mode))
+                        int(self.agg_mode), int(self.wait_spins), int(self.score_mode), int(self.attend_mode),
+                        int(self.attend_slab))
 
     def oracle_dict(self) -> dict:
         return dict(B=self.B, N=self.N, H_q=self.H_q, H_kv=self.H_kv, H_lm=self.H_lm, d=self.d, S=self.S, W=self.W,

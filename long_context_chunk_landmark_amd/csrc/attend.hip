@@ -171,13 +171,17 @@ struct AttendCfg {
 // scan[16].  Selections live in LDS so that reading a
 // row's next selection never waits on the vector-memory counter that
 // tracks the chunk DMA.
-template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE>
+// CM (chunk-major variant): the selected chunks were computed by
+// cm_attend_kernel into weighted fp16 partials part[B, H_q, NS, K, D] (lane
+// order [grp][dt][i] within a row); the block starts each row from their sum
+// and walks the window only.  Rows are the slab s0 = qb0 * QB .. s0 + NS - 1.
+template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE, bool CM>
 __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ sel_idx, const float *__restrict__ sel_score, bf16 *__restrict__ out,
     float *__restrict__ lse, int N, int H_q, int H_kv, int CA, int W, int K, float scale_log2, int NW, int UCAP,
     int nqb, int64_t n_items, int64_t per_xcd, int q0, int Nk, const int32_t *__restrict__ bt, int max_pages,
-    int wait_spins, uint32_t *__restrict__ status) {
+    int wait_spins, uint32_t *__restrict__ status, const f16 *__restrict__ part, int qb0, int NS) {
     using Cf = AttendCfg<D, S, G, TPW, NWAVE, NSTAGE>;
     constexpr int QPT = Cf::QPT, QB = Cf::QB, KS = Cf::KS, KT = Cf::KT, PS = Cf::PS, DT = Cf::DT;
     constexpr int NBK = Cf::NBK, NBV = Cf::NBV, PK = Cf::PK, NP = Cf::NP;
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     // consecutive (b, g, query block) items
     const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (item >= n_items) return;
-    const int qb = (int)(item % nqb);
+    const int qb = qb0 + (int)(item % nqb);
     const int64_t bg = item / nqb;
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
@@ -220,7 +224,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         rel[tid] = 0;
         flag[tid] = -1;
     }
-    for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
+    if constexpr (!CM)
+        for (int t = tid; t < NW; t += NT) bitmap[t] = 0u;
     for (int t = tid; t < QB * K; t += NT) {
         const int iq = i0 + t / K;
         const int c = iq < N ? sel_idx[(bg * N + iq) * K + t % K] : -1;
@@ -231,10 +236,11 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         sc_tmp[t] = iq < N ? sel_score[((b * H_q + g * G + e) * N + iq) * K + rem % K] * LOG2E : -INFINITY;
     }
     __syncthreads();
-    for (int t = tid; t < QB * K; t += NT) {
-        const int c = sel_l[t];
-        if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
-    }
+    if constexpr (!CM)
+        for (int t = tid; t < QB * K; t += NT) {
+            const int c = sel_l[t];
+            if (c >= 0 && c < n) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+        }
 
     // per-tile row state; rows convert their scores to fp16 weights
     bf16x8 qf[TPW][KS];
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         for (int kk = 0; kk < K; ++kk) {
             const float wv = sl[kk] >= 0 ? exp2f(sc[kk] - mh) : 0.f;
             z += wv;
-            if (grp == 0) wt_l[(m * G + e) * K + kk] = (f16)wv;
+            if (!CM && grp == 0) wt_l[(m * G + e) * K + kk] = (f16)wv;
         }
         mrun[t] = mh;
         lrun[t] = z;
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
 
     // ---- ascending union: exclusive prefix sum of per-word popcounts
     int U = 0;
-    {
+    if constexpr (!CM) {
         int base = 0;
         for (int w0 = 0; w0 < NW; w0 += NT) {
             const int wi = w0 + tid;
@@ -453,6 +459,31 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     // exact, so every wave still reaches the end).
     bool expired = false;
     for (int j = wave; j < NSTAGE && j < T; j += NWAVE) issue(j);
+    if constexpr (CM) {
+        // the selected chunks' weighted outputs, summed in slot order while
+        // the first window chunks land
+        constexpr int NV = D / 32;  // 16-byte pieces of a lane's D/4 dims
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int m = qrow[t], iq = i0 + m;
+            if (iq >= N) continue;
+            const int16_t *sl = sel_l + m * K;
+            const f16 *pr = part + ((b * H_q + hrow[t]) * (int64_t)NS + (iq - qb0 * QB)) * K * D + grp * (D / 4);
+            for (int kk = 0; kk < nsel[t]; ++kk) {
+                if (sl[kk] >= n) continue;
+                f16x8 y[NV];
+#pragma unroll
+                for (int j = 0; j < NV; ++j) y[j] = *(const f16x8 *)(pr + (int64_t)kk * D + 8 * j);
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        O[t][2 * j][i] += (float)y[j][i];
+                        O[t][2 * j + 1][i] += (float)y[j][4 + i];
+                    }
+            }
+        }
+    }
     for (int it = 0; it < T; ++it) {
         const int buf = it % NSTAGE;
         const int c = chunk_of(it);
@@ -759,12 +790,13 @@ __global__ __launch_bounds__(256) void sparse_attend_f32_kernel(const float *__r
 
 size_t fused_workspace_bytes(const Shape &s) {
     if (!s.io_bf16) return 0;
-    return FUSED_STATUS_BYTES + align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
+    const size_t base = FUSED_STATUS_BYTES + align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
+    return attend_use_cm(s) ? base + cm_workspace_bytes(s) : base;
 }
 
 // Block shapes: NWAVE waves of one 16-row tile each (QB = NWAVE * 16/G
 // queries, dividing S).  16 waves leave 128 registers per wave, enough for
-// 64-key chunks at d = 128 only.  The ring holds 3 chunks when a chunk is
+// 64-key chunks at d = 128 only.  The ring holds 4 chunks when a chunk is
 // 32 KB, else 2.
 template <int D, int S, int G, int NWAVE, int TPW_ = 1>
 struct AttendPlan {
@@ -779,106 +811,152 @@ struct AttendPlan {
 
 constexpr size_t LDS_BYTES = 160 * 1024;
 
+// The chunk-major variant's extra arguments (part == null: the walk).
+struct WinArgs {
+    const f16 *part;
+    int s0, NS;
+};
+
+// Bitmap words and union capacity of a block's walk (none in the
+// chunk-major variant: it walks the window only).
+template <int QB>
+static void walk_sizes(const Shape &s, bool cm, int &NW, int &UCAP) {
+    NW = cm ? 0 : (s.C + 31) / 32 + 1;
+    UCAP = cm ? 0 : std::min(s.C + 1, QB * s.K + 1);
+}
+
 template <int D, int S, int G, int NWAVE, int TPW>
-static size_t attend_dyn_lds(const Shape &s) {
+static size_t attend_dyn_lds(const Shape &s, bool cm) {
     constexpr int QB = AttendPlan<D, S, G, NWAVE, TPW>::QB;
-    const int NW = (s.C + 31) / 32 + 1;
-    const int UCAP = std::min(s.C + 1, QB * s.K + 1);
+    int NW, UCAP;
+    walk_sizes<QB>(s, cm, NW, UCAP);
     return align_up((size_t)QB * s.K * 2 + (size_t)QB * G * s.K * 2, 16) + (size_t)NW * 4 +
            (size_t)(UCAP + s.W / s.S + 1) * 4 + 16 * 4;
 }
 
-template <int D, int S, int G, int NWAVE, int TPW>
+template <int D, int S, int G, int NWAVE, int TPW, bool CM>
 static hipError_t go_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                            const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
+                            const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
+                            hipStream_t st) {
     using P = AttendPlan<D, S, G, NWAVE, TPW>;
     const int QB = P::QB;
-    const int NW = (s.C + 31) / 32 + 1;
-    const int UCAP = std::min(s.C + 1, QB * s.K + 1);  // union size bound
-    const size_t dyn = attend_dyn_lds<D, S, G, NWAVE, TPW>(s);
-    const int nqb = (s.N + QB - 1) / QB;
+    int NW, UCAP;
+    walk_sizes<P::QB>(s, CM, NW, UCAP);
+    const size_t dyn = attend_dyn_lds<D, S, G, NWAVE, TPW>(s, CM);
+    // query blocks of the rows s0 .. s0 + rows - 1 (s0 % S == 0, QB | S)
+    const int rows = CM ? std::min(wa.NS, s.N - wa.s0) : s.N;
+    const int qb0 = CM ? wa.s0 / QB : 0;
+    const int nqb = (rows + QB - 1) / QB;
     const int64_t n_items = (int64_t)s.B * s.H_kv * nqb;
     const int64_t per_xcd = (n_items + 7) / 8;
     const dim3 grid((unsigned)(8 * per_xcd)), block(NWAVE * 64);
-    auto kern = sparse_attend_kernel<D, S, G, TPW, NWAVE, P::NSTAGE>;
+    auto kern = sparse_attend_kernel<D, S, G, TPW, NWAVE, P::NSTAGE, CM>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, block, dyn, st, (const bf16 *)q, (const bf16 *)k, (const f16 *)vt, sel_idx,
                        sel_score, (bf16 *)out, lse, s.N, s.H_q, s.H_kv, s.CA, s.W, s.K, s.scale * LOG2E, NW, UCAP,
-                       nqb, n_items, per_xcd, s.q0, s.Nk, s.bt, s.max_pages, s.wait_spins, status);
+                       nqb, n_items, per_xcd, s.q0, s.Nk, s.bt, s.max_pages, s.wait_spins, status, wa.part, qb0,
+                       wa.NS);
     return hipGetLastError();
 }
 
 template <int D, int S, int G, int NWAVE, int TPW>
-static bool fits(const Shape &s) {
+static bool fits(const Shape &s, bool cm) {
     using P = AttendPlan<D, S, G, NWAVE, TPW>;
     if constexpr (!P::valid) return false;
     else
-        return P::static_lds + attend_dyn_lds<D, S, G, NWAVE, TPW>(s) <= LDS_BYTES &&
+        return P::static_lds + attend_dyn_lds<D, S, G, NWAVE, TPW>(s, cm) <= LDS_BYTES &&
                (size_t)P::QB * G * s.K * 4 <= P::ring_bytes;  // setup staging of the scores
 }
 
 // Largest block whose LDS (chunk ring + selections + union) fits.
-template <int D, int S, int G, int NWAVE, int TPW>
+template <int D, int S, int G, int NWAVE, int TPW, bool CM>
 static bool try_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                       const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st,
-                       hipError_t &err) {
+                       const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
+                       hipStream_t st, hipError_t &err) {
     if constexpr (!AttendPlan<D, S, G, NWAVE, TPW>::valid) {
         return false;
     } else {
-        if (!fits<D, S, G, NWAVE, TPW>(s)) return false;
-        err = go_attend<D, S, G, NWAVE, TPW>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+        if (!fits<D, S, G, NWAVE, TPW>(s, CM)) return false;
+        err = go_attend<D, S, G, NWAVE, TPW, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
         return true;
     }
 }
 
-template <int D, int S, int G>
+template <int D, int S, int G, bool CM>
 static hipError_t dispatch_w(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                             const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
+                             const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
+                             hipStream_t st) {
     hipError_t err = hipErrorInvalidValue;
-    if (try_attend<D, S, G, 16, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
-    if (try_attend<D, S, G, 8, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
-    if (try_attend<D, S, G, 4, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
-    if (try_attend<D, S, G, 2, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st, err)) return err;
+    if (try_attend<D, S, G, 16, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
+    if (try_attend<D, S, G, 8, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
+    if (try_attend<D, S, G, 4, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
+    if (try_attend<D, S, G, 2, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
     return hipErrorInvalidValue;
 }
 
 template <int D, int S, int G>
-static bool fits_any(const Shape &s) {
-    return fits<D, S, G, 16, 1>(s) || fits<D, S, G, 8, 1>(s) || fits<D, S, G, 4, 1>(s) ||
-           fits<D, S, G, 2, 1>(s);
+static bool fits_any(const Shape &s, bool cm) {
+    return fits<D, S, G, 16, 1>(s, cm) || fits<D, S, G, 8, 1>(s, cm) || fits<D, S, G, 4, 1>(s, cm) ||
+           fits<D, S, G, 2, 1>(s, cm);
 }
 
 template <int D, int S>
-static bool fits_g(const Shape &s) {
+static bool fits_g(const Shape &s, bool cm) {
     switch (s.G) {
-        case 1: return fits_any<D, S, 1>(s);
-        case 2: return fits_any<D, S, 2>(s);
-        case 4: return fits_any<D, S, 4>(s);
-        case 8: return fits_any<D, S, 8>(s);
+        case 1: return fits_any<D, S, 1>(s, cm);
+        case 2: return fits_any<D, S, 2>(s, cm);
+        case 4: return fits_any<D, S, 4>(s, cm);
+        case 8: return fits_any<D, S, 8>(s, cm);
         default: return false;
     }
 }
 
-bool sparse_attend_supported(const Shape &s) {
-    if (!s.io_bf16) return true;
-    if (s.D == 64 && s.S == 64) return fits_g<64, 64>(s);
-    if (s.D == 64 && s.S == 128) return fits_g<64, 128>(s);
-    if (s.D == 128 && s.S == 64) return fits_g<128, 64>(s);
-    if (s.D == 128 && s.S == 128) return fits_g<128, 128>(s);
+static bool fits_shape(const Shape &s, bool cm) {
+    if (s.D == 64 && s.S == 64) return fits_g<64, 64>(s, cm);
+    if (s.D == 64 && s.S == 128) return fits_g<64, 128>(s, cm);
+    if (s.D == 128 && s.S == 64) return fits_g<128, 64>(s, cm);
+    if (s.D == 128 && s.S == 128) return fits_g<128, 128>(s, cm);
     return false;
 }
 
-template <int D, int S>
+bool window_after_cm_supported(const Shape &s) { return s.io_bf16 && fits_shape(s, true); }
+
+bool sparse_attend_supported(const Shape &s) {
+    if (!s.io_bf16) return true;
+    return attend_use_cm(s) || fits_shape(s, false);
+}
+
+template <int D, int S, bool CM>
 static hipError_t dispatch_g(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
-                             const float *sel_score, void *out, float *lse, uint32_t *status, hipStream_t st) {
+                             const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
+                             hipStream_t st) {
     switch (s.G) {
-        case 1: return dispatch_w<D, S, 1>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-        case 2: return dispatch_w<D, S, 2>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-        case 4: return dispatch_w<D, S, 4>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-        case 8: return dispatch_w<D, S, 8>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
+        case 1: return dispatch_w<D, S, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+        case 2: return dispatch_w<D, S, 2, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+        case 4: return dispatch_w<D, S, 4, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+        case 8: return dispatch_w<D, S, 8, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <bool CM>
+static hipError_t dispatch_shape(const Shape &s, const void *q, const void *k, const void *vt,
+                                 const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                 uint32_t *status, const WinArgs &wa, hipStream_t st) {
+    if (s.D == 64 && s.S == 64) return dispatch_g<64, 64, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+    if (s.D == 64 && s.S == 128) return dispatch_g<64, 128, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+    if (s.D == 128 && s.S == 64) return dispatch_g<128, 64, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+    if (s.D == 128 && s.S == 128)
+        return dispatch_g<128, 128, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_window_after_cm(const Shape &s, const void *q, const void *k, const void *vt,
+                                  const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                  uint32_t *status, const void *part, int s0, int NS, hipStream_t st) {
+    const WinArgs wa{(const f16 *)part, s0, NS};
+    return dispatch_shape<true>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
 }
 
 hipError_t launch_vt_prepass(const Shape &s, const void *v, void *vt, uint32_t *status, hipStream_t st) {
@@ -914,15 +992,16 @@ hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, co
         return hipGetLastError();
     }
     f16 *vt = (f16 *)vt_ws;
+    if (attend_use_cm(s)) {
+        char *cm_ws = (char *)vt_ws + align_up((size_t)s.B * s.H_kv * s.CA * s.D * s.S * 2, 256);
+        return launch_sparse_attend_cm(s, q, k, v, sel_idx, sel_score, out, lse, status, vt_ws, cm_ws, st);
+    }
     {
         const hipError_t e = launch_vt_prepass(s, v, vt, status, st);
         if (e != hipSuccess) return e;
     }
-    if (s.D == 64 && s.S == 64) return dispatch_g<64, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-    if (s.D == 64 && s.S == 128) return dispatch_g<64, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-    if (s.D == 128 && s.S == 64) return dispatch_g<128, 64>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-    if (s.D == 128 && s.S == 128) return dispatch_g<128, 128>(s, q, k, vt, sel_idx, sel_score, out, lse, status, st);
-    return hipErrorInvalidValue;
+    const WinArgs wa{nullptr, 0, s.N};
+    return dispatch_shape<false>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st);
 }
 
 }  // namespace hils

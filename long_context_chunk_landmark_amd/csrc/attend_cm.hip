@@ -1,0 +1,480 @@
+// attend_cm.hip -- chunk-major form of the selected-chunk part of kernel 3.
+//
+// hyper.ai HiLS summary, section 方法 (partition estimate and hierarchical
+// factorisation): every selected chunk c of a query contributes its own
+// exact softmax output o_c, weighted by exp(s^_c) / Z^.  The contributions
+// of different chunks never interact before that weighted sum, so they can
+// be computed in any order.
+//
+// The query-major walk (attend.hip) reuses a staged chunk only across the
+// queries of one block.  When selections scatter (i.i.d. inputs select
+// nearly disjoint chunks even for adjacent queries), a staged 32-64 KB chunk
+// then serves a handful of rows.  This form turns the loop around:
+//   1. cm_count: per (b, g) and chunk, how many rows of the slab selected it;
+//      per row and head, the max of the row's selected scores (log2 units);
+//   2. cm_scan: per (b, g), exclusive offsets of every chunk's list and of
+//      its fixed-size segments (SEG entries each);
+//   3. cm_fill: each selection (row i, slot kk) is written into its chunk's
+//      list (order within a list is arbitrary: a row's result never depends
+//      on the other rows of its MFMA tile);
+//   4. cm_attend: one block per segment stages chunk c (K bf16, V^T fp16) in
+//      LDS once and runs packed 16-row tiles (16/G entries x the G heads of
+//      the group) over the segment: S^T = K Q^T on bf16 MFMA, the exact
+//      softmax over the chunk's S keys, O^T = V^T P^T on fp16 MFMA, then the
+//      row's weight exp(s^_c - m^) / l_c, where m^ is the row's largest
+//      selected score.  The weighted output goes to a partial buffer
+//      [B, H_q, slab rows, K, d] in fp16, one row per (query, head, slot);
+//   5. the window kernel (attend.hip, chunk-major variant) starts each row
+//      from O = sum over its slots of the partials (fp32, slot order),
+//      running max m^ and mass sum_c exp(s^_c - m^), exactly the state the
+//      query-major walk reaches after its selected chunks, and continues
+//      with the window's online softmax.
+// Rows are processed in slabs of NS queries so that the partial buffer
+// stays bounded; every slab runs steps 1-5.
+#include "hils_device.hpp"
+
+#include "hils_internal.hpp"
+
+namespace hils {
+
+namespace {
+
+constexpr int CM_SCAN_THREADS = 1024;
+
+// 16-byte-block XOR swizzle of an LDS row (same rule as the walk kernel's
+// ring): rows of 16 blocks use r & 15, rows of 8 blocks (r & 7) ^ ((r >> 3) & 1).
+template <int NB>
+__device__ __forceinline__ int cm_swz(int row) {
+    static_assert(NB == 8 || NB == 16, "rows of 8 or 16 blocks");
+    return NB == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+
+// Schedule of n LDS fragment reads each feeding one MFMA: LA reads issued
+// ahead, then one MFMA per read, so about LA fragments are live (the
+// scheduler would otherwise hoist every read and run out of registers).
+template <int n, int LA>
+__device__ __forceinline__ void cm_pipeline() {
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < n - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
+}  // namespace
+
+__global__ void cm_zero_kernel(int32_t *__restrict__ p, int64_t n) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x)
+        p[t] = 0;
+}
+
+// One thread per row (b, g, i) of the slab [s0, s0 + NS).
+__global__ __launch_bounds__(256) void cm_count_kernel(const int32_t *__restrict__ sel_idx,
+                                                       const float *__restrict__ sel_score,
+                                                       int32_t *__restrict__ cnt, float *__restrict__ mhat, int N,
+                                                       int H_q, int H_kv, int G, int K, int C, int S, int W, int s0,
+                                                       int NS, int64_t nrows) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nrows) return;  // nrows = B * H_kv * NS
+    const int il = (int)(t % NS);
+    const int64_t bg = t / NS;
+    const int i = s0 + il;
+    if (i >= N) return;
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int n = max(0, i / S - W / S);  // candidates of row i
+    const int32_t *sl = sel_idx + (bg * N + i) * K;
+    for (int kk = 0; kk < K; ++kk) {
+        const int c = sl[kk];
+        if (c >= 0 && c < n) atomicAdd(&cnt[bg * C + c], 1);
+    }
+    for (int e = 0; e < G; ++e) {
+        const int64_t hr = (b * H_q + g * G + e);
+        const float *sc = sel_score + (hr * N + i) * K;
+        float mh = -INFINITY;
+        for (int kk = 0; kk < K; ++kk)
+            if (sl[kk] >= 0) mh = fmaxf(mh, sc[kk] * LOG2E);
+        mhat[hr * NS + il] = mh;
+    }
+}
+
+// One block per (b, g): exclusive scans of the chunk counts (list offsets)
+// and of their segment counts ceil(cnt / SEG).  off and segoff hold C + 1
+// entries each; entry C is the total.
+__global__ __launch_bounds__(CM_SCAN_THREADS) void cm_scan_kernel(const int32_t *__restrict__ cnt,
+                                                                  int32_t *__restrict__ off,
+                                                                  int32_t *__restrict__ segoff, int C, int SEG) {
+    __shared__ int wa[CM_SCAN_THREADS / WAVE], ws[CM_SCAN_THREADS / WAVE];
+    const int64_t bg = blockIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int per = (C + CM_SCAN_THREADS - 1) / CM_SCAN_THREADS;
+    const int c0 = min(C, tid * per), c1 = min(C, c0 + per);
+    const int32_t *cb = cnt + bg * C;
+    int a = 0, sg = 0;
+    for (int c = c0; c < c1; ++c) {
+        a += cb[c];
+        sg += (cb[c] + SEG - 1) / SEG;
+    }
+    int ia = a, is = sg;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int ya = __shfl_up(ia, o, WAVE), ys = __shfl_up(is, o, WAVE);
+        if (lane >= o) {
+            ia += ya;
+            is += ys;
+        }
+    }
+    if (lane == WAVE - 1) {
+        wa[wave] = ia;
+        ws[wave] = is;
+    }
+    __syncthreads();
+    int ba = 0, bs = 0, ta = 0, ts = 0;
+    for (int x = 0; x < CM_SCAN_THREADS / WAVE; ++x) {
+        if (x < wave) {
+            ba += wa[x];
+            bs += ws[x];
+        }
+        ta += wa[x];
+        ts += ws[x];
+    }
+    int pa = ba + ia - a, ps = bs + is - sg;
+    int32_t *ob = off + bg * (C + 1), *sb = segoff + bg * (C + 1);
+    for (int c = c0; c < c1; ++c) {
+        ob[c] = pa;
+        sb[c] = ps;
+        pa += cb[c];
+        ps += (cb[c] + SEG - 1) / SEG;
+    }
+    if (tid == 0) {
+        ob[C] = ta;
+        sb[C] = ts;
+    }
+}
+
+// Same rows as cm_count; each selection takes a place in its chunk's list
+// (counting cnt back down to zero).  Entry = (slab row << 8) | slot.
+__global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict__ sel_idx, int32_t *__restrict__ cnt,
+                                                      const int32_t *__restrict__ off, int32_t *__restrict__ list,
+                                                      int N, int H_kv, int K, int C, int S, int W, int s0, int NS,
+                                                      int64_t lstride, int64_t nrows) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nrows) return;
+    const int il = (int)(t % NS);
+    const int64_t bg = t / NS;
+    const int i = s0 + il;
+    if (i >= N) return;
+    const int n = max(0, i / S - W / S);
+    const int32_t *sl = sel_idx + (bg * N + i) * K;
+    for (int kk = 0; kk < K; ++kk) {
+        const int c = sl[kk];
+        if (c >= 0 && c < n) {
+            const int pos = atomicSub(&cnt[bg * C + c], 1) - 1;
+            list[bg * lstride + off[bg * (C + 1) + c] + pos] = (il << 8) | kk;
+        }
+    }
+}
+
+// Per-tile operands gathered from global memory: the Q fragments of the
+// tile's rows, and where the row's partial goes.
+template <int KS>
+struct CmTile {
+    bf16x8 qf[KS];
+    float w;        // exp2(s^ - m^) of the row's slot, 0 for an empty row
+    int64_t prow;   // partial row index, -1 for an empty row
+};
+
+template <int D, int S, int G, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
+    const int32_t *__restrict__ list, const int32_t *__restrict__ off, const int32_t *__restrict__ segoff,
+    const float *__restrict__ sel_score, const float *__restrict__ mhat, f16 *__restrict__ part, int N, int H_q,
+    int H_kv, int CA, int C, int K, float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd) {
+    constexpr int TE = 16 / G;      // entries (queries) per 16-row tile
+    constexpr int KS = D / 32;      // k-steps of Q K^T
+    constexpr int KT = S / 16;      // 16-key tiles of S^T
+    constexpr int PS = S / 32;      // k-steps of V^T P^T
+    constexpr int DT = D / 16;      // 16-dim tiles of O^T
+    constexpr int NBK = D / 8;      // 16-byte blocks per K row
+    constexpr int NBV = S / 8;      // 16-byte blocks per V^T row
+    constexpr int NT = NWAVE * 64;
+    __shared__ u32x4 kt_l[S][NBK];
+    __shared__ u32x4 vt_l[D][NBV];
+
+    const int64_t bg = blockIdx.y;
+    // XCD-aware: consecutive segments (mostly of one chunk) on one XCD's L2
+    const int x = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    const int32_t *sb = segoff + bg * (C + 1);
+    if (x >= sb[C]) return;
+    // chunk c: the largest with sb[c] <= x (chunks without entries have
+    // sb[c] == sb[c + 1] and are passed over)
+    int lo = 0, hi = C - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sb[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    const int c = lo;
+    const int32_t *ob = off + bg * (C + 1);
+    const int e0 = ob[c] + (x - sb[c]) * SEG;
+    const int e1 = min(ob[c + 1], e0 + SEG);
+    const int g = (int)(bg % H_kv);
+    const int64_t b = bg / H_kv;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4, r = lane & 15;
+
+    // ---- stage the chunk: K rows (bf16) and its V^T copy (fp16, slot order)
+    {
+        const u32x4 *ks = (const u32x4 *)(k + (bg * N + (int64_t)c * S) * D);
+        for (int t = tid; t < S * NBK; t += NT) {
+            const int row = t / NBK, blk = t % NBK;
+            kt_l[row][blk ^ cm_swz<NBK>(row)] = ks[t];
+        }
+        const u32x4 *vs = (const u32x4 *)(vt + (bg * CA + c) * (int64_t)D * S);
+        for (int t = tid; t < D * NBV; t += NT) {
+            const int row = t / NBV, blk = t % NBV;
+            vt_l[row][blk ^ cm_swz<NBV>(row)] = vs[t];
+        }
+    }
+    __syncthreads();
+
+    const int ntile = (e1 - e0 + TE - 1) / TE;
+    const int e = r % G;
+    const int64_t hr = b * H_q + g * G + e;  // row's (batch, head)
+    auto gather = [&](int t, CmTile<KS> &tl) {
+        const int ei = e0 + t * TE + r / G;
+        if (t < ntile && ei < e1) {
+            const int ent = list[bg * lstride + ei];
+            const int il = ent >> 8, kk = ent & 255;
+            const bf16 *qr = q + (hr * N + s0 + il) * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
+            const float sc = sel_score[(hr * N + s0 + il) * K + kk];
+            tl.w = exp2_hw(sc * LOG2E - mhat[hr * NS + il]);
+            tl.prow = (hr * NS + il) * K + kk;
+        } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) tl.qf[s] = bf16x8{};
+            tl.w = 0.f;
+            tl.prow = -1;
+        }
+    };
+
+    CmTile<KS> cur;
+    gather(wave, cur);
+    for (int t = wave; t < ntile; t += NWAVE) {
+        CmTile<KS> nxt;
+        gather(t + NWAVE, nxt);  // next tile's loads fly during this tile's products
+        // S^T = K Q^T: acc[kt][i] = q_row . k_{16 kt + 4 grp + i}
+        f32x4 acc[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int row = 16 * kt + r;
+                const u32x4 raw = kt_l[row][(4 * s + grp) ^ cm_swz<NBK>(row)];
+                bf16x8 a;
+                __builtin_memcpy(&a, &raw, 16);
+                acc[kt] = mfma16(a, cur.qf[s], acc[kt]);
+            }
+        cm_pipeline<KS * KT, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+        // exact softmax over the chunk's S keys, per row (lane column)
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, acc[kt][i]);
+        cmax = rows4_max(cmax) * scale_log2;
+        float lc = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[kt][i] = exp2_hw(fmaf(acc[kt][i], scale_log2, -cmax));
+                lc += acc[kt][i];
+            }
+        lc = rows4_sum(lc);  // >= 1: the largest key contributes 2^0
+        // O^T = V^T P^T, P^T packed from the S^T accumulators (fp16 in [0, 1])
+        f16x8 bp[PS];
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bp[ps][i] = (f16)acc[2 * ps][i];
+                bp[ps][4 + i] = (f16)acc[2 * ps + 1][i];
+            }
+        f32x4 O[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int row = 16 * dt + r;
+                const u32x4 raw = vt_l[row][(4 * ps + grp) ^ cm_swz<NBV>(row)];
+                f16x8 a;
+                __builtin_memcpy(&a, &raw, 16);
+                O[dt] = mfma16h(a, bp[ps], O[dt]);
+            }
+        cm_pipeline<PS * DT, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+        // weighted partial, fp16: lane (r, grp) holds dims 16 dt + 4 grp + i
+        // of its row; stored lane-contiguous as [grp][dt][i]
+        if (cur.prow >= 0) {
+            const float f = cur.w * __builtin_amdgcn_rcpf(lc);
+            f16 *pr = part + cur.prow * D + grp * (D / 4);
+#pragma unroll
+            for (int j = 0; j < DT / 2; ++j) {
+                f16x8 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[i] = (f16)(O[2 * j][i] * f);
+                    y[4 + i] = (f16)(O[2 * j + 1][i] * f);
+                }
+                *(f16x8 *)(pr + 8 * j) = y;
+            }
+        }
+        cur = nxt;
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+namespace {
+
+constexpr size_t CM_PART_CAP = (size_t)16 << 30;  // partial buffer bound (bytes)
+
+struct CmLayout {
+    int NS;               // slab rows (multiple of S)
+    int SEG;              // entries per cm_attend block
+    size_t cnt, off, segoff, mhat, list, part, total;  // byte offsets after the V^T copy
+};
+
+template <int G>
+constexpr int cm_seg() {
+    return 8 * 4 * (16 / G);  // 8 waves x 4 tiles of 16/G entries
+}
+
+CmLayout cm_layout(const Shape &s) {
+    CmLayout L{};
+    const int64_t per_row = (int64_t)s.B * s.H_q * s.K * s.D * 2;  // partial bytes per slab row
+    int64_t ns = ((int64_t)s.N + s.S - 1) / s.S * s.S;
+    if (s.attend_slab > 0) {
+        ns = std::min<int64_t>(ns, ((int64_t)s.attend_slab + s.S - 1) / s.S * s.S);
+    } else if (per_row > 0 && (size_t)(ns * per_row) > CM_PART_CAP) {
+        ns = std::max<int64_t>(s.S, (int64_t)(CM_PART_CAP / per_row) / s.S * s.S);
+    }
+    L.NS = (int)std::max<int64_t>(ns, s.S);
+    switch (s.G) {
+        case 1: L.SEG = cm_seg<1>(); break;
+        case 2: L.SEG = cm_seg<2>(); break;
+        case 4: L.SEG = cm_seg<4>(); break;
+        default: L.SEG = cm_seg<8>(); break;
+    }
+    const size_t bg = (size_t)s.B * s.H_kv;
+    size_t o = 0;
+    L.cnt = o;
+    o = align_up(o + bg * s.C * 4, 256);
+    L.off = o;
+    o = align_up(o + bg * (s.C + 1) * 4, 256);
+    L.segoff = o;
+    o = align_up(o + bg * (s.C + 1) * 4, 256);
+    L.mhat = o;
+    o = align_up(o + (size_t)s.B * s.H_q * L.NS * 4, 256);
+    L.list = o;
+    o = align_up(o + bg * (size_t)L.NS * s.K * 4, 256);
+    L.part = o;
+    o = align_up(o + (size_t)s.B * s.H_q * L.NS * s.K * s.D * 2, 256);
+    L.total = o;
+    return L;
+}
+
+template <int D, int S, int G>
+hipError_t go_cm_attend(const Shape &s, const CmLayout &L, const void *q, const void *k, const f16 *vt,
+                        const int32_t *list, const int32_t *off, const int32_t *segoff, const float *sel_score,
+                        const float *mhat, f16 *part, int s0, hipStream_t st) {
+    constexpr int NWAVE = 8;
+    const int rows = std::min(L.NS, s.N - s0);
+    // segments per (b, g) are at most ceil(entries / SEG) + C
+    const int64_t bound = ((int64_t)rows * s.K + L.SEG - 1) / L.SEG + s.C;
+    const int per_xcd = (int)((bound + 7) / 8);
+    const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(s.B * s.H_kv)), block(NWAVE * 64);
+    hipLaunchKernelGGL((cm_attend_kernel<D, S, G, NWAVE>), grid, block, 0, st, (const bf16 *)q, (const bf16 *)k, vt,
+                       list, off, segoff, sel_score, mhat, part, s.N, s.H_q, s.H_kv, s.CA, s.C, s.K,
+                       s.scale * LOG2E, s0, L.NS, (int64_t)L.NS * s.K, L.SEG, per_xcd);
+    return hipGetLastError();
+}
+
+template <int D, int S>
+hipError_t cm_attend_g(const Shape &s, const CmLayout &L, const void *q, const void *k, const f16 *vt,
+                       const int32_t *list, const int32_t *off, const int32_t *segoff, const float *sel_score,
+                       const float *mhat, f16 *part, int s0, hipStream_t st) {
+    switch (s.G) {
+        case 1: return go_cm_attend<D, S, 1>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        case 2: return go_cm_attend<D, S, 2>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        case 4: return go_cm_attend<D, S, 4>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        case 8: return go_cm_attend<D, S, 8>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool attend_use_cm(const Shape &s) {
+    if (!s.io_bf16 || s.max_pages > 0 || s.K == 0 || s.C == 0) return false;
+    if (s.attend_mode == 1) return false;                 // the query-major walk
+    if (!window_after_cm_supported(s)) return false;
+    if (s.attend_mode == 2) return true;                  // chunk-major, asked for
+    return false;
+}
+
+size_t cm_workspace_bytes(const Shape &s) { return cm_layout(s).total; }
+
+int cm_slab_rows(const Shape &s) { return cm_layout(s).NS; }
+
+hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k, const void *v,
+                                   const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                   uint32_t *status, void *vt_ws, void *cm_ws, hipStream_t st) {
+    f16 *vt = (f16 *)vt_ws;
+    hipError_t e = launch_vt_prepass(s, v, vt, status, st);
+    if (e != hipSuccess) return e;
+    const CmLayout L = cm_layout(s);
+    char *base = (char *)cm_ws;
+    int32_t *cnt = (int32_t *)(base + L.cnt);
+    int32_t *off = (int32_t *)(base + L.off);
+    int32_t *segoff = (int32_t *)(base + L.segoff);
+    float *mhat = (float *)(base + L.mhat);
+    int32_t *list = (int32_t *)(base + L.list);
+    f16 *part = (f16 *)(base + L.part);
+    const int64_t ncnt = (int64_t)s.B * s.H_kv * s.C;
+    for (int s0 = 0; s0 < s.N; s0 += L.NS) {
+        hipLaunchKernelGGL(cm_zero_kernel, dim3((unsigned)std::min<int64_t>(1024, (ncnt + 255) / 256)), dim3(256), 0,
+                           st, cnt, ncnt);
+        // one thread per row t = (b * H_kv + g) * NS + il of the slab
+        const int64_t nrows = (int64_t)s.B * s.H_kv * L.NS;
+        const dim3 rgrid((unsigned)((nrows + 255) / 256));
+        hipLaunchKernelGGL(cm_count_kernel, rgrid, dim3(256), 0, st, sel_idx, sel_score, cnt, mhat, s.N, s.H_q,
+                           s.H_kv, s.G, s.K, s.C, s.S, s.W, s0, L.NS, nrows);
+        hipLaunchKernelGGL(cm_scan_kernel, dim3((unsigned)(s.B * s.H_kv)), dim3(CM_SCAN_THREADS), 0, st, cnt, off,
+                           segoff, s.C, L.SEG);
+        hipLaunchKernelGGL(cm_fill_kernel, rgrid, dim3(256), 0, st, sel_idx, cnt, off, list, s.N, s.H_kv, s.K, s.C,
+                           s.S, s.W, s0, L.NS, (int64_t)L.NS * s.K, nrows);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        else if (s.S == 64) e = cm_attend_g<128, 64>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        else e = cm_attend_g<128, 128>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        if (e != hipSuccess) return e;
+        e = launch_window_after_cm(s, q, k, vt, sel_idx, sel_score, out, lse, status, part, s0, L.NS, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace hils

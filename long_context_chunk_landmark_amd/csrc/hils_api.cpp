@@ -76,6 +76,11 @@ hils_status_t resolve(const hils_config_t *cfg, bool need_seq, hils::Shape &s) {
     if (cfg->score_mode < HILS_SCORE_AUTO || cfg->score_mode > HILS_SCORE_STREAMING)
         return fail(HILS_ERR_INVALID_ARG, "score_mode=%d unknown", cfg->score_mode);
     s.score_mode = cfg->score_mode;
+    if (cfg->attend_mode < HILS_ATTEND_AUTO || cfg->attend_mode > HILS_ATTEND_CHUNK_MAJOR)
+        return fail(HILS_ERR_INVALID_ARG, "attend_mode=%d unknown", cfg->attend_mode);
+    if (cfg->attend_slab < 0) return fail(HILS_ERR_INVALID_ARG, "attend_slab=%d must be >= 0", cfg->attend_slab);
+    s.attend_mode = cfg->attend_mode;
+    s.attend_slab = cfg->attend_slab;
     s.lm_mode = cfg->landmark_mode;
     s.agg_mode = cfg->agg_mode;
     s.wait_spins = cfg->wait_spins > 0 ? cfg->wait_spins : (1 << 18);

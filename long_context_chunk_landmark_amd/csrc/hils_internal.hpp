@@ -24,6 +24,8 @@ struct Shape {
     int agg_mode;  // group aggregation: 0 max of s^, 1 max of s^ - LSE over the candidates
     int wait_spins;  // bound on each wait of the fused kernel (pauses)
     int score_mode;  // score/select form: 0 auto, 1 two-pass, 2 streaming
+    int attend_mode; // selected-chunk attention form: 0 auto, 1 query-major walk, 2 chunk-major
+    int attend_slab; // chunk-major: query rows per slab (0: bounded by the partial buffer cap)
     // Paged prefill (q0 = 0, Nk = N, bt = null for the contiguous layout):
     // the N query rows are positions q0 .. q0 + N - 1 (q0 % S == 0) of
     // sequences whose keys 0 .. Nk - 1 = q0 + N - 1 live in a paged cache
@@ -90,6 +92,24 @@ bool sparse_attend_supported(const Shape &s);
 hipError_t launch_sparse_attend(const Shape &s, const void *q, const void *k, const void *v, const int32_t *sel_idx,
                                 const float *sel_score, void *out, float *lse, uint32_t *status, void *vt_ws,
                                 hipStream_t st);
+
+// Chunk-major form of the selected chunks (attend_cm.hip): whether it runs
+// for this shape and mode, its workspace (after the V^T copy: chunk lists,
+// row maxima and the fp16 partial buffer of one slab), the slab rows, and
+// the launch (V^T pre-pass, then per slab: count, scan, fill, chunk-major
+// attention, and the window kernel started from the partials).
+bool attend_use_cm(const Shape &s);
+size_t cm_workspace_bytes(const Shape &s);
+int cm_slab_rows(const Shape &s);
+hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k, const void *v,
+                                   const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                   uint32_t *status, void *vt_ws, void *cm_ws, hipStream_t st);
+// The window kernel's chunk-major variant (attend.hip): rows s0 .. s0 + NS - 1
+// start from the summed partials part [B, H_q, NS, K, D] and walk the window.
+bool window_after_cm_supported(const Shape &s);
+hipError_t launch_window_after_cm(const Shape &s, const void *q, const void *k, const void *vt,
+                                  const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
+                                  uint32_t *status, const void *part, int s0, int NS, hipStream_t st);
 
 // Status word cleared, then v [B, H_kv, Nk, D] (or the paged cache with
 // s.bt) copied to vt as fp16 [B, H_kv, CA, D, S] with the keys of each 32-key
