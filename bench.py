@@ -148,6 +148,7 @@ def bench_prefill(args, torch, hb, W, workload=None, steps=None, warmup=None):
     lse = torch.empty((cfg.B, cfg.H_q, cfg.N), dtype=torch.float32, device=dev)
     ws_s = torch.empty(hb.workspace_size(cfg, hb.WS_SCORE_QCAL if qcal else hb.WS_SCORE), dtype=torch.uint8,
                        device=dev)
+    ws_f = torch.empty(max(1, hb.workspace_size(cfg, hb.WS_FUSED)), dtype=torch.uint8, device=dev)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step():
@@ -157,14 +158,50 @@ def bench_prefill(args, torch, hb, W, workload=None, steps=None, warmup=None):
         e[1].record()
         hb.score_select(cfg, q, k_sum, b_sum, qcal=qcal, sel_idx=sel, sel_score=ss, workspace=ws_s)
         e[2].record()
-        hb.sparse_attend_fused(cfg, q, k, v, sel, ss, out=out, lse=lse)
+        hb.sparse_attend_fused(cfg, q, k, v, sel, ss, out=out, lse=lse, workspace=ws_f)
         e[3].record()
         return {"summary": (e[0], e[1]), "score_select": (e[1], e[2]), "fused": (e[2], e[3])}
 
     steps = steps or args.steps
     total_ms, per = _timed(step, steps, args.warmup if warmup is None else warmup, torch)
-    res = dict(cfg=cfg, inp=inp, ms_per_step=total_ms / steps, per_call_ms=per, sel=sel, out=out, lse=lse)
+    res = dict(cfg=cfg, inp=inp, ms_per_step=total_ms / steps, per_call_ms=per, sel=sel, ss=ss, out=out, lse=lse,
+               fused_workspace_bytes=ws_f.numel())
+    del ws_f
     return res
+
+
+def attend_form(hb, cfg):
+    """The selected-chunk form hils_sparse_attend_fused takes for cfg (auto:
+    chunk-major for 128-key chunks at d = 128, the walk otherwise)."""
+    m = cfg.attend_mode
+    if m == hb.ATTEND_AUTO:
+        m = hb.ATTEND_CHUNK_MAJOR if cfg.S * cfg.d >= 128 * 128 else hb.ATTEND_WALK
+    return "chunk-major" if m == hb.ATTEND_CHUNK_MAJOR else "walk"
+
+
+def fused_other_form(torch, hb, pre, reps=2):
+    """hils_sparse_attend_fused in the form auto does not take, on the same
+    inputs and selection (one untimed call, then reps timed calls): ms per call."""
+    import dataclasses
+
+    dev = torch.device("cuda:0")
+    cfg, inp = pre["cfg"], pre["inp"]
+    other = hb.ATTEND_WALK if attend_form(hb, cfg) == "chunk-major" else hb.ATTEND_CHUNK_MAJOR
+    c = dataclasses.replace(cfg, attend_mode=other)
+    ws = torch.empty(max(1, hb.workspace_size(c, hb.WS_FUSED)), dtype=torch.uint8, device=dev)
+    out, lse = torch.empty_like(pre["out"]), torch.empty_like(pre["lse"])
+    hb.sparse_attend_fused(c, inp["q"], inp["k"], inp["v"], pre["sel"], pre["ss"], out=out, lse=lse, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        hb.sparse_attend_fused(c, inp["q"], inp["k"], inp["v"], pre["sel"], pre["ss"], out=out, lse=lse,
+                               workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    nb = ws.numel()
+    del ws, out, lse
+    torch.cuda.empty_cache()
+    return {"form": attend_form(hb, c), "ms": e0.elapsed_time(e1) / reps, "workspace_bytes": nb}
 
 
 def bench_decode(args, torch, hb, W):
@@ -568,7 +605,10 @@ def bench_stress(args, torch, hb, W):
                                           "frac": fl_score / (per["score_select"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                           "flops": fl_score},
                "fused": {"ms": per["fused"], "bound": "mfma", "tflops": tfl, "frac": tfl / PEAK_BF16_TFLOPS,
-                         "flops": fl_att}}}
+                         "flops": fl_att, "form": attend_form(hb, cfg),
+                         "workspace_bytes": pre["fused_workspace_bytes"]}}}
+    print("[bench] stress: fused attention in the other form", file=sys.stderr, flush=True)
+    out["kernels"]["fused_other_form"] = fused_other_form(torch, hb, pre, reps=1)
     if not args.no_dense:
         print("[bench] stress: dense causal attention baseline", file=sys.stderr, flush=True)
         out["dense"] = bench_dense(torch, hb, pre, 1, pre["ms_per_step"])
@@ -653,10 +693,12 @@ def main():
                         "frac": by_sum / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by_sum},
             "score_select": {"ms": ms_s, "bound": "mfma", "tflops": fl_score / (ms_s * 1e-3) / 1e12,
                              "frac": fl_score / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl_score},
-            "fused": {"ms": ms_f, "tflops": achieved, "flops": fl_att},
+            "fused": {"ms": ms_f, "tflops": achieved, "flops": fl_att, "form": attend_form(hb, cfg)},
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }
+    print("[bench] fused attention in the other form", file=sys.stderr, flush=True)
+    result["kernels"]["fused_other_form"] = fused_other_form(torch, hb, pre)
     if not args.no_dense:
         print("[bench] dense causal attention baseline", file=sys.stderr, flush=True)
         result["dense"] = bench_dense(torch, hb, pre, max(2, args.steps // 3), pre["ms_per_step"])

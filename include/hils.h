@@ -132,8 +132,11 @@ typedef struct {
  * query that selected it, its weighted output exp(s^_c - m^) o_c goes to an
  * fp16 partial buffer, and the window pass starts each row from the sum of
  * its partials; it pays when adjacent queries select different chunks.
- * Workspace grows by about B * H_q * min(N, slab) * K * d * 2 bytes.  The
- * paged prefill always walks.  AUTO takes the walk. */
+ * Workspace grows by about B * H_q * min(N, slab) * K * (d * 2 + 8) bytes
+ * (16 GiB of partials at most with the default slab).  fp32 I/O and the paged
+ * prefill always walk.  AUTO takes CHUNK_MAJOR for S = 128 with d = 128
+ * (64 KB chunks, where the walk stages two chunks at a time) and the walk
+ * otherwise. */
 typedef enum {
     HILS_ATTEND_AUTO = 0,
     HILS_ATTEND_WALK = 1,
@@ -212,8 +215,10 @@ hils_status_t hils_score_select(const hils_config_t *cfg, const void *q, const v
  *   lse [B,H_q,N] fp32 (written, may be NULL).
  *   workspace: hils_workspace_size(cfg, HILS_WS_FUSED, 0, 0) bytes (0 for
  *   fp32 I/O).  bf16 I/O: bytes 0..255 are a status block, followed by a
- *   transposed fp16 copy of v.  Word 0 of the status block (uint32) is
- *   written by the call; read it once the stream is synchronised.  0: the
+ *   transposed fp16 copy of v and, in the chunk-major form (attend_mode),
+ *   the chunk lists and the fp16 partial buffer of one slab of rows.
+ *   Word 0 of the status block (uint32) is written by the call; read it
+ *   once the stream is synchronised.  0: the
  *   call completed normally.  Bit 0: an internal wait of the kernel gave up
  *   after cfg->wait_spins pauses; the rows of the waves that gave up hold
  *   NaN in out and lse.  Bit 1: some value of v is not finite or has

@@ -461,26 +461,35 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     for (int j = wave; j < NSTAGE && j < T; j += NWAVE) issue(j);
     if constexpr (CM) {
         // the selected chunks' weighted outputs, summed in slot order while
-        // the first window chunks land
-        constexpr int NV = D / 32;  // 16-byte pieces of a lane's D/4 dims
+        // the first window chunks land.  Piece j of a lane (dims of dt = 2j,
+        // 2j + 1) sits at 32 j + 8 grp of the row; four slots per round keep
+        // 4 * D / 32 loads of 16 bytes in flight.
+        constexpr int NV = D / 32, UR = 4;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int m = qrow[t], iq = i0 + m;
-            if (iq >= N) continue;
             const int16_t *sl = sel_l + m * K;
-            const f16 *pr = part + ((b * H_q + hrow[t]) * (int64_t)NS + (iq - qb0 * QB)) * K * D + grp * (D / 4);
-            for (int kk = 0; kk < nsel[t]; ++kk) {
-                if (sl[kk] >= n) continue;
-                f16x8 y[NV];
+            const f16 *pr = part + ((b * H_q + hrow[t]) * (int64_t)NS + (iq - qb0 * QB)) * K * D + 8 * grp;
+            const int ns = iq < N ? nsel[t] : 0;
+            for (int k0 = 0; k0 < ns; k0 += UR) {
+                f16x8 y[UR][NV];
 #pragma unroll
-                for (int j = 0; j < NV; ++j) y[j] = *(const f16x8 *)(pr + (int64_t)kk * D + 8 * j);
+                for (int u = 0; u < UR; ++u) {
+                    const int kk = k0 + u;
+                    const bool use = kk < ns && sl[min(kk, K - 1)] < n;
 #pragma unroll
-                for (int j = 0; j < NV; ++j)
+                    for (int j = 0; j < NV; ++j)
+                        y[u][j] = use ? *(const f16x8 *)(pr + (int64_t)kk * D + 32 * j) : f16x8{};
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        O[t][2 * j][i] += (float)y[j][i];
-                        O[t][2 * j + 1][i] += (float)y[j][4 + i];
-                    }
+                for (int u = 0; u < UR; ++u)
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            O[t][2 * j][i] += (float)y[u][j][i];
+                            O[t][2 * j + 1][i] += (float)y[u][j][4 + i];
+                        }
             }
         }
     }

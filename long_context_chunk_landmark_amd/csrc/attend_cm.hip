@@ -70,34 +70,64 @@ __global__ void cm_zero_kernel(int32_t *__restrict__ p, int64_t n) {
         p[t] = 0;
 }
 
-// One thread per row (b, g, i) of the slab [s0, s0 + NS).
-__global__ __launch_bounds__(256) void cm_count_kernel(const int32_t *__restrict__ sel_idx,
-                                                       const float *__restrict__ sel_score,
-                                                       int32_t *__restrict__ cnt, float *__restrict__ mhat, int N,
-                                                       int H_q, int H_kv, int G, int K, int C, int S, int W, int s0,
-                                                       int NS, int64_t nrows) {
+// Row blocks: one block takes CM_RB consecutive rows of one (b, g) and
+// counts their selections in an LDS histogram over the C chunks, so global
+// atomics are one per (block, chunk) instead of one per selection.
+constexpr int CM_RB = 1024;
+
+// Rows of block (bg, x) inside the slab and below N: [i0, i0 + nr).
+__device__ __forceinline__ int cm_block_rows(int N, int s0, int NS, int r0) {
+    return max(0, min(min(CM_RB, NS - r0), N - s0 - r0));
+}
+
+__global__ __launch_bounds__(256) void cm_count_kernel(const int32_t *__restrict__ sel_idx, int32_t *__restrict__ cnt,
+                                                       int N, int K, int C, int S, int W, int s0, int NS) {
+    extern __shared__ int hist[];  // [C]
+    const int64_t bg = blockIdx.y;
+    const int r0 = blockIdx.x * CM_RB, nr = cm_block_rows(N, s0, NS, r0);
+    for (int c = threadIdx.x; c < C; c += blockDim.x) hist[c] = 0;
+    __syncthreads();
+    const int32_t *base = sel_idx + (bg * N + s0 + r0) * K;
+    for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
+        const int i = s0 + r0 + e / K;
+        const int c = base[e];
+        if (c >= 0 && c < max(0, i / S - W / S)) atomicAdd(&hist[c], 1);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += blockDim.x)
+        if (hist[c]) atomicAdd(&cnt[bg * C + c], hist[c]);
+}
+
+// m^ of every (b, h, row) of the slab: the largest selected score, in log2
+// units.  16 lanes per row, reading its K scores 16 at a time.
+__global__ __launch_bounds__(256) void cm_rowmax_kernel(const int32_t *__restrict__ sel_idx,
+                                                        const float *__restrict__ sel_score,
+                                                        float *__restrict__ mhat, int N, int H_q, int H_kv, int G,
+                                                        int K, int s0, int NS, int64_t npairs) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= nrows) return;  // nrows = B * H_kv * NS
-    const int il = (int)(t % NS);
-    const int64_t bg = t / NS;
-    const int i = s0 + il;
-    if (i >= N) return;
-    const int g = (int)(bg % H_kv);
-    const int64_t b = bg / H_kv;
-    const int n = max(0, i / S - W / S);  // candidates of row i
-    const int32_t *sl = sel_idx + (bg * N + i) * K;
-    for (int kk = 0; kk < K; ++kk) {
-        const int c = sl[kk];
-        if (c >= 0 && c < n) atomicAdd(&cnt[bg * C + c], 1);
+    const int64_t pair = t >> 4;
+    const int j = (int)(t & 15);
+    float mh = -INFINITY;
+    int64_t hr = 0;
+    int il = 0;
+    bool ok = false;
+    if (pair < npairs) {
+        hr = pair / NS;
+        il = (int)(pair % NS);
+        const int i = s0 + il;
+        ok = i < N;
+        if (ok) {
+            const int h = (int)(hr % H_q);
+            const int64_t b = hr / H_q;
+            const float *sc = sel_score + (hr * N + i) * K;
+            const int32_t *sl = sel_idx + ((b * H_kv + h / G) * N + i) * K;
+            for (int kk = j; kk < K; kk += 16)
+                if (sl[kk] >= 0) mh = fmaxf(mh, sc[kk] * LOG2E);
+        }
     }
-    for (int e = 0; e < G; ++e) {
-        const int64_t hr = (b * H_q + g * G + e);
-        const float *sc = sel_score + (hr * N + i) * K;
-        float mh = -INFINITY;
-        for (int kk = 0; kk < K; ++kk)
-            if (sl[kk] >= 0) mh = fmaxf(mh, sc[kk] * LOG2E);
-        mhat[hr * NS + il] = mh;
-    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) mh = fmaxf(mh, __shfl_xor(mh, o, 16));
+    if (ok && j == 0) mhat[hr * NS + il] = mh;
 }
 
 // One block per (b, g): exclusive scans of the chunk counts (list offsets)
@@ -154,25 +184,51 @@ __global__ __launch_bounds__(CM_SCAN_THREADS) void cm_scan_kernel(const int32_t 
     }
 }
 
-// Same rows as cm_count; each selection takes a place in its chunk's list
-// (counting cnt back down to zero).  Entry = (slab row << 8) | slot.
+// Same row blocks as cm_count; each selection takes a place in its chunk's
+// list.  The block reserves a range per chunk with one global atomic
+// (counting cnt back down to zero), then ranks its own selections in LDS.
+// Entry = (slab row << 8) | slot; beside it, wl holds the weights
+// exp2(s^ - m^) of the entry's G heads (the row's chunk masses relative to
+// its largest selected one), so the attention reads them with the entry.
 __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict__ sel_idx, int32_t *__restrict__ cnt,
                                                       const int32_t *__restrict__ off, int32_t *__restrict__ list,
-                                                      int N, int H_kv, int K, int C, int S, int W, int s0, int NS,
-                                                      int64_t lstride, int64_t nrows) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= nrows) return;
-    const int il = (int)(t % NS);
-    const int64_t bg = t / NS;
-    const int i = s0 + il;
-    if (i >= N) return;
-    const int n = max(0, i / S - W / S);
-    const int32_t *sl = sel_idx + (bg * N + i) * K;
-    for (int kk = 0; kk < K; ++kk) {
-        const int c = sl[kk];
-        if (c >= 0 && c < n) {
-            const int pos = atomicSub(&cnt[bg * C + c], 1) - 1;
-            list[bg * lstride + off[bg * (C + 1) + c] + pos] = (il << 8) | kk;
+                                                      float *__restrict__ wl, const float *__restrict__ sel_score,
+                                                      const float *__restrict__ mhat, int N, int H_q, int H_kv,
+                                                      int G, int K, int C, int S, int W, int s0, int NS,
+                                                      int64_t lstride) {
+    extern __shared__ int sh[];  // hist[C], then base[C]
+    int *hist = sh, *basep = sh + C;
+    const int64_t bg = blockIdx.y;
+    const int r0 = blockIdx.x * CM_RB, nr = cm_block_rows(N, s0, NS, r0);
+    for (int c = threadIdx.x; c < C; c += blockDim.x) hist[c] = 0;
+    __syncthreads();
+    const int32_t *base = sel_idx + (bg * N + s0 + r0) * K;
+    for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
+        const int i = s0 + r0 + e / K;
+        const int c = base[e];
+        if (c >= 0 && c < max(0, i / S - W / S)) atomicAdd(&hist[c], 1);
+    }
+    __syncthreads();
+    const int32_t *ob = off + bg * (C + 1);
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+        const int h = hist[c];
+        basep[c] = h ? ob[c] + atomicSub(&cnt[bg * C + c], h) - h : 0;
+        hist[c] = 0;
+    }
+    __syncthreads();
+    int32_t *lb = list + bg * lstride;
+    float *wb = wl + bg * lstride * G;
+    const int64_t hr0 = (bg / H_kv) * H_q + (bg % H_kv) * G;  // first head of the group
+    for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
+        const int il = r0 + e / K, i = s0 + il, kk = e % K;
+        const int c = base[e];
+        if (c >= 0 && c < max(0, i / S - W / S)) {
+            const int p = basep[c] + atomicAdd(&hist[c], 1);
+            lb[p] = (il << 8) | kk;
+            for (int x = 0; x < G; ++x) {
+                const int64_t hr = hr0 + x;
+                wb[(int64_t)p * G + x] = exp2_hw(sel_score[(hr * N + i) * K + kk] * LOG2E - mhat[hr * NS + il]);
+            }
         }
     }
 }
@@ -182,16 +238,18 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
 template <int KS>
 struct CmTile {
     bf16x8 qf[KS];
-    float w;        // exp2(s^ - m^) of the row's slot, 0 for an empty row
-    int64_t prow;   // partial row index, -1 for an empty row
+    int64_t prow;   // partial row index (the trash row for an empty row)
 };
+
+// Tiles per wave per segment.
+constexpr int CM_TPW = 8;
 
 template <int D, int S, int G, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
-    const int32_t *__restrict__ list, const int32_t *__restrict__ off, const int32_t *__restrict__ segoff,
-    const float *__restrict__ sel_score, const float *__restrict__ mhat, f16 *__restrict__ part, int N, int H_q,
-    int H_kv, int CA, int C, int K, float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd) {
+    const int32_t *__restrict__ list, const float *__restrict__ wl, const int32_t *__restrict__ off,
+    const int32_t *__restrict__ segoff, f16 *__restrict__ part, int N, int H_q, int H_kv, int CA, int C, int K,
+    float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd, int64_t trash) {
     constexpr int TE = 16 / G;      // entries (queries) per 16-row tile
     constexpr int KS = D / 32;      // k-steps of Q K^T
     constexpr int KT = S / 16;      // 16-key tiles of S^T
@@ -223,49 +281,65 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     const int g = (int)(bg % H_kv);
     const int64_t b = bg / H_kv;
     const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id(), grp = lane >> 4, r = lane & 15;
+    const int e = r % G;
+    const int64_t hr = b * H_q + g * G + e;  // row's (batch, head)
 
-    // ---- stage the chunk: K rows (bf16) and its V^T copy (fp16, slot order)
+    // Every global load and store below is issued unconditionally (empty
+    // rows read row 0 and write the trash row): the compiler then counts the
+    // loads in flight exactly and waits only for the ones a step needs.
+    // ---- the list entries of this wave's tiles (tile wave + NWAVE u), all
+    // loaded at once so that no Q gather waits on its entry's load
+    int ent[CM_TPW + 2];
+    float wt[CM_TPW + 2];  // the row's weight exp2(s^ - m^) for this slot
+#pragma unroll
+    for (int u = 0; u < CM_TPW; ++u) {
+        const int ei = e0 + (wave + NWAVE * u) * TE + r / G;
+        const int64_t ec = bg * lstride + min(ei, e1 - 1);
+        const int en = list[ec];
+        const float w = wl[ec * G + e];
+        ent[u] = ei < e1 ? en : -1;
+        wt[u] = w;
+    }
+    ent[CM_TPW] = ent[CM_TPW + 1] = -1;
+    wt[CM_TPW] = wt[CM_TPW + 1] = 0.f;
+    auto gather = [&](int u, CmTile<KS> &tl) {
+        const int en = ent[u];
+        const int il = en >= 0 ? en >> 8 : 0, kk = en >= 0 ? en & 255 : 0;
+        const bf16 *qr = q + (hr * N + s0 + il) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
+        tl.prow = en >= 0 ? (hr * NS + il) * K + kk : trash;
+    };
+    const int nu = ((e1 - e0 + TE - 1) / TE - wave + NWAVE - 1) / NWAVE;  // this wave's tiles
+
+    // ---- stage the chunk: K rows (bf16) and its V^T copy (fp16, slot
+    // order); every piece is loaded before any is written to LDS
+    constexpr int NPK = (S * NBK + NT - 1) / NT, NPV = (D * NBV + NT - 1) / NT;
+    u32x4 kst[NPK], vst[NPV];
     {
         const u32x4 *ks = (const u32x4 *)(k + (bg * N + (int64_t)c * S) * D);
-        for (int t = tid; t < S * NBK; t += NT) {
-            const int row = t / NBK, blk = t % NBK;
-            kt_l[row][blk ^ cm_swz<NBK>(row)] = ks[t];
-        }
         const u32x4 *vs = (const u32x4 *)(vt + (bg * CA + c) * (int64_t)D * S);
-        for (int t = tid; t < D * NBV; t += NT) {
-            const int row = t / NBV, blk = t % NBV;
-            vt_l[row][blk ^ cm_swz<NBV>(row)] = vs[t];
-        }
+#pragma unroll
+        for (int p = 0; p < NPK; ++p) kst[p] = ks[min(tid + p * NT, S * NBK - 1)];
+#pragma unroll
+        for (int p = 0; p < NPV; ++p) vst[p] = vs[min(tid + p * NT, D * NBV - 1)];
+    }
+    CmTile<KS> ta, tb;
+    gather(0, ta);
+    gather(1, tb);
+#pragma unroll
+    for (int p = 0; p < NPK; ++p) {
+        const int t = tid + p * NT, row = t / NBK, blk = t % NBK;
+        if (t < S * NBK) kt_l[row][blk ^ cm_swz<NBK>(row)] = kst[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NPV; ++p) {
+        const int t = tid + p * NT, row = t / NBV, blk = t % NBV;
+        if (t < D * NBV) vt_l[row][blk ^ cm_swz<NBV>(row)] = vst[p];
     }
     __syncthreads();
 
-    const int ntile = (e1 - e0 + TE - 1) / TE;
-    const int e = r % G;
-    const int64_t hr = b * H_q + g * G + e;  // row's (batch, head)
-    auto gather = [&](int t, CmTile<KS> &tl) {
-        const int ei = e0 + t * TE + r / G;
-        if (t < ntile && ei < e1) {
-            const int ent = list[bg * lstride + ei];
-            const int il = ent >> 8, kk = ent & 255;
-            const bf16 *qr = q + (hr * N + s0 + il) * D;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
-            const float sc = sel_score[(hr * N + s0 + il) * K + kk];
-            tl.w = exp2_hw(sc * LOG2E - mhat[hr * NS + il]);
-            tl.prow = (hr * NS + il) * K + kk;
-        } else {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) tl.qf[s] = bf16x8{};
-            tl.w = 0.f;
-            tl.prow = -1;
-        }
-    };
-
-    CmTile<KS> cur;
-    gather(wave, cur);
-    for (int t = wave; t < ntile; t += NWAVE) {
-        CmTile<KS> nxt;
-        gather(t + NWAVE, nxt);  // next tile's loads fly during this tile's products
+    auto compute = [&](const CmTile<KS> &cur, float w) {
         // S^T = K Q^T: acc[kt][i] = q_row . k_{16 kt + 4 grp + i}
         f32x4 acc[KT];
 #pragma unroll
@@ -325,10 +399,11 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
         cm_pipeline<PS * DT, 4>();
         __builtin_amdgcn_sched_barrier(0);
         // weighted partial, fp16: lane (r, grp) holds dims 16 dt + 4 grp + i
-        // of its row; stored lane-contiguous as [grp][dt][i]
-        if (cur.prow >= 0) {
-            const float f = cur.w * __builtin_amdgcn_rcpf(lc);
-            f16 *pr = part + cur.prow * D + grp * (D / 4);
+        // of its row; piece j (dims of dt = 2j, 2j + 1) of the four lanes of
+        // a row is stored as 64 contiguous bytes: position 32 j + 8 grp + ...
+        {
+            const float f = w * __builtin_amdgcn_rcpf(lc);
+            f16 *pr = part + cur.prow * D + 8 * grp;
 #pragma unroll
             for (int j = 0; j < DT / 2; ++j) {
                 f16x8 y;
@@ -337,10 +412,21 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
                     y[i] = (f16)(O[2 * j][i] * f);
                     y[4 + i] = (f16)(O[2 * j + 1][i] * f);
                 }
-                *(f16x8 *)(pr + 8 * j) = y;
+                *(f16x8 *)(pr + 32 * j) = y;
             }
         }
-        cur = nxt;
+    };
+    // two tile buffers in turn: a buffer is refilled right after its tile's
+    // products have read it, so each gather has a whole tile of slack
+    // (with an odd count the last round's second tile is an empty one)
+    // (unrolled: the entry index stays a compile-time register index)
+#pragma unroll
+    for (int u = 0; u < CM_TPW; u += 2) {
+        if (u >= nu) break;
+        compute(ta, wt[u]);
+        gather(u + 2, ta);
+        compute(tb, wt[u + 1]);
+        gather(u + 3 < CM_TPW + 2 ? u + 3 : CM_TPW + 1, tb);
     }
 }
 
@@ -353,12 +439,12 @@ constexpr size_t CM_PART_CAP = (size_t)16 << 30;  // partial buffer bound (bytes
 struct CmLayout {
     int NS;               // slab rows (multiple of S)
     int SEG;              // entries per cm_attend block
-    size_t cnt, off, segoff, mhat, list, part, total;  // byte offsets after the V^T copy
+    size_t cnt, off, segoff, mhat, list, wl, part, total;  // byte offsets after the V^T copy
 };
 
 template <int G>
 constexpr int cm_seg() {
-    return 8 * 4 * (16 / G);  // 8 waves x 4 tiles of 16/G entries
+    return 8 * CM_TPW * (16 / G);  // 8 waves x CM_TPW tiles of 16/G entries
 }
 
 CmLayout cm_layout(const Shape &s) {
@@ -389,16 +475,18 @@ CmLayout cm_layout(const Shape &s) {
     o = align_up(o + (size_t)s.B * s.H_q * L.NS * 4, 256);
     L.list = o;
     o = align_up(o + bg * (size_t)L.NS * s.K * 4, 256);
-    L.part = o;
-    o = align_up(o + (size_t)s.B * s.H_q * L.NS * s.K * s.D * 2, 256);
+    L.wl = o;
+    o = align_up(o + bg * (size_t)L.NS * s.K * s.G * 4, 256);
+    L.part = o;  // one row past the partials: the trash row of empty tile rows
+    o = align_up(o + ((size_t)s.B * s.H_q * L.NS * s.K + 1) * s.D * 2, 256);
     L.total = o;
     return L;
 }
 
 template <int D, int S, int G>
 hipError_t go_cm_attend(const Shape &s, const CmLayout &L, const void *q, const void *k, const f16 *vt,
-                        const int32_t *list, const int32_t *off, const int32_t *segoff, const float *sel_score,
-                        const float *mhat, f16 *part, int s0, hipStream_t st) {
+                        const int32_t *list, const float *wl, const int32_t *off, const int32_t *segoff, f16 *part,
+                        int s0, hipStream_t st) {
     constexpr int NWAVE = 8;
     const int rows = std::min(L.NS, s.N - s0);
     // segments per (b, g) are at most ceil(entries / SEG) + C
@@ -406,20 +494,20 @@ hipError_t go_cm_attend(const Shape &s, const CmLayout &L, const void *q, const 
     const int per_xcd = (int)((bound + 7) / 8);
     const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(s.B * s.H_kv)), block(NWAVE * 64);
     hipLaunchKernelGGL((cm_attend_kernel<D, S, G, NWAVE>), grid, block, 0, st, (const bf16 *)q, (const bf16 *)k, vt,
-                       list, off, segoff, sel_score, mhat, part, s.N, s.H_q, s.H_kv, s.CA, s.C, s.K,
-                       s.scale * LOG2E, s0, L.NS, (int64_t)L.NS * s.K, L.SEG, per_xcd);
+                       list, wl, off, segoff, part, s.N, s.H_q, s.H_kv, s.CA, s.C, s.K, s.scale * LOG2E, s0, L.NS,
+                       (int64_t)L.NS * s.K, L.SEG, per_xcd, (int64_t)s.B * s.H_q * L.NS * s.K);
     return hipGetLastError();
 }
 
 template <int D, int S>
 hipError_t cm_attend_g(const Shape &s, const CmLayout &L, const void *q, const void *k, const f16 *vt,
-                       const int32_t *list, const int32_t *off, const int32_t *segoff, const float *sel_score,
-                       const float *mhat, f16 *part, int s0, hipStream_t st) {
+                       const int32_t *list, const float *wl, const int32_t *off, const int32_t *segoff, f16 *part,
+                       int s0, hipStream_t st) {
     switch (s.G) {
-        case 1: return go_cm_attend<D, S, 1>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        case 2: return go_cm_attend<D, S, 2>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        case 4: return go_cm_attend<D, S, 4>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        case 8: return go_cm_attend<D, S, 8>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        case 1: return go_cm_attend<D, S, 1>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        case 2: return go_cm_attend<D, S, 2>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        case 4: return go_cm_attend<D, S, 4>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        case 8: return go_cm_attend<D, S, 8>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -431,7 +519,14 @@ bool attend_use_cm(const Shape &s) {
     if (s.attend_mode == 1) return false;                 // the query-major walk
     if (!window_after_cm_supported(s)) return false;
     if (s.attend_mode == 2) return true;                  // chunk-major, asked for
-    return false;
+    // auto: 128-key chunks at d = 128.  There a staged chunk is 64 KB, the
+    // walk's ring holds two of them, and a block's union (i.i.d. inputs at
+    // 512K tokens, K = 64: about 1100 chunks for 32 queries) is walked at a
+    // few percent of the MFMA peak; the chunk-major form stages each chunk
+    // once per list segment (measured 109-117 ms against 497 ms for that
+    // workload).  With 64-key chunks the walk's four-stage ring and 64-query
+    // blocks keep it ahead (25 against 27.5 ms at 128K tokens, K = 32).
+    return s.S * s.D >= 128 * 128;
 }
 
 size_t cm_workspace_bytes(const Shape &s) { return cm_layout(s).total; }
@@ -451,25 +546,32 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
     int32_t *segoff = (int32_t *)(base + L.segoff);
     float *mhat = (float *)(base + L.mhat);
     int32_t *list = (int32_t *)(base + L.list);
+    float *wl = (float *)(base + L.wl);
     f16 *part = (f16 *)(base + L.part);
     const int64_t ncnt = (int64_t)s.B * s.H_kv * s.C;
+    // the histogram kernels' LDS: up to 2 x 8192 chunk counters
+    hipFuncSetAttribute((const void *)cm_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, s.C * 4);
+    hipFuncSetAttribute((const void *)cm_fill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, s.C * 8);
     for (int s0 = 0; s0 < s.N; s0 += L.NS) {
         hipLaunchKernelGGL(cm_zero_kernel, dim3((unsigned)std::min<int64_t>(1024, (ncnt + 255) / 256)), dim3(256), 0,
                            st, cnt, ncnt);
-        // one thread per row t = (b * H_kv + g) * NS + il of the slab
-        const int64_t nrows = (int64_t)s.B * s.H_kv * L.NS;
-        const dim3 rgrid((unsigned)((nrows + 255) / 256));
-        hipLaunchKernelGGL(cm_count_kernel, rgrid, dim3(256), 0, st, sel_idx, sel_score, cnt, mhat, s.N, s.H_q,
-                           s.H_kv, s.G, s.K, s.C, s.S, s.W, s0, L.NS, nrows);
+        // row blocks of CM_RB rows per (b, g); LDS histograms over the C chunks
+        const dim3 bgrid((unsigned)((L.NS + CM_RB - 1) / CM_RB), (unsigned)(s.B * s.H_kv));
+        hipLaunchKernelGGL(cm_count_kernel, bgrid, dim3(256), (size_t)s.C * 4, st, sel_idx, cnt, s.N, s.K, s.C, s.S,
+                           s.W, s0, L.NS);
+        const int64_t npairs = (int64_t)s.B * s.H_q * L.NS;
+        hipLaunchKernelGGL(cm_rowmax_kernel, dim3((unsigned)((npairs * 16 + 255) / 256)), dim3(256), 0, st, sel_idx,
+                           sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s0, L.NS, npairs);
         hipLaunchKernelGGL(cm_scan_kernel, dim3((unsigned)(s.B * s.H_kv)), dim3(CM_SCAN_THREADS), 0, st, cnt, off,
                            segoff, s.C, L.SEG);
-        hipLaunchKernelGGL(cm_fill_kernel, rgrid, dim3(256), 0, st, sel_idx, cnt, off, list, s.N, s.H_kv, s.K, s.C,
-                           s.S, s.W, s0, L.NS, (int64_t)L.NS * s.K, nrows);
+        hipLaunchKernelGGL(cm_fill_kernel, bgrid, dim3(256), (size_t)s.C * 8, st, sel_idx, cnt, off, list, wl,
+                           sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s.C, s.S, s.W, s0, L.NS,
+                           (int64_t)L.NS * s.K);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        else if (s.S == 64) e = cm_attend_g<128, 64>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
-        else e = cm_attend_g<128, 128>(s, L, q, k, vt, list, off, segoff, sel_score, mhat, part, s0, st);
+        if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        else if (s.S == 64) e = cm_attend_g<128, 64>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        else e = cm_attend_g<128, 128>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
         if (e != hipSuccess) return e;
         e = launch_window_after_cm(s, q, k, vt, sel_idx, sel_score, out, lse, status, part, s0, L.NS, st);
         if (e != hipSuccess) return e;

@@ -159,12 +159,45 @@ def test_decode_argument_checks(lib):
 
 
 def test_fused_shape_beyond_lds_is_unsupported(lib):
-    """G = 1 at S = 128, d = 128 with K = 128 and 4096 chunks has no block
-    shape whose LDS fits: rejected before launch."""
-    cfg = _cfg(H_q=2, H_kv=2, S=128, W=256, K=128, N=128 * 4096)
+    """G = 1 at S = 128, d = 128 with K = 128 and 4096 chunks: the walk has no
+    block shape whose LDS fits (its union list), so the walk rejects it before
+    launch; the chunk-major form (no union list, auto for this shape) takes it."""
+    cfg = _cfg(H_q=2, H_kv=2, S=128, W=256, K=128, N=128 * 4096, attend_mode=hb.ATTEND_WALK)
     need = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
     st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need, None)
     assert st == hb.HILS_ERR_UNSUPPORTED and "LDS" in hb.last_error()
+    for mode in (hb.ATTEND_AUTO, hb.ATTEND_CHUNK_MAJOR):
+        cfg = _cfg(H_q=2, H_kv=2, S=128, W=256, K=128, N=128 * 4096, attend_mode=mode)
+        need_cm = lib.hils_workspace_size(ctypes.byref(cfg), hb.WS_FUSED, 0, 0)
+        assert need_cm > need
+        st = lib.hils_sparse_attend_fused(ctypes.byref(cfg), A, A, A, A, A, A, None, A2, need_cm - 1, None)
+        assert st == hb.HILS_ERR_WORKSPACE
+
+
+def test_attend_mode_and_workspace(lib):
+    """attend_mode / attend_slab validation; the chunk-major workspace holds
+    the V^T copy plus a slab's lists and fp16 partials, bounded by the slab."""
+    bad = _cfg(attend_mode=3)
+    assert lib.hils_sparse_attend_fused(ctypes.byref(bad), A, A, A, A, A, A, None, A2, 1 << 40, None) == \
+        hb.HILS_ERR_INVALID_ARG and "attend_mode" in hb.last_error()
+    bad = _cfg(attend_slab=-1)
+    assert lib.hils_sparse_attend_fused(ctypes.byref(bad), A, A, A, A, A, A, None, A2, 1 << 40, None) == \
+        hb.HILS_ERR_INVALID_ARG and "attend_slab" in hb.last_error()
+    N, B, H_q, H_kv, d, S, K = 4096, 1, 8, 2, 128, 64, 16
+    ws = lambda **kw: lib.hils_workspace_size(ctypes.byref(_cfg(N=N, **kw)), hb.WS_FUSED, 0, 0)  # noqa: E731
+    walk = ws(attend_mode=hb.ATTEND_WALK)
+    assert ws() == walk  # auto walks 64-key chunks
+    cm = ws(attend_mode=hb.ATTEND_CHUNK_MAJOR)
+    part = B * H_q * N * K * d * 2
+    assert part < cm - walk < part + B * H_q * N * K * 8 + B * H_kv * (3 * (N // S) + 3) * 4 + 8 * 256 + 2 * d
+    # a slab of 1024 rows: a quarter of the partials
+    cm_slab = ws(attend_mode=hb.ATTEND_CHUNK_MAJOR, attend_slab=1000)  # rounded up to a multiple of S
+    assert part // 4 < cm_slab - walk < cm - walk
+    # fp32 I/O walks whatever the mode (no workspace)
+    assert lib.hils_workspace_size(ctypes.byref(hb.Config(H_q=8, H_kv=2, d=128, S=64, W=256, K=16, N=N,
+                                                          io_dtype=__import__("torch").float32,
+                                                          attend_mode=hb.ATTEND_CHUNK_MAJOR).to_c()),
+                                   hb.WS_FUSED, 0, 0) == 0
 
 
 def _paged(lib, cfg, q_start=1024, num_pages=200, max_pages=100, bt=A, ws=A2, nbytes=None, h=None, wd=None,

@@ -3,6 +3,8 @@ times: the whole prefill at 128K and 512K (with Q-Cal) and the batched decode
 step at 512K.  The GPU computes every output; the fp64 oracle checks all
 summaries and a seeded stratified sample of query rows (chunk starts and
 ends, rows without candidates, the final rows), one by one."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -17,6 +19,10 @@ from parity import (agg_lookup, assert_close, check_selection, host, oracle_pref
 pytestmark = pytest.mark.gpu
 
 ROWS = {"prefill_128k": 192, "prefill_512k_qcal": 96}
+# (workload, selected-chunk form): each workload in the form auto takes (the
+# walk at 128K, chunk-major at 512K with S = 128) and in the other one
+CASES = [("prefill_128k", hb.ATTEND_AUTO), ("prefill_512k_qcal", hb.ATTEND_AUTO),
+         ("prefill_128k", hb.ATTEND_CHUNK_MAJOR), ("prefill_512k_qcal", hb.ATTEND_WALK)]
 
 
 @pytest.fixture(scope="module")
@@ -27,11 +33,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("name", list(ROWS))
-def test_prefill_full_size(name, dev):
-    print(f"[fullsize] {name}: inputs", flush=True)
+@pytest.mark.parametrize("name,mode", CASES)
+def test_prefill_full_size(name, mode, dev):
+    print(f"[fullsize] {name} attend_mode={mode}: inputs", flush=True)
     inp = W.make_prefill(name, device=dev)
-    cfg = inp["cfg"]
+    cfg = dataclasses.replace(inp["cfg"], attend_mode=mode)
     qcal = inp.get("qcal")
     print(f"[fullsize] {name}: GPU prefill N={cfg.N}", flush=True)
     res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"], qcal=qcal)

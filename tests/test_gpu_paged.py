@@ -8,6 +8,8 @@ against the fp64 oracle's paged functions (end to end: the GPU and the
 oracle compute their own summaries).  Equivalence tests check that the paged
 path reproduces the whole-sequence prefill bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -209,11 +211,14 @@ def test_prefill_paged_matches_oracle(name, dev):
 @pytest.mark.parametrize("name", ["mid_ragged_b2", "s128_qcal", "g8_bf16sum_d64", "aggnorm_lmshared"])
 def test_prefill_paged_equals_prefill_rows(name, dev):
     """Chunked prefill over the paged cache reproduces rows q_start.. of the
-    whole-sequence prefill bitwise (same summaries, selections, outputs)."""
+    whole-sequence prefill bitwise (same summaries, selections, outputs).
+    The paged prefill walks the selected chunks, so the whole-sequence
+    prefill is asked for the walk too (auto would take the chunk-major form
+    for S = 128 at d = 128, equal only up to rounding)."""
     params, q_start, n = PAGED_CASES[name]
     print(f"[prefill_paged == prefill] {name}", flush=True)
     inp = _paged_inputs(params, q_start, n, dev)
-    cfg_full = inp["cfg"]
+    cfg_full = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)
     full = hb.prefill(cfg_full, inp["q"], inp["k"], inp["v"], inp["q_lm"], qcal=inp.get("qcal"))
     cfg = W.config(params, N=n)
     ks, bs = _summarize_all(cfg_full, inp, dev)
