@@ -225,9 +225,18 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
         if (c >= 0 && c < max(0, i / S - W / S)) {
             const int p = basep[c] + atomicAdd(&hist[c], 1);
             lb[p] = (il << 8) | kk;
-            for (int x = 0; x < G; ++x) {
-                const int64_t hr = hr0 + x;
-                wb[(int64_t)p * G + x] = exp2_hw(sel_score[(hr * N + i) * K + kk] * LOG2E - mhat[hr * NS + il]);
+            // the G weights of the entry, stored four at a time (16 bytes)
+            for (int x0 = 0; x0 < G; x0 += 4) {
+                float w4[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int64_t hr = hr0 + min(x0 + x, G - 1);
+                    w4[x] = exp2_hw(sel_score[(hr * N + i) * K + kk] * LOG2E - mhat[hr * NS + il]);
+                }
+                float *dst = wb + (int64_t)p * G + x0;
+                if (G >= 4) *(f32x4 *)dst = f32x4{w4[0], w4[1], w4[2], w4[3]};
+                else
+                    for (int x = 0; x < G; ++x) dst[x] = w4[x];
             }
         }
     }
