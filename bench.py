@@ -205,9 +205,10 @@ def fused_other_form(torch, hb, pre, reps=2):
 
 
 def bench_decode(args, torch, hb, W):
-    """The decode workload's step, then two secondary summary layouts over the
-    same K/V cache: one landmark head per kv head (H_lm = H_kv, bf16 k') and
-    fp32 k' (H_lm = H_q)."""
+    """The decode workload's step over a summary cache built by kernel 1 from
+    the K cache and seeded landmark queries, then secondary summary layouts
+    over the same K/V cache: one landmark head per kv head (H_lm = H_kv, bf16
+    k'), fp32 k' (H_lm = H_q), and the normalised aggregation."""
     import dataclasses
 
     dev = torch.device("cuda:0")
@@ -234,7 +235,23 @@ def bench_decode(args, torch, hb, W):
         total_ms, per = _timed(step, steps, warmup, torch)
         return 1000.0 * total_ms / steps, 1000.0 * per["decode"]
 
-    us, call_us = run(cfg, inp["ksum_cache"], inp["bsum_cache"], args.steps, args.warmup)
+    def built_summaries(c, seed):
+        """The summary cache as serving builds it: kernel 1 (hils_summarize_pages)
+        over every page of the K cache, with seeded N(0, 1) landmark queries."""
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        q_lm = torch.randn((P, c.H_lm, c.d), generator=g, device=dev).to(c.io_dtype)
+        ks = torch.empty((P, c.H_lm, c.d), dtype=c.summary_dtype, device=dev)
+        bs = torch.empty((P, c.H_lm), dtype=torch.float32, device=dev)
+        hb.summarize_pages(c, inp["k_cache"], q_lm, torch.arange(P, dtype=torch.int32, device=dev), ks, bs)
+        torch.cuda.synchronize()
+        del q_lm
+        return ks, bs
+
+    del inp["ksum_cache"], inp["bsum_cache"]
+    ksum, bsum = built_summaries(cfg, 41)
+    us, call_us = run(cfg, ksum, bsum, args.steps, args.warmup)
+    del ksum, bsum
     seq_lens = inp["seq_lens"].cpu().tolist()
     dense_us = None
     if not args.no_dense:
@@ -253,11 +270,10 @@ def bench_decode(args, torch, hb, W):
         dense_us = 1000.0 * dper["dense"]
         del wsd
     secondary = {}
-    del inp["ksum_cache"], inp["bsum_cache"]
     for name, c in (("H_lm=H_kv, bf16 k'", dataclasses.replace(cfg, H_lm=cfg.H_kv)),
                     ("H_lm=H_q, fp32 k'", dataclasses.replace(cfg, summary_dtype=torch.float32)),
                     ("H_lm=H_q, bf16 k', normalised aggregation", dataclasses.replace(cfg, agg_mode=hb.AGG_NORMALIZED))):
-        ks, bs = W.decode_summary_cache(c, P, seed=41, device=dev)
+        ks, bs = built_summaries(c, 43)
         _, cu = run(c, ks, bs, max(2, args.steps // 2), 1)
         secondary[name] = (c, cu)
         del ks, bs

@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         // the first window chunks land.  Piece j of a lane (dims of dt = 2j,
         // 2j + 1) sits at 32 j + 8 grp of the row; four slots per round keep
         // 4 * D / 32 loads of 16 bytes in flight.
-        constexpr int NV = D / 32, UR = 4;
+        constexpr int NV = D / 32, UR = NWAVE <= 8 ? 8 : 4;  // 8-wave blocks have the registers
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int m = qrow[t], iq = i0 + m;
