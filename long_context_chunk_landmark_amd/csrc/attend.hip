@@ -172,9 +172,11 @@ struct AttendCfg {
 // row's next selection never waits on the vector-memory counter that
 // tracks the chunk DMA.
 // CM (chunk-major variant): the selected chunks were computed by
-// cm_attend_kernel into weighted fp16 partials part[B, H_q, NS, K, D] (lane
-// order [grp][dt][i] within a row); the block starts each row from their sum
-// and walks the window only.  Rows are the slab s0 = qb0 * QB .. s0 + NS - 1.
+// cm_attend_kernel into weighted fp16 partials part[B, H_kv, NS, K, G D]
+// (piece j of head e and lane group grp at 32 (G j + e) + 8 grp within a
+// selection's region); the block starts
+// each row from their sum and walks the window only.  Rows are the slab
+// s0 = qb0 * QB .. s0 + NS - 1.
 template <int D, int S, int G, int TPW, int NWAVE, int NSTAGE, bool CM>
 __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
@@ -469,7 +471,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         for (int t = 0; t < TPW; ++t) {
             const int m = qrow[t], iq = i0 + m;
             const int16_t *sl = sel_l + m * K;
-            const f16 *pr = part + ((b * H_q + hrow[t]) * (int64_t)NS + (iq - qb0 * QB)) * K * D + 8 * grp;
+            // partial regions [B, H_kv, NS, K, G D], ordered [piece j][head][grp][8]
+            const f16 *pr = part + (bg * NS + (iq - qb0 * QB)) * (int64_t)K * G * D + 32 * (hrow[t] - g * G) + 8 * grp;
             const int ns = iq < N ? nsel[t] : 0;
             for (int k0 = 0; k0 < ns; k0 += UR) {
                 f16x8 y[UR][NV];
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
                     const bool use = kk < ns && sl[min(kk, K - 1)] < n;
 #pragma unroll
                     for (int j = 0; j < NV; ++j)
-                        y[u][j] = use ? *(const f16x8 *)(pr + (int64_t)kk * D + 32 * j) : f16x8{};
+                        y[u][j] = use ? *(const f16x8 *)(pr + (int64_t)kk * G * D + 32 * G * j) : f16x8{};
                 }
 #pragma unroll
                 for (int u = 0; u < UR; ++u)

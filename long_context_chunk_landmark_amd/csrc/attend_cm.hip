@@ -23,7 +23,8 @@
 //      softmax over the chunk's S keys, O^T = V^T P^T on fp16 MFMA, then the
 //      row's weight exp(s^_c - m^) / l_c, where m^ is the row's largest
 //      selected score.  The weighted output goes to a partial buffer
-//      [B, H_q, slab rows, K, d] in fp16, one row per (query, head, slot);
+//      [B, H_kv, slab rows, K, G d] in fp16, one region of G d values per
+//      (query, slot) holding the G heads' outputs;
 //   5. the window kernel (attend.hip, chunk-major variant) starts each row
 //      from O = sum over its slots of the partials (fp32, slot order),
 //      running max m^ and mass sum_c exp(s^_c - m^), exactly the state the
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
 template <int KS>
 struct CmTile {
     bf16x8 qf[KS];
-    int64_t prow;   // partial row index (the trash row for an empty row)
+    int64_t pent;   // element offset of the selection's partial region (the trash region for an empty row)
 };
 
 // Tiles per wave per segment.
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     const int64_t hr = b * H_q + g * G + e;  // row's (batch, head)
 
     // Every global load and store below is issued unconditionally (empty
-    // rows read row 0 and write the trash row): the compiler then counts the
+    // rows read row 0 and write the trash region): the compiler then counts the
     // loads in flight exactly and waits only for the ones a step needs.
     // ---- the list entries of this wave's tiles (tile wave + NWAVE u), all
     // loaded at once so that no Q gather waits on its entry's load
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
         const bf16 *qr = q + (hr * N + s0 + il) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
-        tl.prow = en >= 0 ? (hr * NS + il) * K + kk : trash;
+        tl.pent = (en >= 0 ? (bg * NS + il) * K + kk : trash) * G * D;
     };
     const int nu = ((e1 - e0 + TE - 1) / TE - wave + NWAVE - 1) / NWAVE;  // this wave's tiles
 
@@ -408,11 +409,13 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
         cm_pipeline<PS * DT, 4>();
         __builtin_amdgcn_sched_barrier(0);
         // weighted partial, fp16: lane (r, grp) holds dims 16 dt + 4 grp + i
-        // of its row; piece j (dims of dt = 2j, 2j + 1) of the four lanes of
-        // a row is stored as 64 contiguous bytes: position 32 j + 8 grp + ...
+        // of its row (head e).  A selection's G heads share one region of
+        // G d values, ordered [piece j][head][grp][8]: piece j holds the dims
+        // of dt = 2j, 2j + 1, so store j writes 64 G contiguous bytes (two
+        // full cache lines at G = 4) of each selection of the tile
         {
             const float f = w * __builtin_amdgcn_rcpf(lc);
-            f16 *pr = part + cur.prow * D + 8 * grp;
+            f16 *pr = part + cur.pent + 32 * e + 8 * grp;
 #pragma unroll
             for (int j = 0; j < DT / 2; ++j) {
                 f16x8 y;
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
                     y[i] = (f16)(O[2 * j][i] * f);
                     y[4 + i] = (f16)(O[2 * j + 1][i] * f);
                 }
-                *(f16x8 *)(pr + 32 * j) = y;
+                *(f16x8 *)(pr + 32 * G * j) = y;
             }
         }
     };
@@ -486,8 +489,8 @@ CmLayout cm_layout(const Shape &s) {
     o = align_up(o + bg * (size_t)L.NS * s.K * 4, 256);
     L.wl = o;
     o = align_up(o + bg * (size_t)L.NS * s.K * s.G * 4, 256);
-    L.part = o;  // one row past the partials: the trash row of empty tile rows
-    o = align_up(o + ((size_t)s.B * s.H_q * L.NS * s.K + 1) * s.D * 2, 256);
+    L.part = o;  // one region past the partials: the trash region of empty tile rows
+    o = align_up(o + ((size_t)s.B * s.H_kv * L.NS * s.K + 1) * s.G * s.D * 2, 256);
     L.total = o;
     return L;
 }
@@ -504,7 +507,7 @@ hipError_t go_cm_attend(const Shape &s, const CmLayout &L, const void *q, const 
     const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(s.B * s.H_kv)), block(NWAVE * 64);
     hipLaunchKernelGGL((cm_attend_kernel<D, S, G, NWAVE>), grid, block, 0, st, (const bf16 *)q, (const bf16 *)k, vt,
                        list, wl, off, segoff, part, s.N, s.H_q, s.H_kv, s.CA, s.C, s.K, s.scale * LOG2E, s0, L.NS,
-                       (int64_t)L.NS * s.K, L.SEG, per_xcd, (int64_t)s.B * s.H_q * L.NS * s.K);
+                       (int64_t)L.NS * s.K, L.SEG, per_xcd, (int64_t)s.B * s.H_kv * L.NS * s.K);
     return hipGetLastError();
 }
 

@@ -105,7 +105,7 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
                                    const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
                                    uint32_t *status, void *vt_ws, void *cm_ws, hipStream_t st);
 // The window kernel's chunk-major variant (attend.hip): rows s0 .. s0 + NS - 1
-// start from the summed partials part [B, H_q, NS, K, D] and walk the window.
+// start from the summed partials part [B, H_kv, NS, K, G D] and walk the window.
 bool window_after_cm_supported(const Shape &s);
 hipError_t launch_window_after_cm(const Shape &s, const void *q, const void *k, const void *vt,
                                   const int32_t *sel_idx, const float *sel_score, void *out, float *lse,
