@@ -172,10 +172,11 @@ def bench_prefill(args, torch, hb, W, workload=None, steps=None, warmup=None):
 
 def attend_form(hb, cfg):
     """The selected-chunk form hils_sparse_attend_fused takes for cfg (auto:
-    chunk-major for 128-key chunks at d = 128, the walk otherwise)."""
+    chunk-major for bf16 I/O with selections, the walk otherwise)."""
     m = cfg.attend_mode
     if m == hb.ATTEND_AUTO:
-        m = hb.ATTEND_CHUNK_MAJOR if cfg.S * cfg.d >= 128 * 128 else hb.ATTEND_WALK
+        import torch
+        m = hb.ATTEND_CHUNK_MAJOR if cfg.io_dtype == torch.bfloat16 and cfg.K > 0 else hb.ATTEND_WALK
     return "chunk-major" if m == hb.ATTEND_CHUNK_MAJOR else "walk"
 
 
@@ -683,7 +684,10 @@ def main():
     ms_s = pre["per_call_ms"]["score_select"]
     ms_m = pre["per_call_ms"]["summary"]
     achieved = fl_att / (ms_f * 1e-3) / 1e12
-    traffic = traffic_from_profile("sparse_attend", args.workload, ["attend.hip", "hils_device.hpp"])
+    form = attend_form(hb, cfg)
+    # the fused call's HBM bytes (all its kernels), from the committed counter summary
+    traffic = traffic_from_profile("sparse_attend_fused", args.workload,
+                                   ["attend.hip", "attend_cm.hip", "hils_device.hpp"])
     result = {
         "metric": METRIC,
         "value": cfg.N * cfg.B / (pre["ms_per_step"] * 1e-3),
@@ -700,7 +704,9 @@ def main():
         "config": {"workload": args.workload, "B": cfg.B, "N": cfg.N, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
                    "H_lm": cfg.H_lm, "d": cfg.d, "S": cfg.S, "W": cfg.W, "K": cfg.K, "M": cfg.M,
                    "summary_dtype": "bf16" if sum_b == 2 else "f32"},
-        "roofline": {"kernel": "sparse_attend_kernel (hils_sparse_attend_fused)", "bound": "mfma",
+        "roofline": {"kernel": ("hils_sparse_attend_fused, chunk-major: v_transpose, list build, cm_attend_kernel, "
+                                "window pass" if form == "chunk-major" else
+                                "hils_sparse_attend_fused, walk: v_transpose, sparse_attend_kernel"), "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_tflop_per_launch": fl_att / 1e12},
@@ -709,7 +715,8 @@ def main():
                         "frac": by_sum / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by_sum},
             "score_select": {"ms": ms_s, "bound": "mfma", "tflops": fl_score / (ms_s * 1e-3) / 1e12,
                              "frac": fl_score / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops": fl_score},
-            "fused": {"ms": ms_f, "tflops": achieved, "flops": fl_att, "form": attend_form(hb, cfg)},
+            "fused": {"ms": ms_f, "tflops": achieved, "flops": fl_att, "form": form,
+                      "workspace_bytes": pre["fused_workspace_bytes"]},
         },
         "union_overlap_M": union_overlap(pre["sel"], cfg.M),
     }

@@ -466,7 +466,8 @@ __global__ __launch_bounds__(NWAVE * 64) void sparse_attend_kernel(
         // the first window chunks land.  Piece j of a lane (dims of dt = 2j,
         // 2j + 1) sits at 32 j + 8 grp of the row; four slots per round keep
         // 4 * D / 32 loads of 16 bytes in flight.
-        constexpr int NV = D / 32, UR = NWAVE <= 8 ? 8 : 4;  // 8-wave blocks have the registers
+        // 8-wave blocks alone on a CU (64 KB chunks) have the registers for 8
+        constexpr int NV = D / 32, UR = (NWAVE <= 8 && S * D > 128 * 64) ? 8 : 4;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int m = qrow[t], iq = i0 + m;
@@ -810,13 +811,16 @@ size_t fused_workspace_bytes(const Shape &s) {
 // queries, dividing S).  16 waves leave 128 registers per wave, enough for
 // 64-key chunks at d = 128 only.  The ring holds 4 chunks when a chunk is
 // 32 KB, else 2.
-template <int D, int S, int G, int NWAVE, int TPW_ = 1>
+// The window pass after the chunk-major form (CMF) walks ~W/S chunks per
+// block: it keeps two stages, so that two blocks share a CU and one block's
+// partial reads overlap the other's chunks.
+template <int D, int S, int G, int NWAVE, int TPW_ = 1, bool CMF = false>
 struct AttendPlan {
     static constexpr int TPW = TPW_;
     static constexpr int QB = NWAVE * TPW * (16 / G);
     static constexpr bool valid = QB <= S && S % QB == 0 && !(NWAVE == 16 && D * S > 128 * 64) &&
                                   !(TPW == 2 && D * S > 128 * 64);
-    static constexpr int NSTAGE = (S * D * 4 <= 32 * 1024) ? 4 : 2;
+    static constexpr int NSTAGE = (!CMF && S * D * 4 <= 32 * 1024) ? 4 : 2;
     static constexpr size_t ring_bytes = (size_t)NSTAGE * 2 * S * D * 2;
     static constexpr size_t static_lds = ring_bytes + 64;
 };
@@ -850,7 +854,7 @@ template <int D, int S, int G, int NWAVE, int TPW, bool CM>
 static hipError_t go_attend(const Shape &s, const void *q, const void *k, const void *vt, const int32_t *sel_idx,
                             const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
                             hipStream_t st) {
-    using P = AttendPlan<D, S, G, NWAVE, TPW>;
+    using P = AttendPlan<D, S, G, NWAVE, TPW, CM>;
     const int QB = P::QB;
     int NW, UCAP;
     walk_sizes<P::QB>(s, CM, NW, UCAP);
@@ -872,13 +876,18 @@ static hipError_t go_attend(const Shape &s, const void *q, const void *k, const 
     return hipGetLastError();
 }
 
-template <int D, int S, int G, int NWAVE, int TPW>
-static bool fits(const Shape &s, bool cm) {
-    using P = AttendPlan<D, S, G, NWAVE, TPW>;
+template <int D, int S, int G, int NWAVE, int TPW, bool CM>
+static bool fits_plan(const Shape &s) {
+    using P = AttendPlan<D, S, G, NWAVE, TPW, CM>;
     if constexpr (!P::valid) return false;
     else
-        return P::static_lds + attend_dyn_lds<D, S, G, NWAVE, TPW>(s, cm) <= LDS_BYTES &&
+        return P::static_lds + attend_dyn_lds<D, S, G, NWAVE, TPW>(s, CM) <= LDS_BYTES &&
                (size_t)P::QB * G * s.K * 4 <= P::ring_bytes;  // setup staging of the scores
+}
+
+template <int D, int S, int G, int NWAVE, int TPW>
+static bool fits(const Shape &s, bool cm) {
+    return cm ? fits_plan<D, S, G, NWAVE, TPW, true>(s) : fits_plan<D, S, G, NWAVE, TPW, false>(s);
 }
 
 // Largest block whose LDS (chunk ring + selections + union) fits.
@@ -900,6 +909,8 @@ static hipError_t dispatch_w(const Shape &s, const void *q, const void *k, const
                              const float *sel_score, void *out, float *lse, uint32_t *status, const WinArgs &wa,
                              hipStream_t st) {
     hipError_t err = hipErrorInvalidValue;
+    // the window pass prefers 8-wave blocks (two per CU with its 2-stage ring)
+    if (CM && try_attend<D, S, G, 8, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
     if (try_attend<D, S, G, 16, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
     if (try_attend<D, S, G, 8, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;
     if (try_attend<D, S, G, 4, 1, CM>(s, q, k, vt, sel_idx, sel_score, out, lse, status, wa, st, err)) return err;

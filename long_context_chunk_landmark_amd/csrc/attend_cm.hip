@@ -531,14 +531,13 @@ bool attend_use_cm(const Shape &s) {
     if (s.attend_mode == 1) return false;                 // the query-major walk
     if (!window_after_cm_supported(s)) return false;
     if (s.attend_mode == 2) return true;                  // chunk-major, asked for
-    // auto: 128-key chunks at d = 128.  There a staged chunk is 64 KB, the
-    // walk's ring holds two of them, and a block's union (i.i.d. inputs at
-    // 512K tokens, K = 64: about 1100 chunks for 32 queries) is walked at a
-    // few percent of the MFMA peak; the chunk-major form stages each chunk
-    // once per list segment (measured 109-117 ms against 497 ms for that
-    // workload).  With 64-key chunks the walk's four-stage ring and 64-query
-    // blocks keep it ahead (25 against 27.5 ms at 128K tokens, K = 32).
-    return s.S * s.D >= 128 * 128;
+    // auto: chunk-major wherever it runs.  Measured against the walk: 101-102
+    // against 497 ms at 512K tokens (i.i.d. inputs, S = 128, K = 64: a
+    // 32-query block's union is about 1100 chunks, so the walk stages each
+    // 64 KB chunk for ~2 queries) and 23.2 against 25.2-25.5 ms at 128K
+    // tokens (drifting inputs, S = 64, K = 32).
+    (void)s;
+    return true;
 }
 
 size_t cm_workspace_bytes(const Shape &s) { return cm_layout(s).total; }

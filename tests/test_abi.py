@@ -186,8 +186,8 @@ def test_attend_mode_and_workspace(lib):
     N, B, H_q, H_kv, d, S, K = 4096, 1, 8, 2, 128, 64, 16
     ws = lambda **kw: lib.hils_workspace_size(ctypes.byref(_cfg(N=N, **kw)), hb.WS_FUSED, 0, 0)  # noqa: E731
     walk = ws(attend_mode=hb.ATTEND_WALK)
-    assert ws() == walk  # auto walks 64-key chunks
     cm = ws(attend_mode=hb.ATTEND_CHUNK_MAJOR)
+    assert ws() == cm  # auto takes the chunk-major form
     part = B * H_q * N * K * d * 2
     assert part < cm - walk < part + B * H_q * N * K * 8 + B * H_kv * (3 * (N // S) + 3) * 4 + 8 * 256 + 2 * d
     # a slab of 1024 rows: a quarter of the partials

@@ -213,8 +213,8 @@ def test_prefill_paged_equals_prefill_rows(name, dev):
     """Chunked prefill over the paged cache reproduces rows q_start.. of the
     whole-sequence prefill bitwise (same summaries, selections, outputs).
     The paged prefill walks the selected chunks, so the whole-sequence
-    prefill is asked for the walk too (auto would take the chunk-major form
-    for S = 128 at d = 128, equal only up to rounding)."""
+    prefill is asked for the walk too (auto takes the chunk-major form,
+    equal only up to rounding)."""
     params, q_start, n = PAGED_CASES[name]
     print(f"[prefill_paged == prefill] {name}", flush=True)
     inp = _paged_inputs(params, q_start, n, dev)
@@ -240,7 +240,7 @@ def test_serving_in_chunks_equals_whole_prefill(dev):
     params = dict(seed=78, io=BF, B=2, H_q=8, H_kv=2, d=128, S=64, W=256, K=8)
     splits = [0, 1024, 2048, 2600]
     inp = _paged_inputs(params, 0, splits[-1], dev)
-    cfg_full = inp["cfg"]
+    cfg_full = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)  # the paged prefill walks
     full = hb.prefill(cfg_full, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     S = cfg_full.S
     P = inp["k_cache"].shape[0]

@@ -83,7 +83,8 @@ def test_streaming_exact_ties_take_lower_index(name, dev):
 def test_streaming_paged_prefill_equals_contiguous(dev):
     p = dict(seed=77, io=BF, B=1, H_q=8, H_kv=2, d=128, N=6144, S=64, W=256, K=8)
     inp = W.make_prefill(p, device=dev)
-    cfg = dataclasses.replace(inp["cfg"], score_mode=hb.SCORE_STREAMING)
+    # the paged prefill walks the selected chunks: the contiguous one walks too
+    cfg = dataclasses.replace(inp["cfg"], score_mode=hb.SCORE_STREAMING, attend_mode=hb.ATTEND_WALK)
     print("[streaming paged]", flush=True)
     res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=5)

@@ -141,7 +141,7 @@ def test_prefill_ties_paged_equals_contiguous(dev):
     way (its selection passes the same ranking)."""
     p = dict(PREFILL_TIES["g4_fp32sum"])
     inp = W.make_prefill(p, device=dev)
-    cfg = inp["cfg"]
+    cfg = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)  # as the paged prefill
     _twin_chunks(inp, cfg.S)
     res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=5)

@@ -55,7 +55,7 @@ def test_paged_prefill_status_word_is_clear(dev):
     """The chunked prefill's workspace carries the same status word at offset 0."""
     p = dict(seed=71, io=torch.bfloat16, B=1, H_q=8, H_kv=2, d=128, N=4096, S=64, W=256, K=8)
     inp = W.make_prefill(p, device=dev)
-    cfg = inp["cfg"]
+    cfg = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)  # the paged prefill walks
     res = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     kc, vc, bt = W.paged_layout(inp["k"], inp["v"], cfg.S, seed=3)
     P = kc.shape[0]
