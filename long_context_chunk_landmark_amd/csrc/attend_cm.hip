@@ -243,6 +243,29 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
     }
 }
 
+// q [B, H_q, N, D] copied once per call into per-query regions
+// qt [B, H_kv, N, G D]: the G heads of a query side by side, ordered
+// [k-step s][head][lane group][8] so that the Q K^T fragment load for k-step s
+// reads 64 G contiguous bytes of each query of a tile (as the partial stores).
+// One thread per 16-byte piece of qt.
+__global__ __launch_bounds__(256) void cm_qt_kernel(const bf16 *__restrict__ q, bf16 *__restrict__ qt, int N,
+                                                    int H_q, int H_kv, int G, int D, int64_t npieces) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= npieces) return;
+    const int grp = (int)(t & 3);
+    const int64_t r1 = t >> 2;
+    const int e = (int)(r1 % G);
+    const int64_t r2 = r1 / G;
+    const int KS = D / 32;
+    const int s = (int)(r2 % KS);
+    const int64_t r3 = r2 / KS;  // (b * H_kv + g) * N + i
+    const int i = (int)(r3 % N);
+    const int64_t bg = r3 / N;
+    const int64_t b = bg / H_kv, g = bg % H_kv;
+    const bf16 *src = q + ((b * H_q + g * G + e) * N + i) * D + 32 * s + 8 * grp;
+    *(u32x4 *)(qt + t * 8) = *(const u32x4 *)src;
+}
+
 // Per-tile operands gathered from global memory: the Q fragments of the
 // tile's rows, and where the row's partial goes.
 template <int KS>
@@ -256,7 +279,7 @@ constexpr int CM_TPW = 8;
 
 template <int D, int S, int G, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
+    const bf16 *__restrict__ qt, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ list, const float *__restrict__ wl, const int32_t *__restrict__ off,
     const int32_t *__restrict__ segoff, f16 *__restrict__ part, int N, int H_q, int H_kv, int CA, int C, int K,
     float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd, int64_t trash) {
@@ -315,9 +338,10 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     auto gather = [&](int u, CmTile<KS> &tl) {
         const int en = ent[u];
         const int il = en >= 0 ? en >> 8 : 0, kk = en >= 0 ? en & 255 : 0;
-        const bf16 *qr = q + (hr * N + s0 + il) * D;
+        // the query's region of qt: piece (s, e, grp) at 32 (G s + e) + 8 grp
+        const bf16 *qr = qt + (bg * N + s0 + il) * (int64_t)G * D + 32 * e + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * s + 8 * grp);
+        for (int s = 0; s < KS; ++s) tl.qf[s] = *(const bf16x8 *)(qr + 32 * G * s);
         tl.pent = (en >= 0 ? (bg * NS + il) * K + kk : trash) * G * D;
     };
     const int nu = ((e1 - e0 + TE - 1) / TE - wave + NWAVE - 1) / NWAVE;  // this wave's tiles
@@ -451,7 +475,7 @@ constexpr size_t CM_PART_CAP = (size_t)16 << 30;  // partial buffer bound (bytes
 struct CmLayout {
     int NS;               // slab rows (multiple of S)
     int SEG;              // entries per cm_attend block
-    size_t cnt, off, segoff, mhat, list, wl, part, total;  // byte offsets after the V^T copy
+    size_t qt, cnt, off, segoff, mhat, list, wl, part, total;  // byte offsets after the V^T copy
 };
 
 template <int G>
@@ -477,6 +501,8 @@ CmLayout cm_layout(const Shape &s) {
     }
     const size_t bg = (size_t)s.B * s.H_kv;
     size_t o = 0;
+    L.qt = o;  // q regrouped per query (all rows of the call)
+    o = align_up(o + (size_t)s.B * s.H_q * s.N * s.D * 2, 256);
     L.cnt = o;
     o = align_up(o + bg * s.C * 4, 256);
     L.off = o;
@@ -556,10 +582,16 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
     int32_t *off = (int32_t *)(base + L.off);
     int32_t *segoff = (int32_t *)(base + L.segoff);
     float *mhat = (float *)(base + L.mhat);
+    bf16 *qt = (bf16 *)(base + L.qt);
     int32_t *list = (int32_t *)(base + L.list);
     float *wl = (float *)(base + L.wl);
     f16 *part = (f16 *)(base + L.part);
     const int64_t ncnt = (int64_t)s.B * s.H_kv * s.C;
+    {
+        const int64_t npieces = (int64_t)s.B * s.H_q * s.N * (s.D / 8);
+        hipLaunchKernelGGL(cm_qt_kernel, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0, st, (const bf16 *)q, qt,
+                           s.N, s.H_q, s.H_kv, s.G, s.D, npieces);
+    }
     // the histogram kernels' LDS: up to 2 x 8192 chunk counters
     hipFuncSetAttribute((const void *)cm_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, s.C * 4);
     hipFuncSetAttribute((const void *)cm_fill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, s.C * 8);
@@ -579,10 +611,10 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
                            sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s.C, s.S, s.W, s0, L.NS,
                            (int64_t)L.NS * s.K);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
-        else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
-        else if (s.S == 64) e = cm_attend_g<128, 64>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
-        else e = cm_attend_g<128, 128>(s, L, q, k, vt, list, wl, off, segoff, part, s0, st);
+        if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);
+        else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);
+        else if (s.S == 64) e = cm_attend_g<128, 64>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);
+        else e = cm_attend_g<128, 128>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);
         if (e != hipSuccess) return e;
         e = launch_window_after_cm(s, q, k, vt, sel_idx, sel_score, out, lse, status, part, s0, L.NS, st);
         if (e != hipSuccess) return e;

@@ -189,7 +189,11 @@ def test_attend_mode_and_workspace(lib):
     cm = ws(attend_mode=hb.ATTEND_CHUNK_MAJOR)
     assert ws() == cm  # auto takes the chunk-major form
     part = B * H_q * N * K * d * 2
-    assert part < cm - walk < part + B * H_q * N * K * 8 + B * H_kv * (3 * (N // S) + 3) * 4 + 8 * 256 + 2 * d
+    qt = B * H_q * N * d * 2  # q regrouped per query
+    # the partials (and a trash region of G d values), the regrouped q, the lists with their weights,
+    # row maxima and per-chunk counters and offsets, each region 256-byte aligned
+    assert part + qt < cm - walk < (part + qt + B * H_q * N * K * 8 + B * H_kv * (3 * (N // S) + 3) * 4
+                                    + 9 * 256 + 2 * d * (H_q // H_kv))
     # a slab of 1024 rows: a quarter of the partials
     cm_slab = ws(attend_mode=hb.ATTEND_CHUNK_MAJOR, attend_slab=1000)  # rounded up to a multiple of S
     assert part // 4 < cm_slab - walk < cm - walk
