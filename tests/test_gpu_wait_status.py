@@ -28,9 +28,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def test_wait_expiry_sets_status_and_marks_rows(dev):
+@pytest.mark.parametrize("mode", [hb.ATTEND_WALK, hb.ATTEND_CHUNK_MAJOR])
+def test_wait_expiry_sets_status_and_marks_rows(mode, dev):
+    """Both forms: the walk's ring waits, and the chunk-major form's window
+    pass (the same kernel walking the window only)."""
     inp = W.make_prefill(W.PRESETS["gqa_8k"], device=dev)
-    cfg = inp["cfg"]
+    cfg = dataclasses.replace(inp["cfg"], attend_mode=mode)
     ref = hb.prefill(cfg, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     ws = torch.empty(hb.workspace_size(cfg, hb.WS_FUSED), dtype=torch.uint8, device=dev)
     print("[wait status] default bound", flush=True)
