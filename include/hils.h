@@ -133,10 +133,11 @@ typedef struct {
  * fp16 partial buffer, and the window pass starts each row from the sum of
  * its partials; it pays when adjacent queries select different chunks.
  * Workspace grows by about B * H_q * min(N, slab) * K * (d * 2 + 8) bytes
- * (16 GiB of partials at most with the default slab).  fp32 I/O and the paged
- * prefill always walk.  AUTO takes CHUNK_MAJOR wherever it runs (faster on
- * both measured workloads: 128K tokens with 64-key chunks, 512K with
- * 128-key chunks). */
+ * (16 GiB of partials at most with the default slab).  fp32 I/O always
+ * walks.  hils_prefill_paged takes the same form as the whole-sequence call
+ * (and its rows equal that call's bitwise).  AUTO takes CHUNK_MAJOR wherever
+ * it runs (faster on both measured workloads: 128K tokens with 64-key
+ * chunks, 512K with 128-key chunks). */
 typedef enum {
     HILS_ATTEND_AUTO = 0,
     HILS_ATTEND_WALK = 1,

@@ -82,7 +82,7 @@ __device__ __forceinline__ int cm_block_rows(int N, int s0, int NS, int r0) {
 }
 
 __global__ __launch_bounds__(256) void cm_count_kernel(const int32_t *__restrict__ sel_idx, int32_t *__restrict__ cnt,
-                                                       int N, int K, int C, int S, int W, int s0, int NS) {
+                                                       int N, int K, int C, int S, int W, int s0, int NS, int q0) {
     extern __shared__ int hist[];  // [C]
     const int64_t bg = blockIdx.y;
     const int r0 = blockIdx.x * CM_RB, nr = cm_block_rows(N, s0, NS, r0);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void cm_count_kernel(const int32_t *__restrict
     for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
         const int i = s0 + r0 + e / K;
         const int c = base[e];
-        if (c >= 0 && c < max(0, i / S - W / S)) atomicAdd(&hist[c], 1);
+        if (c >= 0 && c < max(0, (q0 + i) / S - W / S)) atomicAdd(&hist[c], 1);
     }
     __syncthreads();
     for (int c = threadIdx.x; c < C; c += blockDim.x)
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
                                                       float *__restrict__ wl, const float *__restrict__ sel_score,
                                                       const float *__restrict__ mhat, int N, int H_q, int H_kv,
                                                       int G, int K, int C, int S, int W, int s0, int NS,
-                                                      int64_t lstride) {
+                                                      int64_t lstride, int q0) {
     extern __shared__ int sh[];  // hist[C], then base[C]
     int *hist = sh, *basep = sh + C;
     const int64_t bg = blockIdx.y;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
     for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
         const int i = s0 + r0 + e / K;
         const int c = base[e];
-        if (c >= 0 && c < max(0, i / S - W / S)) atomicAdd(&hist[c], 1);
+        if (c >= 0 && c < max(0, (q0 + i) / S - W / S)) atomicAdd(&hist[c], 1);
     }
     __syncthreads();
     const int32_t *ob = off + bg * (C + 1);
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void cm_fill_kernel(const int32_t *__restrict_
     for (int e = threadIdx.x; e < nr * K; e += blockDim.x) {
         const int il = r0 + e / K, i = s0 + il, kk = e % K;
         const int c = base[e];
-        if (c >= 0 && c < max(0, i / S - W / S)) {
+        if (c >= 0 && c < max(0, (q0 + i) / S - W / S)) {
             const int p = basep[c] + atomicAdd(&hist[c], 1);
             lb[p] = (il << 8) | kk;
             // the G weights of the entry, stored four at a time (16 bytes)
@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     const bf16 *__restrict__ qt, const bf16 *__restrict__ k, const f16 *__restrict__ vt,
     const int32_t *__restrict__ list, const float *__restrict__ wl, const int32_t *__restrict__ off,
     const int32_t *__restrict__ segoff, f16 *__restrict__ part, int N, int H_q, int H_kv, int CA, int C, int K,
-    float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd, int64_t trash) {
+    float scale_log2, int s0, int NS, int64_t lstride, int SEG, int per_xcd, int64_t trash, int Nk,
+    const int32_t *__restrict__ bt, int max_pages) {
     constexpr int TE = 16 / G;      // entries (queries) per 16-row tile
     constexpr int KS = D / 32;      // k-steps of Q K^T
     constexpr int KT = S / 16;      // 16-key tiles of S^T
@@ -351,7 +352,9 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
     constexpr int NPK = (S * NBK + NT - 1) / NT, NPV = (D * NBV + NT - 1) / NT;
     u32x4 kst[NPK], vst[NPV];
     {
-        const u32x4 *ks = (const u32x4 *)(k + (bg * N + (int64_t)c * S) * D);
+        // chunk c of k [B, H_kv, Nk, D], or page bt[b, c] of a paged cache [P, H_kv, S, D]
+        const u32x4 *ks = (const u32x4 *)(bt ? k + ((int64_t)bt[b * max_pages + c] * H_kv + g) * S * D
+                                             : k + (bg * Nk + (int64_t)c * S) * D);
         const u32x4 *vs = (const u32x4 *)(vt + (bg * CA + c) * (int64_t)D * S);
 #pragma unroll
         for (int p = 0; p < NPK; ++p) kst[p] = ks[min(tid + p * NT, S * NBK - 1)];
@@ -533,7 +536,8 @@ hipError_t go_cm_attend(const Shape &s, const CmLayout &L, const void *q, const 
     const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(s.B * s.H_kv)), block(NWAVE * 64);
     hipLaunchKernelGGL((cm_attend_kernel<D, S, G, NWAVE>), grid, block, 0, st, (const bf16 *)q, (const bf16 *)k, vt,
                        list, wl, off, segoff, part, s.N, s.H_q, s.H_kv, s.CA, s.C, s.K, s.scale * LOG2E, s0, L.NS,
-                       (int64_t)L.NS * s.K, L.SEG, per_xcd, (int64_t)s.B * s.H_kv * L.NS * s.K);
+                       (int64_t)L.NS * s.K, L.SEG, per_xcd, (int64_t)s.B * s.H_kv * L.NS * s.K, s.Nk, s.bt,
+                       s.max_pages);
     return hipGetLastError();
 }
 
@@ -553,7 +557,7 @@ hipError_t cm_attend_g(const Shape &s, const CmLayout &L, const void *q, const v
 }  // namespace
 
 bool attend_use_cm(const Shape &s) {
-    if (!s.io_bf16 || s.max_pages > 0 || s.K == 0 || s.C == 0) return false;
+    if (!s.io_bf16 || s.K == 0 || s.C == 0) return false;
     if (s.attend_mode == 1) return false;                 // the query-major walk
     if (!window_after_cm_supported(s)) return false;
     if (s.attend_mode == 2) return true;                  // chunk-major, asked for
@@ -601,7 +605,7 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
         // row blocks of CM_RB rows per (b, g); LDS histograms over the C chunks
         const dim3 bgrid((unsigned)((L.NS + CM_RB - 1) / CM_RB), (unsigned)(s.B * s.H_kv));
         hipLaunchKernelGGL(cm_count_kernel, bgrid, dim3(256), (size_t)s.C * 4, st, sel_idx, cnt, s.N, s.K, s.C, s.S,
-                           s.W, s0, L.NS);
+                           s.W, s0, L.NS, s.q0);
         const int64_t npairs = (int64_t)s.B * s.H_q * L.NS;
         hipLaunchKernelGGL(cm_rowmax_kernel, dim3((unsigned)((npairs * 16 + 255) / 256)), dim3(256), 0, st, sel_idx,
                            sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s0, L.NS, npairs);
@@ -609,7 +613,7 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
                            segoff, s.C, L.SEG);
         hipLaunchKernelGGL(cm_fill_kernel, bgrid, dim3(256), (size_t)s.C * 8, st, sel_idx, cnt, off, list, wl,
                            sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s.C, s.S, s.W, s0, L.NS,
-                           (int64_t)L.NS * s.K);
+                           (int64_t)L.NS * s.K, s.q0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (s.D == 64 && s.S == 64) e = cm_attend_g<64, 64>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);
         else if (s.D == 64) e = cm_attend_g<64, 128>(s, L, qt, k, vt, list, wl, off, segoff, part, s0, st);

@@ -208,19 +208,18 @@ def test_prefill_paged_matches_oracle(name, dev):
     assert_close(host(lse).numpy(), refl, atol, rtol, "lse")
 
 
+@pytest.mark.parametrize("mode", [hb.ATTEND_AUTO, hb.ATTEND_WALK])
 @pytest.mark.parametrize("name", ["mid_ragged_b2", "s128_qcal", "g8_bf16sum_d64", "aggnorm_lmshared"])
-def test_prefill_paged_equals_prefill_rows(name, dev):
+def test_prefill_paged_equals_prefill_rows(name, mode, dev):
     """Chunked prefill over the paged cache reproduces rows q_start.. of the
-    whole-sequence prefill bitwise (same summaries, selections, outputs).
-    The paged prefill walks the selected chunks, so the whole-sequence
-    prefill is asked for the walk too (auto takes the chunk-major form,
-    equal only up to rounding)."""
+    whole-sequence prefill bitwise (same summaries, selections, outputs), in
+    each attention form (auto: chunk-major; the walk)."""
     params, q_start, n = PAGED_CASES[name]
-    print(f"[prefill_paged == prefill] {name}", flush=True)
+    print(f"[prefill_paged == prefill] {name} mode={mode}", flush=True)
     inp = _paged_inputs(params, q_start, n, dev)
-    cfg_full = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)
+    cfg_full = dataclasses.replace(inp["cfg"], attend_mode=mode)
     full = hb.prefill(cfg_full, inp["q"], inp["k"], inp["v"], inp["q_lm"], qcal=inp.get("qcal"))
-    cfg = W.config(params, N=n)
+    cfg = dataclasses.replace(W.config(params, N=n), attend_mode=mode)
     ks, bs = _summarize_all(cfg_full, inp, dev)
     q, qcal = _new_rows(cfg, inp, q_start)
     out, lse, sel, ssc = hb.prefill_paged(cfg, q_start, q, inp["k_cache"], inp["v_cache"], ks, bs,
@@ -240,7 +239,7 @@ def test_serving_in_chunks_equals_whole_prefill(dev):
     params = dict(seed=78, io=BF, B=2, H_q=8, H_kv=2, d=128, S=64, W=256, K=8)
     splits = [0, 1024, 2048, 2600]
     inp = _paged_inputs(params, 0, splits[-1], dev)
-    cfg_full = dataclasses.replace(inp["cfg"], attend_mode=hb.ATTEND_WALK)  # the paged prefill walks
+    cfg_full = inp["cfg"]
     full = hb.prefill(cfg_full, inp["q"], inp["k"], inp["v"], inp["q_lm"])
     S = cfg_full.S
     P = inp["k_cache"].shape[0]
