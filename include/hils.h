@@ -120,7 +120,7 @@ typedef struct {
                               visits the selected chunks; 0 (auto) by default */
     int32_t attend_slab;   /* chunk-major form: query rows per slab, rounded up to
                               a multiple of S; 0 bounds the slab's partial buffer
-                              by 16 GiB.  Results do not depend on it. */
+                              by 32 GiB.  Results do not depend on it. */
 } hils_config_t;
 
 /* Forms of the selected-chunk attention of hils_sparse_attend_fused (bf16
@@ -133,7 +133,7 @@ typedef struct {
  * fp16 partial buffer, and the window pass starts each row from the sum of
  * its partials; it pays when adjacent queries select different chunks.
  * Workspace grows by about B * H_q * min(N, slab) * K * (d * 2 + 8) bytes
- * (16 GiB of partials at most with the default slab).  fp32 I/O always
+ * (32 GiB of partials at most with the default slab).  fp32 I/O always
  * walks.  hils_prefill_paged takes the same form as the whole-sequence call
  * (and its rows equal that call's bitwise).  AUTO takes CHUNK_MAJOR wherever
  * it runs (faster on both measured workloads: 128K tokens with 64-key

@@ -473,7 +473,7 @@ __global__ __launch_bounds__(NWAVE * 64) void cm_attend_kernel(
 
 namespace {
 
-constexpr size_t CM_PART_CAP = (size_t)16 << 30;  // partial buffer bound (bytes)
+constexpr size_t CM_PART_CAP = (size_t)32 << 30;  // partial buffer bound (bytes)
 
 struct CmLayout {
     int NS;               // slab rows (multiple of S)
