@@ -131,6 +131,45 @@ __global__ __launch_bounds__(256) void cm_rowmax_kernel(const int32_t *__restric
     if (ok && j == 0) mhat[hr * NS + il] = mh;
 }
 
+typedef int32_t cm_i32x4 __attribute__((ext_vector_type(4)));
+
+// The same with 16-byte reads (K % 4 == 0, 16-byte aligned sel_idx and
+// sel_score): 4 lanes per row, each reading 4 slots at a time.
+__global__ __launch_bounds__(256) void cm_rowmax4_kernel(const int32_t *__restrict__ sel_idx,
+                                                         const float *__restrict__ sel_score,
+                                                         float *__restrict__ mhat, int N, int H_q, int H_kv, int G,
+                                                         int K, int s0, int NS, int64_t npairs) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t pair = t >> 2;
+    const int j = (int)(t & 3);
+    float mh = -INFINITY;
+    int64_t hr = 0;
+    int il = 0;
+    bool ok = false;
+    if (pair < npairs) {
+        hr = pair / NS;
+        il = (int)(pair % NS);
+        const int i = s0 + il;
+        ok = i < N;
+        if (ok) {
+            const int h = (int)(hr % H_q);
+            const int64_t b = hr / H_q;
+            const f32x4 *sc = (const f32x4 *)(sel_score + (hr * N + i) * K);
+            const cm_i32x4 *sl = (const cm_i32x4 *)(sel_idx + ((b * H_kv + h / G) * N + i) * K);
+            for (int kq = j; kq < K / 4; kq += 4) {
+                const f32x4 v = sc[kq];
+                const cm_i32x4 c = sl[kq];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    if (c[x] >= 0) mh = fmaxf(mh, v[x] * LOG2E);
+            }
+        }
+    }
+    mh = fmaxf(mh, __shfl_xor(mh, 2, 4));
+    mh = fmaxf(mh, __shfl_xor(mh, 1, 4));
+    if (ok && j == 0) mhat[hr * NS + il] = mh;
+}
+
 // One block per (b, g): exclusive scans of the chunk counts (list offsets)
 // and of their segment counts ceil(cnt / SEG).  off and segoff hold C + 1
 // entries each; entry C is the total.
@@ -607,8 +646,12 @@ hipError_t launch_sparse_attend_cm(const Shape &s, const void *q, const void *k,
         hipLaunchKernelGGL(cm_count_kernel, bgrid, dim3(256), (size_t)s.C * 4, st, sel_idx, cnt, s.N, s.K, s.C, s.S,
                            s.W, s0, L.NS, s.q0);
         const int64_t npairs = (int64_t)s.B * s.H_q * L.NS;
-        hipLaunchKernelGGL(cm_rowmax_kernel, dim3((unsigned)((npairs * 16 + 255) / 256)), dim3(256), 0, st, sel_idx,
-                           sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s0, L.NS, npairs);
+        if (s.K % 4 == 0 && (((uintptr_t)sel_idx | (uintptr_t)sel_score) & 15) == 0)
+            hipLaunchKernelGGL(cm_rowmax4_kernel, dim3((unsigned)((npairs * 4 + 255) / 256)), dim3(256), 0, st,
+                               sel_idx, sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s0, L.NS, npairs);
+        else
+            hipLaunchKernelGGL(cm_rowmax_kernel, dim3((unsigned)((npairs * 16 + 255) / 256)), dim3(256), 0, st,
+                               sel_idx, sel_score, mhat, s.N, s.H_q, s.H_kv, s.G, s.K, s0, L.NS, npairs);
         hipLaunchKernelGGL(cm_scan_kernel, dim3((unsigned)(s.B * s.H_kv)), dim3(CM_SCAN_THREADS), 0, st, cnt, off,
                            segoff, s.C, L.SEG);
         hipLaunchKernelGGL(cm_fill_kernel, bgrid, dim3(256), (size_t)s.C * 8, st, sel_idx, cnt, off, list, wl,
